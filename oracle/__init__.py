@@ -1,0 +1,200 @@
+"""CPU oracle (double precision) -- TEST INFRASTRUCTURE ONLY.
+
+Thin ctypes wrapper over ``oracle/oracle.c``.  Only ``tests/``, the smoke
+check in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may
+import this package.  The HIP library (``row_wise_amd``) never imports it, and
+the two share no code: the only thing both sides consume is the seeded input
+generator in ``rowgen``.
+
+All functions take array-likes (numpy or CPU torch tensors of any float
+dtype), widen them exactly to float64, and return float64 numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+__all__ = [
+    "build", "Oracle", "default", "softmax", "softmax_stats", "online_softmax", "online_stats",
+    "merge", "split_stats", "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
+    "layernorm_gelu",
+]
+
+
+def build(out: str = _LIB, src: str = _SRC) -> str:
+    """Compile the oracle with gcc (-O2, strict IEEE: no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _signatures():
+    P = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    d = ctypes.c_double
+    return {
+        "oracle_softmax": [P, P, i64, i64],
+        "oracle_softmax_stats": [P, i64, P, P],
+        "oracle_online_stats": [P, i64, i64, P, P],
+        "oracle_merge": [d, d, d, d, P, P],
+        "oracle_split_stats": [P, i64, i64, P, P, P, P],
+        "oracle_softmax_apply": [P, P, i64, d, d],
+        "oracle_online_softmax": [P, P, i64, i64, i64],
+        "oracle_split_softmax": [P, P, i64, i64, i64],
+        "oracle_gelu_tanh_array": [P, P, i64],
+        "oracle_layernorm_stats": [P, i64, d, P, P, P],
+        "oracle_layernorm_normalize": [P, P, i64, i64, d],
+        "oracle_layernorm_gelu": [P, P, P, P, i64, i64, d],
+    }
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor (bf16 has no numpy dtype: widen in torch first)
+        import torch
+
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _rows(x):
+    x = _f64(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    assert x.ndim == 2
+    return x
+
+
+class Oracle:
+    """The oracle's functions, bound to one compiled copy of ``oracle.c``."""
+
+    def __init__(self, lib_path: str = _LIB):
+        if lib_path == _LIB and not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(lib_path)
+        for name, args in _signatures().items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = None
+        self.lib = lib
+
+    def softmax(self, x) -> np.ndarray:
+        """Stable row softmax of a [M, N] array."""
+        x = _rows(x)
+        y = np.empty_like(x)
+        self.lib.oracle_softmax(_p(x), _p(y), x.shape[0], x.shape[1])
+        return y
+
+    def softmax_stats(self, row):
+        """(max, sum exp(x - max)) of one row."""
+        r = _f64(row).ravel()
+        m, d = ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_softmax_stats(_p(r), r.size, ctypes.byref(m), ctypes.byref(d))
+        return m.value, d.value
+
+    def online_stats(self, row, block: int):
+        """Streaming (m, d) of one row over blocks of ``block`` elements."""
+        r = _f64(row).ravel()
+        m, d = ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_online_stats(_p(r), r.size, int(block), ctypes.byref(m), ctypes.byref(d))
+        return m.value, d.value
+
+    def merge(self, a, b):
+        """Merge two partial states (m1, d1), (m2, d2)."""
+        m, d = ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_merge(float(a[0]), float(a[1]), float(b[0]), float(b[1]),
+                              ctypes.byref(m), ctypes.byref(d))
+        return m.value, d.value
+
+    def split_stats(self, row, splits: int):
+        """(m, d, m_parts, d_parts) of the split-row variant with ``splits`` chunks."""
+        r = _f64(row).ravel()
+        mp = np.empty(splits)
+        dp = np.empty(splits)
+        m, d = ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_split_stats(_p(r), r.size, int(splits), _p(mp), _p(dp),
+                                    ctypes.byref(m), ctypes.byref(d))
+        return m.value, d.value, mp, dp
+
+    def online_softmax(self, x, block: int) -> np.ndarray:
+        x = _rows(x)
+        y = np.empty_like(x)
+        self.lib.oracle_online_softmax(_p(x), _p(y), x.shape[0], x.shape[1], int(block))
+        return y
+
+    def split_softmax(self, x, splits: int) -> np.ndarray:
+        x = _rows(x)
+        y = np.empty_like(x)
+        self.lib.oracle_split_softmax(_p(x), _p(y), x.shape[0], x.shape[1], int(splits))
+        return y
+
+    def gelu_tanh(self, z) -> np.ndarray:
+        z = _f64(z)
+        shape = z.shape
+        z = z.ravel()
+        y = np.empty_like(z)
+        self.lib.oracle_gelu_tanh_array(_p(z), _p(y), z.size)
+        return y.reshape(shape)
+
+    def layernorm_stats(self, row, eps: float):
+        """(mean, var, rstd) of one row."""
+        r = _f64(row).ravel()
+        mean, var, rstd = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_layernorm_stats(_p(r), r.size, float(eps), ctypes.byref(mean),
+                                        ctypes.byref(var), ctypes.byref(rstd))
+        return mean.value, var.value, rstd.value
+
+    def layernorm_normalize(self, x, eps: float) -> np.ndarray:
+        x = _rows(x)
+        y = np.empty_like(x)
+        self.lib.oracle_layernorm_normalize(_p(x), _p(y), x.shape[0], x.shape[1], float(eps))
+        return y
+
+    def layernorm_gelu(self, x, w, b, eps: float) -> np.ndarray:
+        """Fused LayerNorm + affine + tanh GeLU of a [M, N] array."""
+        x = _rows(x)
+        w = _f64(w).ravel()
+        b = _f64(b).ravel()
+        assert w.size == x.shape[1] and b.size == x.shape[1]
+        y = np.empty_like(x)
+        self.lib.oracle_layernorm_gelu(_p(x), _p(w), _p(b), _p(y), x.shape[0], x.shape[1],
+                                       float(eps))
+        return y
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def _forward(name):
+    def f(*args, **kw):
+        return getattr(default(), name)(*args, **kw)
+
+    f.__name__ = name
+    f.__doc__ = getattr(Oracle, name).__doc__
+    return f
+
+
+for _n in ["softmax", "softmax_stats", "online_stats", "merge", "split_stats", "online_softmax",
+           "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
+           "layernorm_gelu"]:
+    globals()[_n] = _forward(_n)
+del _n

@@ -1,0 +1,245 @@
+/*
+ * CPU oracle for the row-wise kernels -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously correct reference implementations in IEEE double,
+ * one row at a time, single-threaded, no blocking, fusion or reordering
+ * beyond what each definition states.  Only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg may load this code; the product path
+ * (the HIP library) never does, and this file shares no code with it.
+ *
+ * Inputs are the exact fp32 / bf16 values the GPU reads, widened to double by
+ * the caller; outputs are unrounded doubles.  Every array is row-major and
+ * contiguous ([M][N]).
+ *
+ * Pages cited (titles as printed on them):
+ *   [TKE]  "Triton Kernel 实现练习" (Triton kernel exercises)
+ *   [L6]   "第 6 讲：GPU Kernels 与 Triton" (CS336 lecture 6 notes)
+ *   [KTN]  CS336 Lecture 6 "Kernels, Triton" notes, section "Triton Softmax"
+ *   [FLG]  "PyTorch 自定义 CUDA 算子与 Triton 编程从 Python 原型到 GPU 极致性能",
+ *          section 三 "Fused LayerNorm GELU Kernel"
+ *
+ * Parity pins: every function here is pinned by tests under tests/ against
+ * closed forms, invariants, library routines (torch float64) and
+ * high-precision brute force; none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+
+/* ---------------------------------------------------------------------- */
+/* Stable softmax: [TKE] §2.4 "Softmax" (stable version m = max(x),        */
+/* numerator = exp(x - m), denominator = sum(numerator), out = num / den); */
+/* [KTN] "Triton Softmax" (x - max -> exp -> sum -> normalize).            */
+/* ---------------------------------------------------------------------- */
+
+/* Maximum of a row; NaN propagates (any NaN makes the row NaN). */
+static double row_max(const double *x, int64_t n)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        if (isnan(x[j]))
+            return NAN;
+        if (x[j] > m)
+            m = x[j];
+    }
+    return m;
+}
+
+void oracle_softmax(const double *x, double *y, int64_t M, int64_t N)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        const double *xr = x + i * N;
+        double *yr = y + i * N;
+        double m = row_max(xr, N);
+        double den = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            den += exp(xr[j] - m);
+        for (int64_t j = 0; j < N; ++j)
+            yr[j] = exp(xr[j] - m) / den;
+    }
+}
+
+/* Row statistics of the stable softmax: m = max(x), d = sum exp(x - m). */
+void oracle_softmax_stats(const double *x, int64_t N, double *m_out, double *d_out)
+{
+    double m = row_max(x, N);
+    double d = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        d += exp(x[j] - m);
+    *m_out = m;
+    *d_out = d;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Online softmax: [TKE] §2.5 "Online Softmax" -- state m (max of the part */
+/* scanned so far) and d (sum of exp(x - m) over that part); for each new  */
+/* block: m_new = max(m_old, block_max),                                   */
+/*        d_new = d_old * exp(m_old - m_new) + sum(exp(block - m_new)).     */
+/* [L6] §7.2 "Online Softmax": start from m = -inf, l = 0; the rescale     */
+/* factor is exp(m_prev - m_curr).                                         */
+/* ---------------------------------------------------------------------- */
+
+/* The rescale factor exp(m_old - m_new).  With m_old = -inf the old sum is
+ * empty (d_old = 0), and the factor is taken as 0 so that -inf - (-inf) is
+ * never formed. */
+static double rescale(double m_old, double m_new)
+{
+    if (m_old == -INFINITY)
+        return 0.0;
+    return exp(m_old - m_new);
+}
+
+/* Streaming recurrence over blocks of B elements (B >= 1). */
+void oracle_online_stats(const double *x, int64_t N, int64_t B, double *m_out, double *d_out)
+{
+    double m = -INFINITY, d = 0.0;
+    for (int64_t s = 0; s < N; s += B) {
+        int64_t e = s + B < N ? s + B : N;
+        double block_max = row_max(x + s, e - s);
+        double m_new = block_max > m ? block_max : m;
+        if (isnan(block_max) || isnan(m))
+            m_new = NAN;
+        double block_sum = 0.0;
+        for (int64_t j = s; j < e; ++j)
+            block_sum += exp(x[j] - m_new);
+        d = d * rescale(m, m_new) + block_sum;
+        m = m_new;
+    }
+    *m_out = m;
+    *d_out = d;
+}
+
+/* Merge of two partial states (m1,d1) and (m2,d2) of disjoint parts of a
+ * row: the combined max M and the two sums rescaled to it.  (-inf, 0) is the
+ * state of an empty part and is the identity. */
+void oracle_merge(double m1, double d1, double m2, double d2, double *m_out, double *d_out)
+{
+    double M = m1 > m2 ? m1 : m2;
+    if (isnan(m1) || isnan(m2))
+        M = NAN;
+    *m_out = M;
+    *d_out = d1 * rescale(m1, M) + d2 * rescale(m2, M);
+}
+
+/* Split-row online softmax, [TKE] §2.5 second version: per-chunk partial
+ * (m, d), then a reduce of the partials.  The row is cut into S chunks of
+ * C = ceil(N / S) elements, chunk s = [s*C, min(N, (s+1)*C)); an empty chunk
+ * has the state (-inf, 0).  Partials are written to m_parts/d_parts (length
+ * S, may be NULL) and merged left to right. */
+void oracle_split_stats(const double *x, int64_t N, int64_t S, double *m_parts, double *d_parts,
+                        double *m_out, double *d_out)
+{
+    int64_t C = (N + S - 1) / S;
+    double m = -INFINITY, d = 0.0;
+    for (int64_t s = 0; s < S; ++s) {
+        int64_t b = s * C, e = (s + 1) * C;
+        if (b > N)
+            b = N;
+        if (e > N)
+            e = N;
+        double ms = -INFINITY, ds = 0.0;
+        if (e > b)
+            oracle_softmax_stats(x + b, e - b, &ms, &ds);
+        if (m_parts)
+            m_parts[s] = ms;
+        if (d_parts)
+            d_parts[s] = ds;
+        oracle_merge(m, d, ms, ds, &m, &d);
+    }
+    *m_out = m;
+    *d_out = d;
+}
+
+/* Normalize a row with given statistics: y = exp(x - m) / d. */
+void oracle_softmax_apply(const double *x, double *y, int64_t N, double m, double d)
+{
+    for (int64_t j = 0; j < N; ++j)
+        y[j] = exp(x[j] - m) / d;
+}
+
+/* Online softmax of M rows: streaming statistics (block B), then the write. */
+void oracle_online_softmax(const double *x, double *y, int64_t M, int64_t N, int64_t B)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        double m, d;
+        oracle_online_stats(x + i * N, N, B, &m, &d);
+        oracle_softmax_apply(x + i * N, y + i * N, N, m, d);
+    }
+}
+
+/* Split-row online softmax of M rows with S chunks per row. */
+void oracle_split_softmax(const double *x, double *y, int64_t M, int64_t N, int64_t S)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        double m, d;
+        oracle_split_stats(x + i * N, N, S, 0, 0, &m, &d);
+        oracle_softmax_apply(x + i * N, y + i * N, N, m, d);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* GeLU, tanh approximation: [TKE] §3.4 "Approx Activation"               */
+/*   gelu_approx(z) = 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).     */
+/* ---------------------------------------------------------------------- */
+double oracle_gelu_tanh(double z)
+{
+    const double k = sqrt(2.0 / M_PI);
+    return 0.5 * z * (1.0 + tanh(k * (z + 0.044715 * z * z * z)));
+}
+
+void oracle_gelu_tanh_array(const double *z, double *y, int64_t n)
+{
+    for (int64_t j = 0; j < n; ++j)
+        y[j] = oracle_gelu_tanh(z[j]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* LayerNorm: [TKE] §4.1 "LayerNorm"                                       */
+/*   mean = mean(x); var = mean((x - mean)^2);                             */
+/*   out = (x - mean) * rsqrt(var + eps) * weight + bias,                  */
+/* statistics over the N true columns only.  [FLG] fuses the affine       */
+/* output with the tanh GeLU above in one pass over the row.               */
+/* ---------------------------------------------------------------------- */
+
+/* Row statistics: mean, biased variance (divide by N), rstd = 1/sqrt(var+eps). */
+void oracle_layernorm_stats(const double *x, int64_t N, double eps, double *mean_out,
+                            double *var_out, double *rstd_out)
+{
+    double s = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        s += x[j];
+    double mean = s / (double)N;
+    double q = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        q += (x[j] - mean) * (x[j] - mean);
+    double var = q / (double)N;
+    *mean_out = mean;
+    *var_out = var;
+    *rstd_out = 1.0 / sqrt(var + eps);
+}
+
+/* Normalized row x_hat = (x - mean) * rstd (before the affine step). */
+void oracle_layernorm_normalize(const double *x, double *xhat, int64_t M, int64_t N, double eps)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        double mean, var, rstd;
+        oracle_layernorm_stats(x + i * N, N, eps, &mean, &var, &rstd);
+        for (int64_t j = 0; j < N; ++j)
+            xhat[i * N + j] = (x[i * N + j] - mean) * rstd;
+    }
+}
+
+/* Fused LayerNorm + affine + tanh GeLU of M rows. */
+void oracle_layernorm_gelu(const double *x, const double *w, const double *b, double *y, int64_t M,
+                           int64_t N, double eps)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        const double *xr = x + i * N;
+        double *yr = y + i * N;
+        double mean, var, rstd;
+        oracle_layernorm_stats(xr, N, eps, &mean, &var, &rstd);
+        for (int64_t j = 0; j < N; ++j) {
+            double z = (xr[j] - mean) * rstd * w[j] + b[j];
+            yr[j] = oracle_gelu_tanh(z);
+        }
+    }
+}

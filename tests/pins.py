@@ -1,0 +1,313 @@
+"""Pins of the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``check_*`` takes an ``oracle.Oracle`` and raises ``AssertionError`` on a
+violation.  ``tests/test_oracle_pins.py`` runs them against the real oracle;
+``tests/test_oracle_mutants.py`` runs them against copies of the oracle with a
+planted mistake and requires that some check fails for every mutant.
+
+What pins what (citations are to the pages' titles and sections):
+
+* softmax, "Triton Kernel 实现练习" §2.4: rows sum to 1; invariance under adding
+  a constant (bitwise, for shifts exact in double); constant row -> 1/N;
+  N = 2 -> logistic closed form; N = 1 -> 1; the textbook definition
+  exp(x_j) / sum_k exp(x_k) evaluated by brute force at 50 digits (mpmath);
+  torch.softmax in float64.
+* online / split softmax, same page §2.5 and "第 6 讲" §7.2: the streaming
+  recurrence reaches (max, sum exp(x - max)) for every block size; geometric
+  rows whose statistics are closed-form sums; the merge has (-inf, 0) as its
+  identity, is commutative and associative, and merging two halves gives the
+  whole; split statistics equal the whole-row statistics for any chunk count,
+  including empty chunks.
+* LayerNorm, "Triton Kernel 实现练习" §4.1: mean(x_hat) = 0 and
+  var(x_hat) = s2 / (s2 + eps); reduction to torch.nn.functional.layer_norm in
+  float64; a constant row gives x_hat = 0 and y = GeLU(b); an eps-sensitive
+  row pins where eps enters.
+* tanh GeLU, same page §3.4: GeLU(0) = 0; GeLU(z) - GeLU(-z) = z; limits
+  z and 0 at +-large z; torch.nn.functional.gelu(approximate="tanh") in
+  float64; distance to the erf form peaks near 4.73e-4.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+EPS = float(np.float32(1e-5))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-300)))
+
+
+# ---------------------------------------------------------------- softmax
+
+
+def check_softmax_sums_to_one(orc):
+    for n, scale in [(7, 1.0), (768, 1.0), (1000, 4.0), (4096, 8.0), (262144, 3.0)]:
+        x = scale * _rng(n).standard_normal((2, n))
+        y = orc.softmax(x)
+        assert np.all(y > 0), n
+        err = np.abs(y.sum(axis=1) - 1.0).max()
+        assert err <= 1e-13, (n, err)
+
+
+def check_softmax_shift_invariance(orc):
+    # values on a 2^-20 grid, |x| < 2^5: x + c and max + c are exact in double
+    # for |c| <= 2^30, so x - max is formed from the same real numbers
+    x = np.round(4.0 * _rng(3).standard_normal((4, 1000)) * 2.0**20) / 2.0**20
+    y = orc.softmax(x)
+    for c in (1000.0, -37.5, 2.0**20):
+        ys = orc.softmax(x + c)
+        assert np.array_equal(ys, y), c
+
+
+def check_softmax_constant_row(orc):
+    for n in (1, 2, 3, 64, 1000, 4096):
+        y = orc.softmax(np.full((1, n), 1.25))
+        assert np.allclose(y, 1.0 / n, rtol=2e-16, atol=0), n
+    y = orc.softmax(np.array([[5.0]]))
+    assert y[0, 0] == 1.0
+
+
+def check_softmax_two_elements(orc):
+    for a, b in [(0.0, 0.0), (1.0, -2.0), (-30.0, 5.0), (1000.0, 999.0), (0.5, 40.0)]:
+        y = orc.softmax(np.array([[a, b]]))
+        ra = 1.0 / (1.0 + math.exp(b - a))
+        rb = 1.0 / (1.0 + math.exp(a - b))
+        assert _rel(y[0], [ra, rb]) <= 1e-15, (a, b, y)
+
+
+def check_softmax_brute_force(orc):
+    import mpmath
+
+    mpmath.mp.dps = 50
+    r = _rng(11)
+    for n in (1, 2, 3, 5, 8, 13, 16):
+        for scale in (1.0, 10.0):
+            x = scale * r.standard_normal(n)
+            y = orc.softmax(x[None, :])[0]
+            ex = [mpmath.exp(mpmath.mpf(float(v))) for v in x]
+            s = mpmath.fsum(ex)
+            ref = np.array([float(e / s) for e in ex])
+            assert _rel(y, ref) <= 4e-15, (n, scale)
+
+
+def check_softmax_torch(orc):
+    import torch
+
+    x = 6.0 * _rng(5).standard_normal((16, 1000))
+    x[::4] += 1000.0
+    y = orc.softmax(x)
+    ref = torch.softmax(torch.from_numpy(x), dim=1).numpy()
+    assert _rel(y, ref) <= 1e-13
+
+
+# ----------------------------------------------------------- online / split
+
+
+def check_online_stats_match_definition(orc):
+    for n in (1, 5, 1000, 4099, 262144):
+        x = 3.0 * _rng(n + 1).standard_normal(n)
+        m0, d0 = orc.softmax_stats(x)
+        for block in sorted({1, 3, 4096, n, n + 5}):
+            if n >= 100000 and block < 64:
+                continue  # keep the CPU suite short
+            m, d = orc.online_stats(x, block)
+            assert m == m0, (n, block)
+            assert abs(d - d0) <= 1e-12 * d0, (n, block, d, d0)
+
+
+def check_online_geometric_rows(orc):
+    # x_j = -a j: max 0, d = (1 - q^N) / (1 - q) with q = e^-a; every block
+    # starts below the running max.  x_j = +a j: max (N-1) a and the running
+    # max rises in every block, so each step rescales the old sum.
+    a = 0.01
+    for n in (1000, 4099):
+        q = math.exp(-a)
+        dgeo = (1.0 - q**n) / (1.0 - q)
+        j = np.arange(n, dtype=np.float64)
+        for block in (1, 7, 64, n):
+            m, d = orc.online_stats(-a * j, block)
+            assert m == 0.0 and abs(d - dgeo) <= 1e-13 * dgeo, (n, block, d, dgeo)
+            m, d = orc.online_stats(a * j, block)
+            assert m == a * (n - 1), (n, block)
+            assert abs(d - dgeo) <= 1e-12 * dgeo, (n, block, d, dgeo)
+
+
+def check_merge_algebra(orc):
+    ident = (-math.inf, 0.0)
+    for s in [(0.5, 3.0), (-2.0, 1.0), (1000.0, 7.5)]:
+        assert orc.merge(ident, s) == s and orc.merge(s, ident) == s
+    assert orc.merge(ident, ident) == ident
+    r = _rng(21)
+    for _ in range(20):
+        a, b, c = [(float(r.normal() * 5), float(r.uniform(1, 100))) for _ in range(3)]
+        assert orc.merge(a, b) == orc.merge(b, a)
+        l = orc.merge(orc.merge(a, b), c)
+        rr = orc.merge(a, orc.merge(b, c))
+        assert l[0] == rr[0] and abs(l[1] - rr[1]) <= 1e-15 * abs(l[1])
+    # merging the two halves of a row gives the whole row's statistics
+    x = 3.0 * r.standard_normal(1001)
+    for cut in (1, 500, 1000):
+        m, d = orc.merge(orc.softmax_stats(x[:cut]), orc.softmax_stats(x[cut:]))
+        m0, d0 = orc.softmax_stats(x)
+        assert m == m0 and abs(d - d0) <= 1e-14 * d0, cut
+    # the merged sum is rescaled to the larger max: (0, 1) + (ln 2, 1) -> (ln 2, 1.5)
+    m, d = orc.merge((0.0, 1.0), (math.log(2.0), 1.0))
+    assert m == math.log(2.0) and abs(d - 1.5) <= 4e-16
+
+
+def check_split_stats_match_definition(orc):
+    for n in (5, 1000, 262144):
+        x = 3.0 * _rng(n + 2).standard_normal(n)
+        m0, d0 = orc.softmax_stats(x)
+        for S in (1, 2, 3, 64, n, n + 3):
+            if S > 4096:
+                continue
+            m, d, mp, dp = orc.split_stats(x, S)
+            assert m == m0 and abs(d - d0) <= 1e-13 * d0, (n, S)
+            C = -(-n // S)
+            for s in range(S):
+                chunk = x[s * C:min(n, (s + 1) * C)]
+                if chunk.size == 0:
+                    assert mp[s] == -math.inf and dp[s] == 0.0
+                else:
+                    assert mp[s] == chunk.max(), (n, S, s)
+
+
+def check_online_and_split_outputs(orc):
+    x = 3.0 * _rng(9).standard_normal((4, 4099))
+    y0 = orc.softmax(x)
+    for block in (1, 64, 4099):
+        assert _rel(orc.online_softmax(x, block), y0) <= 1e-13, block
+    for S in (1, 2, 64, 4099):
+        assert _rel(orc.split_softmax(x, S), y0) <= 1e-13, S
+
+
+# ---------------------------------------------------------------- GeLU
+
+
+def check_gelu_basic(orc):
+    z = np.array([0.0, 1e-30, -1e-30])
+    y = orc.gelu_tanh(z)
+    assert y[0] == 0.0 and abs(y[1] - 0.5e-30) <= 1e-45
+    zz = np.linspace(-12.0, 12.0, 4801)
+    diff = orc.gelu_tanh(zz) - orc.gelu_tanh(-zz)
+    assert np.all(np.abs(diff - zz) <= 4e-16 * np.maximum(np.abs(zz), 1.0))
+    big = np.array([10.0, 20.0, 40.0])
+    assert np.all(np.abs(orc.gelu_tanh(big) - big) <= 1e-15 * big)
+    neg = orc.gelu_tanh(-big)
+    assert np.all(neg <= 0.0) and np.all(neg > -1e-30)
+
+
+def check_gelu_torch(orc):
+    import torch
+
+    z = np.concatenate([np.linspace(-15, 15, 30001), 5.0 * _rng(4).standard_normal(1000)])
+    y = orc.gelu_tanh(z)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    # 1 + tanh(u) cancels for z << 0 in both evaluations: absolute 1e-15 there
+    assert np.all(np.abs(y - ref) <= 1e-15 * np.maximum(np.abs(ref), 1.0))
+    pos = z > 0
+    assert np.all(np.abs(y[pos] - ref[pos]) <= 1e-15 * np.abs(ref[pos]))
+
+
+def check_gelu_not_erf(orc):
+    z = np.linspace(-6, 6, 120001)
+    y = orc.gelu_tanh(z)
+    erf = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in z])
+    gap = np.abs(y - erf)
+    k = int(gap.argmax())
+    assert 4.6e-4 <= gap[k] <= 4.8e-4 and -2.8 <= z[k] <= -2.6, (gap[k], z[k])
+
+
+# ------------------------------------------------------------- LayerNorm
+
+
+def check_layernorm_normalized_moments(orc):
+    r = _rng(31)
+    for n in (2, 3, 768, 1000, 4096):
+        x = r.standard_normal((3, n)) * np.array([[1.0], [0.003], [50.0]]) + np.array(
+            [[0.0], [1.25], [-7.0]])
+        xh = orc.layernorm_normalize(x, EPS)
+        for i in range(3):
+            s2 = np.var(x[i])
+            # rounding of x - mean is relative to |x|, magnified by rstd
+            scale = 1e-15 * np.abs(x[i]).max() / math.sqrt(s2 + EPS)
+            assert abs(xh[i].mean()) <= scale, (n, i)
+            assert abs(np.mean(xh[i] ** 2) - s2 / (s2 + EPS)) <= 4 * scale, (n, i)
+
+
+def check_layernorm_torch(orc):
+    import torch
+    import torch.nn.functional as F
+
+    r = _rng(33)
+    n = 768
+    x = r.standard_normal((8, n))
+    x[3] = 1.25 + 3e-3 * r.standard_normal(n)  # variance ~ eps
+    w = 1.0 + 0.1 * r.standard_normal(n)
+    b = 0.1 * r.standard_normal(n)
+    xt = torch.from_numpy(x)
+    for ww, bb in [(np.ones(n), np.zeros(n)), (w, b)]:
+        y = orc.layernorm_gelu(x, ww, bb, EPS)
+        ln = F.layer_norm(xt, (n,), torch.from_numpy(ww), torch.from_numpy(bb), EPS)
+        ref = F.gelu(ln, approximate="tanh").numpy()
+        assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1.0)) <= 1e-13
+
+
+def check_layernorm_constant_row(orc):
+    import torch
+    import torch.nn.functional as F
+
+    n = 768
+    b = 0.1 * _rng(35).standard_normal(n)
+    w = 1.0 + 0.1 * _rng(36).standard_normal(n)
+    y = orc.layernorm_gelu(np.full((1, n), 1.25), w, b, EPS)[0]
+    # x_hat is exactly 0, so z is exactly b: bitwise GeLU(b)
+    assert np.array_equal(y, orc.gelu_tanh(b))
+    ref = F.gelu(torch.from_numpy(b), approximate="tanh").numpy()
+    assert np.all(np.abs(y - ref) <= 1e-15 * np.abs(ref))
+    y1 = orc.layernorm_gelu(np.array([[3.0]]), np.array([2.0]), np.array([0.5]), EPS)
+    assert abs(y1[0, 0] - F.gelu(torch.tensor(0.5, dtype=torch.float64),
+                                 approximate="tanh").item()) <= 1e-16
+
+
+def check_layernorm_eps_placement(orc):
+    # Variance ~ eps: rstd is 1 / sqrt(var + eps), and the biased (divide by N)
+    # variance is used.  Compare with numpy's population variance.
+    x = 1.25 + 3e-3 * _rng(37).standard_normal(768)
+    mean, var, rstd = orc.layernorm_stats(x, EPS)
+    assert abs(mean - np.mean(x)) <= 1e-15
+    assert abs(var - np.var(x)) <= 1e-15 * np.var(x) + 1e-22
+    assert abs(rstd - 1.0 / math.sqrt(np.var(x) + EPS)) <= 1e-13 * rstd
+    # the eps-less value differs at O(1) on this row
+    assert abs(rstd * math.sqrt(np.var(x)) - 1.0) > 0.2
+
+
+PINS = [
+    check_softmax_sums_to_one,
+    check_softmax_shift_invariance,
+    check_softmax_constant_row,
+    check_softmax_two_elements,
+    check_softmax_brute_force,
+    check_softmax_torch,
+    check_online_stats_match_definition,
+    check_online_geometric_rows,
+    check_merge_algebra,
+    check_split_stats_match_definition,
+    check_online_and_split_outputs,
+    check_gelu_basic,
+    check_gelu_torch,
+    check_gelu_not_erf,
+    check_layernorm_normalized_moments,
+    check_layernorm_torch,
+    check_layernorm_constant_row,
+    check_layernorm_eps_placement,
+]

@@ -1,0 +1,55 @@
+"""Mutation check of the oracle's pins.
+
+Each case plants one plausible mistake in a copy of ``oracle/oracle.c`` (a
+dropped term, a wrong sign, a swapped index or constant), builds that copy
+with the same compiler flags, and requires that at least one pin in
+``tests/pins.py`` rejects it.  The real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from pins import PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "softmax_den_without_max": ("den += exp(xr[j] - m);", "den += exp(xr[j]);"),
+    "softmax_exp_sign": ("yr[j] = exp(xr[j] - m) / den;", "yr[j] = exp(m - xr[j]) / den;"),
+    "row_max_is_min": ("if (x[j] > m)\n            m = x[j];", "if (x[j] < m || m == -INFINITY)\n            m = x[j];"),
+    "online_rescale_dropped": ("return exp(m_old - m_new);", "return 1.0;"),
+    "online_rescale_inverted": ("return exp(m_old - m_new);", "return exp(m_new - m_old);"),
+    "online_block_sum_old_max": ("block_sum += exp(x[j] - m_new);", "block_sum += exp(x[j] - block_max);"),
+    "merge_second_unscaled": ("d1 * rescale(m1, M) + d2 * rescale(m2, M)", "d1 * rescale(m1, M) + d2"),
+    "split_chunk_size": ("int64_t C = (N + S - 1) / S;", "int64_t C = N / S + 1;"),
+    "gelu_cubic_coeff": ("0.044715 * z * z * z", "0.04715 * z * z * z"),
+    "gelu_half_dropped": ("return 0.5 * z * (1.0 + tanh(", "return z * (1.0 + tanh("),
+    "gelu_scale_constant": ("sqrt(2.0 / M_PI)", "sqrt(M_PI / 2.0)"),
+    "gelu_cubic_sign": ("(z + 0.044715 * z * z * z)", "(z - 0.044715 * z * z * z)"),
+    "ln_unbiased_variance": ("double var = q / (double)N;", "double var = q / (double)(N > 1 ? N - 1 : 1);"),
+    "ln_eps_outside_sqrt": ("*rstd_out = 1.0 / sqrt(var + eps);", "*rstd_out = 1.0 / (sqrt(var) + eps);"),
+    "ln_eps_dropped": ("*rstd_out = 1.0 / sqrt(var + eps);", "*rstd_out = 1.0 / sqrt(var);"),
+    "ln_bias_sign": ("* rstd * w[j] + b[j];", "* rstd * w[j] - b[j];"),
+    "ln_weight_dropped": ("* rstd * w[j] + b[j];", "* rstd + b[j];"),
+    "ln_mean_divisor": ("double mean = s / (double)N;", "double mean = s / (double)(N + 1);"),
+    "ln_var_uncentered": ("q += (x[j] - mean) * (x[j] - mean);", "q += x[j] * x[j];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / "oracle_mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.build(str(tmp_path / "libmutant.so"), str(path))
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for check in PINS:
+        try:
+            check(mutant)
+        except (AssertionError, FloatingPointError, ValueError, OverflowError, ZeroDivisionError):
+            failed.append(check.__name__)
+    assert failed, f"no pin rejects the mutant {name}"

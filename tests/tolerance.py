@@ -1,0 +1,57 @@
+"""Error measures and tolerances used by the parity tests.
+
+Softmax family (stable, online streaming, split-row): pure elementwise relative
+error max |y - r| / |r|.  No reference element of the workloads underflows, so
+the denominator is never zero there; a zero reference element requires an
+exact zero.
+
+LayerNorm + GeLU: max |y - r| / max(|r|, 1), i.e. relative error with the
+denominator floored at the unit scale of normalized activations.  z = w x_hat + b
+cancels near zero, so a pure relative measure would judge rounding noise of
+fp32 arithmetic around z = 0, not the kernel.
+
+Tolerances: 1e-5 for fp32 input/output, 1e-2 for bf16 storage with fp32
+arithmetic.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def _arr(a):
+    if hasattr(a, "detach"):
+        import torch
+
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def rel_err_softmax(y, ref) -> float:
+    y, ref = _arr(y), _arr(ref)
+    if y.shape != ref.shape:
+        raise ValueError(f"shape {y.shape} != {ref.shape}")
+    if y.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    den = np.abs(ref)
+    num = np.abs(y - ref)
+    zero = den == 0
+    if np.any(num[zero] != 0):
+        return float("inf")
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r = np.where(zero, 0.0, num / np.where(zero, 1.0, den))
+    return float(r.max())
+
+
+def rel_err_floor1(y, ref, floor: float = 1.0) -> float:
+    y, ref = _arr(y), _arr(ref)
+    if y.shape != ref.shape:
+        raise ValueError(f"shape {y.shape} != {ref.shape}")
+    if y.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    return float((np.abs(y - ref) / np.maximum(np.abs(ref), floor)).max())
