@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Throughput of the row-wise kernels on one MI355X.
+
+One step = one call of the hot path on one batch of the headline workload:
+fused LayerNorm + affine + tanh GeLU, fp32, x[4096, 768] ~ N(0,1),
+w = 1 + 0.1 N(0,1), b = 0.1 N(0,1), eps = 1e-5.  Inputs are resident in HBM
+before the timed region; consecutive steps rotate over >= 1 GiB of distinct
+input/output buffers so that the 256 MB memory-side cache cannot serve them.
+
+Prints one JSON line.  `value` is achieved HBM GB/s on the algorithmic bytes
+(one read of x, w and b, one write of y) over the wall-clock time of K steps
+bracketed by device synchronizations.  `roofline.achieved` divides the same
+bytes by the kernel's average duration from HIP events on its stream.
+`detail` holds the same measurement for every other workload (softmax fp32
+8192x1000, online softmax fp32 64x262144 streaming and split-row, bf16
+16384x4096 LayerNorm+GeLU and softmax) and the 16-byte copy ceiling.
+`cpu_baseline` is the CPU oracle timed on this host on repeated full batches.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30
+EPS = 1e-5
+METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s for softmax & LayerNorm+GeLU"
+HEADLINE = "ln_gelu_f32_4096x768"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- cases
+
+
+class Case:
+    """One kernel on one workload, with rotating buffer sets and a raw launch."""
+
+    def __init__(self, name, op, workload, splits=None, rows=None):
+        self.name, self.op, self.workload, self.splits = name, op, workload, splits
+        self.rows = rows
+
+    def setup(self, torch, rk, rowgen):
+        d = rowgen.make(self.workload)
+        x = d["x_softmax"] if self.op != "layernorm_gelu" else d["x"]
+        M, N = x.shape
+        es = x.element_size()
+        self.M, self.N, self.dtype = M, N, x.dtype
+        self.dtype_code = rk.RK_F32 if x.dtype == torch.float32 else rk.RK_BF16
+        io = 2 * M * N * es
+        if self.op == "layernorm_gelu":
+            self.bytes = io + 2 * N * es  # x, y, and w, b once
+        elif self.op == "online" and self.splits == 1:
+            self.bytes = 3 * M * N * es  # two reads of x, one write
+        elif self.op == "online":
+            self.bytes = 3 * M * N * es + 2 * M * self.splits * 8  # + partials out and in
+        else:
+            self.bytes = io
+        footprint = io
+        self.R = max(2, math.ceil(ROTATE_BYTES / footprint))
+        dev = torch.device("cuda")
+        xd = x.to(dev)
+        self.xs = [xd] + [xd.clone() for _ in range(self.R - 1)]
+        self.ys = [torch.empty_like(xd) for _ in range(self.R)]
+        self.w = d["w"].to(dev)
+        self.b = d["b"].to(dev)
+        self.ws = None
+        if self.op == "online" and self.splits > 1:
+            nb = rk.rk_online_softmax_workspace_bytes(M, N, self.splits)
+            self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        lib = rk.load()
+        stream = torch.cuda.current_stream().cuda_stream
+        self.stream = stream
+        fp = ctypes.c_float(EPS)
+        if self.op == "layernorm_gelu":
+            fn = lib.rk_layernorm_gelu
+            self.args = [(xx.data_ptr(), self.w.data_ptr(), self.b.data_ptr(), yy.data_ptr(), M,
+                          N, N, N, fp, self.dtype_code, stream)
+                         for xx, yy in zip(self.xs, self.ys)]
+        elif self.op == "softmax":
+            fn = lib.rk_softmax
+            self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, N, self.dtype_code, stream)
+                         for xx, yy in zip(self.xs, self.ys)]
+        else:
+            fn = lib.rk_online_softmax
+            wp = self.ws.data_ptr() if self.ws is not None else None
+            wb = self.ws.numel() if self.ws is not None else 0
+            self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, N, self.dtype_code, self.splits,
+                          wp, wb, stream) for xx, yy in zip(self.xs, self.ys)]
+        self.fn = fn
+        return self
+
+    def launch(self, i):
+        st = self.fn(*self.args[i % self.R])
+        if st != 0:
+            raise RuntimeError(f"{self.name}: status {st}")
+
+    def free(self):
+        self.xs = self.ys = self.args = self.ws = None
+
+
+class CopyCase:
+    """The 16-byte copy kernel: achievable read+write bandwidth."""
+
+    def __init__(self, name, nbytes, max_wg=0):
+        self.name, self.nbytes, self.max_wg = name, nbytes, max_wg
+
+    def setup(self, torch, rk, rowgen):
+        dev = torch.device("cuda")
+        self.bytes = 2 * self.nbytes
+        self.R = max(2, math.ceil(ROTATE_BYTES / self.bytes))
+        self.M = None
+        self.src = [torch.full((self.nbytes // 4,), 1.0, device=dev) for _ in range(self.R)]
+        self.dst = [torch.empty_like(s) for s in self.src]
+        lib = rk.load()
+        self.fn = lib.rk_probe_copy
+        stream = torch.cuda.current_stream().cuda_stream
+        self.args = [(s.data_ptr(), d.data_ptr(), self.nbytes, self.max_wg, stream)
+                     for s, d in zip(self.src, self.dst)]
+        return self
+
+    def launch(self, i):
+        st = self.fn(*self.args[i % self.R])
+        if st != 0:
+            raise RuntimeError(f"{self.name}: status {st}")
+
+    def free(self):
+        self.src = self.dst = self.args = None
+
+
+def all_cases():
+    return [
+        Case("ln_gelu_f32_4096x768", "layernorm_gelu", "ln_gelu_f32_4096x768"),
+        Case("softmax_f32_8192x1000", "softmax", "softmax_f32_8192x1000"),
+        Case("online_stream_f32_64x262144", "online", "online_f32_64x262144", splits=1),
+        Case("online_split64_f32_64x262144", "online", "online_f32_64x262144", splits=64),
+        Case("ln_gelu_bf16_16384x4096", "layernorm_gelu", "bf16_16384x4096"),
+        Case("softmax_bf16_16384x4096", "softmax", "bf16_16384x4096"),
+        CopyCase("copy_256MiB", 256 << 20),
+        CopyCase("copy_64MiB_64wg", 64 << 20, max_wg=64),
+    ]
+
+
+# --------------------------------------------------------------- timing
+
+
+def event_time(torch, case, K, W, reps=3):
+    """Median over `reps` of (elapsed of K back-to-back launches) / K, in s."""
+    for i in range(W):
+        case.launch(i)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(K):
+            case.launch(i)
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e) * 1e-3 / K)
+    return statistics.median(out)
+
+
+def wall_time(torch, case, K, W):
+    """Headline protocol: W untimed steps, then exactly K steps bracketed by
+    device synchronizations; returns (wall seconds, event seconds) for K."""
+    for i in range(W):
+        case.launch(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for i in range(K):
+        case.launch(i)
+    e.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, s.elapsed_time(e) * 1e-3
+
+
+def head_kernel_name(rk, N):
+    i = rk.variant_pick(rk.RK_OP_LAYERNORM_GELU, rk.RK_F32, N)
+    v = rk.variants(rk.RK_OP_LAYERNORM_GELU, rk.RK_F32)[i]
+    return ("layernorm_gelu_tile<float, G={waves_per_row}, V={vecs_per_lane}, "
+            "W={waves_per_block}, R={rows_per_group}>".format(**v))
+
+
+# ------------------------------------------------------- counters / cpu
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("rk_layernorm_gelu.hip", "rk_device.h"):
+        with open(os.path.join(ROOT, "row_wise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(case_name):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
+    None when it is missing or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{case_name}.txt")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^TRAFFIC (\{.*\})\s*$", open(path).read(), flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(seconds):
+    import numpy as np
+
+    import oracle
+    import rowgen
+
+    d = rowgen.make(HEADLINE)
+    x, w, b = (d[k].double().numpy() for k in ("x", "w", "b"))
+    M, N = x.shape
+    nbytes = 2 * M * N * 4 + 2 * N * 4
+    orc = oracle.default()
+    orc.layernorm_gelu(x[:16], w, b, float(np.float32(EPS)))  # load / warm
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.layernorm_gelu(x, w, b, float(np.float32(EPS)))
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": round(passes * nbytes / el / 1e9, 4),
+        "unit": "GB/s",
+        "rows_per_s": round(passes * M / el, 1),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"full {M}x{N} fp32 batch, {passes} passes in {el:.1f} s, single thread, "
+                  f"double precision",
+        "cpu": cpu_model(),
+    }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------------ main
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--case", default=None, help="time only this case (for profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rows shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    import torch
+
+    import row_wise_amd as rk
+    import rowgen
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    rk.load()
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+
+    cases = all_cases()
+    if args.case:
+        cases = [c for c in cases if c.name == args.case]
+        if not cases:
+            sys.exit(f"unknown case {args.case}")
+
+    detail = []
+    head = None
+    for c in cases:
+        log(f"case {c.name}: setup")
+        c.setup(torch, rk, rowgen)
+        if c.name == HEADLINE:
+            wall, evt = wall_time(torch, c, K, W)
+            t_evt = event_time(torch, c, K, W)
+            head = (c, wall, evt, t_evt)
+            t = t_evt
+        else:
+            t = event_time(torch, c, K, W)
+        rec = {"case": c.name, "us_per_call": round(t * 1e6, 3),
+               "GB_per_s": round(c.bytes / t / 1e9, 1),
+               "pct_hbm_peak": round(100 * c.bytes / t / 1e9 / HBM_PEAK_GBS, 1),
+               "bytes_per_call": c.bytes, "rotation_sets": c.R}
+        if c.M is not None:
+            rec["rows_per_s"] = round(c.M / t, 1)
+        detail.append(rec)
+        log(f"case {c.name}: {rec['us_per_call']} us  {rec['GB_per_s']} GB/s "
+            f"({rec['pct_hbm_peak']}% of 8 TB/s)")
+        c.free()
+        torch.cuda.empty_cache()
+
+    if head is None:
+        print(json.dumps({"detail": detail}))
+        return
+
+    c, wall, evt, t_evt = head
+    value = c.bytes * K / wall / 1e9
+    achieved = c.bytes / t_evt / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "op": "fused LayerNorm+affine+tanh-GeLU",
+                   "M": c.M, "N": c.N, "dtype": "f32", "eps": EPS,
+                   "bytes_per_step": c.bytes, "rotation_sets": c.R},
+        "rows_per_s": round(c.M * K / wall, 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(c.name),
+            "kernel": head_kernel_name(rk, c.N),
+            "us_per_launch_events": round(t_evt * 1e6, 3),
+        },
+        "detail": detail,
+    }
+    if not args.no_cpu:
+        log("cpu baseline: oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

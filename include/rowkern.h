@@ -1,0 +1,157 @@
+/*
+ * rowkern: fused row-wise reduce-then-normalize kernels for AMD MI355X (gfx950).
+ *
+ * C ABI of librowkern.so.  Every entry point works on a row-major matrix of M
+ * rows and N columns with unit column stride and a row stride (in elements)
+ * of ld >= N; rows are independent.  Two storage formats are supported:
+ * fp32, and bf16 (storage only: all arithmetic is fp32, outputs are rounded to
+ * nearest even).  Input and output have the same format.
+ *
+ * Pages the operations follow (titles as printed on them):
+ *   [TKE] "Triton Kernel 实现练习" (Triton kernel exercises)
+ *   [L6]  "第 6 讲：GPU Kernels 与 Triton" (CS336 lecture 6 notes)
+ *   [KTN] CS336 Lecture 6 "Kernels, Triton" notes
+ *   [FLG] "PyTorch 自定义 CUDA 算子与 Triton 编程从 Python 原型到 GPU 极致性能"
+ *
+ * Conventions common to all entry points
+ *   Ownership   All pointers are device memory owned by the caller.  The
+ *               library allocates and frees nothing, keeps no mutable global
+ *               state, and is safe to call from several host threads.
+ *   Streams     Work is enqueued on `stream` (0 = the null stream) of the
+ *               current device and the call returns without synchronizing.
+ *               Multi-kernel operations are ordered by the stream alone.
+ *   Alignment   Any element-aligned pointer and any ld >= N are accepted.
+ *               16-byte vector loads and stores are used when the base
+ *               pointers and the row pitches (ld * element size) are 16-byte
+ *               aligned; other rows take a slower element-wise path.
+ *   Aliasing    y may be x exactly (same pointer and same ld: in place);
+ *               any other overlap of an output with an input is rejected.
+ *   Errors      Arguments are validated before any HIP call; a rejected call
+ *               enqueues nothing.  M == 0 is a valid no-op.  A failed kernel
+ *               launch returns RK_ERR_HIP.  Nothing is printed and no C++
+ *               exception crosses the ABI.
+ *   Determinism For fixed arguments the results are bitwise reproducible.
+ */
+#ifndef ROWKERN_H
+#define ROWKERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RK_VERSION 100 /* major * 10000 + minor * 100 + patch */
+
+typedef enum rk_dtype {
+    RK_F32 = 0,  /* IEEE binary32 */
+    RK_BF16 = 1, /* bfloat16 storage, fp32 arithmetic */
+} rk_dtype;
+
+typedef enum rk_status {
+    RK_OK = 0,
+    RK_ERR_INVALID_ARG = 1, /* a size, stride, pointer, dtype or eps is invalid */
+    RK_ERR_UNSUPPORTED = 2, /* valid but beyond what the library handles */
+    RK_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+    RK_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
+} rk_status;
+
+/*
+ * Numerically stable row softmax ([TKE] §2.4 "Softmax", stable version;
+ * [KTN] "Triton Softmax"):
+ *     m_i = max_j x_ij,   y_ij = exp(x_ij - m_i) / sum_k exp(x_ik - m_i).
+ *
+ * x  [M][ldx] input, y [M][ldy] output, both of `dtype`.
+ * Rows that fit on chip (N <= 16384 for fp32, N <= 32768 for bf16, 16-byte
+ * aligned) are held in registers: one HBM read and one HBM write per
+ * element.  Longer or unaligned rows are computed by the streaming online
+ * kernel of rk_online_softmax (two reads, one write), with the same result.
+ * A row that is all -inf, or holds +inf or NaN, yields NaN (the IEEE value
+ * of the definition).
+ *
+ * Returns RK_ERR_INVALID_ARG if M < 0, N < 1, N > INT32_MAX, ldx < N,
+ * ldy < N, x or y is NULL with M > 0, a pointer is not aligned to its
+ * element size, dtype is unknown, or x and y overlap other than exactly;
+ * RK_ERR_UNSUPPORTED if N > 2^30 or the grid would exceed 2^32 work-items.
+ */
+rk_status rk_softmax(const void *x, void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
+                     rk_dtype dtype, hipStream_t stream);
+
+/*
+ * Online softmax for long rows ([TKE] §2.5 "Online Softmax"; [L6] §7.2
+ * "Online Softmax").  Same result as rk_softmax, computed from a running
+ * state (m, d) = (max so far, sum of exp(x - m) so far) that is rescaled by
+ * exp(m_old - m_new) as each block of the row arrives.
+ *
+ * num_splits == 1  one kernel; one workgroup streams its row twice: the
+ *                  first pass builds (m, d), the second writes
+ *                  exp(x - m) / d.  No workspace is used.
+ * num_splits >= 2  split-row variant, two kernels on `stream`: the row is
+ *                  cut into S = num_splits chunks of whole 16-byte vectors
+ *                  (C = ceil(N / S) rounded up to the vector width; trailing
+ *                  chunks may be empty), the first kernel writes each chunk's
+ *                  partial (m_s, d_s) to `workspace`, the second merges the
+ *                  row's S partials with
+ *                      (m1,d1)+(m2,d2) = (M, d1 e^(m1-M) + d2 e^(m2-M)),
+ *                  M = max(m1, m2), (-inf, 0) the identity,
+ *                  and writes its chunk.
+ * num_splits == 0  the library picks S from M and N (S = 1 when M alone
+ *                  fills the GPU).
+ *
+ * workspace  device memory of at least
+ *            rk_online_softmax_workspace_bytes(M, N, num_splits) bytes,
+ *            8-byte aligned, owned by the caller; may be NULL when that size
+ *            is 0.  Its contents on entry do not matter; on return (stream
+ *            order) it holds the partials as float pairs [M][S][2].
+ *
+ * Returns RK_ERR_INVALID_ARG as rk_softmax, and for num_splits < 0 or
+ * num_splits > 65536 or a misaligned workspace; RK_ERR_WORKSPACE if the
+ * workspace is NULL or smaller than required.
+ */
+rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t N, int64_t ldx,
+                            int64_t ldy, rk_dtype dtype, int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes rk_online_softmax needs for these arguments (0 when the
+ * streaming kernel is used or the arguments are invalid). */
+size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t num_splits);
+
+/* The split count rk_online_softmax uses for num_splits == 0. */
+int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N);
+
+/*
+ * Fused LayerNorm + affine + tanh-approximation GeLU, one pass over each row
+ * ([TKE] §4.1 "LayerNorm" and §3.4 "Approx Activation"; [FLG] section 三
+ * "Fused LayerNorm GELU Kernel"):
+ *     mu = sum_j x_j / N,  var = sum_j (x_j - mu)^2 / N  (over the N true
+ *     columns only), rstd = 1 / sqrt(var + eps),
+ *     z_j = (x_j - mu) * rstd * weight_j + bias_j,
+ *     y_j = 0.5 z_j (1 + tanh(sqrt(2/pi) (z_j + 0.044715 z_j^3))).
+ *
+ * x [M][ldx], y [M][ldy], weight [N], bias [N] (contiguous), all of `dtype`.
+ * Rows up to 16384 (fp32) / 32768 (bf16) columns with 16-byte alignment stay
+ * in registers (one HBM read and write per element); other rows are read
+ * three times by a looping kernel with the same arithmetic.
+ *
+ * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight or bias is NULL
+ * with M > 0, eps is not finite and > 0, or y overlaps weight or bias.
+ */
+rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias, void *y,
+                            int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
+                            rk_dtype dtype, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status ("unknown status" for an
+ * unknown value). */
+const char *rk_status_string(rk_status status);
+
+/* RK_VERSION of the built library. */
+int rk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWKERN_H */

@@ -1,0 +1,267 @@
+"""Python binding of librowkern.so (HIP kernels for MI355X / gfx950).
+
+Argument marshalling only: every step of every operation runs in the HIP
+kernels of ``librowkern.so``.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Functions carry the C entry points' names:
+
+* ``rk_softmax(x, out=None)``
+* ``rk_online_softmax(x, num_splits=1, out=None, workspace=None)``
+* ``rk_layernorm_gelu(x, weight, bias, eps=1e-5, out=None)``
+* ``rk_online_softmax_workspace_bytes(M, N, num_splits)``,
+  ``rk_online_softmax_auto_splits(M, N)``, ``rk_status_string(s)``,
+  ``rk_version()``
+* tuning: ``rk_probe_copy(src, dst)``, ``rk__softmax_variant(index, x, out)``,
+  ``rk__layernorm_gelu_variant(index, x, w, b, eps, out)``, ``variants(op, dtype)``
+
+Tensors are 2-D with unit column stride (any row stride >= N); inputs of more
+than two dimensions are flattened to rows when contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LIB_PATH", "RowKernError", "load", "rk_softmax", "rk_online_softmax",
+    "rk_layernorm_gelu", "rk_online_softmax_workspace_bytes", "rk_online_softmax_auto_splits",
+    "rk_status_string", "rk_version", "rk_probe_copy", "rk__softmax_variant",
+    "rk__layernorm_gelu_variant", "variants", "RK_F32", "RK_BF16", "RK_OP_SOFTMAX",
+    "RK_OP_LAYERNORM_GELU",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.so")
+
+RK_F32, RK_BF16 = 0, 1
+RK_OP_SOFTMAX, RK_OP_LAYERNORM_GELU = 0, 1
+RK_OK = 0
+
+
+class RowKernError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {rk_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load():
+    """Load librowkern.so (raising if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m row_wise_amd.build` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz, f32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t,
+                             ctypes.c_float)
+    sig = {
+        "rk_softmax": (i32, [vp, vp, i64, i64, i64, i64, i32, vp]),
+        "rk_online_softmax": (i32, [vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]),
+        "rk_online_softmax_workspace_bytes": (sz, [i64, i64, i32]),
+        "rk_online_softmax_auto_splits": (i32, [i64, i64]),
+        "rk_layernorm_gelu": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
+        "rk_status_string": (ctypes.c_char_p, [i32]),
+        "rk_version": (ctypes.c_int, []),
+        "rk_probe_copy": (i32, [vp, vp, sz, i32, vp]),
+        "rk__variant_count": (i32, [i32, i32]),
+        "rk__variant_info": (i32, [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                   ctypes.POINTER(i64)]),
+        "rk__variant_pick": (i32, [i32, i32, i64]),
+        "rk__softmax_variant": (i32, [i32, vp, vp, i64, i64, i64, i64, i32, vp]),
+        "rk__layernorm_gelu_variant": (i32, [i32, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32,
+                                             vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- helpers
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RK_F32
+    if t.dtype == torch.bfloat16:
+        return RK_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _as_rows(x):
+    """View x as [M, N] rows with unit column stride; returns (view, M, N, ld)."""
+    if x.dim() == 1:
+        v = x.reshape(1, -1)
+    elif x.dim() == 2:
+        v = x
+    elif x.is_contiguous():
+        v = x.reshape(-1, x.shape[-1])
+    else:
+        raise ValueError("inputs of more than two dimensions must be contiguous")
+    M, N = v.shape
+    if M > 0 and N > 1 and v.stride(1) != 1:
+        raise ValueError("rows must have unit column stride")
+    ld = v.stride(0) if M > 1 else N
+    if M > 1 and ld < N:
+        raise ValueError("rows overlap (row stride < N)")
+    return v, M, N, ld
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    if t.is_cuda:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return 0
+
+
+def _check_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(load(), name)(*args)
+    if st != RK_OK:
+        raise RowKernError(name, st)
+
+
+def _out_like(x, v, out):
+    """Output rows for input rows v: a new tensor, or `out` checked; (rows, ld)."""
+    torch = _torch()
+    if out is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    else:
+        if out.dtype != x.dtype or out.device != x.device:
+            raise ValueError("out must have the input's dtype and device")
+        o = out
+    o, Mo, No, ldo = _as_rows(o)
+    if (Mo, No) != tuple(v.shape):
+        raise ValueError("out must have the input's rows and columns")
+    return o, ldo
+
+
+# ------------------------------------------------------------- entry points
+
+
+def rk_status_string(status: int) -> str:
+    return load().rk_status_string(int(status)).decode()
+
+
+def rk_version() -> int:
+    return int(load().rk_version())
+
+
+def rk_online_softmax_workspace_bytes(M: int, N: int, num_splits: int) -> int:
+    return int(load().rk_online_softmax_workspace_bytes(M, N, num_splits))
+
+
+def rk_online_softmax_auto_splits(M: int, N: int) -> int:
+    return int(load().rk_online_softmax_auto_splits(M, N))
+
+
+def rk_softmax(x, out=None):
+    """Stable row softmax of x (rows = last dimension); returns y."""
+    _check_device(x)
+    v, M, N, ldx = _as_rows(x)
+    o, ldy = _out_like(x, v, out)
+    _call("rk_softmax", v.data_ptr(), o.data_ptr(), M, N, ldx, ldy, _dtype_code(x), _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def rk_online_softmax(x, num_splits: int = 1, out=None, workspace=None):
+    """Online softmax (num_splits 1: streaming; >= 2: split-row; 0: auto)."""
+    torch = _torch()
+    _check_device(x)
+    v, M, N, ldx = _as_rows(x)
+    o, ldy = _out_like(x, v, out)
+    need = rk_online_softmax_workspace_bytes(M, N, num_splits) if M > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _call("rk_online_softmax", v.data_ptr(), o.data_ptr(), M, N, ldx, ldy, _dtype_code(x),
+          int(num_splits), wptr, wbytes, _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def rk_layernorm_gelu(x, weight, bias, eps: float = 1e-5, out=None):
+    """Fused LayerNorm + affine + tanh GeLU over the last dimension."""
+    _check_device(x, weight, bias)
+    v, M, N, ldx = _as_rows(x)
+    if weight.shape != (N,) or bias.shape != (N,) or not weight.is_contiguous() \
+            or not bias.is_contiguous():
+        raise ValueError("weight and bias must be contiguous [N]")
+    if weight.dtype != x.dtype or bias.dtype != x.dtype:
+        raise ValueError("weight and bias must have the input's dtype")
+    o, ldy = _out_like(x, v, out)
+    _call("rk_layernorm_gelu", v.data_ptr(), weight.data_ptr(), bias.data_ptr(), o.data_ptr(),
+          M, N, ldx, ldy, float(eps), _dtype_code(x), _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+# ------------------------------------------------------------------ tuning
+
+
+def rk_probe_copy(src, dst, max_workgroups: int = 0):
+    """16-byte copy kernel over the bytes of src into dst (same size)."""
+    _check_device(src, dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _call("rk_probe_copy", src.data_ptr(), dst.data_ptr(), nbytes, int(max_workgroups),
+          _stream(src))
+
+
+def variants(op: int, dtype: int) -> list[dict]:
+    """Geometry of every compiled tile variant of op (RK_OP_*) for dtype."""
+    lib = load()
+    out = []
+    for i in range(lib.rk__variant_count(op, dtype)):
+        g, v, w, r = (ctypes.c_int32() for _ in range(4))
+        n = ctypes.c_int64()
+        st = lib.rk__variant_info(op, dtype, i, ctypes.byref(g), ctypes.byref(v), ctypes.byref(w),
+                                  ctypes.byref(r), ctypes.byref(n))
+        if st != RK_OK:
+            raise RowKernError("rk__variant_info", st)
+        out.append({"index": i, "waves_per_row": g.value, "vecs_per_lane": v.value,
+                    "waves_per_block": w.value, "rows_per_group": r.value, "max_n": n.value})
+    return out
+
+
+def variant_pick(op: int, dtype: int, N: int) -> int:
+    return int(load().rk__variant_pick(op, dtype, N))
+
+
+def rk__softmax_variant(index: int, x, out=None):
+    _check_device(x)
+    v, M, N, ldx = _as_rows(x)
+    o, ldy = _out_like(x, v, out)
+    _call("rk__softmax_variant", int(index), v.data_ptr(), o.data_ptr(), M, N, ldx, ldy,
+          _dtype_code(x), _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def rk__layernorm_gelu_variant(index: int, x, weight, bias, eps: float = 1e-5, out=None):
+    _check_device(x, weight, bias)
+    v, M, N, ldx = _as_rows(x)
+    o, ldy = _out_like(x, v, out)
+    _call("rk__layernorm_gelu_variant", int(index), v.data_ptr(), weight.data_ptr(),
+          bias.data_ptr(), o.data_ptr(), M, N, ldx, ldy, float(eps), _dtype_code(x), _stream(x))
+    return o.reshape(x.shape) if out is None else out

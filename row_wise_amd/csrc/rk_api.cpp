@@ -1,0 +1,389 @@
+// C ABI of librowkern.so: argument validation (before any HIP call) and the
+// choice of kernel for each call.  See include/rowkern.h for the contract.
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "rk_internal.h"
+
+using namespace rk;
+
+namespace {
+
+bool valid_dtype(rk_dtype d) { return d == RK_F32 || d == RK_BF16; }
+
+// Longest row: kernels index vectors of a row with 32-bit integers.
+constexpr int64_t kMaxN = int64_t{1} << 30;
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi) in bytes
+};
+
+Span matrix_span(const void *p, int64_t M, int64_t N, int64_t ld, int es)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + static_cast<uintptr_t>(((M - 1) * ld + N) * es)};
+}
+
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// Byte extent (M-1)*ld + N elements must be representable.
+bool extent_ok(int64_t M, int64_t N, int64_t ld, int es)
+{
+    const int64_t lim = INT64_MAX / es - N;
+    return M - 1 <= lim / ld;
+}
+
+// Validation shared by every row entry point.  Returns RK_OK also for M == 0
+// (the caller then returns without launching).
+rk_status check_rows(const void *x, const void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
+                     rk_dtype dtype)
+{
+    if (!valid_dtype(dtype))
+        return RK_ERR_INVALID_ARG;
+    if (M < 0 || N < 1 || N > INT32_MAX || ldx < N || ldy < N)
+        return RK_ERR_INVALID_ARG;
+    if (N > kMaxN)
+        return RK_ERR_UNSUPPORTED;
+    if (M == 0)
+        return RK_OK;
+    if (x == nullptr || y == nullptr)
+        return RK_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    if (!extent_ok(M, N, ldx, es) || !extent_ok(M, N, ldy, es))
+        return RK_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(x) % es || reinterpret_cast<uintptr_t>(y) % es)
+        return RK_ERR_INVALID_ARG;
+    const bool in_place = x == y && ldx == ldy;
+    if (!in_place && overlaps(matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es)))
+        return RK_ERR_INVALID_ARG;
+    return RK_OK;
+}
+
+// The 16-byte vector path needs aligned bases and row pitches.
+bool rows_aligned(const void *x, const void *y, int64_t ldx, int64_t ldy, int es)
+{
+    return aligned16(x) && aligned16(y) && (ldx * es) % 16 == 0 && (ldy * es) % 16 == 0;
+}
+
+// gridDim.x * blockDim.x must stay below 2^32 work-items.
+bool grid_ok(int64_t blocks, int threads)
+{
+    return blocks >= 1 && blocks <= (int64_t{UINT32_MAX} / threads);
+}
+
+rk_status hip_status(hipError_t e) { return e == hipSuccess ? RK_OK : RK_ERR_HIP; }
+
+RowProblem make_problem(const void *x, void *y, const void *w, const void *b, int64_t M,
+                        int64_t N, int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
+                        hipStream_t stream)
+{
+    return RowProblem{x, y, w, b, M, static_cast<int>(N), ldx, ldy, eps, dtype, stream};
+}
+
+const TileVariant *variants(rk_op op, rk_dtype dtype, int *count)
+{
+    *count = 0;
+    if (!valid_dtype(dtype))
+        return nullptr;
+    if (op == RK_OP_SOFTMAX)
+        return softmax_variants(dtype, count);
+    if (op == RK_OP_LAYERNORM_GELU)
+        return layernorm_gelu_variants(dtype, count);
+    return nullptr;
+}
+
+int pick_variant(rk_op op, rk_dtype dtype, int64_t N)
+{
+    int count = 0;
+    const TileVariant *v = variants(op, dtype, &count);
+    for (int i = 0; i < count; ++i)
+        if (N <= v[i].max_n)
+            return i;
+    return -1;
+}
+
+int64_t tile_blocks(const TileVariant &v, int64_t M)
+{
+    const int64_t rows_per_block = int64_t{v.waves_per_block} / v.waves_per_row * v.rows_per_group;
+    return (M + rows_per_block - 1) / rows_per_block;
+}
+
+constexpr int kStreamThreads = 1024;  // online_stream workgroup size
+constexpr int kSplitThreads = 256;    // online_partials / online_finish
+constexpr int kLoopThreads = 256;     // layernorm_gelu_loop
+constexpr int32_t kMaxSplits = 65536;
+
+int32_t auto_splits(int64_t M, int64_t N)
+{
+    // Enough rows to give every CU workgroups of its own: stream.  Otherwise
+    // aim at >= 2048 workgroups with chunks of >= 2048 elements.
+    if (M >= 512)
+        return 1;
+    int64_t s = (2048 + M - 1) / M;
+    const int64_t by_len = (N + 2047) / 2048;
+    if (s > by_len)
+        s = by_len;
+    if (s > kMaxSplits)
+        s = kMaxSplits;
+    return static_cast<int32_t>(s < 1 ? 1 : s);
+}
+
+rk_status softmax_generic(const RowProblem &p, bool aligned)
+{
+    if (!grid_ok(p.M, kStreamThreads))
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(online_stream_run(p, aligned));
+}
+
+rk_status layernorm_generic(const RowProblem &p, bool aligned)
+{
+    if (!grid_ok(p.M, kLoopThreads))
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(layernorm_gelu_loop_run(p, aligned));
+}
+
+rk_status run_tile(const TileVariant &v, const RowProblem &p)
+{
+    const int64_t blocks = tile_blocks(v, p.M);
+    if (!grid_ok(blocks, v.waves_per_block * 64))
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(v.run(p));
+}
+
+rk_status check_layernorm(const void *x, const void *w, const void *b, const void *y, int64_t M,
+                          int64_t N, int64_t ldx, int64_t ldy, float eps, rk_dtype dtype)
+{
+    rk_status st = check_rows(x, y, M, N, ldx, ldy, dtype);
+    if (st != RK_OK)
+        return st;
+    if (!std::isfinite(eps) || !(eps > 0.0f))
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    if (w == nullptr || b == nullptr)
+        return RK_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    if (reinterpret_cast<uintptr_t>(w) % es || reinterpret_cast<uintptr_t>(b) % es)
+        return RK_ERR_INVALID_ARG;
+    const Span ys = matrix_span(y, M, N, ldy, es);
+    if (overlaps(ys, matrix_span(w, 1, N, N, es)) || overlaps(ys, matrix_span(b, 1, N, N, es)))
+        return RK_ERR_INVALID_ARG;
+    return RK_OK;
+}
+
+bool layernorm_aligned(const RowProblem &p)
+{
+    return rows_aligned(p.x, p.y, p.ldx, p.ldy, elem_size(p.dtype)) && aligned16(p.w) &&
+           aligned16(p.b);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ ABI
+
+RK_EXPORT rk_status rk_softmax(const void *x, void *y, int64_t M, int64_t N, int64_t ldx,
+                               int64_t ldy, rk_dtype dtype, hipStream_t stream)
+{
+    rk_status st = check_rows(x, y, M, N, ldx, ldy, dtype);
+    if (st != RK_OK || M == 0)
+        return st;
+    const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
+    const bool aligned = rows_aligned(x, y, ldx, ldy, elem_size(dtype));
+    const int idx = pick_variant(RK_OP_SOFTMAX, dtype, N);
+    if (aligned && idx >= 0) {
+        int count = 0;
+        return run_tile(softmax_variants(dtype, &count)[idx], p);
+    }
+    return softmax_generic(p, aligned);
+}
+
+RK_EXPORT int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N)
+{
+    if (M < 1 || N < 1)
+        return 1;
+    return auto_splits(M, N);
+}
+
+RK_EXPORT size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t num_splits)
+{
+    if (M < 1 || N < 1 || N > kMaxN || num_splits < 0 || num_splits > kMaxSplits)
+        return 0;
+    const int64_t S = num_splits == 0 ? auto_splits(M, N) : num_splits;
+    if (S <= 1)
+        return 0;
+    if (M > INT64_MAX / 8 / S)
+        return 0;
+    return static_cast<size_t>(M * S * 8);
+}
+
+RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t N, int64_t ldx,
+                                      int64_t ldy, rk_dtype dtype, int32_t num_splits,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    rk_status st = check_rows(x, y, M, N, ldx, ldy, dtype);
+    if (st != RK_OK)
+        return st;
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
+    const bool aligned = rows_aligned(x, y, ldx, ldy, elem_size(dtype));
+    const int32_t S = num_splits == 0 ? auto_splits(M, N) : num_splits;
+    if (S <= 1)
+        return softmax_generic(p, aligned);
+
+    const size_t need = rk_online_softmax_workspace_bytes(M, N, S);
+    if (need == 0)
+        return RK_ERR_UNSUPPORTED;
+    if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+        return RK_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < need)
+        return RK_ERR_WORKSPACE;
+    if (M > INT64_MAX / S || !grid_ok(M * S, kSplitThreads))
+        return RK_ERR_UNSUPPORTED;
+    // the workspace is written by the first kernel: it must not alias x or y
+    const int es = elem_size(dtype);
+    const Span ws{reinterpret_cast<uintptr_t>(workspace),
+                  reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlaps(ws, matrix_span(x, M, N, ldx, es)) || overlaps(ws, matrix_span(y, M, N, ldy, es)))
+        return RK_ERR_INVALID_ARG;
+    const int64_t chunk = split_chunk(N, S, aligned ? vec_elems(dtype) : 1);
+    if (chunk > INT32_MAX)
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(online_split_run(p, S, static_cast<int>(chunk), workspace, aligned));
+}
+
+RK_EXPORT rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias, void *y,
+                                      int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
+                                      rk_dtype dtype, hipStream_t stream)
+{
+    rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
+    if (st != RK_OK || M == 0)
+        return st;
+    const RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
+    const bool aligned = layernorm_aligned(p);
+    const int idx = pick_variant(RK_OP_LAYERNORM_GELU, dtype, N);
+    if (aligned && idx >= 0) {
+        int count = 0;
+        return run_tile(layernorm_gelu_variants(dtype, &count)[idx], p);
+    }
+    return layernorm_generic(p, aligned);
+}
+
+RK_EXPORT const char *rk_status_string(rk_status status)
+{
+    switch (status) {
+    case RK_OK:
+        return "ok";
+    case RK_ERR_INVALID_ARG:
+        return "invalid argument";
+    case RK_ERR_UNSUPPORTED:
+        return "unsupported arguments";
+    case RK_ERR_WORKSPACE:
+        return "workspace missing or too small";
+    case RK_ERR_HIP:
+        return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+RK_EXPORT int rk_version(void) { return RK_VERSION; }
+
+// --------------------------------------------------------- tuning / probe
+
+RK_EXPORT rk_status rk_probe_copy(const void *src, void *dst, size_t bytes, int32_t max_workgroups,
+                                  hipStream_t stream)
+{
+    if (bytes == 0)
+        return RK_OK;
+    if (src == nullptr || dst == nullptr || !aligned16(src) || !aligned16(dst) || bytes % 16 != 0)
+        return RK_ERR_INVALID_ARG;
+    const Span s{reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(src) + bytes};
+    const Span d{reinterpret_cast<uintptr_t>(dst), reinterpret_cast<uintptr_t>(dst) + bytes};
+    if (overlaps(s, d))
+        return RK_ERR_INVALID_ARG;
+    return hip_status(probe_copy_run(src, dst, bytes, max_workgroups, stream));
+}
+
+RK_EXPORT int32_t rk__variant_count(rk_op op, rk_dtype dtype)
+{
+    int count = 0;
+    variants(op, dtype, &count);
+    return count;
+}
+
+RK_EXPORT rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index,
+                                     int32_t *waves_per_row, int32_t *vecs_per_lane,
+                                     int32_t *waves_per_block, int32_t *rows_per_group,
+                                     int64_t *max_n)
+{
+    int count = 0;
+    const TileVariant *v = variants(op, dtype, &count);
+    if (v == nullptr || index < 0 || index >= count)
+        return RK_ERR_INVALID_ARG;
+    if (waves_per_row)
+        *waves_per_row = v[index].waves_per_row;
+    if (vecs_per_lane)
+        *vecs_per_lane = v[index].vecs_per_lane;
+    if (waves_per_block)
+        *waves_per_block = v[index].waves_per_block;
+    if (rows_per_group)
+        *rows_per_group = v[index].rows_per_group;
+    if (max_n)
+        *max_n = v[index].max_n;
+    return RK_OK;
+}
+
+RK_EXPORT int32_t rk__variant_pick(rk_op op, rk_dtype dtype, int64_t N)
+{
+    return pick_variant(op, dtype, N);
+}
+
+RK_EXPORT rk_status rk__softmax_variant(int32_t index, const void *x, void *y, int64_t M, int64_t N,
+                                        int64_t ldx, int64_t ldy, rk_dtype dtype,
+                                        hipStream_t stream)
+{
+    rk_status st = check_rows(x, y, M, N, ldx, ldy, dtype);
+    if (st != RK_OK)
+        return st;
+    int count = 0;
+    const TileVariant *v = variants(RK_OP_SOFTMAX, dtype, &count);
+    if (index < -1 || index >= count)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
+    const bool aligned = rows_aligned(x, y, ldx, ldy, elem_size(dtype));
+    if (index == -1)
+        return softmax_generic(p, aligned);
+    if (!aligned || N > v[index].max_n)
+        return RK_ERR_UNSUPPORTED;
+    return run_tile(v[index], p);
+}
+
+RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, const void *weight,
+                                               const void *bias, void *y, int64_t M, int64_t N,
+                                               int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
+                                               hipStream_t stream)
+{
+    rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
+    if (st != RK_OK)
+        return st;
+    int count = 0;
+    const TileVariant *v = variants(RK_OP_LAYERNORM_GELU, dtype, &count);
+    if (index < -1 || index >= count)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
+    const bool aligned = layernorm_aligned(p);
+    if (index == -1)
+        return layernorm_generic(p, aligned);
+    if (!aligned || N > v[index].max_n)
+        return RK_ERR_UNSUPPORTED;
+    return run_tile(v[index], p);
+}

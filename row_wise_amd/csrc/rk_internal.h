@@ -1,0 +1,85 @@
+// Host-side glue shared by the kernel translation units and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+#include "rowkern.h"
+#include "rowkern_tune.h"
+
+#define RK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace rk {
+
+// Launch a kernel through hipLaunchKernel so that the status of this launch
+// (not a stale error of an earlier call) is returned.  Arguments are
+// converted to the kernel's exact parameter types.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                         Args... args)
+{
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+    void *argv[sizeof...(KArgs)];
+    std::apply(
+        [&](auto &...v) {
+            int i = 0;
+            ((argv[i++] = static_cast<void *>(&v)), ...);
+        },
+        vals);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, stream);
+}
+
+// One row-wise problem as validated by the ABI layer.
+struct RowProblem {
+    const void *x;
+    void *y;
+    const void *w;  // LayerNorm only
+    const void *b;  // LayerNorm only
+    int64_t M;
+    int N;
+    int64_t ldx, ldy;
+    float eps;  // LayerNorm only
+    rk_dtype dtype;
+    hipStream_t stream;
+};
+
+// A compiled register-resident kernel shape.
+struct TileVariant {
+    int waves_per_row;    // G: waves cooperating on a row
+    int vecs_per_lane;    // V: 16-byte vectors per lane
+    int waves_per_block;  // W: waves per workgroup (W / G row groups)
+    int rows_per_group;   // R: rows each row group handles in sequence
+    int max_n;            // largest N the variant holds
+    hipError_t (*run)(const RowProblem &);
+};
+
+// Variant tables (defined next to the kernels), in order of preference: the
+// dispatcher takes the first variant whose max_n covers N.
+const TileVariant *softmax_variants(rk_dtype dtype, int *count);
+const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count);
+
+// Generic paths (any alignment, any N).
+hipError_t online_stream_run(const RowProblem &p, bool vectorized);
+hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
+                            bool vectorized);
+hipError_t layernorm_gelu_loop_run(const RowProblem &p, bool vectorized);
+hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
+                          hipStream_t stream);
+
+inline int elem_size(rk_dtype dt) { return dt == RK_F32 ? 4 : 2; }
+inline int vec_elems(rk_dtype dt) { return 16 / elem_size(dt); }
+
+// Chunk length (elements) of the split-row variant: ceil(N / S) rounded up to
+// whole 16-byte vectors when the vector path is used.
+inline int64_t split_chunk(int64_t N, int64_t S, int vec)
+{
+    int64_t c = (N + S - 1) / S;
+    return (c + vec - 1) / vec * vec;
+}
+
+}  // namespace rk

@@ -1,0 +1,266 @@
+// Fused LayerNorm + affine + tanh GeLU ("Triton Kernel 实现练习" §4.1
+// "LayerNorm" and §3.4 "Approx Activation"; "PyTorch 自定义 CUDA 算子与 Triton
+// 编程从 Python 原型到 GPU 极致性能" section 三, "Fused LayerNorm GELU Kernel").
+//
+// Per row: mu = sum x / N; var = sum (x - mu)^2 / N, both over the N true
+// columns (padding never enters); rstd = 1 / sqrt(var + eps);
+// z = (x - mu) rstd w + b; y = GeLU_tanh(z).
+//
+// layernorm_gelu_tile  the row stays in VGPRs (one HBM read and write per
+//                      element): sum -> wave DPP / LDS -> centre in registers
+//                      -> sum of squares -> wave DPP / LDS -> epilogue.  A row
+//                      group handles R rows in sequence and loads weight and
+//                      bias once for all of them.
+// layernorm_gelu_loop  one workgroup per row, three passes over the row in
+//                      memory (sum, centred sum of squares, output); any N,
+//                      any alignment.
+#include "rk_device.h"
+#include "rk_internal.h"
+
+namespace rk {
+
+template <typename T, int G, int V, int W, int R>
+__global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
+    const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
+    T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float eps)
+{
+    constexpr int E = Elem<T>::kVec;
+    constexpr int RG = W / G;
+    constexpr int L = G * kWave;
+    static_assert(W % G == 0, "whole row groups per workgroup");
+    // two buffers per reduction: a wave may start the next row's reduction
+    // while another still reads this row's partials
+    __shared__ float red_sum[2][RG][G];
+    __shared__ float red_var[2][RG][G];
+
+    const int wave = threadIdx.x / kWave;
+    const int grp = wave / G;
+    const int wig = wave % G;
+    const int li = wig * kWave + static_cast<int>(threadIdx.x % kWave);
+    const RowSplit<E> rs(N);
+    const float n_f = static_cast<float>(N);
+
+    float wv[V][E], bv[V][E];
+    load_row<T, E, V, L>(w, li, rs.count(), rs, 0.0f, wv);
+    load_row<T, E, V, L>(b, li, rs.count(), rs, 0.0f, bv);
+
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp;
+        const bool row_ok = row < M;
+        const int64_t rr = row_ok ? row : 0;
+        const T *xr = x + rr * ldx;
+        T *yr = y + rr * ldy;
+        const int buf = r & 1;
+
+        const int vend = row_ok ? rs.count() : 0;
+
+        float v[V][E];
+        load_row<T, E, V, L>(xr, li, vend, rs, 0.0f, v);
+
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                s += v[k][e];
+        s = wave_sum(s);
+        if constexpr (G > 1) {
+            if (threadIdx.x % kWave == 0)
+                red_sum[buf][grp][wig] = s;
+            __syncthreads();
+            s = red_sum[buf][grp][0];
+#pragma unroll
+            for (int g = 1; g < G; ++g)
+                s += red_sum[buf][grp][g];
+        }
+        const float mean = s / n_f;
+
+        // centre in registers; padded columns are set to 0 so that they add
+        // nothing to the variance
+        float q = 0.0f;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int vi = k * L + li;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool valid = vi < rs.nfull || (vi == rs.nfull && e < rs.tail);
+                const float d = valid ? v[k][e] - mean : 0.0f;
+                v[k][e] = d;
+                q = fmaf(d, d, q);
+            }
+        }
+        q = wave_sum(q);
+        if constexpr (G > 1) {
+            if (threadIdx.x % kWave == 0)
+                red_var[buf][grp][wig] = q;
+            __syncthreads();
+            q = red_var[buf][grp][0];
+#pragma unroll
+            for (int g = 1; g < G; ++g)
+                q += red_var[buf][grp][g];
+        }
+        const float rstd = 1.0f / sqrtf(q / n_f + eps);
+
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[k][e] = gelu_tanh(fmaf(v[k][e] * rstd, wv[k][e], bv[k][e]));
+        store_row<T, E, V, L>(yr, li, vend, rs, v);
+    }
+}
+
+template <typename T, int G, int V, int W, int R>
+static hipError_t layernorm_gelu_tile_run(const RowProblem &p)
+{
+    constexpr int RG = W / G;
+    const int64_t blocks = (p.M + RG * R - 1) / (RG * R);
+    return launch(layernorm_gelu_tile<T, G, V, W, R>, dim3(static_cast<unsigned>(blocks)),
+                  dim3(W * kWave), p.stream, static_cast<const T *>(p.x),
+                  static_cast<const T *>(p.w), static_cast<const T *>(p.b), static_cast<T *>(p.y),
+                  p.M, p.N, p.ldx, p.ldy, p.eps);
+}
+
+template <typename T, int G, int V, int W, int R = 1>
+constexpr TileVariant tile()
+{
+    return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec,
+                       &layernorm_gelu_tile_run<T, G, V, W, R>};
+}
+
+static const TileVariant kLayerNormF32[] = {
+    tile<float, 1, 1, 4>(),   // N <= 256
+    tile<float, 1, 2, 4>(),   // N <= 512
+    tile<float, 1, 3, 4>(),   // N <= 768
+    tile<float, 1, 4, 4>(),   // N <= 1024
+    tile<float, 1, 8, 4>(),   // N <= 2048
+    tile<float, 4, 4, 4>(),   // N <= 4096
+    tile<float, 8, 4, 8>(),   // N <= 8192
+    tile<float, 16, 4, 16>(), // N <= 16384
+    tile<float, 1, 3, 4, 2>(),  // alternatives
+    tile<float, 1, 3, 4, 4>(),
+    tile<float, 2, 2, 4>(),
+    tile<float, 4, 1, 4>(),
+};
+
+static const TileVariant kLayerNormBF16[] = {
+    tile<bf16_t, 1, 1, 4>(),   // N <= 512
+    tile<bf16_t, 1, 2, 4>(),   // N <= 1024
+    tile<bf16_t, 1, 4, 4>(),   // N <= 2048
+    tile<bf16_t, 4, 2, 4>(),   // N <= 4096
+    tile<bf16_t, 8, 2, 8>(),   // N <= 8192
+    tile<bf16_t, 16, 2, 16>(), // N <= 16384
+    tile<bf16_t, 16, 4, 16>(), // N <= 32768
+    tile<bf16_t, 1, 8, 4>(),   // alternatives
+    tile<bf16_t, 2, 4, 4>(),
+    tile<bf16_t, 8, 1, 8>(),
+    tile<bf16_t, 4, 2, 4, 2>(),
+    tile<bf16_t, 4, 2, 8, 2>(),
+};
+
+const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count)
+{
+    if (dtype == RK_F32) {
+        *count = static_cast<int>(sizeof(kLayerNormF32) / sizeof(kLayerNormF32[0]));
+        return kLayerNormF32;
+    }
+    *count = static_cast<int>(sizeof(kLayerNormBF16) / sizeof(kLayerNormBF16[0]));
+    return kLayerNormBF16;
+}
+
+// ------------------------------------------------------- looping kernel
+
+template <int W>
+__device__ __forceinline__ float block_sum(float v, float *red)
+{
+    v = wave_sum(v);
+    if constexpr (W > 1) {
+        const int wave = threadIdx.x / kWave;
+        if (threadIdx.x % kWave == 0)
+            red[wave] = v;
+        __syncthreads();
+        v = red[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i)
+            v += red[i];
+    }
+    return v;
+}
+
+template <typename T, int E, int W, int U>
+__global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
+    const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
+    T *__restrict__ y, int N, int64_t ldx, int64_t ldy, float eps)
+{
+    constexpr int NT = W * kWave;
+    __shared__ float red[2][W];
+    const int64_t row = blockIdx.x;
+    const T *xr = x + row * ldx;
+    T *yr = y + row * ldy;
+    const RowSplit<E> rs(N);
+    const int nv = rs.count();
+    const float n_f = static_cast<float>(N);
+    const int tid = static_cast<int>(threadIdx.x);
+
+    float s = 0.0f;
+    for (int base = 0; base < nv; base += NT * U) {
+        float v[U][E];
+        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                s += v[u][e];
+    }
+    const float mean = block_sum<W>(s, red[0]) / n_f;
+
+    float q = 0.0f;
+    for (int base = 0; base < nv; base += NT * U) {
+        float v[U][E];
+        load_row<T, E, U, NT>(xr, base + tid, nv, rs, mean, v);  // padding centres to 0
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float d = v[u][e] - mean;
+                q = fmaf(d, d, q);
+            }
+    }
+    const float rstd = 1.0f / sqrtf(block_sum<W>(q, red[1]) / n_f + eps);
+
+    for (int base = 0; base < nv; base += NT * U) {
+        float v[U][E], wv[U][E], bv[U][E];
+        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
+        load_row<T, E, U, NT>(w, base + tid, nv, rs, 0.0f, wv);
+        load_row<T, E, U, NT>(b, base + tid, nv, rs, 0.0f, bv);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[u][e] = gelu_tanh(fmaf((v[u][e] - mean) * rstd, wv[u][e], bv[u][e]));
+        store_row<T, E, U, NT>(yr, base + tid, nv, rs, v);
+    }
+}
+
+namespace {
+constexpr int kLoopW = 4;
+constexpr int kLoopU = 4;
+
+template <typename T, int E>
+hipError_t loop_run(const RowProblem &p)
+{
+    return launch(layernorm_gelu_loop<T, E, kLoopW, kLoopU>, dim3(static_cast<unsigned>(p.M)),
+                  dim3(kLoopW * kWave), p.stream, static_cast<const T *>(p.x),
+                  static_cast<const T *>(p.w), static_cast<const T *>(p.b), static_cast<T *>(p.y),
+                  p.N, p.ldx, p.ldy, p.eps);
+}
+}  // namespace
+
+hipError_t layernorm_gelu_loop_run(const RowProblem &p, bool vectorized)
+{
+    if (p.dtype == RK_F32)
+        return vectorized ? loop_run<float, 4>(p) : loop_run<float, 1>(p);
+    return vectorized ? loop_run<bf16_t, 8>(p) : loop_run<bf16_t, 1>(p);
+}
+
+}  // namespace rk

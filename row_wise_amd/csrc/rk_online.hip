@@ -1,0 +1,233 @@
+// Online softmax for long rows ("Triton Kernel 实现练习" §2.5 "Online Softmax";
+// "第 6 讲：GPU Kernels 与 Triton" §7.2 "Online Softmax").
+//
+// State of a scanned part of a row: (m, d) = (its max, sum of exp(x - m) over
+// it).  A new block moves the state to m' = max(m, block max),
+// d' = d exp(m - m') + sum exp(block - m').  Two partial states of disjoint
+// parts merge with the same rescaling (rk::merge).
+//
+// online_stream    one workgroup per row.  Pass 1: every lane folds the
+//                  blocks it loads into its own state; lanes merge through
+//                  DPP, waves through LDS.  Pass 2 re-reads the row and
+//                  writes exp(x - m) / d.  2 reads + 1 write per element.
+// online_partials  split-row, first kernel: one workgroup per (row, chunk)
+//                  writes the chunk's (m_s, d_s) to the workspace.
+// online_finish    split-row, second kernel: one workgroup per (row, chunk)
+//                  merges the row's S partials (each lane a subset, then
+//                  DPP) and writes its chunk.
+#include "rk_device.h"
+#include "rk_internal.h"
+
+namespace rk {
+
+template <typename T>
+__device__ __forceinline__ float softmax_exp(float x, float m, float m_log2e)
+{
+    if constexpr (sizeof(T) == 4)
+        return exp_shifted_accurate(x, m);
+    else
+        return exp_shifted_fast(x, m_log2e);
+}
+
+// Fold U vectors of E elements into a lane state.
+template <typename T, int U, int E>
+__device__ __forceinline__ SoftmaxState fold(SoftmaxState st, const float (&v)[U][E])
+{
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            bm = fmaxf(bm, v[u][e]);
+    const float mn = fmaxf(st.m, bm);
+    float sum = 0.0f;
+    if (mn != -INFINITY) {  // else every value seen is -inf: nothing to add
+        const float mL = mn * 1.4426950408889634f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                sum += softmax_exp<T>(v[u][e], mn, mL);
+    }
+    SoftmaxState r;
+    r.m = mn;
+    r.d = st.d * rescale_factor(st.m, mn) + sum;
+    return r;
+}
+
+// Merge the lane states of a workgroup of W waves; every thread returns the
+// same state.  `sm`/`sd` are W-entry LDS arrays.
+template <int W>
+__device__ __forceinline__ SoftmaxState block_merge(SoftmaxState st, float *sm, float *sd)
+{
+    st = wave_merge(st);
+    if constexpr (W > 1) {
+        const int wave = threadIdx.x / kWave;
+        if (threadIdx.x % kWave == 0) {
+            sm[wave] = st.m;
+            sd[wave] = st.d;
+        }
+        __syncthreads();
+        st = SoftmaxState{sm[0], sd[0]};
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            st = merge(st, SoftmaxState{sm[w], sd[w]});
+    }
+    return st;
+}
+
+// Vectors [vbeg, vend) of a row (vector index space of RowSplit<E>), U
+// vectors per thread per step, folded into the thread's state.
+template <typename T, int E, int W, int U>
+__device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xr, RowSplit<E> rs,
+                                                   int vbeg, int vend)
+{
+    constexpr int NT = W * kWave;
+    SoftmaxState st{-INFINITY, 0.0f};
+    for (int base = vbeg; base < vend; base += NT * U) {
+        float v[U][E];
+        load_row<T, E, U, NT>(xr, base + static_cast<int>(threadIdx.x), vend, rs, -INFINITY, v);
+        st = fold<T, U, E>(st, v);
+    }
+    return st;
+}
+
+// Write exp(x - m) / d for vectors [vbeg, vend) of a row.
+template <typename T, int E, int W, int U>
+__device__ __forceinline__ void write_range(const T *__restrict__ xr, T *__restrict__ yr,
+                                            RowSplit<E> rs, int vbeg, int vend, SoftmaxState st)
+{
+    constexpr int NT = W * kWave;
+    const float inv = 1.0f / st.d;
+    const float mL = st.m * 1.4426950408889634f;
+    for (int base = vbeg; base < vend; base += NT * U) {
+        const int vi0 = base + static_cast<int>(threadIdx.x);
+        float v[U][E];
+        load_row<T, E, U, NT>(xr, vi0, vend, rs, -INFINITY, v);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[u][e] = softmax_exp<T>(v[u][e], st.m, mL) * inv;
+        store_row<T, E, U, NT>(yr, vi0, vend, rs, v);
+    }
+}
+
+template <typename T, int E, int W, int U>
+__global__ __launch_bounds__(W *kWave) void online_stream(const T *__restrict__ x,
+                                                           T *__restrict__ y, int N, int64_t ldx,
+                                                           int64_t ldy)
+{
+    __shared__ float sm[W], sd[W];
+    const int64_t row = blockIdx.x;
+    const T *xr = x + row * ldx;
+    T *yr = y + row * ldy;
+    const RowSplit<E> rs(N);
+    const int nv = rs.count();
+    SoftmaxState st = scan_range<T, E, W, U>(xr, rs, 0, nv);
+    st = block_merge<W>(st, sm, sd);
+    write_range<T, E, W, U>(xr, yr, rs, 0, nv, st);
+}
+
+// Partials of chunk s = blockIdx.x % S of row blockIdx.x / S; chunk length C
+// elements (a multiple of E).
+template <typename T, int E, int W, int U>
+__global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict__ x, int N,
+                                                             int64_t ldx, int S, int C,
+                                                             float2 *__restrict__ ws)
+{
+    __shared__ float sm[W], sd[W];
+    const int64_t row = blockIdx.x / S;
+    const int s = static_cast<int>(blockIdx.x % S);
+    const T *xr = x + row * ldx;
+    const RowSplit<E> rs(N);
+    const int nv = rs.count();
+    const int64_t c0 = static_cast<int64_t>(s) * C;
+    const int vbeg = static_cast<int>(c0 < N ? c0 / E : nv);
+    const int vend = static_cast<int>(c0 + C < N ? (c0 + C) / E : nv);
+    SoftmaxState st = scan_range<T, E, W, U>(xr, rs, vbeg, vend);
+    st = block_merge<W>(st, sm, sd);
+    if (threadIdx.x == 0)
+        ws[blockIdx.x] = make_float2(st.m, st.d);
+}
+
+template <typename T, int E, int W, int U>
+__global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ x,
+                                                           T *__restrict__ y, int N, int64_t ldx,
+                                                           int64_t ldy, int S, int C,
+                                                           const float2 *__restrict__ ws)
+{
+    const int64_t row = blockIdx.x / S;
+    const int s = static_cast<int>(blockIdx.x % S);
+    // Every wave merges the row's S partials on its own (lane l takes
+    // partials l, l + 64, ...), so no LDS or barrier is needed, and every
+    // workgroup of the row forms the same bits.
+    SoftmaxState st{-INFINITY, 0.0f};
+    const float2 *wr = ws + row * S;
+    for (int i = static_cast<int>(threadIdx.x % kWave); i < S; i += kWave) {
+        const float2 p = wr[i];
+        st = merge(st, SoftmaxState{p.x, p.y});
+    }
+    st = wave_merge(st);
+
+    const T *xr = x + row * ldx;
+    T *yr = y + row * ldy;
+    const RowSplit<E> rs(N);
+    const int nv = rs.count();
+    const int64_t c0 = static_cast<int64_t>(s) * C;
+    const int vbeg = static_cast<int>(c0 < N ? c0 / E : nv);
+    const int vend = static_cast<int>(c0 + C < N ? (c0 + C) / E : nv);
+    write_range<T, E, W, U>(xr, yr, rs, vbeg, vend, st);
+}
+
+// ------------------------------------------------------------------ host
+
+namespace {
+
+constexpr int kStreamW = 16;  // 1024 threads per row
+constexpr int kStreamU = 4;
+constexpr int kSplitW = 4;    // 256 threads per chunk
+constexpr int kSplitU = 4;
+
+template <typename T, int E>
+hipError_t stream_run(const RowProblem &p)
+{
+    return launch(online_stream<T, E, kStreamW, kStreamU>, dim3(static_cast<unsigned>(p.M)),
+                  dim3(kStreamW * kWave), p.stream, static_cast<const T *>(p.x),
+                  static_cast<T *>(p.y), p.N, p.ldx, p.ldy);
+}
+
+template <typename T, int E>
+hipError_t split_run(const RowProblem &p, int S, int C, void *ws)
+{
+    const dim3 grid(static_cast<unsigned>(p.M * S));
+    hipError_t err = launch(online_partials<T, E, kSplitW, kSplitU>, grid, dim3(kSplitW * kWave),
+                            p.stream, static_cast<const T *>(p.x), p.N, p.ldx, S, C,
+                            static_cast<float2 *>(ws));
+    if (err != hipSuccess)
+        return err;
+    return launch(online_finish<T, E, kSplitW, kSplitU>, grid, dim3(kSplitW * kWave), p.stream,
+                  static_cast<const T *>(p.x), static_cast<T *>(p.y), p.N, p.ldx, p.ldy, S, C,
+                  static_cast<const float2 *>(ws));
+}
+
+}  // namespace
+
+hipError_t online_stream_run(const RowProblem &p, bool vectorized)
+{
+    if (p.dtype == RK_F32)
+        return vectorized ? stream_run<float, 4>(p) : stream_run<float, 1>(p);
+    return vectorized ? stream_run<bf16_t, 8>(p) : stream_run<bf16_t, 1>(p);
+}
+
+hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
+                            bool vectorized)
+{
+    if (p.dtype == RK_F32)
+        return vectorized ? split_run<float, 4>(p, splits, chunk, workspace)
+                          : split_run<float, 1>(p, splits, chunk, workspace);
+    return vectorized ? split_run<bf16_t, 8>(p, splits, chunk, workspace)
+                      : split_run<bf16_t, 1>(p, splits, chunk, workspace);
+}
+
+}  // namespace rk

@@ -1,0 +1,158 @@
+// Register-resident stable row softmax ("Triton Kernel 实现练习" §2.4 "Softmax",
+// stable version; CS336 "Kernels, Triton" notes, "Triton Softmax").
+//
+// A row group of G waves (G x 64 lanes) holds one row in VGPRs as V 16-byte
+// vectors per lane, so each element is read from HBM once and written once:
+//   load -> per-lane max -> wave64 DPP max -> (G > 1) LDS combine
+//        -> e = exp(x - m) kept in registers, per-lane sum -> wave / LDS sum
+//        -> y = e * (1 / sum) -> store.
+// Lanes of a row are contiguous 16-byte vectors, so a wave's load instruction
+// covers 1 KiB of consecutive memory.  Columns beyond N are padded with -inf
+// in registers (never loaded).
+#include "rk_device.h"
+#include "rk_internal.h"
+
+namespace rk {
+
+template <typename T, int G, int V, int W>
+__global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x,
+                                                          T *__restrict__ y, int64_t M, int N,
+                                                          int64_t ldx, int64_t ldy)
+{
+    constexpr int E = Elem<T>::kVec;
+    constexpr int RG = W / G;    // row groups per workgroup
+    constexpr int L = G * kWave; // lanes per row
+    static_assert(W % G == 0, "whole row groups per workgroup");
+    __shared__ float red_max[RG][G];
+    __shared__ float red_sum[RG][G];
+
+    const int wave = threadIdx.x / kWave;
+    const int grp = wave / G;
+    const int wig = wave % G;
+    const int li = wig * kWave + static_cast<int>(threadIdx.x % kWave);
+    const RowSplit<E> rs(N);
+
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RG + grp;
+    const bool row_ok = row < M;
+    const int64_t r = row_ok ? row : 0;
+    const T *xr = x + r * ldx;
+    T *yr = y + r * ldy;
+
+    const int vend = row_ok ? rs.count() : 0;
+
+    float v[V][E];
+    load_row<T, E, V, L>(xr, li, vend, rs, -INFINITY, v);
+
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            m = fmaxf(m, v[k][e]);
+    m = wave_max(m);
+    if constexpr (G > 1) {
+        if (threadIdx.x % kWave == 0)
+            red_max[grp][wig] = m;
+        __syncthreads();
+        m = red_max[grp][0];
+#pragma unroll
+        for (int g = 1; g < G; ++g)
+            m = fmaxf(m, red_max[grp][g]);
+    }
+
+    float s = 0.0f;
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                v[k][e] = exp_shifted_accurate(v[k][e], m);
+                s += v[k][e];
+            }
+    } else {
+        const float mL = m * 1.4426950408889634f;
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                v[k][e] = exp_shifted_fast(v[k][e], mL);
+                s += v[k][e];
+            }
+    }
+    s = wave_sum(s);
+    if constexpr (G > 1) {
+        if (threadIdx.x % kWave == 0)
+            red_sum[grp][wig] = s;
+        __syncthreads();
+        s = red_sum[grp][0];
+#pragma unroll
+        for (int g = 1; g < G; ++g)
+            s += red_sum[grp][g];
+    }
+
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            v[k][e] *= inv;
+    store_row<T, E, V, L>(yr, li, vend, rs, v);
+}
+
+template <typename T, int G, int V, int W>
+static hipError_t softmax_tile_run(const RowProblem &p)
+{
+    constexpr int RG = W / G;
+    const int64_t blocks = (p.M + RG - 1) / RG;
+    return launch(softmax_tile<T, G, V, W>, dim3(static_cast<unsigned>(blocks)), dim3(W * kWave),
+                  p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), p.M, p.N, p.ldx,
+                  p.ldy);
+}
+
+template <typename T, int G, int V, int W>
+constexpr TileVariant tile()
+{
+    return TileVariant{G, V, W, 1, G * V * kWave * Elem<T>::kVec, &softmax_tile_run<T, G, V, W>};
+}
+
+// Preference order: the dispatcher takes the first entry whose max_n covers
+// N.  Entries after the largest one are alternatives reachable by index.
+static const TileVariant kSoftmaxF32[] = {
+    tile<float, 1, 1, 4>(),   // N <= 256
+    tile<float, 1, 2, 4>(),   // N <= 512
+    tile<float, 1, 3, 4>(),   // N <= 768
+    tile<float, 1, 4, 4>(),   // N <= 1024
+    tile<float, 1, 8, 4>(),   // N <= 2048
+    tile<float, 4, 4, 4>(),   // N <= 4096
+    tile<float, 8, 4, 8>(),   // N <= 8192
+    tile<float, 16, 4, 16>(), // N <= 16384
+    tile<float, 2, 2, 4>(),   // alternatives
+    tile<float, 4, 1, 4>(),
+    tile<float, 2, 8, 4>(),
+};
+
+static const TileVariant kSoftmaxBF16[] = {
+    tile<bf16_t, 1, 1, 4>(),   // N <= 512
+    tile<bf16_t, 1, 2, 4>(),   // N <= 1024
+    tile<bf16_t, 1, 4, 4>(),   // N <= 2048
+    tile<bf16_t, 4, 2, 4>(),   // N <= 4096
+    tile<bf16_t, 8, 2, 8>(),   // N <= 8192
+    tile<bf16_t, 16, 2, 16>(), // N <= 16384
+    tile<bf16_t, 16, 4, 16>(), // N <= 32768
+    tile<bf16_t, 1, 8, 4>(),   // alternatives
+    tile<bf16_t, 2, 4, 4>(),
+    tile<bf16_t, 8, 1, 8>(),
+    tile<bf16_t, 2, 4, 8>(),
+};
+
+const TileVariant *softmax_variants(rk_dtype dtype, int *count)
+{
+    if (dtype == RK_F32) {
+        *count = static_cast<int>(sizeof(kSoftmaxF32) / sizeof(kSoftmaxF32[0]));
+        return kSoftmaxF32;
+    }
+    *count = static_cast<int>(sizeof(kSoftmaxBF16) / sizeof(kSoftmaxBF16[0]));
+    return kSoftmaxBF16;
+}
+
+}  // namespace rk

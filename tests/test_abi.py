@@ -1,0 +1,170 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects invalid arguments before any HIP call.  (Nothing here
+launches a kernel.)"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import row_wise_amd as rk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+F32, BF16 = rk.RK_F32, rk.RK_BF16
+A = 0x100000  # fake, 16-byte aligned device addresses: never dereferenced
+B = 0x900000
+INT32_MAX = 2**31 - 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rk.load()
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(rk_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert {"rk_softmax", "rk_online_softmax", "rk_layernorm_gelu"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_only_rk_symbols_exported():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", rk.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    text_syms = [l.split()[-1] for l in out.splitlines() if " T " in l]
+    assert text_syms and all(s.startswith("rk_") for s in text_syms), text_syms
+    assert set(text_syms) == set(declared_symbols())
+
+
+def test_status_strings_and_version(lib):
+    assert rk.rk_version() == 100
+    assert rk.rk_status_string(0) == "ok"
+    assert rk.rk_status_string(INVALID) == "invalid argument"
+    assert rk.rk_status_string(WORKSPACE) == "workspace missing or too small"
+    assert rk.rk_status_string(99) == "unknown status"
+
+
+def sm(lib, x=A, y=B, M=4, N=8, ldx=None, ldy=None, dt=F32):
+    return lib.rk_softmax(x, y, M, N, N if ldx is None else ldx, N if ldy is None else ldy, dt,
+                          None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dt=2), dict(dt=-1), dict(M=-1), dict(N=0), dict(N=-3), dict(N=INT32_MAX + 1,
+                                                                    ldx=2**32, ldy=2**32),
+    dict(ldx=7), dict(ldy=7), dict(x=None), dict(y=None), dict(x=A + 2), dict(y=B + 1, dt=BF16),
+    dict(y=A + 16), dict(x=A, y=A, ldx=8, ldy=16), dict(M=2**62, ldx=2**20, ldy=2**20),
+])
+def test_softmax_rejects(lib, kw):
+    assert sm(lib, **kw) == INVALID
+
+
+def test_rows_beyond_2_30_unsupported(lib):
+    n = 2**30 + 1
+    assert sm(lib, M=1, N=n) == UNSUPPORTED
+
+
+def test_m_zero_is_a_noop(lib):
+    assert sm(lib, x=None, y=None, M=0) == 0
+    assert lib.rk_online_softmax(None, None, 0, 8, 8, 8, F32, 64, None, 0, None) == 0
+    assert lib.rk_layernorm_gelu(None, None, None, None, 0, 8, 8, 8, 1e-5, F32, None) == 0
+    # but sizes are still checked
+    assert sm(lib, x=None, y=None, M=0, N=0) == INVALID
+
+
+def ln(lib, x=A, w=A + 0x80000, b=A + 0x90000, y=B, M=4, N=8, ldx=8, ldy=8, eps=1e-5, dt=F32):
+    return lib.rk_layernorm_gelu(x, w, b, y, M, N, ldx, ldy, eps, dt, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(eps=0.0), dict(eps=-1e-5), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(w=None), dict(b=None), dict(x=None), dict(w=B + 8), dict(b=B), dict(dt=7), dict(N=0),
+    dict(ldy=4), dict(w=A + 0x80001), dict(y=A + 64),
+])
+def test_layernorm_rejects(lib, kw):
+    assert ln(lib, **kw) == INVALID
+
+
+def online(lib, x=A, y=B, M=4, N=4096, S=64, ws=A + 0x400000, wb=4 * 64 * 8, dt=F32):
+    return lib.rk_online_softmax(x, y, M, N, N, N, dt, S, ws, wb, None)
+
+
+def test_online_rejects(lib):
+    assert online(lib, S=-1) == INVALID
+    assert online(lib, S=65537) == INVALID
+    assert online(lib, ws=None) == WORKSPACE
+    assert online(lib, wb=4 * 64 * 8 - 1) == WORKSPACE
+    assert online(lib, ws=A + 0x400004) == INVALID  # misaligned workspace
+    assert online(lib, ws=A + 16) == INVALID  # workspace overlaps x
+    assert online(lib, N=0) == INVALID
+
+
+def test_workspace_bytes(lib):
+    assert rk.rk_online_softmax_workspace_bytes(64, 262144, 64) == 64 * 64 * 8
+    assert rk.rk_online_softmax_workspace_bytes(64, 262144, 1) == 0
+    assert rk.rk_online_softmax_workspace_bytes(64, 262144, -1) == 0
+    assert rk.rk_online_softmax_workspace_bytes(0, 10, 4) == 0
+    s = rk.rk_online_softmax_auto_splits(64, 262144)
+    assert s >= 2 and rk.rk_online_softmax_workspace_bytes(64, 262144, 0) == 64 * s * 8
+    assert rk.rk_online_softmax_auto_splits(16384, 4096) == 1
+    assert rk.rk_online_softmax_auto_splits(1, 10) == 1
+
+
+def test_probe_copy_rejects(lib):
+    assert lib.rk_probe_copy(A, B, 0, 0, None) == 0
+    assert lib.rk_probe_copy(A + 4, B, 64, 0, None) == INVALID
+    assert lib.rk_probe_copy(A, B, 60, 0, None) == INVALID
+    assert lib.rk_probe_copy(A, A + 32, 64, 0, None) == INVALID
+    assert lib.rk_probe_copy(None, B, 64, 0, None) == INVALID
+
+
+def test_variant_tables():
+    for op in (rk.RK_OP_SOFTMAX, rk.RK_OP_LAYERNORM_GELU):
+        for dt, E, cap in ((F32, 4, 16384), (BF16, 8, 32768)):
+            vs = rk.variants(op, dt)
+            assert vs
+            for v in vs:
+                assert v["max_n"] == v["waves_per_row"] * v["vecs_per_lane"] * 64 * E
+                assert v["waves_per_block"] % v["waves_per_row"] == 0
+                assert v["waves_per_block"] * 64 <= 1024
+            assert max(v["max_n"] for v in vs) == cap
+            for N in (1, 7, 255, 256, 257, 768, 1000, 4096, cap):
+                i = rk.variant_pick(op, dt, N)
+                assert i >= 0 and vs[i]["max_n"] >= N
+            assert rk.variant_pick(op, dt, cap + 1) == -1
+
+
+def test_variant_entry_points_reject(lib):
+    n = lib.rk__variant_count(0, F32)
+    assert lib.rk__variant_count(5, F32) == 0 and lib.rk__variant_count(0, 9) == 0
+    assert lib.rk__variant_info(0, F32, n, None, None, None, None, None) == INVALID
+    assert lib.rk__softmax_variant(n, A, B, 4, 8, 8, 8, F32, None) == INVALID
+    assert lib.rk__softmax_variant(-2, A, B, 4, 8, 8, 8, F32, None) == INVALID
+    assert lib.rk__layernorm_gelu_variant(0, A, A + 0x80000, A + 0x90000, B, 4, 8, 8, 8, 0.0,
+                                          F32, None) == INVALID
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    pkg = os.path.join(ROOT, "row_wise_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if not path.endswith((".py", ".hip", ".cpp", ".h")):
+            continue
+        text = open(path).read()
+        assert "import oracle" not in text and "from oracle" not in text, path
+        assert "liboracle" not in text, path
+        if path.endswith(".py"):
+            for fn in ("torch.softmax", "F.softmax", "layer_norm(", "F.gelu", ".softmax("):
+                assert fn not in text, (path, fn)

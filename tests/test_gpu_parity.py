@@ -1,0 +1,283 @@
+"""Parity of the HIP path with the CPU oracle, element by element, on seeded
+inputs.  Every call goes through the C ABI (ctypes binding in row_wise_amd).
+
+Tolerances (tests/tolerance.py): softmax family max relative error 1e-5 for
+fp32, 1e-2 for bf16 storage; LayerNorm + GeLU relative error with the
+denominator floored at 1, same bounds.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import row_wise_amd as rk
+import rowgen
+from tolerance import TOL, rel_err_floor1, rel_err_softmax
+
+pytestmark = pytest.mark.gpu
+EPS = float(np.float32(1e-5))
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rk.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def tol_of(dtype):
+    return TOL["f32"] if dtype == torch.float32 else TOL["bf16"]
+
+
+def key(dtype):
+    return "f32" if dtype == torch.float32 else "bf16"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------- the workloads
+
+
+def test_tiny_f32_64x768():
+    d = rowgen.make("tiny_f32_64x768")
+    x = d["x"].to(DEV)
+    y = rk.rk_softmax(x)
+    assert rel_err_softmax(y, oracle.softmax(d["x"])) <= TOL["f32"]
+    z = rk.rk_layernorm_gelu(x, d["w"].to(DEV), d["b"].to(DEV), EPS)
+    assert rel_err_floor1(z, oracle.layernorm_gelu(d["x"], d["w"], d["b"], EPS)) <= TOL["f32"]
+
+
+def test_ln_gelu_f32_4096x768():
+    d = rowgen.make("ln_gelu_f32_4096x768")
+    y = rk.rk_layernorm_gelu(d["x"].to(DEV), d["w"].to(DEV), d["b"].to(DEV), EPS)
+    ref = oracle.layernorm_gelu(d["x"], d["w"], d["b"], EPS)
+    err = rel_err_floor1(y, ref)
+    say(f"ln_gelu_f32_4096x768 err={err:.3e}")
+    assert err <= TOL["f32"]
+
+
+def test_softmax_f32_8192x1000():
+    d = rowgen.make("softmax_f32_8192x1000")
+    x = d["x_softmax"]
+    y = rk.rk_softmax(x.to(DEV))
+    ref = oracle.softmax(x)
+    err = rel_err_softmax(y, ref)
+    say(f"softmax_f32_8192x1000 err={err:.3e}")
+    assert err <= TOL["f32"]
+    # the +1000 rows are as accurate as the others
+    assert rel_err_softmax(y[::16], ref[::16]) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("splits", [1, 64, 0])
+def test_online_f32_64x262144(splits):
+    d = rowgen.make("online_f32_64x262144")
+    x = d["x_softmax"]
+    y = rk.rk_online_softmax(x.to(DEV), num_splits=splits)
+    err = rel_err_softmax(y, oracle.softmax(x))
+    say(f"online_f32_64x262144 S={splits} err={err:.3e}")
+    assert err <= TOL["f32"]
+
+
+def test_softmax_long_rows_route_to_streaming():
+    d = rowgen.make("online_f32_64x262144", rows=8)
+    x = d["x_softmax"]
+    y = rk.rk_softmax(x.to(DEV))
+    assert rel_err_softmax(y, oracle.softmax(x)) <= TOL["f32"]
+
+
+def test_bf16_16384x4096_layernorm_gelu():
+    d = rowgen.make("bf16_16384x4096")
+    y = rk.rk_layernorm_gelu(d["x"].to(DEV), d["w"].to(DEV), d["b"].to(DEV), EPS)
+    ref = oracle.layernorm_gelu(d["x"], d["w"], d["b"], EPS)
+    err = rel_err_floor1(y, ref)
+    say(f"bf16 layernorm_gelu err={err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_bf16_16384x4096_softmax():
+    d = rowgen.make("bf16_16384x4096")
+    xs = d["x_softmax"]
+    y = rk.rk_softmax(xs.to(DEV))
+    ref = oracle.softmax(xs)
+    err = rel_err_softmax(y, ref)
+    say(f"bf16 softmax err={err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+# ------------------------------------------------------- every tile variant
+
+
+def _variant_cases(op):
+    cases = []
+    for dtype, code in ((torch.float32, rk.RK_F32), (torch.bfloat16, rk.RK_BF16)):
+        for v in rk.variants(op, code):
+            cap = v["max_n"]
+            E = 4 if code == rk.RK_F32 else 8
+            for N in sorted({cap, cap - E, cap - 3 * E - 2, max(1, cap // 3 + 1)}):
+                cases.append((dtype, v["index"], N))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,index,N", _variant_cases(rk.RK_OP_SOFTMAX),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_softmax_variant(dtype, index, N):
+    M = 37
+    E = 4 if dtype == torch.float32 else 8
+    ld = (N + E - 1) // E * E  # 16-byte aligned pitch (N % E != 0 exercises the tail)
+    base = rowgen.randn(M, ld, seed=N * 31 + index, scale=4.0, dtype=dtype)
+    x = base.to(DEV)[:, :N]
+    y = rk.rk__softmax_variant(index, x, out=torch.empty(M, ld, dtype=dtype, device=DEV)[:, :N])
+    assert rel_err_softmax(y, oracle.softmax(base[:, :N])) <= tol_of(dtype)
+
+
+@pytest.mark.parametrize("dtype,index,N", _variant_cases(rk.RK_OP_LAYERNORM_GELU),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_layernorm_gelu_variant(dtype, index, N):
+    M = 37
+    E = 4 if dtype == torch.float32 else 8
+    ld = (N + E - 1) // E * E
+    g = torch.Generator().manual_seed(N * 17 + index)
+    base = torch.randn(M, ld, generator=g).to(dtype)
+    w, b = rowgen.ln_params(N, g, dtype)
+    x = base.to(DEV)[:, :N]
+    y = rk.rk__layernorm_gelu_variant(index, x, w.to(DEV), b.to(DEV), EPS,
+                                      out=torch.empty(M, ld, dtype=dtype, device=DEV)[:, :N])
+    assert rel_err_floor1(y, oracle.layernorm_gelu(base[:, :N], w, b, EPS)) <= tol_of(dtype)
+
+
+# ------------------------------------------------------ shapes and layouts
+
+EDGE_N = [1, 2, 3, 63, 64, 65, 767, 769, 1000, 1025, 4095, 4097, 16384, 16385, 40000]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+@pytest.mark.parametrize("N", EDGE_N)
+def test_edge_shapes(dtype, N):
+    tol = tol_of(dtype)
+    for M in (1, 257):
+        say(f"edge {key(dtype)} M={M} N={N}")
+        x = rowgen.randn(M, N, seed=M * 7 + N, scale=3.0, dtype=dtype)
+        xd = x.to(DEV)
+        ref = oracle.softmax(x)
+        assert rel_err_softmax(rk.rk_softmax(xd), ref) <= tol
+        for S in (1, 3, 0):
+            assert rel_err_softmax(rk.rk_online_softmax(xd, num_splits=S), ref) <= tol, S
+        g = torch.Generator().manual_seed(N)
+        w, b = rowgen.ln_params(N, g, dtype)
+        y = rk.rk_layernorm_gelu(xd, w.to(DEV), b.to(DEV), EPS)
+        assert rel_err_floor1(y, oracle.layernorm_gelu(x, w, b, EPS)) <= tol
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+def test_padded_pitch_leaves_gaps_untouched(dtype):
+    M, N, ldx, ldy = 33, 1000, 1040, 1064
+    canary = -12345.0
+    xb = rowgen.randn(M, ldx, seed=5, scale=2.0, dtype=dtype)
+    x = xb.to(DEV)[:, :N]
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(5), dtype)
+    checks = [
+        ("softmax", lambda o: rk.rk_softmax(x, out=o), oracle.softmax(xb[:, :N]),
+         rel_err_softmax),
+        ("online S=4", lambda o: rk.rk_online_softmax(x, num_splits=4, out=o),
+         oracle.softmax(xb[:, :N]), rel_err_softmax),
+        ("layernorm_gelu", lambda o: rk.rk_layernorm_gelu(x, w.to(DEV), b.to(DEV), EPS, out=o),
+         oracle.layernorm_gelu(xb[:, :N], w, b, EPS), rel_err_floor1),
+    ]
+    for name, fn, ref, measure in checks:
+        buf = torch.full((M + 2, ldy), canary, dtype=dtype, device=DEV)
+        out = buf[1:M + 1, :N]
+        fn(out)
+        assert measure(out, ref) <= tol_of(dtype), name
+        host = buf.cpu().float()
+        assert torch.all(host[0] == canary) and torch.all(host[M + 1] == canary), name
+        assert torch.all(host[1:M + 1, N:] == canary), name
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+def test_misaligned_base_takes_elementwise_path(dtype):
+    M, N = 19, 1000
+    flat = rowgen.randn(1, M * N + 1, seed=9, scale=3.0, dtype=dtype)[0]
+    xd = flat.to(DEV)[1:].view(M, N)  # one element off 16-byte alignment
+    x = flat[1:].view(M, N)
+    ref = oracle.softmax(x)
+    assert rel_err_softmax(rk.rk_softmax(xd), ref) <= tol_of(dtype)
+    assert rel_err_softmax(rk.rk_online_softmax(xd, num_splits=5), ref) <= tol_of(dtype)
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(9), dtype)
+    y = rk.rk_layernorm_gelu(xd, w.to(DEV), b.to(DEV), EPS)
+    assert rel_err_floor1(y, oracle.layernorm_gelu(x, w, b, EPS)) <= tol_of(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+def test_generic_paths_forced(dtype):
+    M, N = 65, 4099
+    x = rowgen.randn(M, N, seed=11, scale=3.0, dtype=dtype)
+    xd = x.to(DEV)
+    assert rel_err_softmax(rk.rk__softmax_variant(-1, xd), oracle.softmax(x)) <= tol_of(dtype)
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(11), dtype)
+    y = rk.rk__layernorm_gelu_variant(-1, xd, w.to(DEV), b.to(DEV), EPS)
+    assert rel_err_floor1(y, oracle.layernorm_gelu(x, w, b, EPS)) <= tol_of(dtype)
+
+
+def test_in_place():
+    M, N = 64, 768
+    d = rowgen.make("tiny_f32_64x768")
+    x = d["x"].to(DEV).clone()
+    rk.rk_softmax(x, out=x)
+    assert rel_err_softmax(x, oracle.softmax(d["x"])) <= TOL["f32"]
+    x = d["x"].to(DEV).clone()
+    rk.rk_layernorm_gelu(x, d["w"].to(DEV), d["b"].to(DEV), EPS, out=x)
+    assert rel_err_floor1(x, oracle.layernorm_gelu(d["x"], d["w"], d["b"], EPS)) <= TOL["f32"]
+    x = rowgen.randn(8, 50000, seed=3).to(DEV)
+    ref = oracle.softmax(x.cpu())
+    rk.rk_online_softmax(x, num_splits=1, out=x)
+    assert rel_err_softmax(x, ref) <= TOL["f32"]
+
+
+def test_deterministic():
+    d = rowgen.make("bf16_16384x4096", rows=2048)
+    x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
+    for fn in (lambda: rk.rk_softmax(x), lambda: rk.rk_layernorm_gelu(x, w, b, EPS),
+               lambda: rk.rk_online_softmax(x, num_splits=8)):
+        a, c = fn(), fn()
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+def test_infinities(dtype):
+    M, N = 6, 3000
+    x = rowgen.randn(M, N, seed=13, dtype=dtype)
+    x[0, ::7] = -math.inf  # some -inf: those outputs are exactly 0
+    x[1, :] = -math.inf  # all -inf: NaN (the definition's IEEE value)
+    x[2, 5] = math.inf  # +inf: NaN
+    ref = oracle.softmax(x)
+    for y in (rk.rk_softmax(x.to(DEV)), rk.rk_online_softmax(x.to(DEV), num_splits=1),
+              rk.rk_online_softmax(x.to(DEV), num_splits=4)):
+        yc = y.cpu().double().numpy()
+        assert np.all(yc[0, ::7] == 0.0)
+        assert rel_err_softmax(yc[[0, 3, 4, 5]], ref[[0, 3, 4, 5]]) <= tol_of(dtype)
+        assert np.all(np.isnan(yc[1])) and np.all(np.isnan(ref[1]))
+        assert np.all(np.isnan(yc[2])) and np.all(np.isnan(ref[2]))
+
+
+def test_empty_rows_is_noop():
+    x = torch.empty(0, 128, device=DEV)
+    assert rk.rk_softmax(x).shape == (0, 128)
+    assert rk.rk_online_softmax(x, num_splits=4).shape == (0, 128)
+    w = torch.ones(128, device=DEV)
+    assert rk.rk_layernorm_gelu(x, w, w, EPS).shape == (0, 128)
+
+
+def test_probe_copy():
+    src = torch.randn(1 << 20, device=DEV)
+    dst = torch.empty_like(src)
+    rk.rk_probe_copy(src, dst)
+    assert torch.equal(src, dst)
+    dst.zero_()
+    rk.rk_probe_copy(src, dst, max_workgroups=64)
+    assert torch.equal(src, dst)
