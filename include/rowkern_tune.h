@@ -19,11 +19,12 @@ extern "C" {
 #endif
 
 /*
- * Copy `bytes` bytes from src to dst with 16-byte vector loads and stores,
- * one HBM read and one write per byte, at most `max_workgroups` workgroups of
- * 256 threads (<= 0: enough to cover the copy once, capped at 65536) striding
- * over the buffer.  src and dst must be 16-byte aligned, bytes a multiple of
- * 16, and the ranges disjoint; otherwise RK_ERR_INVALID_ARG.
+ * Copy `bytes` bytes from src to dst with 16-byte non-temporal vector loads
+ * and stores (four per thread per step), one HBM read and one write per byte,
+ * at most `max_workgroups` workgroups of 256 threads (<= 0: enough to cover
+ * the copy once, capped at 65536) striding over the buffer.  src and dst must
+ * be 16-byte aligned, bytes a multiple of 16, and the ranges disjoint;
+ * otherwise RK_ERR_INVALID_ARG.
  */
 rk_status rk_probe_copy(const void *src, void *dst, size_t bytes, int32_t max_workgroups,
                         hipStream_t stream);

@@ -7,8 +7,8 @@
 //    the row's value, then one permlane32 swap and two readlanes combine the
 //    four rows.  Every lane ends with the same bits, and the order of
 //    operations is fixed, so results are deterministic run to run.
-//  * exp(x - m) in two precisions: a compensated form for fp32 I/O (error a
-//    few ulp whatever |x - m|), and a single fma + hardware exp2 for bf16 I/O.
+//  * exp(x - m) in two precisions: a compensated form for fp32 I/O, and a
+//    single fma + hardware exp2 for bf16 I/O.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -86,22 +86,22 @@ __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, SumOp
 
 // ----------------------------------------------------------------- exp
 
-// exp(x - m) for fp32 I/O.  The subtraction's rounding error is recovered
-// exactly (two-sum), the product with log2(e) is split into a head and a
-// tail (fma), and the tail corrects the hardware exp2 of the head to first
-// order.  Accuracy: a few ulp for any x - m, not growing with |x - m|.
+// exp(x - m) for fp32 I/O.  d = x - m is formed in fp32 (exact when x and m
+// are within a factor of two, e.g. rows offset far from zero); the product
+// d log2(e) is split into a head t and a tail (fma), and the tail corrects the
+// hardware exp2 of the head to first order.  Relative error about
+// |d| * 6e-8 from the rounding of d (<= 2e-6 for |d| <= 30) plus an ulp or
+// two, instead of |d| * 1.7e-7 for exp2(d * log2e) alone.
 __device__ __forceinline__ float exp_shifted_accurate(float x, float m)
 {
     constexpr float kL = 1.44269502162933349609375f;      // fp32(log2 e)
-    constexpr float kLlo = 1.9259629911266175e-08f;      // log2 e - kL
+    constexpr float kLlo = 1.9259629911266175e-08f;       // log2 e - kL
     constexpr float kLn2 = 0.693147180559945309f;
-    float d = x - m;
-    float bp = d - x;
-    float dl = (x - (d - bp)) + (-m - bp);  // d + dl == x - m exactly
-    float t = d * kL;
-    float tl = fmaf(d, kL, -t) + fmaf(dl, kL, d * kLlo);
-    float e = __builtin_amdgcn_exp2f(t);
-    float r = fmaf(e, tl * kLn2, e);
+    const float d = x - m;
+    const float t = d * kL;
+    const float tl = fmaf(d, kL, -t) + d * kLlo;
+    const float e = __builtin_amdgcn_exp2f(t);
+    const float r = fmaf(e, tl * kLn2, e);
     // x = -inf (padding) or an underflowed exp: the tail may be inf/NaN there
     return e == 0.0f ? 0.0f : r;
 }
@@ -210,22 +210,50 @@ struct Elem<bf16_t> {
     }
 };
 
+// Cache policy of a memory stream.  Row data is touched once per pass, so
+// its loads and stores are marked non-temporal ("nt"): they do not displace
+// reused lines (weight, bias, partial states) and leave no dirty lines in L2
+// to be written back when the kernel ends.
+enum CachePolicy { kCached = 0, kStreaming = 1 };
+
+template <int CP, typename R>
+__device__ __forceinline__ R ld(const R *p)
+{
+    if constexpr (CP == kStreaming)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <int CP, typename R>
+__device__ __forceinline__ void st(R *p, R v)
+{
+    if constexpr (CP == kStreaming)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // Store E consecutive elements (E is the 16-byte width or 1).
-template <typename T, int E>
+template <typename T, int E, int CP>
 __device__ __forceinline__ void store_vec(T *__restrict__ p, const float (&v)[E])
 {
     if constexpr (E == 1) {
-        *p = Elem<T>::from_f32(v[0]);
+        st<CP>(p, Elem<T>::from_f32(v[0]));
     } else if constexpr (sizeof(T) == 4) {
-        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        const f32x4_t q = {v[0], v[1], v[2], v[3]};
+        st<CP>(reinterpret_cast<f32x4_t *>(p), q);
     } else {
-        uint32_t w[4];
+        u32x4_t q;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x2_t f = {v[2 * i], v[2 * i + 1]};
-            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+            q[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
         }
-        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+        st<CP>(reinterpret_cast<u32x4_t *>(p), q);
     }
 }
 
@@ -244,7 +272,7 @@ template <typename T, int E>
 struct RawVec;
 template <>
 struct RawVec<float, 4> {
-    typedef float4 type;
+    typedef f32x4_t type;
 };
 template <>
 struct RawVec<float, 1> {
@@ -252,7 +280,7 @@ struct RawVec<float, 1> {
 };
 template <>
 struct RawVec<bf16_t, 8> {
-    typedef uint4 type;
+    typedef u32x4_t type;
 };
 template <>
 struct RawVec<bf16_t, 1> {
@@ -279,50 +307,97 @@ __device__ __forceinline__ void unpack(const typename RawVec<T, E>::type &q, flo
     }
 }
 
-// Load V vectors of a row: vector k of this lane is vi = vi0 + k * STRIDE.
-// Vectors at or beyond `vend` (<= rs.count()) are padded with `pad`; a
-// partial last vector loads its `tail` elements and pads the rest.  All
-// full-vector loads are issued before any result is used (no wait between
-// them); the partial vector is handled behind a branch that is uniform over
-// the grid, so rows whose N is a multiple of E never enter it.
-template <typename T, int E, int V, int STRIDE>
-__device__ __forceinline__ void load_row(const T *__restrict__ row, int vi0, int vend,
-                                         RowSplit<E> rs, float pad, float (&v)[V][E])
+// A raw vector whose every element is `pad` (pad must be exact in T).
+template <typename T, int E>
+__device__ __forceinline__ typename RawVec<T, E>::type raw_splat(float pad)
 {
-    typedef typename RawVec<T, E>::type R;
-    const int lim = vend < rs.nfull ? vend : rs.nfull;
-    R q[V];
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        q[k] = R{};
-        const int vi = vi0 + k * STRIDE;
-        if (vi < lim)
-            q[k] = *reinterpret_cast<const R *>(row + static_cast<int64_t>(vi) * E);
-    }
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        unpack<T, E>(q[k], v[k]);
-        const bool full = vi0 + k * STRIDE < lim;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            v[k][e] = full ? v[k][e] : pad;
-    }
-    if (rs.tail != 0 && rs.nfull < vend) {
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const int vi = vi0 + k * STRIDE;
-            if (vi == rs.nfull) {
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (e < rs.tail)
-                        v[k][e] = Elem<T>::to_f32(row[static_cast<int64_t>(vi) * E + e]);
-            }
-        }
+    if constexpr (E == 1) {
+        return Elem<T>::from_f32(pad);
+    } else if constexpr (sizeof(T) == 4) {
+        return f32x4_t{pad, pad, pad, pad};
+    } else {
+        const uint32_t h = Elem<T>::from_f32(pad);
+        const uint32_t w = h | (h << 16);
+        return u32x4_t{w, w, w, w};
     }
 }
 
+// V vectors of a row in flight: vector k of this lane is vi = vi0 + k * STRIDE.
+// issue() starts the loads of the complete vectors below `vend` (<= the row's
+// vector count) and leaves the others holding the pad value; it never waits.
+// finish() unpacks to fp32 and fills in a partial last vector element by
+// element, behind a branch that is uniform over the grid (rows whose N is a
+// multiple of E never take it).  Issuing every row's loads before finishing
+// any of them keeps all of them in flight at once.
+template <typename T, int E, int V, int STRIDE, int CP = kStreaming>
+struct RowLoad {
+    typedef typename RawVec<T, E>::type R;
+    R q[V];
+    float tl[E];  // elements of a partial last vector, if this lane holds it
+    int vi0, vend;
+
+    __device__ __forceinline__ bool has_tail(RowSplit<E> rs) const
+    {
+        return rs.tail != 0 && rs.nfull < vend;
+    }
+
+    __device__ __forceinline__ void issue(const T *__restrict__ row, int vi0_, int vend_,
+                                          RowSplit<E> rs, float pad)
+    {
+        vi0 = vi0_;
+        vend = vend_;
+        const int lim = vend < rs.nfull ? vend : rs.nfull;
+        const R p = raw_splat<T, E>(pad);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            q[k] = p;
+            const int vi = vi0 + k * STRIDE;
+            if (vi < lim)
+                q[k] = ld<CP>(reinterpret_cast<const R *>(row + static_cast<int64_t>(vi) * E));
+        }
+        // The partial vector is loaded element by element into registers of
+        // its own, so that waiting for the full vectors never waits for it.
+        if (has_tail(rs)) {
+            const int off = rs.nfull - vi0;
+            const bool mine = off >= 0 && off % STRIDE == 0 && off / STRIDE < V;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                tl[e] = pad;
+                if (mine && e < rs.tail)
+                    tl[e] = Elem<T>::to_f32(row[static_cast<int64_t>(rs.nfull) * E + e]);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void finish(float (&v)[V][E], RowSplit<E> rs) const
+    {
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            unpack<T, E>(q[k], v[k]);
+        if (has_tail(rs)) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                if (vi0 + k * STRIDE == rs.nfull) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        v[k][e] = tl[e];
+                }
+        }
+    }
+};
+
+// issue + finish in one step (for rows that are used right away).
+template <typename T, int E, int V, int STRIDE, int CP = kStreaming>
+__device__ __forceinline__ void load_row(const T *__restrict__ row, int vi0, int vend,
+                                         RowSplit<E> rs, float pad, float (&v)[V][E])
+{
+    RowLoad<T, E, V, STRIDE, CP> l;
+    l.issue(row, vi0, vend, rs, pad);
+    l.finish(v, rs);
+}
+
 // Store the vectors load_row covered (those below `vend`).
-template <typename T, int E, int V, int STRIDE>
+template <typename T, int E, int V, int STRIDE, int CP = kStreaming>
 __device__ __forceinline__ void store_row(T *__restrict__ row, int vi0, int vend, RowSplit<E> rs,
                                           const float (&v)[V][E])
 {
@@ -331,7 +406,7 @@ __device__ __forceinline__ void store_row(T *__restrict__ row, int vi0, int vend
     for (int k = 0; k < V; ++k) {
         const int vi = vi0 + k * STRIDE;
         if (vi < lim)
-            store_vec<T, E>(row + static_cast<int64_t>(vi) * E, v[k]);
+            store_vec<T, E, CP>(row + static_cast<int64_t>(vi) * E, v[k]);
     }
     if (rs.tail != 0 && rs.nfull < vend) {
 #pragma unroll

@@ -38,24 +38,43 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     const int wig = wave % G;
     const int li = wig * kWave + static_cast<int>(threadIdx.x % kWave);
     const RowSplit<E> rs(N);
+    const int nv = rs.count();
     const float n_f = static_cast<float>(N);
 
-    float wv[V][E], bv[V][E];
-    load_row<T, E, V, L>(w, li, rs.count(), rs, 0.0f, wv);
-    load_row<T, E, V, L>(b, li, rs.count(), rs, 0.0f, bv);
+    // Row r of this row group, its input / output rows, and whether it exists.
+    auto row_of = [&](int r) { return (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp; };
 
+    // Loads in flight before any is waited for: the first row, then weight
+    // and bias (shared by all R rows).  Each later row is issued while the
+    // previous one is reduced.
+    RowLoad<T, E, V, L> xl;
+    {
+        const int64_t row = row_of(0);
+        const bool ok = row < M;
+        xl.issue(x + (ok ? row : 0) * ldx, li, ok ? nv : 0, rs, 0.0f);
+    }
+    RowLoad<T, E, V, L, kCached> wl, bl;
+    wl.issue(w, li, nv, rs, 0.0f);
+    bl.issue(b, li, nv, rs, 0.0f);
+    float wv[V][E], bv[V][E];
+
+#pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int64_t row = (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp;
+        const int64_t row = row_of(r);
         const bool row_ok = row < M;
         const int64_t rr = row_ok ? row : 0;
         const T *xr = x + rr * ldx;
         T *yr = y + rr * ldy;
+        const int vend = row_ok ? nv : 0;
         const int buf = r & 1;
 
-        const int vend = row_ok ? rs.count() : 0;
-
         float v[V][E];
-        load_row<T, E, V, L>(xr, li, vend, rs, 0.0f, v);
+        xl.finish(v, rs);
+        if (r + 1 < R) {
+            const int64_t nrow = row_of(r + 1);
+            const bool nok = nrow < M;
+            xl.issue(x + (nok ? nrow : 0) * ldx, li, nok ? nv : 0, rs, 0.0f);
+        }
 
         float s = 0.0f;
 #pragma unroll
@@ -101,6 +120,10 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         }
         const float rstd = 1.0f / sqrtf(q / n_f + eps);
 
+        if (r == 0) {
+            wl.finish(wv, rs);
+            bl.finish(bv, rs);
+        }
 #pragma unroll
         for (int k = 0; k < V; ++k)
 #pragma unroll
@@ -217,12 +240,13 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
     float q = 0.0f;
     for (int base = 0; base < nv; base += NT * U) {
         float v[U][E];
-        load_row<T, E, U, NT>(xr, base + tid, nv, rs, mean, v);  // padding centres to 0
+        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const float d = v[u][e] - mean;
+                const int col = (base + tid + u * NT) * E + e;  // < N: a true column
+                const float d = col < N ? v[u][e] - mean : 0.0f;
                 q = fmaf(d, d, q);
             }
     }
@@ -231,8 +255,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
     for (int base = 0; base < nv; base += NT * U) {
         float v[U][E], wv[U][E], bv[U][E];
         load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
-        load_row<T, E, U, NT>(w, base + tid, nv, rs, 0.0f, wv);
-        load_row<T, E, U, NT>(b, base + tid, nv, rs, 0.0f, bv);
+        load_row<T, E, U, NT, kCached>(w, base + tid, nv, rs, 0.0f, wv);
+        load_row<T, E, U, NT, kCached>(b, base + tid, nv, rs, 0.0f, bv);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll

@@ -83,11 +83,21 @@ __device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xr, Row
                                                    int vbeg, int vend)
 {
     constexpr int NT = W * kWave;
+    const int tid = static_cast<int>(threadIdx.x);
     SoftmaxState st{-INFINITY, 0.0f};
+    // software pipeline: the next step's loads are in flight while this
+    // step's values are folded
+    RowLoad<T, E, U, NT> cur;
+    cur.issue(xr, vbeg + tid, vend, rs, -INFINITY);
     for (int base = vbeg; base < vend; base += NT * U) {
+        RowLoad<T, E, U, NT> nxt;
+        const bool more = base + NT * U < vend;
+        if (more)
+            nxt.issue(xr, base + NT * U + tid, vend, rs, -INFINITY);
         float v[U][E];
-        load_row<T, E, U, NT>(xr, base + static_cast<int>(threadIdx.x), vend, rs, -INFINITY, v);
+        cur.finish(v, rs);
         st = fold<T, U, E>(st, v);
+        cur = nxt;
     }
     return st;
 }
@@ -98,18 +108,25 @@ __device__ __forceinline__ void write_range(const T *__restrict__ xr, T *__restr
                                             RowSplit<E> rs, int vbeg, int vend, SoftmaxState st)
 {
     constexpr int NT = W * kWave;
+    const int tid = static_cast<int>(threadIdx.x);
     const float inv = 1.0f / st.d;
     const float mL = st.m * 1.4426950408889634f;
+    RowLoad<T, E, U, NT> cur;
+    cur.issue(xr, vbeg + tid, vend, rs, -INFINITY);
     for (int base = vbeg; base < vend; base += NT * U) {
-        const int vi0 = base + static_cast<int>(threadIdx.x);
+        RowLoad<T, E, U, NT> nxt;
+        const bool more = base + NT * U < vend;
+        if (more)
+            nxt.issue(xr, base + NT * U + tid, vend, rs, -INFINITY);
         float v[U][E];
-        load_row<T, E, U, NT>(xr, vi0, vend, rs, -INFINITY, v);
+        cur.finish(v, rs);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[u][e] = softmax_exp<T>(v[u][e], st.m, mL) * inv;
-        store_row<T, E, U, NT>(yr, vi0, vend, rs, v);
+        store_row<T, E, U, NT>(yr, base + tid, vend, rs, v);
+        cur = nxt;
     }
 }
 
