@@ -38,20 +38,23 @@ int32_t rk__variant_count(rk_op op, rk_dtype dtype);
 /*
  * Geometry of tile variant `index`: waves cooperating on one row, 16-byte
  * vectors held per lane, waves per workgroup, rows each row-group handles in
- * sequence, and the largest N it accepts.  Any output pointer may be NULL.
+ * sequence, the largest N it accepts, and whether it is compiled for
+ * N == max_n only (every register slot a column: no masks, no padding).  Any
+ * output pointer may be NULL.
  */
 rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index, int32_t *waves_per_row,
                            int32_t *vecs_per_lane, int32_t *waves_per_block,
-                           int32_t *rows_per_group, int64_t *max_n);
+                           int32_t *rows_per_group, int64_t *max_n, int32_t *exact);
 
-/* Index of the variant rk_softmax / rk_layernorm_gelu pick for N (-1 when
- * N is beyond every tile variant and the generic path runs). */
+/* Index of the variant rk_softmax / rk_layernorm_gelu pick for N: the first
+ * exact variant with max_n == N, else the first general one that holds N
+ * (-1 when N is beyond every tile variant and the generic path runs). */
 int32_t rk__variant_pick(rk_op op, rk_dtype dtype, int64_t N);
 
 /*
  * rk_softmax / rk_layernorm_gelu forced onto one path: variant `index`
- * (RK_ERR_UNSUPPORTED if the data is not 16-byte aligned or N exceeds its
- * max_n), or index -1 for the generic path (streaming online kernel for
+ * (RK_ERR_UNSUPPORTED if the data is not 16-byte aligned or the variant does
+ * not accept N), or index -1 for the generic path (streaming online kernel for
  * softmax, three-pass looping kernel for LayerNorm+GeLU), which takes any
  * input.  Arguments otherwise as in rowkern.h.
  */

@@ -99,10 +99,14 @@ int pick_variant(rk_op op, rk_dtype dtype, int64_t N)
 {
     int count = 0;
     const TileVariant *v = variants(op, dtype, &count);
-    for (int i = 0; i < count; ++i)
-        if (N <= v[i].max_n)
+    int general = -1;
+    for (int i = 0; i < count; ++i) {
+        if (v[i].exact && N == v[i].max_n)
             return i;
-    return -1;
+        if (!v[i].exact && general < 0 && N <= v[i].max_n)
+            general = i;
+    }
+    return general;
 }
 
 int64_t tile_blocks(const TileVariant &v, int64_t M)
@@ -319,7 +323,7 @@ RK_EXPORT int32_t rk__variant_count(rk_op op, rk_dtype dtype)
 RK_EXPORT rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index,
                                      int32_t *waves_per_row, int32_t *vecs_per_lane,
                                      int32_t *waves_per_block, int32_t *rows_per_group,
-                                     int64_t *max_n)
+                                     int64_t *max_n, int32_t *exact)
 {
     int count = 0;
     const TileVariant *v = variants(op, dtype, &count);
@@ -335,6 +339,8 @@ RK_EXPORT rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index,
         *rows_per_group = v[index].rows_per_group;
     if (max_n)
         *max_n = v[index].max_n;
+    if (exact)
+        *exact = v[index].exact ? 1 : 0;
     return RK_OK;
 }
 
@@ -360,7 +366,7 @@ RK_EXPORT rk_status rk__softmax_variant(int32_t index, const void *x, void *y, i
     const bool aligned = rows_aligned(x, y, ldx, ldy, elem_size(dtype));
     if (index == -1)
         return softmax_generic(p, aligned);
-    if (!aligned || N > v[index].max_n)
+    if (!aligned || !v[index].accepts(N))
         return RK_ERR_UNSUPPORTED;
     return run_tile(v[index], p);
 }
@@ -383,7 +389,7 @@ RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, con
     const bool aligned = layernorm_aligned(p);
     if (index == -1)
         return layernorm_generic(p, aligned);
-    if (!aligned || N > v[index].max_n)
+    if (!aligned || !v[index].accepts(N))
         return RK_ERR_UNSUPPORTED;
     return run_tile(v[index], p);
 }

@@ -32,11 +32,12 @@ enum : int {
     kHalfMirror = 0x141,  // lane i of an 8-lane half-row reads lane 7-i
 };
 
+// All rows and banks enabled and bound_ctrl set: the compiler can fold the
+// lane move into the consuming ALU instruction (v_add_f32_dpp and the like).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
-    int i = __float_as_int(v);
-    return __int_as_float(__builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // op(v[l], v[l ^ 32]) in every lane l.  permlane32_swap exchanges the upper
@@ -341,11 +342,21 @@ struct RowLoad {
         return rs.tail != 0 && rs.nfull < vend;
     }
 
+    // `full` (uniform over the wave) promises that every vector of every
+    // lane is complete and below vend: the loads then need no masks and no
+    // padding.
     __device__ __forceinline__ void issue(const T *__restrict__ row, int vi0_, int vend_,
-                                          RowSplit<E> rs, float pad)
+                                          RowSplit<E> rs, float pad, bool full = false)
     {
         vi0 = vi0_;
-        vend = vend_;
+        vend = full ? 0 : vend_;  // a full load has no partial vector to finish
+        if (full) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                q[k] = ld<CP>(reinterpret_cast<const R *>(
+                    row + static_cast<int64_t>(vi0 + k * STRIDE) * E));
+            return;
+        }
         const int lim = vend < rs.nfull ? vend : rs.nfull;
         const R p = raw_splat<T, E>(pad);
 #pragma unroll
@@ -389,18 +400,26 @@ struct RowLoad {
 // issue + finish in one step (for rows that are used right away).
 template <typename T, int E, int V, int STRIDE, int CP = kStreaming>
 __device__ __forceinline__ void load_row(const T *__restrict__ row, int vi0, int vend,
-                                         RowSplit<E> rs, float pad, float (&v)[V][E])
+                                         RowSplit<E> rs, float pad, float (&v)[V][E],
+                                         bool full = false)
 {
     RowLoad<T, E, V, STRIDE, CP> l;
-    l.issue(row, vi0, vend, rs, pad);
+    l.issue(row, vi0, vend, rs, pad, full);
     l.finish(v, rs);
 }
 
-// Store the vectors load_row covered (those below `vend`).
+// Store the vectors load_row covered (those below `vend`; all of them,
+// without masks, when `full`).
 template <typename T, int E, int V, int STRIDE, int CP = kStreaming>
 __device__ __forceinline__ void store_row(T *__restrict__ row, int vi0, int vend, RowSplit<E> rs,
-                                          const float (&v)[V][E])
+                                          const float (&v)[V][E], bool full = false)
 {
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            store_vec<T, E, CP>(row + static_cast<int64_t>(vi0 + k * STRIDE) * E, v[k]);
+        return;
+    }
     const int lim = vend < rs.nfull ? vend : rs.nfull;
 #pragma unroll
     for (int k = 0; k < V; ++k) {

@@ -55,11 +55,15 @@ struct TileVariant {
     int waves_per_block;  // W: waves per workgroup (W / G row groups)
     int rows_per_group;   // R: rows each row group handles in sequence
     int max_n;            // largest N the variant holds
+    bool exact;           // compiled for N == max_n only: no masks, no padding
     hipError_t (*run)(const RowProblem &);
+
+    bool accepts(int64_t n) const { return exact ? n == max_n : n <= max_n; }
 };
 
 // Variant tables (defined next to the kernels), in order of preference: the
-// dispatcher takes the first variant whose max_n covers N.
+// dispatcher takes the first exact variant with max_n == N, else the first
+// general variant whose max_n covers N.
 const TileVariant *softmax_variants(rk_dtype dtype, int *count);
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count);
 

@@ -19,10 +19,13 @@
 
 namespace rk {
 
-template <typename T, int G, int V, int W, int R>
+// EXACT: compiled for N == V * L * E, i.e. every register slot of a row group
+// is a column of its row: no masks, no padding, no excluded columns.  Rows
+// past M (the last workgroup) then read row 0 and store nothing.
+template <typename T, int G, int V, int W, int R, bool EXACT>
 __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
-    T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float eps)
+    T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
 {
     constexpr int E = Elem<T>::kVec;
     constexpr int RG = W / G;
@@ -39,9 +42,10 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     const int li = wig * kWave + static_cast<int>(threadIdx.x % kWave);
     const RowSplit<E> rs(N);
     const int nv = rs.count();
-    const float n_f = static_cast<float>(N);
+    // every vector slot of a row group holds a complete vector of the row
+    const bool slots_full = EXACT || V * L <= rs.nfull;
 
-    // Row r of this row group, its input / output rows, and whether it exists.
+    // Row r of this row group.
     auto row_of = [&](int r) { return (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp; };
 
     // Loads in flight before any is waited for: the first row, then weight
@@ -51,11 +55,12 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     {
         const int64_t row = row_of(0);
         const bool ok = row < M;
-        xl.issue(x + (ok ? row : 0) * ldx, li, ok ? nv : 0, rs, 0.0f);
+        xl.issue(x + (ok ? row : 0) * ldx, li, ok ? nv : 0, rs, 0.0f,
+                 EXACT || (ok && slots_full));
     }
     RowLoad<T, E, V, L, kCached> wl, bl;
-    wl.issue(w, li, nv, rs, 0.0f);
-    bl.issue(b, li, nv, rs, 0.0f);
+    wl.issue(w, li, nv, rs, 0.0f, slots_full);
+    bl.issue(b, li, nv, rs, 0.0f, slots_full);
     float wv[V][E], bv[V][E];
 
 #pragma unroll
@@ -73,7 +78,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         if (r + 1 < R) {
             const int64_t nrow = row_of(r + 1);
             const bool nok = nrow < M;
-            xl.issue(x + (nok ? nrow : 0) * ldx, li, nok ? nv : 0, rs, 0.0f);
+            xl.issue(x + (nok ? nrow : 0) * ldx, li, nok ? nv : 0, rs, 0.0f,
+                     EXACT || (nok && slots_full));
         }
 
         float s = 0.0f;
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
             for (int g = 1; g < G; ++g)
                 s += red_sum[buf][grp][g];
         }
-        const float mean = s / n_f;
+        const float mean = s * inv_n;
 
         // centre in registers; padded columns are set to 0 so that they add
         // nothing to the variance
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
             const int vi = k * L + li;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const bool valid = vi < rs.nfull || (vi == rs.nfull && e < rs.tail);
+                const bool valid = EXACT || vi < rs.nfull || (vi == rs.nfull && e < rs.tail);
                 const float d = valid ? v[k][e] - mean : 0.0f;
                 v[k][e] = d;
                 q = fmaf(d, d, q);
@@ -118,7 +124,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
             for (int g = 1; g < G; ++g)
                 q += red_var[buf][grp][g];
         }
-        const float rstd = 1.0f / sqrtf(q / n_f + eps);
+        // hardware reciprocal square root (1 ulp), once per row
+        const float rstd = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
 
         if (r == 0) {
             wl.finish(wv, rs);
@@ -129,56 +136,85 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[k][e] = gelu_tanh(fmaf(v[k][e] * rstd, wv[k][e], bv[k][e]));
-        store_row<T, E, V, L>(yr, li, vend, rs, v);
+        if (EXACT) {
+            if (row_ok)
+                store_row<T, E, V, L>(yr, li, vend, rs, v, true);
+        } else {
+            store_row<T, E, V, L>(yr, li, vend, rs, v, row_ok && slots_full);
+        }
     }
 }
 
-template <typename T, int G, int V, int W, int R>
+template <typename T, int G, int V, int W, int R, bool EXACT>
 static hipError_t layernorm_gelu_tile_run(const RowProblem &p)
 {
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG * R - 1) / (RG * R);
-    return launch(layernorm_gelu_tile<T, G, V, W, R>, dim3(static_cast<unsigned>(blocks)),
+    const float inv_n = static_cast<float>(1.0 / p.N);
+    return launch(layernorm_gelu_tile<T, G, V, W, R, EXACT>, dim3(static_cast<unsigned>(blocks)),
                   dim3(W * kWave), p.stream, static_cast<const T *>(p.x),
                   static_cast<const T *>(p.w), static_cast<const T *>(p.b), static_cast<T *>(p.y),
-                  p.M, p.N, p.ldx, p.ldy, p.eps);
+                  p.M, p.N, p.ldx, p.ldy, inv_n, p.eps);
 }
 
-template <typename T, int G, int V, int W, int R = 1>
+template <typename T, int G, int V, int W, int R = 1, bool EXACT = false>
 constexpr TileVariant tile()
 {
-    return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec,
-                       &layernorm_gelu_tile_run<T, G, V, W, R>};
+    return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec, EXACT,
+                       &layernorm_gelu_tile_run<T, G, V, W, R, EXACT>};
+}
+template <typename T, int G, int V, int W, int R = 1>
+constexpr TileVariant exact()
+{
+    return tile<T, G, V, W, R, true>();
 }
 
+// Preference order as for softmax: first exact entry with max_n == N, else
+// the first general entry that holds N; the rest are alternatives.
 static const TileVariant kLayerNormF32[] = {
-    tile<float, 1, 1, 4>(),   // N <= 256
-    tile<float, 1, 2, 4>(),   // N <= 512
-    tile<float, 1, 3, 4>(),   // N <= 768
-    tile<float, 1, 4, 4>(),   // N <= 1024
-    tile<float, 1, 8, 4>(),   // N <= 2048
-    tile<float, 4, 4, 4>(),   // N <= 4096
-    tile<float, 8, 4, 8>(),   // N <= 8192
-    tile<float, 16, 4, 16>(), // N <= 16384
+    exact<float, 1, 1, 4>(),    // N = 256
+    exact<float, 1, 2, 4>(),    // N = 512
+    exact<float, 1, 3, 4>(),    // N = 768
+    exact<float, 1, 4, 4>(),    // N = 1024
+    exact<float, 1, 8, 4>(),    // N = 2048
+    exact<float, 4, 4, 4>(),    // N = 4096
+    exact<float, 8, 4, 8>(),    // N = 8192
+    exact<float, 16, 4, 16>(),  // N = 16384
+    tile<float, 1, 1, 4>(),     // N <= 256
+    tile<float, 1, 2, 4>(),     // N <= 512
+    tile<float, 1, 3, 4>(),     // N <= 768
+    tile<float, 1, 4, 4>(),     // N <= 1024
+    tile<float, 1, 8, 4>(),     // N <= 2048
+    tile<float, 4, 4, 4>(),     // N <= 4096
+    tile<float, 8, 4, 8>(),     // N <= 8192
+    tile<float, 16, 4, 16>(),   // N <= 16384
     tile<float, 1, 3, 4, 2>(),  // alternatives
-    tile<float, 1, 3, 4, 4>(),
     tile<float, 2, 2, 4>(),
-    tile<float, 4, 1, 4>(),
+    exact<float, 1, 3, 4, 2>(),
+    exact<float, 1, 3, 4, 4>(),
 };
 
 static const TileVariant kLayerNormBF16[] = {
-    tile<bf16_t, 1, 1, 4>(),   // N <= 512
-    tile<bf16_t, 1, 2, 4>(),   // N <= 1024
-    tile<bf16_t, 1, 4, 4>(),   // N <= 2048
-    tile<bf16_t, 4, 2, 4>(),   // N <= 4096
-    tile<bf16_t, 8, 2, 8>(),   // N <= 8192
-    tile<bf16_t, 16, 2, 16>(), // N <= 16384
-    tile<bf16_t, 16, 4, 16>(), // N <= 32768
-    tile<bf16_t, 1, 8, 4>(),   // alternatives
-    tile<bf16_t, 2, 4, 4>(),
-    tile<bf16_t, 8, 1, 8>(),
-    tile<bf16_t, 4, 2, 4, 2>(),
-    tile<bf16_t, 4, 2, 8, 2>(),
+    exact<bf16_t, 1, 1, 4>(),   // N = 512
+    exact<bf16_t, 1, 2, 4>(),   // N = 1024
+    exact<bf16_t, 1, 4, 4>(),   // N = 2048
+    exact<bf16_t, 4, 2, 4, 2>(), // N = 4096
+    exact<bf16_t, 8, 2, 8>(),   // N = 8192
+    exact<bf16_t, 16, 2, 16>(), // N = 16384
+    exact<bf16_t, 16, 4, 16>(), // N = 32768
+    tile<bf16_t, 1, 1, 4>(),    // N <= 512
+    tile<bf16_t, 1, 2, 4>(),    // N <= 1024
+    tile<bf16_t, 1, 4, 4>(),    // N <= 2048
+    tile<bf16_t, 2, 4, 4>(),    // N <= 4096
+    tile<bf16_t, 8, 2, 8>(),    // N <= 8192
+    tile<bf16_t, 16, 2, 16>(),  // N <= 16384
+    tile<bf16_t, 16, 4, 16>(),  // N <= 32768
+    tile<bf16_t, 4, 2, 4>(),    // alternatives
+    tile<bf16_t, 1, 8, 4>(),
+    exact<bf16_t, 4, 2, 4>(),
+    exact<bf16_t, 2, 4, 4>(),
+    exact<bf16_t, 1, 8, 4>(),
+    exact<bf16_t, 2, 4, 4, 2>(),
 };
 
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count)
@@ -213,7 +249,7 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 template <typename T, int E, int W, int U>
 __global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
-    T *__restrict__ y, int N, int64_t ldx, int64_t ldy, float eps)
+    T *__restrict__ y, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
 {
     constexpr int NT = W * kWave;
     __shared__ float red[2][W];
@@ -222,7 +258,6 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
     T *yr = y + row * ldy;
     const RowSplit<E> rs(N);
     const int nv = rs.count();
-    const float n_f = static_cast<float>(N);
     const int tid = static_cast<int>(threadIdx.x);
 
     float s = 0.0f;
@@ -235,7 +270,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
             for (int e = 0; e < E; ++e)
                 s += v[u][e];
     }
-    const float mean = block_sum<W>(s, red[0]) / n_f;
+    const float mean = block_sum<W>(s, red[0]) * inv_n;
 
     float q = 0.0f;
     for (int base = 0; base < nv; base += NT * U) {
@@ -250,7 +285,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
                 q = fmaf(d, d, q);
             }
     }
-    const float rstd = 1.0f / sqrtf(block_sum<W>(q, red[1]) / n_f + eps);
+    const float rstd = __builtin_amdgcn_rsqf(fmaf(block_sum<W>(q, red[1]), inv_n, eps));
 
     for (int base = 0; base < nv; base += NT * U) {
         float v[U][E], wv[U][E], bv[U][E];
@@ -276,7 +311,7 @@ hipError_t loop_run(const RowProblem &p)
     return launch(layernorm_gelu_loop<T, E, kLoopW, kLoopU>, dim3(static_cast<unsigned>(p.M)),
                   dim3(kLoopW * kWave), p.stream, static_cast<const T *>(p.x),
                   static_cast<const T *>(p.w), static_cast<const T *>(p.b), static_cast<T *>(p.y),
-                  p.N, p.ldx, p.ldy, p.eps);
+                  p.N, p.ldx, p.ldy, static_cast<float>(1.0 / p.N), p.eps);
 }
 }  // namespace
 

@@ -14,7 +14,11 @@
 
 namespace rk {
 
-template <typename T, int G, int V, int W>
+// EXACT: compiled for N == V * L * E, i.e. every register slot of a row group
+// is a column of its row: loads and stores need no masks and nothing is
+// padded.  Rows past M (the last workgroup) then read row 0 and store
+// nothing.
+template <typename T, int G, int V, int W, bool EXACT>
 __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x,
                                                           T *__restrict__ y, int64_t M, int N,
                                                           int64_t ldx, int64_t ldy)
@@ -39,9 +43,11 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
     T *yr = y + r * ldy;
 
     const int vend = row_ok ? rs.count() : 0;
+    // every vector slot of the row group holds a complete vector of a row
+    const bool full = EXACT || (row_ok && V * L <= rs.nfull);
 
     float v[V][E];
-    load_row<T, E, V, L>(xr, li, vend, rs, -INFINITY, v);
+    load_row<T, E, V, L>(xr, li, vend, rs, -INFINITY, v, full);
 
     float m = -INFINITY;
 #pragma unroll
@@ -90,59 +96,93 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
             s += red_sum[grp][g];
     }
 
-    const float inv = 1.0f / s;
+    // 1/s by the hardware reciprocal (1 ulp): one rounding more than a
+    // division, once per row
+    const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int k = 0; k < V; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e)
             v[k][e] *= inv;
-    store_row<T, E, V, L>(yr, li, vend, rs, v);
+    if (EXACT) {
+        if (row_ok)
+            store_row<T, E, V, L>(yr, li, vend, rs, v, true);
+    } else {
+        store_row<T, E, V, L>(yr, li, vend, rs, v, full);
+    }
 }
 
-template <typename T, int G, int V, int W>
+template <typename T, int G, int V, int W, bool EXACT>
 static hipError_t softmax_tile_run(const RowProblem &p)
 {
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG - 1) / RG;
-    return launch(softmax_tile<T, G, V, W>, dim3(static_cast<unsigned>(blocks)), dim3(W * kWave),
-                  p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), p.M, p.N, p.ldx,
-                  p.ldy);
+    return launch(softmax_tile<T, G, V, W, EXACT>, dim3(static_cast<unsigned>(blocks)),
+                  dim3(W * kWave), p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y),
+                  p.M, p.N, p.ldx, p.ldy);
 }
 
-template <typename T, int G, int V, int W>
+// A general variant (any N up to its capacity) and an exact one (N equal to
+// its capacity).
+template <typename T, int G, int V, int W, bool EXACT = false>
 constexpr TileVariant tile()
 {
-    return TileVariant{G, V, W, 1, G * V * kWave * Elem<T>::kVec, &softmax_tile_run<T, G, V, W>};
+    return TileVariant{G, V, W, 1, G * V * kWave * Elem<T>::kVec, EXACT,
+                       &softmax_tile_run<T, G, V, W, EXACT>};
+}
+template <typename T, int G, int V, int W>
+constexpr TileVariant exact()
+{
+    return tile<T, G, V, W, true>();
 }
 
-// Preference order: the dispatcher takes the first entry whose max_n covers
-// N.  Entries after the largest one are alternatives reachable by index.
+// Preference order: the dispatcher takes the first exact entry whose max_n is
+// N, else the first general entry whose max_n covers N.  General entries after
+// the largest one are alternatives reachable by index.
 static const TileVariant kSoftmaxF32[] = {
-    tile<float, 1, 1, 4>(),   // N <= 256
-    tile<float, 1, 2, 4>(),   // N <= 512
-    tile<float, 1, 3, 4>(),   // N <= 768
-    tile<float, 1, 4, 4>(),   // N <= 1024
-    tile<float, 1, 8, 4>(),   // N <= 2048
-    tile<float, 4, 4, 4>(),   // N <= 4096
-    tile<float, 8, 4, 8>(),   // N <= 8192
-    tile<float, 16, 4, 16>(), // N <= 16384
-    tile<float, 2, 2, 4>(),   // alternatives
+    exact<float, 1, 1, 4>(),   // N = 256
+    exact<float, 1, 2, 4>(),   // N = 512
+    exact<float, 1, 3, 4>(),   // N = 768
+    exact<float, 2, 2, 4>(),   // N = 1024
+    exact<float, 1, 8, 4>(),   // N = 2048
+    exact<float, 4, 4, 4>(),   // N = 4096
+    exact<float, 8, 4, 8>(),   // N = 8192
+    exact<float, 16, 4, 16>(), // N = 16384
+    tile<float, 1, 1, 4>(),    // N <= 256
+    tile<float, 1, 2, 4>(),    // N <= 512
+    tile<float, 1, 3, 4>(),    // N <= 768
+    tile<float, 2, 2, 4>(),    // N <= 1024
+    tile<float, 1, 8, 4>(),    // N <= 2048
+    tile<float, 4, 4, 4>(),    // N <= 4096
+    tile<float, 8, 4, 8>(),    // N <= 8192
+    tile<float, 16, 4, 16>(),  // N <= 16384
+    tile<float, 1, 4, 4>(),    // alternatives
     tile<float, 4, 1, 4>(),
     tile<float, 2, 8, 4>(),
+    exact<float, 1, 4, 4>(),
 };
 
 static const TileVariant kSoftmaxBF16[] = {
-    tile<bf16_t, 1, 1, 4>(),   // N <= 512
-    tile<bf16_t, 1, 2, 4>(),   // N <= 1024
-    tile<bf16_t, 1, 4, 4>(),   // N <= 2048
-    tile<bf16_t, 4, 2, 4>(),   // N <= 4096
-    tile<bf16_t, 8, 2, 8>(),   // N <= 8192
-    tile<bf16_t, 16, 2, 16>(), // N <= 16384
-    tile<bf16_t, 16, 4, 16>(), // N <= 32768
-    tile<bf16_t, 1, 8, 4>(),   // alternatives
+    exact<bf16_t, 1, 1, 4>(),   // N = 512
+    exact<bf16_t, 1, 2, 4>(),   // N = 1024
+    exact<bf16_t, 1, 4, 4>(),   // N = 2048
+    exact<bf16_t, 4, 2, 4>(),   // N = 4096
+    exact<bf16_t, 8, 2, 8>(),   // N = 8192
+    exact<bf16_t, 16, 2, 16>(), // N = 16384
+    exact<bf16_t, 16, 4, 16>(), // N = 32768
+    tile<bf16_t, 1, 1, 4>(),    // N <= 512
+    tile<bf16_t, 1, 2, 4>(),    // N <= 1024
+    tile<bf16_t, 1, 4, 4>(),    // N <= 2048
+    tile<bf16_t, 4, 2, 4>(),    // N <= 4096
+    tile<bf16_t, 8, 2, 8>(),    // N <= 8192
+    tile<bf16_t, 16, 2, 16>(),  // N <= 16384
+    tile<bf16_t, 16, 4, 16>(),  // N <= 32768
+    tile<bf16_t, 1, 8, 4>(),    // alternatives
     tile<bf16_t, 2, 4, 4>(),
     tile<bf16_t, 8, 1, 8>(),
-    tile<bf16_t, 2, 4, 8>(),
+    exact<bf16_t, 1, 8, 4>(),
+    exact<bf16_t, 2, 4, 4>(),
+    exact<bf16_t, 8, 1, 8>(),
 };
 
 const TileVariant *softmax_variants(rk_dtype dtype, int *count)

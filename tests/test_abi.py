@@ -143,14 +143,21 @@ def test_variant_tables():
             assert max(v["max_n"] for v in vs) == cap
             for N in (1, 7, 255, 256, 257, 768, 1000, 4096, cap):
                 i = rk.variant_pick(op, dt, N)
-                assert i >= 0 and vs[i]["max_n"] >= N
+                assert i >= 0
+                assert vs[i]["max_n"] == N if vs[i]["exact"] else vs[i]["max_n"] >= N
             assert rk.variant_pick(op, dt, cap + 1) == -1
+            # every N has a general variant; exact ones are preferred when they fit
+            caps = {v["max_n"] for v in vs if not v["exact"]}
+            for v in vs:
+                if v["exact"]:
+                    assert v["max_n"] in caps
+                    assert vs[rk.variant_pick(op, dt, v["max_n"])]["exact"]
 
 
 def test_variant_entry_points_reject(lib):
     n = lib.rk__variant_count(0, F32)
     assert lib.rk__variant_count(5, F32) == 0 and lib.rk__variant_count(0, 9) == 0
-    assert lib.rk__variant_info(0, F32, n, None, None, None, None, None) == INVALID
+    assert lib.rk__variant_info(0, F32, n, None, None, None, None, None, None) == INVALID
     assert lib.rk__softmax_variant(n, A, B, 4, 8, 8, 8, F32, None) == INVALID
     assert lib.rk__softmax_variant(-2, A, B, 4, 8, 8, 8, F32, None) == INVALID
     assert lib.rk__layernorm_gelu_variant(0, A, A + 0x80000, A + 0x90000, B, 4, 8, 8, 8, 0.0,
