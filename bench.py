@@ -66,6 +66,8 @@ class Case:
         elif self.op == "online" and self.splits == 1:
             self.bytes = 3 * M * N * es  # two reads of x, one write
         elif self.op == "online":
+            if self.splits == 0:
+                self.splits = rk.rk_online_softmax_auto_splits(M, N)
             self.bytes = 3 * M * N * es + 2 * M * self.splits * 8  # + partials out and in
         else:
             self.bytes = io
@@ -147,9 +149,14 @@ def all_cases():
         Case("softmax_f32_8192x1000", "softmax", "softmax_f32_8192x1000"),
         Case("online_stream_f32_64x262144", "online", "online_f32_64x262144", splits=1),
         Case("online_split64_f32_64x262144", "online", "online_f32_64x262144", splits=64),
+        Case("online_auto_f32_64x262144", "online", "online_f32_64x262144", splits=0),
         Case("ln_gelu_bf16_16384x4096", "layernorm_gelu", "bf16_16384x4096"),
         Case("softmax_bf16_16384x4096", "softmax", "bf16_16384x4096"),
         CopyCase("copy_256MiB", 256 << 20),
+        # copies of the same total traffic as the small workloads: the
+        # achievable ceiling at that size (launch and latency included)
+        CopyCase("copy_12MiB", 12 << 20),
+        CopyCase("copy_32MiB", 32 << 20),
         CopyCase("copy_64MiB_64wg", 64 << 20, max_wg=64),
     ]
 
@@ -323,6 +330,8 @@ def main():
                "bytes_per_call": c.bytes, "rotation_sets": c.R}
         if c.M is not None:
             rec["rows_per_s"] = round(c.M / t, 1)
+        if getattr(c, "splits", None):
+            rec["splits"] = c.splits
         detail.append(rec)
         log(f"case {c.name}: {rec['us_per_call']} us  {rec['GB_per_s']} GB/s "
             f"({rec['pct_hbm_peak']}% of 8 TB/s)")
