@@ -20,11 +20,22 @@
 
 namespace rk {
 
+// exp(x - m) of an output element: compensated for fp32 I/O.
 template <typename T>
 __device__ __forceinline__ float softmax_exp(float x, float m, float m_log2e)
 {
     if constexpr (sizeof(T) == 4)
         return exp_shifted_accurate(x, m);
+    else
+        return exp_shifted_fast(x, m_log2e);
+}
+
+// exp(x - m) of a term of a partial sum d: errors average out there.
+template <typename T>
+__device__ __forceinline__ float softmax_term(float x, float m, float m_log2e)
+{
+    if constexpr (sizeof(T) == 4)
+        return exp_shifted_term(x, m);
     else
         return exp_shifted_fast(x, m_log2e);
 }
@@ -47,7 +58,7 @@ __device__ __forceinline__ SoftmaxState fold(SoftmaxState st, const float (&v)[U
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                sum += softmax_exp<T>(v[u][e], mn, mL);
+                sum += softmax_term<T>(v[u][e], mn, mL);
     }
     SoftmaxState r;
     r.m = mn;
