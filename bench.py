@@ -281,7 +281,7 @@ def cpu_model():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--case", default=None, help="time only this case (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

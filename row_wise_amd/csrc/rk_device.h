@@ -58,8 +58,15 @@ __device__ __forceinline__ float lane_value(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Maximum that propagates NaN (v_maximum_f32): a NaN anywhere in a row makes
+// its max NaN, and with it every output of the row, as the definition says.
+__device__ __forceinline__ float nanmax(float a, float b)
+{
+    return __builtin_elementwise_maximum(a, b);
+}
+
 struct MaxOp {
-    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+    __device__ __forceinline__ float operator()(float a, float b) const { return nanmax(a, b); }
 };
 struct SumOp {
     __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
@@ -93,18 +100,21 @@ __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, SumOp
 // hardware exp2 of the head to first order.  Relative error about
 // |d| * 6e-8 from the rounding of d (<= 2e-6 for |d| <= 30) plus an ulp or
 // two, instead of |d| * 1.7e-7 for exp2(d * log2e) alone.
+//
+// d is clamped at -150 (exp2 of the head is then 0 and the tail finite), so
+// that x = -inf (padding) gives 0 without a select.  The clamp maps a NaN d
+// to 0 as well; the callers' NaN-propagating row max and the resulting zero
+// sum still make every output of such a row NaN.
 __device__ __forceinline__ float exp_shifted_accurate(float x, float m)
 {
-    constexpr float kL = 1.44269502162933349609375f;      // fp32(log2 e)
-    constexpr float kLlo = 1.9259629911266175e-08f;       // log2 e - kL
+    constexpr float kL = 1.44269502162933349609375f;       // fp32(log2 e)
     constexpr float kLn2 = 0.693147180559945309f;
-    const float d = x - m;
+    constexpr float kLloLn2 = 1.3349758171622139e-08f;     // (log2 e - kL) ln 2
+    const float d = fmaxf(x - m, -150.0f);
     const float t = d * kL;
-    const float tl = fmaf(d, kL, -t) + d * kLlo;
+    const float tl = fmaf(fmaf(d, kL, -t), kLn2, d * kLloLn2);  // tail, times ln 2
     const float e = __builtin_amdgcn_exp2f(t);
-    const float r = fmaf(e, tl * kLn2, e);
-    // x = -inf (padding) or an underflowed exp: the tail may be inf/NaN there
-    return e == 0.0f ? 0.0f : r;
+    return fmaf(e, tl, e);
 }
 
 // exp(x - m) as a term of a sum: the shift is formed in fp32 (exact when x and
@@ -145,7 +155,7 @@ struct SoftmaxState {
 
 __device__ __forceinline__ SoftmaxState merge(SoftmaxState a, SoftmaxState b)
 {
-    float M = fmaxf(a.m, b.m);
+    float M = nanmax(a.m, b.m);
     SoftmaxState r;
     r.m = M;
     r.d = a.d * rescale_factor(a.m, M) + b.d * rescale_factor(b.m, M);

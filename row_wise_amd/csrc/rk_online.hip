@@ -49,8 +49,8 @@ __device__ __forceinline__ SoftmaxState fold(SoftmaxState st, const float (&v)[U
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            bm = fmaxf(bm, v[u][e]);
-    const float mn = fmaxf(st.m, bm);
+            bm = nanmax(bm, v[u][e]);
+    const float mn = nanmax(st.m, bm);
     float sum = 0.0f;
     if (mn != -INFINITY) {  // else every value seen is -inf: nothing to add
         const float mL = mn * 1.4426950408889634f;

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
     for (int k = 0; k < V; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            m = fmaxf(m, v[k][e]);
+            m = nanmax(m, v[k][e]);
     m = wave_max(m);
     if constexpr (G > 1) {
         if (threadIdx.x % kWave == 0)
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
         m = red_max[grp][0];
 #pragma unroll
         for (int g = 1; g < G; ++g)
-            m = fmaxf(m, red_max[grp][g]);
+            m = nanmax(m, red_max[grp][g]);
     }
 
     float s = 0.0f;

@@ -253,19 +253,21 @@ def test_deterministic():
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
 def test_infinities(dtype):
-    M, N = 6, 3000
+    M, N = 7, 3000
     x = rowgen.randn(M, N, seed=13, dtype=dtype)
     x[0, ::7] = -math.inf  # some -inf: those outputs are exactly 0
     x[1, :] = -math.inf  # all -inf: NaN (the definition's IEEE value)
     x[2, 5] = math.inf  # +inf: NaN
+    x[3, 2999] = math.nan  # NaN anywhere: NaN
     ref = oracle.softmax(x)
     for y in (rk.rk_softmax(x.to(DEV)), rk.rk_online_softmax(x.to(DEV), num_splits=1),
-              rk.rk_online_softmax(x.to(DEV), num_splits=4)):
+              rk.rk_online_softmax(x.to(DEV), num_splits=4),
+              rk.rk__softmax_variant(-1, x.to(DEV))):
         yc = y.cpu().double().numpy()
         assert np.all(yc[0, ::7] == 0.0)
-        assert rel_err_softmax(yc[[0, 3, 4, 5]], ref[[0, 3, 4, 5]]) <= tol_of(dtype)
-        assert np.all(np.isnan(yc[1])) and np.all(np.isnan(ref[1]))
-        assert np.all(np.isnan(yc[2])) and np.all(np.isnan(ref[2]))
+        assert rel_err_softmax(yc[[0, 4, 5, 6]], ref[[0, 4, 5, 6]]) <= tol_of(dtype)
+        for r in (1, 2, 3):
+            assert np.all(np.isnan(yc[r])) and np.all(np.isnan(ref[r])), r
 
 
 def test_empty_rows_is_noop():
