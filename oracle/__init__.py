@@ -54,6 +54,9 @@ def _signatures():
         "oracle_layernorm_stats": [P, i64, d, P, P, P],
         "oracle_layernorm_normalize": [P, P, i64, i64, d],
         "oracle_layernorm_gelu": [P, P, P, P, i64, i64, d],
+        "oracle_rms_stats": [P, i64, d, P, P],
+        "oracle_rmsnorm": [P, P, P, i64, i64, d],
+        "oracle_residual_rmsnorm": [P, P, P, P, P, i64, i64, d],
     }
 
 
@@ -173,6 +176,34 @@ class Oracle:
                                        float(eps))
         return y
 
+    def rms_stats(self, row, eps: float):
+        """(mean square, inv_rms) of one row."""
+        r = _f64(row).ravel()
+        ms, inv = ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_rms_stats(_p(r), r.size, float(eps), ctypes.byref(ms), ctypes.byref(inv))
+        return ms.value, inv.value
+
+    def rmsnorm(self, x, w, eps: float) -> np.ndarray:
+        """RMSNorm of a [M, N] array: x * rsqrt(mean(x^2) + eps) * w."""
+        x = _rows(x)
+        w = _f64(w).ravel()
+        assert w.size == x.shape[1]
+        y = np.empty_like(x)
+        self.lib.oracle_rmsnorm(_p(x), _p(w), _p(y), x.shape[0], x.shape[1], float(eps))
+        return y
+
+    def residual_rmsnorm(self, x, residual, w, eps: float):
+        """(out, residual_out) of the fused residual RMSNorm."""
+        x = _rows(x)
+        res = _rows(residual)
+        w = _f64(w).ravel()
+        assert res.shape == x.shape and w.size == x.shape[1]
+        y = np.empty_like(x)
+        r = np.empty_like(x)
+        self.lib.oracle_residual_rmsnorm(_p(x), _p(res), _p(w), _p(y), _p(r), x.shape[0],
+                                         x.shape[1], float(eps))
+        return y, r
+
 
 _default = None
 
@@ -195,6 +226,6 @@ def _forward(name):
 
 for _n in ["softmax", "softmax_stats", "online_stats", "merge", "split_stats", "online_softmax",
            "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
-           "layernorm_gelu"]:
+           "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm"]:
     globals()[_n] = _forward(_n)
 del _n

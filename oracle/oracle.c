@@ -243,3 +243,49 @@ void oracle_layernorm_gelu(const double *x, const double *w, const double *b, do
         }
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* RMSNorm: [TKE] §4.2 "RMSNorm"                                           */
+/*   inv_rms = rsqrt(mean(x^2) + eps); out = x * inv_rms * weight,         */
+/* no centring (the difference from LayerNorm the page points out).       */
+/* ---------------------------------------------------------------------- */
+
+/* Mean square of a row and inv_rms = 1 / sqrt(mean square + eps). */
+void oracle_rms_stats(const double *x, int64_t N, double eps, double *ms_out, double *inv_out)
+{
+    double q = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        q += x[j] * x[j];
+    double ms = q / (double)N;
+    *ms_out = ms;
+    *inv_out = 1.0 / sqrt(ms + eps);
+}
+
+void oracle_rmsnorm(const double *x, const double *w, double *y, int64_t M, int64_t N, double eps)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        double ms, inv;
+        oracle_rms_stats(x + i * N, N, eps, &ms, &inv);
+        for (int64_t j = 0; j < N; ++j)
+            y[i * N + j] = x[i * N + j] * inv * w[j];
+    }
+}
+
+/* Fused residual RMSNorm: [TKE] §4.3 "Fused Residual RMSNorm"
+ *   residual_out = x + residual;
+ *   out = residual_out * rsqrt(mean(residual_out^2) + eps) * weight;
+ * both outputs returned.  The sum of two fp32 or bf16 inputs is exact in
+ * double. */
+void oracle_residual_rmsnorm(const double *x, const double *res, const double *w, double *y,
+                             double *r_out, int64_t M, int64_t N, double eps)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        double *rr = r_out + i * N;
+        for (int64_t j = 0; j < N; ++j)
+            rr[j] = x[i * N + j] + res[i * N + j];
+        double ms, inv;
+        oracle_rms_stats(rr, N, eps, &ms, &inv);
+        for (int64_t j = 0; j < N; ++j)
+            y[i * N + j] = rr[j] * inv * w[j];
+    }
+}

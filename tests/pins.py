@@ -25,6 +25,11 @@ What pins what (citations are to the pages' titles and sections):
 * tanh GeLU, same page §3.4: GeLU(0) = 0; GeLU(z) - GeLU(-z) = z; limits
   z and 0 at +-large z; torch.nn.functional.gelu(approximate="tanh") in
   float64; distance to the erf form peaks near 4.73e-4.
+* RMSNorm, same page §4.2: torch.nn.functional.rms_norm in float64;
+  mean((y / w)^2) = ms / (ms + eps); odd symmetry; a constant row in closed
+  form; an eps-sensitive row against numpy's mean of squares.
+* fused residual RMSNorm, same page §4.3: residual_out is x + residual
+  exactly; out is RMSNorm of residual_out (torch, float64).
 """
 from __future__ import annotations
 
@@ -291,6 +296,67 @@ def check_layernorm_eps_placement(orc):
     assert abs(rstd * math.sqrt(np.var(x)) - 1.0) > 0.2
 
 
+# --------------------------------------------------------------- RMSNorm
+
+
+def check_rmsnorm_torch(orc):
+    import torch
+    import torch.nn.functional as F
+
+    r = _rng(41)
+    for n in (1, 7, 768, 4096):
+        x = r.standard_normal((6, n)) * np.array([[1.0], [1e-3], [30.0], [1.0], [5.0], [0.1]])
+        x[3] += 2.5  # rows with a mean: RMSNorm does not centre
+        w = 1.0 + 0.1 * r.standard_normal(n)
+        y = orc.rmsnorm(x, w, EPS)
+        ref = F.rms_norm(torch.from_numpy(x), (n,), torch.from_numpy(w), EPS).numpy()
+        assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1.0)) <= 1e-14, n
+
+
+def check_rmsnorm_invariants(orc):
+    r = _rng(43)
+    n = 1000
+    x = r.standard_normal((4, n)) * np.array([[1.0], [1e-3], [8.0], [0.02]]) + np.array(
+        [[0.0], [0.0], [3.0], [0.0]])
+    w = 1.0 + 0.1 * r.standard_normal(n)
+    y = orc.rmsnorm(x, w, EPS)
+    for i in range(4):
+        ms = np.mean(x[i] ** 2)
+        assert abs(np.mean((y[i] / w) ** 2) - ms / (ms + EPS)) <= 1e-13
+    assert np.array_equal(orc.rmsnorm(-x, w, EPS), -y)
+    # constant row c: y = c / sqrt(c^2 + eps) w
+    c = 0.75
+    yc = orc.rmsnorm(np.full((1, n), c), w, EPS)[0]
+    assert np.all(np.abs(yc - c / math.sqrt(c * c + EPS) * w) <= 1e-15 * np.abs(w) + 1e-16)
+    # eps-sensitive row: mean square ~ eps
+    xe = 3e-3 * r.standard_normal(n)
+    ms, inv = orc.rms_stats(xe, EPS)
+    assert abs(ms - np.mean(xe * xe)) <= 1e-15 * ms
+    assert abs(inv - 1.0 / math.sqrt(np.mean(xe * xe) + EPS)) <= 1e-13 * inv
+    assert abs(inv * math.sqrt(ms) - 1.0) > 0.2
+
+
+def check_residual_rmsnorm(orc):
+    import torch
+    import torch.nn.functional as F
+
+    r = _rng(47)
+    n = 768
+    x = np.float32(1.0) * r.standard_normal((5, n)).astype(np.float32)
+    res = (3.0 * r.standard_normal((5, n))).astype(np.float32)
+    w = (1.0 + 0.1 * r.standard_normal(n)).astype(np.float32)
+    y, ro = orc.residual_rmsnorm(x, res, w, EPS)
+    # the sum of two fp32 values is exact in double
+    assert np.array_equal(ro, x.astype(np.float64) + res.astype(np.float64))
+    ref = F.rms_norm(torch.from_numpy(ro), (n,), torch.from_numpy(w.astype(np.float64)),
+                     EPS).numpy()
+    assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1.0)) <= 1e-14
+    # residual of zero: plain RMSNorm of x
+    y0, ro0 = orc.residual_rmsnorm(x, np.zeros_like(x), w, EPS)
+    assert np.array_equal(ro0, x.astype(np.float64))
+    assert np.array_equal(y0, orc.rmsnorm(x, w, EPS))
+
+
 PINS = [
     check_softmax_sums_to_one,
     check_softmax_shift_invariance,
@@ -310,4 +376,7 @@ PINS = [
     check_layernorm_torch,
     check_layernorm_constant_row,
     check_layernorm_eps_placement,
+    check_rmsnorm_torch,
+    check_rmsnorm_invariants,
+    check_residual_rmsnorm,
 ]

@@ -34,6 +34,12 @@ MUTANTS = {
     "ln_weight_dropped": ("* rstd * w[j] + b[j];", "* rstd + b[j];"),
     "ln_mean_divisor": ("double mean = s / (double)N;", "double mean = s / (double)(N + 1);"),
     "ln_var_uncentered": ("q += (x[j] - mean) * (x[j] - mean);", "q += x[j] * x[j];"),
+    "rms_sum_not_mean": ("double ms = q / (double)N;", "double ms = q;"),
+    "rms_eps_outside_sqrt": ("*inv_out = 1.0 / sqrt(ms + eps);", "*inv_out = 1.0 / (sqrt(ms) + eps);"),
+    "rms_centred": ("        q += x[j] * x[j];\n    double ms", "        q += (x[j] - x[0]) * (x[j] - x[0]);\n    double ms"),
+    "rms_weight_dropped": ("y[i * N + j] = x[i * N + j] * inv * w[j];", "y[i * N + j] = x[i * N + j] * inv;"),
+    "residual_sign": ("rr[j] = x[i * N + j] + res[i * N + j];", "rr[j] = x[i * N + j] - res[i * N + j];"),
+    "residual_not_normalized": ("y[i * N + j] = rr[j] * inv * w[j];", "y[i * N + j] = x[i * N + j] * inv * w[j];"),
 }
 
 
