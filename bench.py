@@ -13,7 +13,8 @@ bracketed by device synchronizations.  `roofline.achieved` divides the same
 bytes by the kernel's average duration from HIP events on its stream.
 `detail` holds the same measurement for every other workload (softmax fp32
 8192x1000, online softmax fp32 64x262144 streaming and split-row, bf16
-16384x4096 LayerNorm+GeLU and softmax) and the 16-byte copy ceiling.
+16384x4096 LayerNorm+GeLU and softmax, RMSNorm and fused residual RMSNorm on
+the fp32 4096x768 and bf16 16384x4096 inputs) and the 16-byte copy ceiling.
 `cpu_baseline` is the CPU oracle timed on this host on repeated full batches.
 """
 from __future__ import annotations
@@ -55,14 +56,21 @@ class Case:
 
     def setup(self, torch, rk, rowgen):
         d = rowgen.make(self.workload)
-        x = d["x_softmax"] if self.op != "layernorm_gelu" else d["x"]
+        norm = self.op in ("layernorm_gelu", "rmsnorm", "residual_rmsnorm")
+        x = d["x"] if norm else d["x_softmax"]
         M, N = x.shape
         es = x.element_size()
         self.M, self.N, self.dtype = M, N, x.dtype
         self.dtype_code = rk.RK_F32 if x.dtype == torch.float32 else rk.RK_BF16
         io = 2 * M * N * es
+        footprint = io
         if self.op == "layernorm_gelu":
             self.bytes = io + 2 * N * es  # x, y, and w, b once
+        elif self.op == "rmsnorm":
+            self.bytes = io + N * es  # x, y, and w once
+        elif self.op == "residual_rmsnorm":
+            self.bytes = 2 * io + N * es  # x, residual, y, residual_out, and w once
+            footprint = 2 * io
         elif self.op == "online" and self.splits == 1:
             self.bytes = 3 * M * N * es  # two reads of x, one write
         elif self.op == "online":
@@ -71,12 +79,15 @@ class Case:
             self.bytes = 3 * M * N * es + 2 * M * self.splits * 8  # + partials out and in
         else:
             self.bytes = io
-        footprint = io
         self.R = max(2, math.ceil(ROTATE_BYTES / footprint))
         dev = torch.device("cuda")
         xd = x.to(dev)
         self.xs = [xd] + [xd.clone() for _ in range(self.R - 1)]
         self.ys = [torch.empty_like(xd) for _ in range(self.R)]
+        if self.op == "residual_rmsnorm":
+            rd = rowgen.residual(self.workload).to(dev)
+            self.rs = [rd] + [rd.clone() for _ in range(self.R - 1)]
+            self.ros = [torch.empty_like(xd) for _ in range(self.R)]
         self.w = d["w"].to(dev)
         self.b = d["b"].to(dev)
         self.ws = None
@@ -92,6 +103,15 @@ class Case:
             self.args = [(xx.data_ptr(), self.w.data_ptr(), self.b.data_ptr(), yy.data_ptr(), M,
                           N, N, N, fp, self.dtype_code, stream)
                          for xx, yy in zip(self.xs, self.ys)]
+        elif self.op == "rmsnorm":
+            fn = lib.rk_rmsnorm
+            self.args = [(xx.data_ptr(), self.w.data_ptr(), yy.data_ptr(), M, N, N, N, fp,
+                          self.dtype_code, stream) for xx, yy in zip(self.xs, self.ys)]
+        elif self.op == "residual_rmsnorm":
+            fn = lib.rk_residual_rmsnorm
+            self.args = [(xx.data_ptr(), rr.data_ptr(), self.w.data_ptr(), yy.data_ptr(),
+                          oo.data_ptr(), M, N, N, N, N, N, fp, self.dtype_code, stream)
+                         for xx, rr, yy, oo in zip(self.xs, self.rs, self.ys, self.ros)]
         elif self.op == "softmax":
             fn = lib.rk_softmax
             self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, N, self.dtype_code, stream)
@@ -112,6 +132,7 @@ class Case:
 
     def free(self):
         self.xs = self.ys = self.args = self.ws = None
+        self.rs = self.ros = None
 
 
 class CopyCase:
@@ -152,6 +173,10 @@ def all_cases():
         Case("online_auto_f32_64x262144", "online", "online_f32_64x262144", splits=0),
         Case("ln_gelu_bf16_16384x4096", "layernorm_gelu", "bf16_16384x4096"),
         Case("softmax_bf16_16384x4096", "softmax", "bf16_16384x4096"),
+        Case("rmsnorm_f32_4096x768", "rmsnorm", "ln_gelu_f32_4096x768"),
+        Case("residual_rmsnorm_f32_4096x768", "residual_rmsnorm", "ln_gelu_f32_4096x768"),
+        Case("rmsnorm_bf16_16384x4096", "rmsnorm", "bf16_16384x4096"),
+        Case("residual_rmsnorm_bf16_16384x4096", "residual_rmsnorm", "bf16_16384x4096"),
         CopyCase("copy_256MiB", 256 << 20),
         # copies of the same total traffic as the small workloads: the
         # achievable ceiling at that size (launch and latency included)

@@ -143,6 +143,45 @@ rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias,
                             int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
                             rk_dtype dtype, hipStream_t stream);
 
+/*
+ * RMSNorm ([TKE] §4.2 "RMSNorm"):
+ *     inv_rms = 1 / sqrt(sum_j x_j^2 / N + eps),  y_j = x_j * inv_rms * weight_j,
+ * with no centring; fp32 accumulation, output in `dtype`.
+ *
+ * x [M][ldx], y [M][ldy], weight [N] (contiguous), all of `dtype`.  Register
+ * resident up to the same N as rk_layernorm_gelu (one read and one write
+ * per element); other rows are read twice by a looping kernel.
+ *
+ * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight is NULL with
+ * M > 0, eps is not finite and > 0, or y overlaps weight.
+ */
+rk_status rk_rmsnorm(const void *x, const void *weight, void *y, int64_t M, int64_t N,
+                     int64_t ldx, int64_t ldy, float eps, rk_dtype dtype, hipStream_t stream);
+
+/*
+ * Fused residual add + RMSNorm ([TKE] §4.3 "Fused Residual RMSNorm"), two
+ * outputs from one pass:
+ *     residual_out = x + residual,
+ *     y = residual_out * rsqrt(mean(residual_out^2) + eps) * weight.
+ * The sum is formed in fp32 and rounded to `dtype`; the norm is taken of
+ * that stored value, so y equals rk_rmsnorm(residual_out) as with an unfused
+ * add followed by a norm (identical for fp32).
+ *
+ * x [M][ldx], residual [M][ldr], y [M][ldy], residual_out [M][ldo],
+ * weight [N] (contiguous), all of `dtype`.  Each output may be one of the
+ * inputs exactly (same pointer and pitch: e.g. residual_out = residual to
+ * update the residual stream in place); y and residual_out must not overlap
+ * each other, the weight, or an input other than exactly.
+ *
+ * Returns RK_ERR_INVALID_ARG for M < 0, N < 1, any pitch < N, a NULL or
+ * misaligned pointer with M > 0, an unknown dtype, eps not finite and > 0,
+ * or a forbidden overlap; RK_ERR_UNSUPPORTED if N > 2^30.
+ */
+rk_status rk_residual_rmsnorm(const void *x, const void *residual, const void *weight, void *y,
+                              void *residual_out, int64_t M, int64_t N, int64_t ldx,
+                              int64_t ldr, int64_t ldy, int64_t ldo, float eps, rk_dtype dtype,
+                              hipStream_t stream);
+
 /* Static, NUL-terminated description of a status ("unknown status" for an
  * unknown value). */
 const char *rk_status_string(rk_status status);

@@ -30,7 +30,12 @@ rk_status rk_probe_copy(const void *src, void *dst, size_t bytes, int32_t max_wo
                         hipStream_t stream);
 
 /* Operations with tile variants. */
-typedef enum rk_op { RK_OP_SOFTMAX = 0, RK_OP_LAYERNORM_GELU = 1 } rk_op;
+typedef enum rk_op {
+    RK_OP_SOFTMAX = 0,
+    RK_OP_LAYERNORM_GELU = 1,
+    RK_OP_RMSNORM = 2,
+    RK_OP_RESIDUAL_RMSNORM = 3,
+} rk_op;
 
 /* Number of compiled tile variants of `op` for `dtype` (0 if invalid). */
 int32_t rk__variant_count(rk_op op, rk_dtype dtype);
@@ -64,6 +69,17 @@ rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, const void *w
                                      const void *bias, void *y, int64_t M, int64_t N,
                                      int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
                                      hipStream_t stream);
+
+/* rk_rmsnorm / rk_residual_rmsnorm forced onto one path, as above (index -1:
+ * the two-pass looping kernel). */
+rk_status rk__rmsnorm_variant(int32_t index, const void *x, const void *weight, void *y,
+                              int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
+                              rk_dtype dtype, hipStream_t stream);
+rk_status rk__residual_rmsnorm_variant(int32_t index, const void *x, const void *residual,
+                                       const void *weight, void *y, void *residual_out,
+                                       int64_t M, int64_t N, int64_t ldx, int64_t ldr,
+                                       int64_t ldy, int64_t ldo, float eps, rk_dtype dtype,
+                                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,8 @@ Functions carry the C entry points' names:
 * ``rk_softmax(x, out=None)``
 * ``rk_online_softmax(x, num_splits=1, out=None, workspace=None)``
 * ``rk_layernorm_gelu(x, weight, bias, eps=1e-5, out=None)``
+* ``rk_rmsnorm(x, weight, eps=1e-5, out=None)``
+* ``rk_residual_rmsnorm(x, residual, weight, eps=1e-5, out=None, residual_out=None)``
 * ``rk_online_softmax_workspace_bytes(M, N, num_splits)``,
   ``rk_online_softmax_auto_splits(M, N)``, ``rk_status_string(s)``,
   ``rk_version()``
@@ -29,13 +31,14 @@ __all__ = [
     "rk_layernorm_gelu", "rk_online_softmax_workspace_bytes", "rk_online_softmax_auto_splits",
     "rk_status_string", "rk_version", "rk_probe_copy", "rk__softmax_variant",
     "rk__layernorm_gelu_variant", "variants", "RK_F32", "RK_BF16", "RK_OP_SOFTMAX",
-    "RK_OP_LAYERNORM_GELU",
+    "RK_OP_LAYERNORM_GELU", "rk_rmsnorm", "rk_residual_rmsnorm", "rk__rmsnorm_variant",
+    "rk__residual_rmsnorm_variant", "RK_OP_RMSNORM", "RK_OP_RESIDUAL_RMSNORM",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.so")
 
 RK_F32, RK_BF16 = 0, 1
-RK_OP_SOFTMAX, RK_OP_LAYERNORM_GELU = 0, 1
+RK_OP_SOFTMAX, RK_OP_LAYERNORM_GELU, RK_OP_RMSNORM, RK_OP_RESIDUAL_RMSNORM = 0, 1, 2, 3
 RK_OK = 0
 
 
@@ -77,6 +80,12 @@ def load():
         "rk__softmax_variant": (i32, [i32, vp, vp, i64, i64, i64, i64, i32, vp]),
         "rk__layernorm_gelu_variant": (i32, [i32, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32,
                                              vp]),
+        "rk_rmsnorm": (i32, [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
+        "rk_residual_rmsnorm": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32,
+                                      vp]),
+        "rk__rmsnorm_variant": (i32, [i32, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
+        "rk__residual_rmsnorm_variant": (i32, [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                               i64, f32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -216,6 +225,41 @@ def rk_layernorm_gelu(x, weight, bias, eps: float = 1e-5, out=None):
     return o.reshape(x.shape) if out is None else out
 
 
+def _check_weight(weight, x, N):
+    if weight.shape != (N,) or not weight.is_contiguous():
+        raise ValueError("weight must be contiguous [N]")
+    if weight.dtype != x.dtype:
+        raise ValueError("weight must have the input's dtype")
+
+
+def rk_rmsnorm(x, weight, eps: float = 1e-5, out=None):
+    """RMSNorm over the last dimension: x * rsqrt(mean(x^2) + eps) * weight."""
+    _check_device(x, weight)
+    v, M, N, ldx = _as_rows(x)
+    _check_weight(weight, x, N)
+    o, ldy = _out_like(x, v, out)
+    _call("rk_rmsnorm", v.data_ptr(), weight.data_ptr(), o.data_ptr(), M, N, ldx, ldy,
+          float(eps), _dtype_code(x), _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def rk_residual_rmsnorm(x, residual, weight, eps: float = 1e-5, out=None, residual_out=None):
+    """(y, residual_out): residual_out = x + residual, y = RMSNorm(residual_out)."""
+    _check_device(x, residual, weight)
+    v, M, N, ldx = _as_rows(x)
+    if residual.shape != x.shape or residual.dtype != x.dtype:
+        raise ValueError("residual must match x")
+    rv, _, _, ldr = _as_rows(residual)
+    _check_weight(weight, x, N)
+    o, ldy = _out_like(x, v, out)
+    ro, ldo = _out_like(x, v, residual_out)
+    _call("rk_residual_rmsnorm", v.data_ptr(), rv.data_ptr(), weight.data_ptr(), o.data_ptr(),
+          ro.data_ptr(), M, N, ldx, ldr, ldy, ldo, float(eps), _dtype_code(x), _stream(x))
+    y = o.reshape(x.shape) if out is None else out
+    r = ro.reshape(x.shape) if residual_out is None else residual_out
+    return y, r
+
+
 # ------------------------------------------------------------------ tuning
 
 
@@ -266,3 +310,27 @@ def rk__layernorm_gelu_variant(index: int, x, weight, bias, eps: float = 1e-5, o
     _call("rk__layernorm_gelu_variant", int(index), v.data_ptr(), weight.data_ptr(),
           bias.data_ptr(), o.data_ptr(), M, N, ldx, ldy, float(eps), _dtype_code(x), _stream(x))
     return o.reshape(x.shape) if out is None else out
+
+
+def rk__rmsnorm_variant(index: int, x, weight, eps: float = 1e-5, out=None):
+    _check_device(x, weight)
+    v, M, N, ldx = _as_rows(x)
+    o, ldy = _out_like(x, v, out)
+    _call("rk__rmsnorm_variant", int(index), v.data_ptr(), weight.data_ptr(), o.data_ptr(), M, N,
+          ldx, ldy, float(eps), _dtype_code(x), _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def rk__residual_rmsnorm_variant(index: int, x, residual, weight, eps: float = 1e-5, out=None,
+                                 residual_out=None):
+    _check_device(x, residual, weight)
+    v, M, N, ldx = _as_rows(x)
+    rv, _, _, ldr = _as_rows(residual)
+    o, ldy = _out_like(x, v, out)
+    ro, ldo = _out_like(x, v, residual_out)
+    _call("rk__residual_rmsnorm_variant", int(index), v.data_ptr(), rv.data_ptr(),
+          weight.data_ptr(), o.data_ptr(), ro.data_ptr(), M, N, ldx, ldr, ldy, ldo, float(eps),
+          _dtype_code(x), _stream(x))
+    y = o.reshape(x.shape) if out is None else out
+    r = ro.reshape(x.shape) if residual_out is None else residual_out
+    return y, r

@@ -92,6 +92,10 @@ const TileVariant *variants(rk_op op, rk_dtype dtype, int *count)
         return softmax_variants(dtype, count);
     if (op == RK_OP_LAYERNORM_GELU)
         return layernorm_gelu_variants(dtype, count);
+    if (op == RK_OP_RMSNORM)
+        return rmsnorm_variants(dtype, false, count);
+    if (op == RK_OP_RESIDUAL_RMSNORM)
+        return rmsnorm_variants(dtype, true, count);
     return nullptr;
 }
 
@@ -182,6 +186,107 @@ bool layernorm_aligned(const RowProblem &p)
 {
     return rows_aligned(p.x, p.y, p.ldx, p.ldy, elem_size(p.dtype)) && aligned16(p.w) &&
            aligned16(p.b);
+}
+
+bool valid_eps(float eps) { return std::isfinite(eps) && eps > 0.0f; }
+
+bool elem_aligned(const void *p, int es) { return reinterpret_cast<uintptr_t>(p) % es == 0; }
+
+// An output may be an input exactly (same pointer, same pitch) or be disjoint
+// from it.
+bool alias_ok(const void *out, int64_t ldo, const void *in, int64_t ldi, int64_t M, int64_t N,
+              int es)
+{
+    if (out == in && ldo == ldi)
+        return true;
+    return !overlaps(matrix_span(out, M, N, ldo, es), matrix_span(in, M, N, ldi, es));
+}
+
+rk_status check_rmsnorm(const void *x, const void *w, const void *y, int64_t M, int64_t N,
+                        int64_t ldx, int64_t ldy, float eps, rk_dtype dtype)
+{
+    rk_status st = check_rows(x, y, M, N, ldx, ldy, dtype);
+    if (st != RK_OK)
+        return st;
+    if (!valid_eps(eps))
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const int es = elem_size(dtype);
+    if (w == nullptr || !elem_aligned(w, es))
+        return RK_ERR_INVALID_ARG;
+    if (overlaps(matrix_span(y, M, N, ldy, es), matrix_span(w, 1, N, N, es)))
+        return RK_ERR_INVALID_ARG;
+    return RK_OK;
+}
+
+rk_status check_residual_rmsnorm(const void *x, const void *r, const void *w, const void *y,
+                                 const void *ro, int64_t M, int64_t N, int64_t ldx, int64_t ldr,
+                                 int64_t ldy, int64_t ldo, float eps, rk_dtype dtype)
+{
+    if (!valid_dtype(dtype))
+        return RK_ERR_INVALID_ARG;
+    if (M < 0 || N < 1 || N > INT32_MAX || ldx < N || ldr < N || ldy < N || ldo < N)
+        return RK_ERR_INVALID_ARG;
+    if (N > kMaxN)
+        return RK_ERR_UNSUPPORTED;
+    if (!valid_eps(eps))
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const int es = elem_size(dtype);
+    for (const void *p : {x, r, w, static_cast<const void *>(y), static_cast<const void *>(ro)})
+        if (p == nullptr || !elem_aligned(p, es))
+            return RK_ERR_INVALID_ARG;
+    for (int64_t ld : {ldx, ldr, ldy, ldo})
+        if (!extent_ok(M, N, ld, es))
+            return RK_ERR_INVALID_ARG;
+    // outputs: each may be an input exactly, never the other output or the weight
+    if (!alias_ok(y, ldy, x, ldx, M, N, es) || !alias_ok(y, ldy, r, ldr, M, N, es) ||
+        !alias_ok(ro, ldo, x, ldx, M, N, es) || !alias_ok(ro, ldo, r, ldr, M, N, es))
+        return RK_ERR_INVALID_ARG;
+    if (overlaps(matrix_span(y, M, N, ldy, es), matrix_span(ro, M, N, ldo, es)))
+        return RK_ERR_INVALID_ARG;
+    const Span ws = matrix_span(w, 1, N, N, es);
+    if (overlaps(matrix_span(y, M, N, ldy, es), ws) || overlaps(matrix_span(ro, M, N, ldo, es), ws))
+        return RK_ERR_INVALID_ARG;
+    return RK_OK;
+}
+
+bool rmsnorm_aligned(const RowProblem &p, bool residual)
+{
+    const int es = elem_size(p.dtype);
+    bool ok = rows_aligned(p.x, p.y, p.ldx, p.ldy, es) && aligned16(p.w);
+    if (residual)
+        ok = ok && rows_aligned(p.r, p.ro, p.ldr, p.ldo, es);
+    return ok;
+}
+
+rk_status rmsnorm_generic(const RowProblem &p, bool residual, bool aligned)
+{
+    if (!grid_ok(p.M, kLoopThreads))
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(rmsnorm_loop_run(p, residual, aligned));
+}
+
+rk_status rmsnorm_dispatch(const RowProblem &p, bool residual, int32_t index, bool forced)
+{
+    int count = 0;
+    const TileVariant *v = rmsnorm_variants(p.dtype, residual, &count);
+    const bool aligned = rmsnorm_aligned(p, residual);
+    if (forced) {
+        if (index < -1 || index >= count)
+            return RK_ERR_INVALID_ARG;
+        if (index == -1)
+            return rmsnorm_generic(p, residual, aligned);
+        if (!aligned || !v[index].accepts(p.N))
+            return RK_ERR_UNSUPPORTED;
+        return run_tile(v[index], p);
+    }
+    const int idx = pick_variant(residual ? RK_OP_RESIDUAL_RMSNORM : RK_OP_RMSNORM, p.dtype, p.N);
+    if (aligned && idx >= 0)
+        return run_tile(v[idx], p);
+    return rmsnorm_generic(p, residual, aligned);
 }
 
 }  // namespace
@@ -276,6 +381,34 @@ RK_EXPORT rk_status rk_layernorm_gelu(const void *x, const void *weight, const v
         return run_tile(layernorm_gelu_variants(dtype, &count)[idx], p);
     }
     return layernorm_generic(p, aligned);
+}
+
+RK_EXPORT rk_status rk_rmsnorm(const void *x, const void *weight, void *y, int64_t M, int64_t N,
+                               int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
+                               hipStream_t stream)
+{
+    rk_status st = check_rmsnorm(x, weight, y, M, N, ldx, ldy, eps, dtype);
+    if (st != RK_OK || M == 0)
+        return st;
+    const RowProblem p = make_problem(x, y, weight, nullptr, M, N, ldx, ldy, eps, dtype, stream);
+    return rmsnorm_dispatch(p, false, 0, false);
+}
+
+RK_EXPORT rk_status rk_residual_rmsnorm(const void *x, const void *residual, const void *weight,
+                                        void *y, void *residual_out, int64_t M, int64_t N,
+                                        int64_t ldx, int64_t ldr, int64_t ldy, int64_t ldo,
+                                        float eps, rk_dtype dtype, hipStream_t stream)
+{
+    rk_status st = check_residual_rmsnorm(x, residual, weight, y, residual_out, M, N, ldx, ldr,
+                                          ldy, ldo, eps, dtype);
+    if (st != RK_OK || M == 0)
+        return st;
+    RowProblem p = make_problem(x, y, weight, nullptr, M, N, ldx, ldy, eps, dtype, stream);
+    p.r = residual;
+    p.ro = residual_out;
+    p.ldr = ldr;
+    p.ldo = ldo;
+    return rmsnorm_dispatch(p, true, 0, false);
 }
 
 RK_EXPORT const char *rk_status_string(rk_status status)
@@ -392,4 +525,45 @@ RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, con
     if (!aligned || !v[index].accepts(N))
         return RK_ERR_UNSUPPORTED;
     return run_tile(v[index], p);
+}
+
+RK_EXPORT rk_status rk__rmsnorm_variant(int32_t index, const void *x, const void *weight, void *y,
+                                        int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
+                                        rk_dtype dtype, hipStream_t stream)
+{
+    rk_status st = check_rmsnorm(x, weight, y, M, N, ldx, ldy, eps, dtype);
+    if (st != RK_OK)
+        return st;
+    int count = 0;
+    rmsnorm_variants(dtype, false, &count);
+    if (index < -1 || index >= count)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const RowProblem p = make_problem(x, y, weight, nullptr, M, N, ldx, ldy, eps, dtype, stream);
+    return rmsnorm_dispatch(p, false, index, true);
+}
+
+RK_EXPORT rk_status rk__residual_rmsnorm_variant(int32_t index, const void *x, const void *residual,
+                                                 const void *weight, void *y, void *residual_out,
+                                                 int64_t M, int64_t N, int64_t ldx, int64_t ldr,
+                                                 int64_t ldy, int64_t ldo, float eps,
+                                                 rk_dtype dtype, hipStream_t stream)
+{
+    rk_status st = check_residual_rmsnorm(x, residual, weight, y, residual_out, M, N, ldx, ldr,
+                                          ldy, ldo, eps, dtype);
+    if (st != RK_OK)
+        return st;
+    int count = 0;
+    rmsnorm_variants(dtype, true, &count);
+    if (index < -1 || index >= count)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    RowProblem p = make_problem(x, y, weight, nullptr, M, N, ldx, ldy, eps, dtype, stream);
+    p.r = residual;
+    p.ro = residual_out;
+    p.ldr = ldr;
+    p.ldo = ldo;
+    return rmsnorm_dispatch(p, true, index, true);
 }

@@ -38,14 +38,17 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStr
 struct RowProblem {
     const void *x;
     void *y;
-    const void *w;  // LayerNorm only
-    const void *b;  // LayerNorm only
+    const void *w;  // normalizations: weight
+    const void *b;  // LayerNorm: bias
     int64_t M;
     int N;
     int64_t ldx, ldy;
-    float eps;  // LayerNorm only
+    float eps;  // normalizations
     rk_dtype dtype;
     hipStream_t stream;
+    const void *r = nullptr;  // residual RMSNorm: residual input
+    void *ro = nullptr;       // residual RMSNorm: residual output
+    int64_t ldr = 0, ldo = 0;
 };
 
 // A compiled register-resident kernel shape.
@@ -66,12 +69,14 @@ struct TileVariant {
 // general variant whose max_n covers N.
 const TileVariant *softmax_variants(rk_dtype dtype, int *count);
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count);
+const TileVariant *rmsnorm_variants(rk_dtype dtype, bool residual, int *count);
 
 // Generic paths (any alignment, any N).
 hipError_t online_stream_run(const RowProblem &p, bool vectorized);
 hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
                             bool vectorized);
 hipError_t layernorm_gelu_loop_run(const RowProblem &p, bool vectorized);
+hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, bool vectorized);
 hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
                           hipStream_t stream);
 

@@ -16,6 +16,10 @@ Recipes (one per named workload; seeds are ``1000 + k``):
 
 Draw order is always x, then w, then b.  bf16 values are produced by torch's
 round-to-nearest-even cast of the fp32 draw.
+
+RMSNorm runs on the same workloads: its input is ``x``, its weight ``w``; the
+fused residual variant adds ``residual(name)``, an independent N(0,1) draw of
+the workload's shape and dtype from seed ``seed + 100``.
 """
 from __future__ import annotations
 
@@ -23,7 +27,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make", "randn", "ln_params", "bf16_round"]
+__all__ = ["Workload", "WORKLOADS", "make", "randn", "ln_params", "bf16_round", "residual"]
 
 
 @dataclass(frozen=True)
@@ -105,3 +109,11 @@ def make(name: str, rows: int | None = None) -> dict:
     if rows is not None:
         x, xs = x[:rows].contiguous(), xs[:rows].contiguous()
     return {"x": x, "x_softmax": xs, "w": w, "b": b, "workload": wl}
+
+
+def residual(name: str, rows: int | None = None) -> torch.Tensor:
+    """The residual-stream input paired with workload ``name``'s x: N(0,1) of
+    the same shape and dtype, seed ``seed + 100`` (first ``rows`` rows if given)."""
+    wl = WORKLOADS[name]
+    r = randn(wl.M, wl.N, seed=wl.seed + 100, dtype=wl.dtype)
+    return r if rows is None else r[:rows].contiguous()

@@ -81,6 +81,9 @@ def test_m_zero_is_a_noop(lib):
     assert sm(lib, x=None, y=None, M=0) == 0
     assert lib.rk_online_softmax(None, None, 0, 8, 8, 8, F32, 64, None, 0, None) == 0
     assert lib.rk_layernorm_gelu(None, None, None, None, 0, 8, 8, 8, 1e-5, F32, None) == 0
+    assert lib.rk_rmsnorm(None, None, None, 0, 8, 8, 8, 1e-5, F32, None) == 0
+    assert lib.rk_residual_rmsnorm(None, None, None, None, None, 0, 8, 8, 8, 8, 8, 1e-5, F32,
+                                   None) == 0
     # but sizes are still checked
     assert sm(lib, x=None, y=None, M=0, N=0) == INVALID
 
@@ -96,6 +99,50 @@ def ln(lib, x=A, w=A + 0x80000, b=A + 0x90000, y=B, M=4, N=8, ldx=8, ldy=8, eps=
 ])
 def test_layernorm_rejects(lib, kw):
     assert ln(lib, **kw) == INVALID
+
+
+def rms(lib, x=A, w=A + 0x80000, y=B, M=4, N=8, ldx=8, ldy=8, eps=1e-5, dt=F32):
+    return lib.rk_rmsnorm(x, w, y, M, N, ldx, ldy, eps, dt, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(eps=0.0), dict(eps=-1.0), dict(eps=float("nan")), dict(eps=float("inf")), dict(w=None),
+    dict(x=None), dict(y=None), dict(w=B + 8), dict(w=A + 0x80002), dict(dt=3), dict(N=0),
+    dict(ldx=7), dict(y=A + 32), dict(x=A + 1, dt=BF16),
+])
+def test_rmsnorm_rejects(lib, kw):
+    assert rms(lib, **kw) == INVALID
+
+
+C = 0x1100000
+D = 0x1900000
+
+
+def res_rms(lib, x=A, r=C, w=A + 0x80000, y=B, ro=D, M=4, N=8, ldx=8, ldr=8, ldy=8, ldo=8,
+            eps=1e-5, dt=F32):
+    return lib.rk_residual_rmsnorm(x, r, w, y, ro, M, N, ldx, ldr, ldy, ldo, eps, dt, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(eps=0.0), dict(eps=float("nan")), dict(w=None), dict(r=None), dict(ro=None),
+    dict(x=None), dict(y=None), dict(dt=2), dict(N=0), dict(M=-1), dict(ldr=7), dict(ldo=7),
+    dict(ro=D + 2), dict(r=C + 2, dt=F32),
+    dict(ro=B),  # the two outputs coincide
+    dict(ro=B + 64),  # the outputs overlap
+    dict(ro=A + 0x80000 - 16),  # residual_out overlaps the weight
+    dict(y=A + 0x80000),  # y is the weight
+    dict(ro=A + 16),  # partial overlap with x
+    dict(y=C + 32),  # partial overlap with residual
+    dict(ro=C, ldo=16),  # same pointer, other pitch
+])
+def test_residual_rmsnorm_rejects(lib, kw):
+    assert res_rms(lib, **kw) == INVALID
+
+
+def test_residual_rmsnorm_limits(lib):
+    n = 2**30 + 1
+    assert res_rms(lib, M=1, N=n, ldx=n, ldr=n, ldy=n, ldo=n) == UNSUPPORTED
+    assert rms(lib, M=1, N=n, ldx=n, ldy=n) == UNSUPPORTED
 
 
 def online(lib, x=A, y=B, M=4, N=4096, S=64, ws=A + 0x400000, wb=4 * 64 * 8, dt=F32):
@@ -131,8 +178,11 @@ def test_probe_copy_rejects(lib):
     assert lib.rk_probe_copy(None, B, 64, 0, None) == INVALID
 
 
+OPS = (rk.RK_OP_SOFTMAX, rk.RK_OP_LAYERNORM_GELU, rk.RK_OP_RMSNORM, rk.RK_OP_RESIDUAL_RMSNORM)
+
+
 def test_variant_tables():
-    for op in (rk.RK_OP_SOFTMAX, rk.RK_OP_LAYERNORM_GELU):
+    for op in OPS:
         for dt, E, cap in ((F32, 4, 16384), (BF16, 8, 32768)):
             vs = rk.variants(op, dt)
             assert vs
@@ -162,6 +212,14 @@ def test_variant_entry_points_reject(lib):
     assert lib.rk__softmax_variant(-2, A, B, 4, 8, 8, 8, F32, None) == INVALID
     assert lib.rk__layernorm_gelu_variant(0, A, A + 0x80000, A + 0x90000, B, 4, 8, 8, 8, 0.0,
                                           F32, None) == INVALID
+    n = lib.rk__variant_count(rk.RK_OP_RMSNORM, F32)
+    assert n == lib.rk__variant_count(rk.RK_OP_RESIDUAL_RMSNORM, F32) > 0
+    assert lib.rk__rmsnorm_variant(n, A, A + 0x80000, B, 4, 8, 8, 8, 1e-5, F32, None) == INVALID
+    assert lib.rk__rmsnorm_variant(-2, A, A + 0x80000, B, 4, 8, 8, 8, 1e-5, F32, None) == INVALID
+    assert lib.rk__residual_rmsnorm_variant(n, A, C, A + 0x80000, B, D, 4, 8, 8, 8, 8, 8, 1e-5,
+                                            F32, None) == INVALID
+    assert lib.rk__residual_rmsnorm_variant(0, A, C, A + 0x80000, B, B, 4, 8, 8, 8, 8, 8, 1e-5,
+                                            F32, None) == INVALID
 
 
 def test_product_path_has_no_oracle_or_cpu_fallback():
@@ -173,5 +231,6 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
         assert "import oracle" not in text and "from oracle" not in text, path
         assert "liboracle" not in text, path
         if path.endswith(".py"):
-            for fn in ("torch.softmax", "F.softmax", "layer_norm(", "F.gelu", ".softmax("):
+            for fn in ("torch.softmax", "F.softmax", "layer_norm(", "F.gelu", ".softmax(",
+                       "rms_norm", ".rsqrt("):
                 assert fn not in text, (path, fn)

@@ -30,3 +30,12 @@ def test_rows_prefix():
     part = rowgen.make("ln_gelu_f32_4096x768", rows=10)
     assert torch.equal(full["x"][:10], part["x"])
     assert torch.equal(full["w"], part["w"])
+
+
+def test_residual_is_independent_and_seeded():
+    d = rowgen.make("ln_gelu_f32_4096x768", rows=16)
+    r = rowgen.residual("ln_gelu_f32_4096x768", rows=16)
+    assert r.shape == d["x"].shape and r.dtype == d["x"].dtype
+    assert torch.equal(r, rowgen.residual("ln_gelu_f32_4096x768")[:16])
+    assert not torch.equal(r, d["x"])
+    assert rowgen.residual("bf16_16384x4096", rows=2).dtype == torch.bfloat16

@@ -10,6 +10,11 @@ denominator floored at the unit scale of normalized activations.  z = w x_hat + 
 cancels near zero, so a pure relative measure would judge rounding noise of
 fp32 arithmetic around z = 0, not the kernel.
 
+RMSNorm and fused residual RMSNorm: pure relative error (rel_err), as for
+softmax.  y = v * inv_rms * w is a product with no cancellation, and
+residual_out = x + residual is one correctly rounded addition; an exact zero
+reference (v = 0) demands an exact zero.
+
 Tolerances: 1e-5 for fp32 input/output, 1e-2 for bf16 storage with fp32
 arithmetic.
 """
@@ -55,3 +60,8 @@ def rel_err_floor1(y, ref, floor: float = 1.0) -> float:
     if not np.all(np.isfinite(y)):
         return float("inf")
     return float((np.abs(y - ref) / np.maximum(np.abs(ref), floor)).max())
+
+
+def rel_err(y, ref) -> float:
+    """max |y - r| / |r| (zero references require exact zeros)."""
+    return rel_err_softmax(y, ref)
