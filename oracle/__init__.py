@@ -24,7 +24,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 __all__ = [
     "build", "Oracle", "default", "softmax", "softmax_stats", "online_softmax", "online_stats",
     "merge", "split_stats", "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
-    "layernorm_gelu",
+    "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf", "chunk_moments",
+    "chan_merge", "split_moments", "layernorm_gelu_ex",
 ]
 
 
@@ -57,6 +58,11 @@ def _signatures():
         "oracle_rms_stats": [P, i64, d, P, P],
         "oracle_rmsnorm": [P, P, P, i64, i64, d],
         "oracle_residual_rmsnorm": [P, P, P, P, P, i64, i64, d],
+        "oracle_gelu_erf_array": [P, P, i64],
+        "oracle_chunk_moments": [P, i64, P, P],
+        "oracle_chan_merge": [d, d, d, d, d, d, P, P, P],
+        "oracle_split_moments": [P, i64, i64, P, P, P, P, P],
+        "oracle_layernorm_gelu_ex": [P, P, P, P, i64, i64, d, ctypes.c_int, i64],
     }
 
 
@@ -204,6 +210,51 @@ class Oracle:
                                          x.shape[1], float(eps))
         return y, r
 
+    def gelu_erf(self, z) -> np.ndarray:
+        """Exact GeLU 0.5 z (1 + erf(z / sqrt 2)), elementwise."""
+        z = _f64(z)
+        y = np.empty_like(z)
+        self.lib.oracle_gelu_erf_array(_p(z), _p(y), z.size)
+        return y
+
+    def chunk_moments(self, row):
+        """(mean, M2) of a row: M2 = sum of squared deviations from the mean."""
+        r = _f64(row).ravel()
+        mean, m2 = ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_chunk_moments(_p(r), r.size, ctypes.byref(mean), ctypes.byref(m2))
+        return mean.value, m2.value
+
+    def chan_merge(self, a, b):
+        """Combine two (n, mean, M2) summaries of disjoint parts of a row."""
+        n, mean, m2 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_chan_merge(float(a[0]), float(a[1]), float(a[2]), float(b[0]),
+                                   float(b[1]), float(b[2]), ctypes.byref(n), ctypes.byref(mean),
+                                   ctypes.byref(m2))
+        return n.value, mean.value, m2.value
+
+    def split_moments(self, row, splits: int):
+        """(mean, M2, n_parts, mean_parts, m2_parts) of the split-row statistics."""
+        r = _f64(row).ravel()
+        parts = [np.empty(splits) for _ in range(3)]
+        mean, m2 = ctypes.c_double(), ctypes.c_double()
+        self.lib.oracle_split_moments(_p(r), r.size, int(splits), _p(parts[0]), _p(parts[1]),
+                                      _p(parts[2]), ctypes.byref(mean), ctypes.byref(m2))
+        return (mean.value, m2.value, *parts)
+
+    def layernorm_gelu_ex(self, x, w, b, eps: float, gelu: str = "tanh",
+                          splits: int = 0) -> np.ndarray:
+        """LayerNorm + affine + GeLU ("tanh" or "erf"); splits = 0 takes the
+        whole-row statistics, splits >= 1 the Chan-merged split statistics."""
+        x = _rows(x)
+        w = _f64(w).ravel()
+        b = _f64(b).ravel()
+        assert w.size == x.shape[1] and b.size == x.shape[1]
+        kind = {"tanh": 0, "erf": 1}[gelu]
+        y = np.empty_like(x)
+        self.lib.oracle_layernorm_gelu_ex(_p(x), _p(w), _p(b), _p(y), x.shape[0], x.shape[1],
+                                          float(eps), kind, int(splits))
+        return y
+
 
 _default = None
 
@@ -226,6 +277,7 @@ def _forward(name):
 
 for _n in ["softmax", "softmax_stats", "online_stats", "merge", "split_stats", "online_softmax",
            "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
-           "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm"]:
+           "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf",
+           "chunk_moments", "chan_merge", "split_moments", "layernorm_gelu_ex"]:
     globals()[_n] = _forward(_n)
 del _n

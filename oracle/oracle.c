@@ -23,6 +23,7 @@
  * high-precision brute force; none is "parity unpinned".
  */
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 /* ---------------------------------------------------------------------- */
@@ -287,5 +288,120 @@ void oracle_residual_rmsnorm(const double *x, const double *res, const double *w
         oracle_rms_stats(rr, N, eps, &ms, &inv);
         for (int64_t j = 0; j < N; ++j)
             y[i * N + j] = rr[j] * inv * w[j];
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Exact GeLU: [TKE] §3.4 "Approx Activation" gives the exact form next to */
+/* the tanh approximation:  gelu_exact(z) = 0.5 z (1 + erf(z / sqrt(2))).  */
+/* ---------------------------------------------------------------------- */
+double oracle_gelu_erf(double z)
+{
+    return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+}
+
+void oracle_gelu_erf_array(const double *z, double *y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = oracle_gelu_erf(z[i]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* LayerNorm statistics of long rows by parts.  [TKE] §6.3 "使用 online    */
+/* reduction": when the reduced dimension is long, reduce it in pieces     */
+/* instead of holding the whole row.  For LayerNorm a piece is summarised  */
+/* by (n, mean, M2), M2 = sum of squared deviations from the piece's own   */
+/* mean, and two pieces combine by the pairwise update of Chan, Golub and  */
+/* LeVeque ("Updating formulae and a pairwise algorithm for computing      */
+/* sample variances", 1979):                                               */
+/*   n = n1 + n2,  delta = mean2 - mean1,                                  */
+/*   mean = mean1 + delta * n2 / n,  M2 = M2_1 + M2_2 + delta^2 n1 n2 / n.  */
+/* The row's biased variance is M2 / N.                                    */
+/* ---------------------------------------------------------------------- */
+
+/* (mean, M2) of n values by two passes (n >= 1). */
+void oracle_chunk_moments(const double *x, int64_t n, double *mean_out, double *m2_out)
+{
+    double s = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        s += x[j];
+    double mean = s / (double)n;
+    double q = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        q += (x[j] - mean) * (x[j] - mean);
+    *mean_out = mean;
+    *m2_out = q;
+}
+
+/* Combine two summaries; a side with n = 0 is empty and is the identity. */
+void oracle_chan_merge(double n1, double mean1, double m2_1, double n2, double mean2, double m2_2,
+                       double *n_out, double *mean_out, double *m2_out)
+{
+    if (n1 == 0.0) {
+        *n_out = n2, *mean_out = mean2, *m2_out = m2_2;
+        return;
+    }
+    if (n2 == 0.0) {
+        *n_out = n1, *mean_out = mean1, *m2_out = m2_1;
+        return;
+    }
+    double n = n1 + n2;
+    double delta = mean2 - mean1;
+    *n_out = n;
+    *mean_out = mean1 + delta * n2 / n;
+    *m2_out = m2_1 + m2_2 + delta * delta * n1 * n2 / n;
+}
+
+/* Split-row statistics: S chunks of C = ceil(N / S) elements, chunk s =
+ * [s*C, min(N, (s+1)*C)) (empty chunks have n = 0); per-chunk summaries go
+ * to the *_parts arrays (length S, may be NULL) and are merged left to
+ * right.  Returns the row's mean and M2. */
+void oracle_split_moments(const double *x, int64_t N, int64_t S, double *n_parts,
+                          double *mean_parts, double *m2_parts, double *mean_out, double *m2_out)
+{
+    int64_t C = (N + S - 1) / S;
+    double n = 0.0, mean = 0.0, m2 = 0.0;
+    for (int64_t s = 0; s < S; ++s) {
+        int64_t lo = s * C;
+        int64_t hi = lo + C < N ? lo + C : N;
+        double cn = 0.0, cmean = 0.0, cm2 = 0.0;
+        if (hi > lo) {
+            cn = (double)(hi - lo);
+            oracle_chunk_moments(x + lo, hi - lo, &cmean, &cm2);
+        }
+        if (n_parts)
+            n_parts[s] = cn;
+        if (mean_parts)
+            mean_parts[s] = cmean;
+        if (m2_parts)
+            m2_parts[s] = cm2;
+        oracle_chan_merge(n, mean, m2, cn, cmean, cm2, &n, &mean, &m2);
+    }
+    *mean_out = mean;
+    *m2_out = m2;
+}
+
+/* LayerNorm + affine + GeLU with a choice of statistics and activation:
+ * S = 0 takes the whole-row two-pass statistics of oracle_layernorm_stats,
+ * S >= 1 the split statistics above (rstd = 1 / sqrt(M2 / N + eps));
+ * gelu = 0 is the tanh approximation, 1 the exact erf form. */
+void oracle_layernorm_gelu_ex(const double *x, const double *w, const double *b, double *y,
+                              int64_t M, int64_t N, double eps, int gelu, int64_t S)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        const double *xr = x + i * N;
+        double *yr = y + i * N;
+        double mean, var, rstd;
+        if (S == 0) {
+            oracle_layernorm_stats(xr, N, eps, &mean, &var, &rstd);
+        } else {
+            double m2;
+            oracle_split_moments(xr, N, S, NULL, NULL, NULL, &mean, &m2);
+            rstd = 1.0 / sqrt(m2 / (double)N + eps);
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double z = (xr[j] - mean) * rstd * w[j] + b[j];
+            yr[j] = gelu ? oracle_gelu_erf(z) : oracle_gelu_tanh(z);
+        }
     }
 }

@@ -30,6 +30,16 @@ What pins what (citations are to the pages' titles and sections):
   form; an eps-sensitive row against numpy's mean of squares.
 * fused residual RMSNorm, same page §4.3: residual_out is x + residual
   exactly; out is RMSNorm of residual_out (torch, float64).
+* exact GeLU, same page §3.4: GeLU(0) = 0; GeLU(z) - GeLU(-z) = z; z times the
+  standard normal CDF at 50 digits (mpmath); torch gelu(approximate="none")
+  in float64; its largest distance to the tanh form is 4.73e-4 near -2.70.
+* split LayerNorm statistics (same page §6.3, reduction by parts, merged by
+  Chan, Golub and LeVeque's pairwise update): arithmetic progressions in
+  closed form; the merge has n = 0 as identity, is commutative and
+  associative, and merging pieces gives the whole-row two-pass moments; the
+  split statistics of any chunk count equal the whole row's; LayerNorm + GeLU
+  on them equals the whole-row version, and with erf equals torch's
+  layer_norm followed by the exact gelu.
 """
 from __future__ import annotations
 
@@ -357,6 +367,138 @@ def check_residual_rmsnorm(orc):
     assert np.array_equal(y0, orc.rmsnorm(x, w, EPS))
 
 
+# ------------------------------------------------------------ exact GeLU
+
+
+def check_gelu_erf_basic(orc):
+    z = np.linspace(-12.0, 12.0, 2401)
+    y = orc.gelu_erf(z)
+    assert orc.gelu_erf(np.array([0.0]))[0] == 0.0
+    # erf is odd: GeLU(z) - GeLU(-z) = z
+    assert np.max(np.abs((y - orc.gelu_erf(-z)) - z) / np.maximum(np.abs(z), 1e-300)) <= 4e-16
+    assert np.all(np.abs(y[z >= 9.0] - z[z >= 9.0]) <= 1e-15 * z[z >= 9.0])
+    assert np.all(np.abs(y[z <= -9.0]) <= 1e-17)
+
+
+def check_gelu_erf_brute_force(orc):
+    import mpmath
+
+    mpmath.mp.dps = 50
+    z = np.array([-6.0, -3.5, -2.7, -1.0, -0.25, 1e-3, 0.5, 1.0, 2.0, 4.75])
+    y = orc.gelu_erf(z)
+    ref = np.array([float(mpmath.mpf(float(v)) * mpmath.ncdf(mpmath.mpf(float(v)))) for v in z])
+    # relative where 1 + erf does not cancel; in the negative tail the literal
+    # form is accurate to ~1e-16 absolute (the unit scale of the comparisons)
+    ok = z >= -1.0
+    assert _rel(y[ok], ref[ok]) <= 2e-15
+    assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1.0)) <= 2e-15
+
+
+def check_gelu_erf_torch_and_tanh_gap(orc):
+    import torch
+    import torch.nn.functional as F
+
+    z = np.linspace(-8.0, 8.0, 16001)
+    y = orc.gelu_erf(z)
+    ref = F.gelu(torch.from_numpy(z), approximate="none").numpy()
+    assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1.0)) <= 1e-15
+    gap = np.abs(y - orc.gelu_tanh(z))
+    k = int(np.argmax(gap))
+    assert 4.70e-4 <= gap[k] <= 4.76e-4 and abs(z[k] + 2.70) <= 0.02, (gap[k], z[k])
+
+
+# ------------------------------------------------- split LayerNorm statistics
+
+
+def check_chunk_moments_closed_form(orc):
+    for n, a, d in [(1, 3.5, 0.0), (2, -1.0, 2.0), (10, 0.0, 1.0), (1001, 7.25, -0.125),
+                    (65536, -3.0, 2.0**-10)]:
+        x = a + d * np.arange(n, dtype=np.float64)
+        mean, m2 = orc.chunk_moments(x)
+        assert abs(mean - (a + d * (n - 1) / 2.0)) <= 1e-15 * max(abs(a), 1.0) * 4, (n, mean)
+        ref = d * d * n * (n * n - 1) / 12.0
+        assert abs(m2 - ref) <= 1e-13 * max(ref, 1e-300), (n, m2, ref)
+    # a constant whose partial sums are exact: mean exactly c, M2 exactly 0
+    mean, m2 = orc.chunk_moments(np.full(777, 0.375))
+    assert mean == 0.375 and m2 == 0.0
+
+
+def check_chan_merge_algebra(orc):
+    r = _rng(53)
+    x = 5.0 + 2.0 * r.standard_normal(1000)
+    whole = orc.chunk_moments(x)
+    for cut in (1, 2, 333, 500, 999):
+        a = (cut, *orc.chunk_moments(x[:cut]))
+        b = (1000 - cut, *orc.chunk_moments(x[cut:]))
+        n, mean, m2 = orc.chan_merge(a, b)
+        assert n == 1000
+        assert abs(mean - whole[0]) <= 1e-14 * abs(whole[0]), cut
+        assert abs(m2 - whole[1]) <= 1e-13 * whole[1], cut
+        n2, mean2, m22 = orc.chan_merge(b, a)  # commutative (up to rounding)
+        assert abs(mean2 - mean) <= 1e-14 * abs(mean) and abs(m22 - m2) <= 1e-13 * m2
+    e = (0.0, 0.0, 0.0)
+    s = (17.0, 1.5, 4.25)
+    assert orc.chan_merge(e, s) == s and orc.chan_merge(s, e) == s
+    # two single points: mean (a+b)/2, M2 = (a-b)^2/2
+    n, mean, m2 = orc.chan_merge((1.0, 3.0, 0.0), (1.0, -1.0, 0.0))
+    assert (n, mean, m2) == (2.0, 1.0, 8.0)
+    # associativity over three pieces
+    p = [(k, *orc.chunk_moments(x[i:i + k])) for i, k in ((0, 100), (100, 650), (750, 250))]
+    left = orc.chan_merge(orc.chan_merge(p[0], p[1]), p[2])
+    right = orc.chan_merge(p[0], orc.chan_merge(p[1], p[2]))
+    assert abs(left[1] - right[1]) <= 1e-14 * abs(left[1])
+    assert abs(left[2] - right[2]) <= 1e-13 * left[2]
+    # arithmetic progression halves merge to the closed form
+    ap = np.arange(64, dtype=np.float64)
+    n, mean, m2 = orc.chan_merge((32.0, *orc.chunk_moments(ap[:32])),
+                                 (32.0, *orc.chunk_moments(ap[32:])))
+    assert mean == 31.5 and abs(m2 - 64 * (64 * 64 - 1) / 12.0) <= 1e-12
+
+
+def check_split_moments_match_whole_row(orc):
+    r = _rng(59)
+    for n in (1, 5, 768, 4099, 262144):
+        x = -2.0 + 3.0 * r.standard_normal(n)
+        mean, m2 = orc.chunk_moments(x)
+        for S in sorted({1, 2, 3, 7, 64, n, n + 3}):
+            sm, sm2, npart, mpart, m2part = orc.split_moments(x, S)
+            assert abs(sm - mean) <= 1e-13 * max(abs(mean), 1.0), (n, S)
+            assert abs(sm2 - m2) <= 1e-12 * max(m2, 1e-300), (n, S, sm2, m2)
+            assert npart.sum() == n and np.all(npart >= 0)
+            C = -(-n // S)
+            for s in (0, S // 2, S - 1):
+                lo, hi = s * C, min(n, (s + 1) * C)
+                if hi > lo:
+                    cm, cm2 = orc.chunk_moments(x[lo:hi])
+                    assert npart[s] == hi - lo and mpart[s] == cm and m2part[s] == cm2
+                else:
+                    assert npart[s] == 0
+
+
+def check_layernorm_gelu_ex(orc):
+    import torch
+    import torch.nn.functional as F
+
+    r = _rng(61)
+    n = 3000
+    x = r.standard_normal((5, n)) * np.array([[1.0], [10.0], [1e-3], [1.0], [4.0]])
+    x[3] += 100.0  # a large mean: the split statistics must still centre
+    w = 1.0 + 0.1 * r.standard_normal(n)
+    b = 0.1 * r.standard_normal(n)
+    base = orc.layernorm_gelu(x, w, b, EPS)
+    assert np.array_equal(orc.layernorm_gelu_ex(x, w, b, EPS, "tanh", 0), base)
+    for S in (1, 5, 64, n + 1):
+        y = orc.layernorm_gelu_ex(x, w, b, EPS, "tanh", S)
+        assert np.max(np.abs(y - base) / np.maximum(np.abs(base), 1.0)) <= 1e-13, S
+    xt = torch.from_numpy(x)
+    ln = F.layer_norm(xt, (n,), torch.from_numpy(w), torch.from_numpy(b), EPS)
+    ref = F.gelu(ln, approximate="none").numpy()
+    for S in (0, 7):
+        y = orc.layernorm_gelu_ex(x, w, b, EPS, "erf", S)
+        assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1.0)) <= 1e-13, S
+    assert np.max(np.abs(orc.layernorm_gelu_ex(x, w, b, EPS, "erf", 0) - base)) > 1e-4
+
+
 PINS = [
     check_softmax_sums_to_one,
     check_softmax_shift_invariance,
@@ -379,4 +521,11 @@ PINS = [
     check_rmsnorm_torch,
     check_rmsnorm_invariants,
     check_residual_rmsnorm,
+    check_gelu_erf_basic,
+    check_gelu_erf_brute_force,
+    check_gelu_erf_torch_and_tanh_gap,
+    check_chunk_moments_closed_form,
+    check_chan_merge_algebra,
+    check_split_moments_match_whole_row,
+    check_layernorm_gelu_ex,
 ]

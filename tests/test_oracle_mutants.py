@@ -22,7 +22,7 @@ MUTANTS = {
     "online_rescale_inverted": ("return exp(m_old - m_new);", "return exp(m_new - m_old);"),
     "online_block_sum_old_max": ("block_sum += exp(x[j] - m_new);", "block_sum += exp(x[j] - block_max);"),
     "merge_second_unscaled": ("d1 * rescale(m1, M) + d2 * rescale(m2, M)", "d1 * rescale(m1, M) + d2"),
-    "split_chunk_size": ("int64_t C = (N + S - 1) / S;", "int64_t C = N / S + 1;"),
+    "split_chunk_size": ("int64_t C = (N + S - 1) / S;\n    double m = -INFINITY", "int64_t C = N / S + 1;\n    double m = -INFINITY"),
     "gelu_cubic_coeff": ("0.044715 * z * z * z", "0.04715 * z * z * z"),
     "gelu_half_dropped": ("return 0.5 * z * (1.0 + tanh(", "return z * (1.0 + tanh("),
     "gelu_scale_constant": ("sqrt(2.0 / M_PI)", "sqrt(M_PI / 2.0)"),
@@ -30,16 +30,27 @@ MUTANTS = {
     "ln_unbiased_variance": ("double var = q / (double)N;", "double var = q / (double)(N > 1 ? N - 1 : 1);"),
     "ln_eps_outside_sqrt": ("*rstd_out = 1.0 / sqrt(var + eps);", "*rstd_out = 1.0 / (sqrt(var) + eps);"),
     "ln_eps_dropped": ("*rstd_out = 1.0 / sqrt(var + eps);", "*rstd_out = 1.0 / sqrt(var);"),
-    "ln_bias_sign": ("* rstd * w[j] + b[j];", "* rstd * w[j] - b[j];"),
-    "ln_weight_dropped": ("* rstd * w[j] + b[j];", "* rstd + b[j];"),
+    "ln_bias_sign": ("* rstd * w[j] + b[j];\n            yr[j] = oracle_gelu_tanh(z);", "* rstd * w[j] - b[j];\n            yr[j] = oracle_gelu_tanh(z);"),
+    "ln_weight_dropped": ("* rstd * w[j] + b[j];\n            yr[j] = oracle_gelu_tanh(z);", "* rstd + b[j];\n            yr[j] = oracle_gelu_tanh(z);"),
+    "ex_bias_sign": ("* rstd * w[j] + b[j];\n            yr[j] = gelu", "* rstd * w[j] - b[j];\n            yr[j] = gelu"),
     "ln_mean_divisor": ("double mean = s / (double)N;", "double mean = s / (double)(N + 1);"),
-    "ln_var_uncentered": ("q += (x[j] - mean) * (x[j] - mean);", "q += x[j] * x[j];"),
+    "ln_var_uncentered": ("q += (x[j] - mean) * (x[j] - mean);\n    double var", "q += x[j] * x[j];\n    double var"),
+    "chunk_mean_divisor": ("double mean = s / (double)n;", "double mean = s / (double)(n + 1);"),
     "rms_sum_not_mean": ("double ms = q / (double)N;", "double ms = q;"),
     "rms_eps_outside_sqrt": ("*inv_out = 1.0 / sqrt(ms + eps);", "*inv_out = 1.0 / (sqrt(ms) + eps);"),
     "rms_centred": ("        q += x[j] * x[j];\n    double ms", "        q += (x[j] - x[0]) * (x[j] - x[0]);\n    double ms"),
     "rms_weight_dropped": ("y[i * N + j] = x[i * N + j] * inv * w[j];", "y[i * N + j] = x[i * N + j] * inv;"),
     "residual_sign": ("rr[j] = x[i * N + j] + res[i * N + j];", "rr[j] = x[i * N + j] - res[i * N + j];"),
     "residual_not_normalized": ("y[i * N + j] = rr[j] * inv * w[j];", "y[i * N + j] = x[i * N + j] * inv * w[j];"),
+    "gelu_erf_no_sqrt2": ("erf(z / sqrt(2.0))", "erf(z)"),
+    "gelu_erf_half_dropped": ("return 0.5 * z * (1.0 + erf(", "return z * (1.0 + erf("),
+    "chunk_m2_uncentred": ("        q += (x[j] - mean) * (x[j] - mean);\n    *mean_out = mean;", "        q += x[j] * x[j];\n    *mean_out = mean;"),
+    "chan_delta_term_dropped": ("*m2_out = m2_1 + m2_2 + delta * delta * n1 * n2 / n;", "*m2_out = m2_1 + m2_2;"),
+    "chan_mean_weight": ("*mean_out = mean1 + delta * n2 / n;", "*mean_out = mean1 + delta * n1 / n;"),
+    "chan_identity_swapped": ("*n_out = n2, *mean_out = mean2, *m2_out = m2_2;", "*n_out = n1, *mean_out = mean1, *m2_out = m2_1;"),
+    "split_var_divisor": ("rstd = 1.0 / sqrt(m2 / (double)N + eps);", "rstd = 1.0 / sqrt(m2 / (double)(N - 1) + eps);"),
+    "ex_gelu_kind_ignored": ("yr[j] = gelu ? oracle_gelu_erf(z) : oracle_gelu_tanh(z);", "yr[j] = oracle_gelu_tanh(z);"),
+    "split_moments_chunk_floor": ("    int64_t C = (N + S - 1) / S;\n    double n = 0.0", "    int64_t C = N / S;\n    if (C < 1)\n        C = 1;\n    double n = 0.0"),
 }
 
 
