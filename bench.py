@@ -56,7 +56,7 @@ class Case:
 
     def setup(self, torch, rk, rowgen):
         d = rowgen.make(self.workload)
-        norm = self.op in ("layernorm_gelu", "rmsnorm", "residual_rmsnorm")
+        norm = self.op in ("layernorm_gelu", "layernorm_gelu_ex", "rmsnorm", "residual_rmsnorm")
         x = d["x"] if norm else d["x_softmax"]
         M, N = x.shape
         es = x.element_size()
@@ -66,6 +66,13 @@ class Case:
         footprint = io
         if self.op == "layernorm_gelu":
             self.bytes = io + 2 * N * es  # x, y, and w, b once
+        elif self.op == "layernorm_gelu_ex":
+            if self.splits == 0:
+                self.splits = rk.rk_layernorm_gelu_auto_splits(M, N, self.dtype_code)
+            # two reads of x, one write of y, w and b once (+ partials out and in)
+            self.bytes = 3 * M * N * es + 2 * N * es
+            if self.splits > 1:
+                self.bytes += 2 * M * self.splits * 8
         elif self.op == "rmsnorm":
             self.bytes = io + N * es  # x, y, and w once
         elif self.op == "residual_rmsnorm":
@@ -94,6 +101,9 @@ class Case:
         if self.op == "online" and self.splits > 1:
             nb = rk.rk_online_softmax_workspace_bytes(M, N, self.splits)
             self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        if self.op == "layernorm_gelu_ex" and self.splits > 1:
+            nb = rk.rk_layernorm_gelu_workspace_bytes(M, N, self.splits, self.dtype_code)
+            self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         lib = rk.load()
         stream = torch.cuda.current_stream().cuda_stream
         self.stream = stream
@@ -102,6 +112,13 @@ class Case:
             fn = lib.rk_layernorm_gelu
             self.args = [(xx.data_ptr(), self.w.data_ptr(), self.b.data_ptr(), yy.data_ptr(), M,
                           N, N, N, fp, self.dtype_code, stream)
+                         for xx, yy in zip(self.xs, self.ys)]
+        elif self.op == "layernorm_gelu_ex":
+            fn = lib.rk_layernorm_gelu_ex
+            wp = self.ws.data_ptr() if self.ws is not None else None
+            wb = self.ws.numel() if self.ws is not None else 0
+            self.args = [(xx.data_ptr(), self.w.data_ptr(), self.b.data_ptr(), yy.data_ptr(), M,
+                          N, N, N, fp, self.dtype_code, 0, self.splits, wp, wb, stream)
                          for xx, yy in zip(self.xs, self.ys)]
         elif self.op == "rmsnorm":
             fn = lib.rk_rmsnorm
@@ -173,6 +190,12 @@ def all_cases():
         Case("online_auto_f32_64x262144", "online", "online_f32_64x262144", splits=0),
         Case("ln_gelu_bf16_16384x4096", "layernorm_gelu", "bf16_16384x4096"),
         Case("softmax_bf16_16384x4096", "softmax", "bf16_16384x4096"),
+        Case("ln_gelu_stream_f32_64x262144", "layernorm_gelu_ex", "ln_long_f32_64x262144",
+             splits=1),
+        Case("ln_gelu_split64_f32_64x262144", "layernorm_gelu_ex", "ln_long_f32_64x262144",
+             splits=64),
+        Case("ln_gelu_auto_f32_64x262144", "layernorm_gelu_ex", "ln_long_f32_64x262144",
+             splits=0),
         Case("rmsnorm_f32_4096x768", "rmsnorm", "ln_gelu_f32_4096x768"),
         Case("residual_rmsnorm_f32_4096x768", "residual_rmsnorm", "ln_gelu_f32_4096x768"),
         Case("rmsnorm_bf16_16384x4096", "rmsnorm", "bf16_16384x4096"),

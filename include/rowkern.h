@@ -51,6 +51,12 @@ typedef enum rk_dtype {
     RK_BF16 = 1, /* bfloat16 storage, fp32 arithmetic */
 } rk_dtype;
 
+/* GeLU of the LayerNorm epilogue ([TKE] §3.4 gives both forms). */
+typedef enum rk_gelu {
+    RK_GELU_TANH = 0, /* 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
+    RK_GELU_ERF = 1,  /* 0.5 z (1 + erf(z / sqrt(2))), the exact form */
+} rk_gelu;
+
 typedef enum rk_status {
     RK_OK = 0,
     RK_ERR_INVALID_ARG = 1, /* a size, stride, pointer, dtype or eps is invalid */
@@ -133,8 +139,10 @@ int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N);
  *
  * x [M][ldx], y [M][ldy], weight [N], bias [N] (contiguous), all of `dtype`.
  * Rows up to 16384 (fp32) / 32768 (bf16) columns with 16-byte alignment stay
- * in registers (one HBM read and write per element); other rows are read
- * three times by a looping kernel with the same arithmetic.
+ * in registers (one HBM read and write per element); other rows take one
+ * workgroup per row that reads the row twice (statistics by parts merged as
+ * in rk_layernorm_gelu_ex, then the output).  Same as rk_layernorm_gelu_ex
+ * with RK_GELU_TANH and num_splits = 1.
  *
  * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight or bias is NULL
  * with M > 0, eps is not finite and > 0, or y overlaps weight or bias.
@@ -142,6 +150,47 @@ int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N);
 rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias, void *y,
                             int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
                             rk_dtype dtype, hipStream_t stream);
+
+/*
+ * rk_layernorm_gelu with a choice of activation and of how long rows are
+ * split ([TKE] §4.1 "LayerNorm", §3.4 "Approx Activation", and §6.3 on
+ * reducing a long dimension in pieces).
+ *
+ * gelu        RK_GELU_TANH or RK_GELU_ERF.
+ * num_splits  1: one workgroup (or register tile) per row, as
+ *             rk_layernorm_gelu.  S > 1: each row is cut into S chunks of
+ *             C = ceil(N / S) elements (rounded up to whole 16-byte vectors
+ *             on the vector path); a first kernel writes a summary of each
+ *             chunk to the workspace (its mean, taken relative to the row's
+ *             first element, and M2, the sum of squared deviations from
+ *             it), a second merges the row's S summaries by the
+ *             Chan-Golub-LeVeque pairwise update and writes the chunk:
+ *             2 reads + 1 write per element, all CUs busy even for a few
+ *             long rows.  0: rk_layernorm_gelu_auto_splits.
+ * workspace   for S > 1: caller-owned device memory of at least
+ *             rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype)
+ *             bytes, 8-byte aligned, not overlapping x, y, weight or bias;
+ *             ignored (may be NULL) for S = 1.
+ *
+ * Returns as rk_layernorm_gelu, plus RK_ERR_INVALID_ARG for an unknown gelu,
+ * num_splits outside [0, 65536], a misaligned or overlapping workspace;
+ * RK_ERR_WORKSPACE when it is NULL or too small; RK_ERR_UNSUPPORTED when
+ * M * S workgroups exceed the launch limits.
+ */
+rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, const void *bias, void *y,
+                               int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
+                               rk_dtype dtype, rk_gelu gelu, int32_t num_splits,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes rk_layernorm_gelu_ex needs: M * S * 8 for S > 1 (S the
+ * resolved split count), 0 for S = 1 or invalid arguments. */
+size_t rk_layernorm_gelu_workspace_bytes(int64_t M, int64_t N, int32_t num_splits,
+                                         rk_dtype dtype);
+
+/* The split count rk_layernorm_gelu_ex uses for num_splits == 0: 1 when a
+ * register tile holds the row (N up to 16384 fp32 / 32768 bf16) or M >= 512,
+ * else enough chunks of >= 2048 elements to give about 2048 workgroups. */
+int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
 
 /*
  * RMSNorm ([TKE] §4.2 "RMSNorm"):

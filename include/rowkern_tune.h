@@ -57,18 +57,18 @@ rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index, int32_t *wav
 int32_t rk__variant_pick(rk_op op, rk_dtype dtype, int64_t N);
 
 /*
- * rk_softmax / rk_layernorm_gelu forced onto one path: variant `index`
- * (RK_ERR_UNSUPPORTED if the data is not 16-byte aligned or the variant does
- * not accept N), or index -1 for the generic path (streaming online kernel for
- * softmax, three-pass looping kernel for LayerNorm+GeLU), which takes any
- * input.  Arguments otherwise as in rowkern.h.
+ * rk_softmax / rk_layernorm_gelu_ex (one workgroup per row) forced onto one
+ * path: variant `index` (RK_ERR_UNSUPPORTED if the data is not 16-byte
+ * aligned or the variant does not accept N), or index -1 for the generic path
+ * (the streaming kernels: online softmax, LayerNorm statistics by parts),
+ * which takes any input.  Arguments otherwise as in rowkern.h.
  */
 rk_status rk__softmax_variant(int32_t index, const void *x, void *y, int64_t M, int64_t N,
                               int64_t ldx, int64_t ldy, rk_dtype dtype, hipStream_t stream);
 rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, const void *weight,
                                      const void *bias, void *y, int64_t M, int64_t N,
                                      int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
-                                     hipStream_t stream);
+                                     rk_gelu gelu, hipStream_t stream);
 
 /* rk_rmsnorm / rk_residual_rmsnorm forced onto one path, as above (index -1:
  * the two-pass looping kernel). */

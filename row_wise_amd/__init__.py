@@ -10,6 +10,9 @@ Functions carry the C entry points' names:
 * ``rk_softmax(x, out=None)``
 * ``rk_online_softmax(x, num_splits=1, out=None, workspace=None)``
 * ``rk_layernorm_gelu(x, weight, bias, eps=1e-5, out=None)``
+* ``rk_layernorm_gelu_ex(x, weight, bias, eps=1e-5, gelu="tanh", num_splits=1, out=None,
+  workspace=None)``, ``rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype)``,
+  ``rk_layernorm_gelu_auto_splits(M, N, dtype)``
 * ``rk_rmsnorm(x, weight, eps=1e-5, out=None)``
 * ``rk_residual_rmsnorm(x, residual, weight, eps=1e-5, out=None, residual_out=None)``
 * ``rk_online_softmax_workspace_bytes(M, N, num_splits)``,
@@ -33,12 +36,16 @@ __all__ = [
     "rk__layernorm_gelu_variant", "variants", "RK_F32", "RK_BF16", "RK_OP_SOFTMAX",
     "RK_OP_LAYERNORM_GELU", "rk_rmsnorm", "rk_residual_rmsnorm", "rk__rmsnorm_variant",
     "rk__residual_rmsnorm_variant", "RK_OP_RMSNORM", "RK_OP_RESIDUAL_RMSNORM",
+    "rk_layernorm_gelu_ex", "rk_layernorm_gelu_workspace_bytes", "rk_layernorm_gelu_auto_splits",
+    "RK_GELU_TANH", "RK_GELU_ERF",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.so")
 
 RK_F32, RK_BF16 = 0, 1
 RK_OP_SOFTMAX, RK_OP_LAYERNORM_GELU, RK_OP_RMSNORM, RK_OP_RESIDUAL_RMSNORM = 0, 1, 2, 3
+RK_GELU_TANH, RK_GELU_ERF = 0, 1
+_GELU = {"tanh": RK_GELU_TANH, "erf": RK_GELU_ERF}
 RK_OK = 0
 
 
@@ -79,7 +86,11 @@ def load():
         "rk__variant_pick": (i32, [i32, i32, i64]),
         "rk__softmax_variant": (i32, [i32, vp, vp, i64, i64, i64, i64, i32, vp]),
         "rk__layernorm_gelu_variant": (i32, [i32, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32,
-                                             vp]),
+                                             i32, vp]),
+        "rk_layernorm_gelu_ex": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, i32, vp,
+                                       sz, vp]),
+        "rk_layernorm_gelu_workspace_bytes": (sz, [i64, i64, i32, i32]),
+        "rk_layernorm_gelu_auto_splits": (i32, [i64, i64, i32]),
         "rk_rmsnorm": (i32, [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
         "rk_residual_rmsnorm": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32,
                                       vp]),
@@ -210,18 +221,50 @@ def rk_online_softmax(x, num_splits: int = 1, out=None, workspace=None):
     return o.reshape(x.shape) if out is None else out
 
 
-def rk_layernorm_gelu(x, weight, bias, eps: float = 1e-5, out=None):
-    """Fused LayerNorm + affine + tanh GeLU over the last dimension."""
-    _check_device(x, weight, bias)
-    v, M, N, ldx = _as_rows(x)
+def _check_affine(weight, bias, x, N):
     if weight.shape != (N,) or bias.shape != (N,) or not weight.is_contiguous() \
             or not bias.is_contiguous():
         raise ValueError("weight and bias must be contiguous [N]")
     if weight.dtype != x.dtype or bias.dtype != x.dtype:
         raise ValueError("weight and bias must have the input's dtype")
+
+
+def rk_layernorm_gelu(x, weight, bias, eps: float = 1e-5, out=None):
+    """Fused LayerNorm + affine + tanh GeLU over the last dimension."""
+    _check_device(x, weight, bias)
+    v, M, N, ldx = _as_rows(x)
+    _check_affine(weight, bias, x, N)
     o, ldy = _out_like(x, v, out)
     _call("rk_layernorm_gelu", v.data_ptr(), weight.data_ptr(), bias.data_ptr(), o.data_ptr(),
           M, N, ldx, ldy, float(eps), _dtype_code(x), _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def rk_layernorm_gelu_workspace_bytes(M: int, N: int, num_splits: int, dtype: int) -> int:
+    return int(load().rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype))
+
+
+def rk_layernorm_gelu_auto_splits(M: int, N: int, dtype: int) -> int:
+    return int(load().rk_layernorm_gelu_auto_splits(M, N, dtype))
+
+
+def rk_layernorm_gelu_ex(x, weight, bias, eps: float = 1e-5, gelu: str = "tanh",
+                         num_splits: int = 1, out=None, workspace=None):
+    """LayerNorm + affine + GeLU ("tanh" or "erf"); num_splits 1: one
+    workgroup or tile per row, >= 2: split-row, 0: auto."""
+    torch = _torch()
+    _check_device(x, weight, bias)
+    v, M, N, ldx = _as_rows(x)
+    _check_affine(weight, bias, x, N)
+    o, ldy = _out_like(x, v, out)
+    dt = _dtype_code(x)
+    need = rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dt) if M > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _call("rk_layernorm_gelu_ex", v.data_ptr(), weight.data_ptr(), bias.data_ptr(), o.data_ptr(),
+          M, N, ldx, ldy, float(eps), dt, _GELU[gelu], int(num_splits), wptr, wbytes, _stream(x))
     return o.reshape(x.shape) if out is None else out
 
 
@@ -303,12 +346,14 @@ def rk__softmax_variant(index: int, x, out=None):
     return o.reshape(x.shape) if out is None else out
 
 
-def rk__layernorm_gelu_variant(index: int, x, weight, bias, eps: float = 1e-5, out=None):
+def rk__layernorm_gelu_variant(index: int, x, weight, bias, eps: float = 1e-5, out=None,
+                               gelu: str = "tanh"):
     _check_device(x, weight, bias)
     v, M, N, ldx = _as_rows(x)
     o, ldy = _out_like(x, v, out)
     _call("rk__layernorm_gelu_variant", int(index), v.data_ptr(), weight.data_ptr(),
-          bias.data_ptr(), o.data_ptr(), M, N, ldx, ldy, float(eps), _dtype_code(x), _stream(x))
+          bias.data_ptr(), o.data_ptr(), M, N, ldx, ldy, float(eps), _dtype_code(x), _GELU[gelu],
+          _stream(x))
     return o.reshape(x.shape) if out is None else out
 
 

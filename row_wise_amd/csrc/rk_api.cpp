@@ -1,6 +1,7 @@
 // C ABI of librowkern.so: argument validation (before any HIP call) and the
 // choice of kernel for each call.  See include/rowkern.h for the contract.
 #include <climits>
+#include <initializer_list>
 #include <cmath>
 #include <cstdint>
 
@@ -121,7 +122,7 @@ int64_t tile_blocks(const TileVariant &v, int64_t M)
 
 constexpr int kStreamThreads = 1024;  // online_stream workgroup size
 constexpr int kSplitThreads = 256;    // online_partials / online_finish
-constexpr int kLoopThreads = 256;     // layernorm_gelu_loop
+constexpr int kLoopThreads = 256;     // rmsnorm_loop
 constexpr int32_t kMaxSplits = 65536;
 
 int32_t auto_splits(int64_t M, int64_t N)
@@ -148,9 +149,60 @@ rk_status softmax_generic(const RowProblem &p, bool aligned)
 
 rk_status layernorm_generic(const RowProblem &p, bool aligned)
 {
-    if (!grid_ok(p.M, kLoopThreads))
+    if (!grid_ok(p.M, kStreamThreads))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(layernorm_gelu_loop_run(p, aligned));
+    return hip_status(layernorm_stream_run(p, aligned));
+}
+
+bool valid_gelu(rk_gelu g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
+
+// Largest N a LayerNorm register tile holds for `dtype`.
+int64_t layernorm_tile_cap(rk_dtype dtype)
+{
+    int count = 0;
+    const TileVariant *v = layernorm_gelu_variants(dtype, &count);
+    int64_t cap = 0;
+    for (int i = 0; i < count; ++i)
+        cap = v[i].max_n > cap ? v[i].max_n : cap;
+    return cap;
+}
+
+int32_t layernorm_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
+{
+    // rows a register tile holds are read once there: no split
+    if (N <= layernorm_tile_cap(dtype))
+        return 1;
+    return auto_splits(M, N);
+}
+
+// Bytes of the split-row workspace: (mean, M2) as two floats per chunk.
+size_t split_workspace_bytes(int64_t M, int64_t S)
+{
+    if (S <= 1 || M > INT64_MAX / 8 / S)
+        return 0;
+    return static_cast<size_t>(M * S * 8);
+}
+
+// Workspace checks shared by the split-row entry points: `spans` are the
+// caller's matrices, which the workspace (written by the first kernel) must
+// not overlap.
+rk_status check_workspace(void *workspace, size_t workspace_bytes, size_t need, int64_t M,
+                          int32_t S, std::initializer_list<Span> spans)
+{
+    if (need == 0)
+        return RK_ERR_UNSUPPORTED;
+    if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+        return RK_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < need)
+        return RK_ERR_WORKSPACE;
+    if (M > INT64_MAX / S || !grid_ok(M * S, kSplitThreads))
+        return RK_ERR_UNSUPPORTED;
+    const Span ws{reinterpret_cast<uintptr_t>(workspace),
+                  reinterpret_cast<uintptr_t>(workspace) + need};
+    for (const Span &sp : spans)
+        if (overlaps(ws, sp))
+            return RK_ERR_INVALID_ARG;
+    return RK_OK;
 }
 
 rk_status run_tile(const TileVariant &v, const RowProblem &p)
@@ -321,11 +373,7 @@ RK_EXPORT size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t
     if (M < 1 || N < 1 || N > kMaxN || num_splits < 0 || num_splits > kMaxSplits)
         return 0;
     const int64_t S = num_splits == 0 ? auto_splits(M, N) : num_splits;
-    if (S <= 1)
-        return 0;
-    if (M > INT64_MAX / 8 / S)
-        return 0;
-    return static_cast<size_t>(M * S * 8);
+    return split_workspace_bytes(M, S);
 }
 
 RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t N, int64_t ldx,
@@ -345,42 +393,77 @@ RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t
     if (S <= 1)
         return softmax_generic(p, aligned);
 
-    const size_t need = rk_online_softmax_workspace_bytes(M, N, S);
-    if (need == 0)
-        return RK_ERR_UNSUPPORTED;
-    if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
-        return RK_ERR_INVALID_ARG;
-    if (workspace == nullptr || workspace_bytes < need)
-        return RK_ERR_WORKSPACE;
-    if (M > INT64_MAX / S || !grid_ok(M * S, kSplitThreads))
-        return RK_ERR_UNSUPPORTED;
-    // the workspace is written by the first kernel: it must not alias x or y
     const int es = elem_size(dtype);
-    const Span ws{reinterpret_cast<uintptr_t>(workspace),
-                  reinterpret_cast<uintptr_t>(workspace) + need};
-    if (overlaps(ws, matrix_span(x, M, N, ldx, es)) || overlaps(ws, matrix_span(y, M, N, ldy, es)))
-        return RK_ERR_INVALID_ARG;
+    st = check_workspace(workspace, workspace_bytes, rk_online_softmax_workspace_bytes(M, N, S), M,
+                         S, {matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es)});
+    if (st != RK_OK)
+        return st;
     const int64_t chunk = split_chunk(N, S, aligned ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
     return hip_status(online_split_run(p, S, static_cast<int>(chunk), workspace, aligned));
 }
 
+RK_EXPORT int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
+{
+    if (M < 1 || N < 1 || !valid_dtype(dtype))
+        return 1;
+    return layernorm_auto_splits(M, N, dtype);
+}
+
+RK_EXPORT size_t rk_layernorm_gelu_workspace_bytes(int64_t M, int64_t N, int32_t num_splits,
+                                                   rk_dtype dtype)
+{
+    if (M < 1 || N < 1 || N > kMaxN || num_splits < 0 || num_splits > kMaxSplits ||
+        !valid_dtype(dtype))
+        return 0;
+    const int64_t S = num_splits == 0 ? layernorm_auto_splits(M, N, dtype) : num_splits;
+    return split_workspace_bytes(M, S);
+}
+
+RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, const void *bias,
+                                         void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
+                                         float eps, rk_dtype dtype, rk_gelu gelu,
+                                         int32_t num_splits, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream)
+{
+    rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
+    if (st != RK_OK)
+        return st;
+    if (!valid_gelu(gelu) || num_splits < 0 || num_splits > kMaxSplits)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
+    p.gelu = gelu;
+    const bool aligned = layernorm_aligned(p);
+    const int32_t S = num_splits == 0 ? layernorm_auto_splits(M, N, dtype) : num_splits;
+    if (S <= 1) {
+        const int idx = pick_variant(RK_OP_LAYERNORM_GELU, dtype, N);
+        if (aligned && idx >= 0) {
+            int count = 0;
+            return run_tile(layernorm_gelu_variants(dtype, &count)[idx], p);
+        }
+        return layernorm_generic(p, aligned);
+    }
+    const int es = elem_size(dtype);
+    st = check_workspace(workspace, workspace_bytes, split_workspace_bytes(M, S), M, S,
+                         {matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es),
+                          matrix_span(weight, 1, N, N, es), matrix_span(bias, 1, N, N, es)});
+    if (st != RK_OK)
+        return st;
+    const int64_t chunk = split_chunk(N, S, aligned ? vec_elems(dtype) : 1);
+    if (chunk > INT32_MAX)
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), workspace, aligned));
+}
+
 RK_EXPORT rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias, void *y,
                                       int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
                                       rk_dtype dtype, hipStream_t stream)
 {
-    rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
-    if (st != RK_OK || M == 0)
-        return st;
-    const RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
-    const bool aligned = layernorm_aligned(p);
-    const int idx = pick_variant(RK_OP_LAYERNORM_GELU, dtype, N);
-    if (aligned && idx >= 0) {
-        int count = 0;
-        return run_tile(layernorm_gelu_variants(dtype, &count)[idx], p);
-    }
-    return layernorm_generic(p, aligned);
+    return rk_layernorm_gelu_ex(x, weight, bias, y, M, N, ldx, ldy, eps, dtype, RK_GELU_TANH, 1,
+                                nullptr, 0, stream);
 }
 
 RK_EXPORT rk_status rk_rmsnorm(const void *x, const void *weight, void *y, int64_t M, int64_t N,
@@ -507,18 +590,21 @@ RK_EXPORT rk_status rk__softmax_variant(int32_t index, const void *x, void *y, i
 RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, const void *weight,
                                                const void *bias, void *y, int64_t M, int64_t N,
                                                int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
-                                               hipStream_t stream)
+                                               rk_gelu gelu, hipStream_t stream)
 {
     rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
     if (st != RK_OK)
         return st;
+    if (!valid_gelu(gelu))
+        return RK_ERR_INVALID_ARG;
     int count = 0;
     const TileVariant *v = variants(RK_OP_LAYERNORM_GELU, dtype, &count);
     if (index < -1 || index >= count)
         return RK_ERR_INVALID_ARG;
     if (M == 0)
         return RK_OK;
-    const RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
+    RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
+    p.gelu = gelu;
     const bool aligned = layernorm_aligned(p);
     if (index == -1)
         return layernorm_generic(p, aligned);

@@ -203,6 +203,83 @@ __device__ __forceinline__ float gelu_tanh(float z)
     return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Exact GeLU, 0.5 z (1 + erf(z / sqrt 2)), evaluated as 0.5 z erfc(-z / sqrt 2):
+// the same function without the cancellation of 1 + erf for z < 0.  erfc is
+// the device math library's.
+__device__ __forceinline__ float gelu_erf(float z)
+{
+    constexpr float kRsqrt2 = 0.70710678118654752f;
+    return 0.5f * z * erfcf(-z * kRsqrt2);
+}
+
+// GeLU by kind: 0 the tanh approximation, 1 the exact erf form.
+template <int GK>
+__device__ __forceinline__ float gelu(float z)
+{
+    if constexpr (GK == 0)
+        return gelu_tanh(z);
+    else
+        return gelu_erf(z);
+}
+
+// ----------------------------------------------------- LayerNorm moments
+
+// Summary of a part of a row for LayerNorm statistics: count, mean and M2,
+// the sum of squared deviations from that mean.  Two summaries of disjoint
+// parts combine by the pairwise update of Chan, Golub and LeVeque:
+//   n = n1 + n2, delta = mean2 - mean1,
+//   mean = mean1 + delta n2 / n,  M2 = M2_1 + M2_2 + delta^2 n1 n2 / n,
+// with n = 0 (mean 0, M2 0) as the identity.
+struct Moments {
+    float n, mean, m2;
+};
+
+__device__ __forceinline__ Moments merge(Moments a, Moments b)
+{
+    const float n = a.n + b.n;
+    const float r = b.n * __builtin_amdgcn_rcpf(n);  // share of b
+    const float delta = b.mean - a.mean;
+    Moments o;
+    o.n = n;
+    o.mean = fmaf(delta, r, a.mean);
+    o.m2 = fmaf(delta * delta, a.n * r, a.m2 + b.m2);
+    // exact identities: an empty side returns the other one unchanged
+    if (a.n == 0.0f)
+        o = b;
+    if (b.n == 0.0f)
+        o = a;
+    return o;
+}
+
+template <int CTRL>
+__device__ __forceinline__ Moments dpp(Moments s)
+{
+    return Moments{dpp<CTRL>(s.n), dpp<CTRL>(s.mean), dpp<CTRL>(s.m2)};
+}
+
+// Merge of the 64 lanes' summaries of a wave; every lane returns the same
+// summary (the merge is not commutative bit for bit, so the wave-wide result
+// is taken from lanes 0 and 16 as uniform values).
+__device__ __forceinline__ Moments wave_merge(Moments s)
+{
+    s = merge(s, dpp<kQuadSwap1>(s));
+    s = merge(s, dpp<kQuadSwap2>(s));
+    s = merge(s, dpp<kHalfMirror>(s));
+    s = merge(s, dpp<kRowMirror>(s));
+    {
+        uint32_t un = __float_as_uint(s.n), um = __float_as_uint(s.mean),
+                 uq = __float_as_uint(s.m2);
+        auto rn = __builtin_amdgcn_permlane32_swap(un, un, false, false);
+        auto rm = __builtin_amdgcn_permlane32_swap(um, um, false, false);
+        auto rq = __builtin_amdgcn_permlane32_swap(uq, uq, false, false);
+        s = merge(Moments{__uint_as_float(rn[0]), __uint_as_float(rm[0]), __uint_as_float(rq[0])},
+                  Moments{__uint_as_float(rn[1]), __uint_as_float(rm[1]), __uint_as_float(rq[1])});
+    }
+    Moments a{lane_value(s.n, 0), lane_value(s.mean, 0), lane_value(s.m2, 0)};
+    Moments b{lane_value(s.n, 16), lane_value(s.mean, 16), lane_value(s.m2, 16)};
+    return merge(a, b);
+}
+
 // ------------------------------------------------------ row vectors
 
 template <typename T>

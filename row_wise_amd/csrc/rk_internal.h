@@ -49,6 +49,7 @@ struct RowProblem {
     const void *r = nullptr;  // residual RMSNorm: residual input
     void *ro = nullptr;       // residual RMSNorm: residual output
     int64_t ldr = 0, ldo = 0;
+    rk_gelu gelu = RK_GELU_TANH;  // LayerNorm: activation
 };
 
 // A compiled register-resident kernel shape.
@@ -75,7 +76,9 @@ const TileVariant *rmsnorm_variants(rk_dtype dtype, bool residual, int *count);
 hipError_t online_stream_run(const RowProblem &p, bool vectorized);
 hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
                             bool vectorized);
-hipError_t layernorm_gelu_loop_run(const RowProblem &p, bool vectorized);
+hipError_t layernorm_stream_run(const RowProblem &p, bool vectorized);
+hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
+                               bool vectorized);
 hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, bool vectorized);
 hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
                           hipStream_t stream);

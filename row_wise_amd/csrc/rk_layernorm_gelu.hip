@@ -1,19 +1,19 @@
-// Fused LayerNorm + affine + tanh GeLU ("Triton Kernel 实现练习" §4.1
-// "LayerNorm" and §3.4 "Approx Activation"; "PyTorch 自定义 CUDA 算子与 Triton
-// 编程从 Python 原型到 GPU 极致性能" section 三, "Fused LayerNorm GELU Kernel").
+// Fused LayerNorm + affine + GeLU ("Triton Kernel 实现练习" §4.1 "LayerNorm"
+// and §3.4 "Approx Activation"; "PyTorch 自定义 CUDA 算子与 Triton 编程从 Python
+// 原型到 GPU 极致性能" section 三, "Fused LayerNorm GELU Kernel").
 //
 // Per row: mu = sum x / N; var = sum (x - mu)^2 / N, both over the N true
 // columns (padding never enters); rstd = 1 / sqrt(var + eps);
-// z = (x - mu) rstd w + b; y = GeLU_tanh(z).
+// z = (x - mu) rstd w + b; y = GeLU(z), the tanh approximation (GK = 0) or the
+// exact erf form (GK = 1).
 //
 // layernorm_gelu_tile  the row stays in VGPRs (one HBM read and write per
 //                      element): sum -> wave DPP / LDS -> centre in registers
 //                      -> sum of squares -> wave DPP / LDS -> epilogue.  A row
 //                      group handles R rows in sequence and loads weight and
 //                      bias once for all of them.
-// layernorm_gelu_loop  one workgroup per row, three passes over the row in
-//                      memory (sum, centred sum of squares, output); any N,
-//                      any alignment.
+// Rows beyond the register capacity, or not 16-byte aligned, go to the
+// streaming and split-row kernels of rk_layernorm_long.hip.
 #include "rk_device.h"
 #include "rk_internal.h"
 
@@ -22,7 +22,7 @@ namespace rk {
 // EXACT: compiled for N == V * L * E, i.e. every register slot of a row group
 // is a column of its row: no masks, no padding, no excluded columns.  Rows
 // past M (the last workgroup) then read row 0 and store nothing.
-template <typename T, int G, int V, int W, int R, bool EXACT>
+template <typename T, int G, int V, int W, int R, bool EXACT, int GK>
 __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
     T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         for (int k = 0; k < V; ++k)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                v[k][e] = gelu_tanh(fmaf(v[k][e] * rstd, wv[k][e], bv[k][e]));
+                v[k][e] = gelu<GK>(fmaf(v[k][e] * rstd, wv[k][e], bv[k][e]));
         if (EXACT) {
             if (row_ok)
                 store_row<T, E, V, L>(yr, li, vend, rs, v, true);
@@ -151,10 +151,12 @@ static hipError_t layernorm_gelu_tile_run(const RowProblem &p)
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG * R - 1) / (RG * R);
     const float inv_n = static_cast<float>(1.0 / p.N);
-    return launch(layernorm_gelu_tile<T, G, V, W, R, EXACT>, dim3(static_cast<unsigned>(blocks)),
-                  dim3(W * kWave), p.stream, static_cast<const T *>(p.x),
-                  static_cast<const T *>(p.w), static_cast<const T *>(p.b), static_cast<T *>(p.y),
-                  p.M, p.N, p.ldx, p.ldy, inv_n, p.eps);
+    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 1>
+                                        : layernorm_gelu_tile<T, G, V, W, R, EXACT, 0>;
+    return launch(kernel, dim3(static_cast<unsigned>(blocks)), dim3(W * kWave), p.stream,
+                  static_cast<const T *>(p.x), static_cast<const T *>(p.w),
+                  static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,
+                  inv_n, p.eps);
 }
 
 template <typename T, int G, int V, int W, int R = 1, bool EXACT = false>
@@ -225,101 +227,6 @@ const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count)
     }
     *count = static_cast<int>(sizeof(kLayerNormBF16) / sizeof(kLayerNormBF16[0]));
     return kLayerNormBF16;
-}
-
-// ------------------------------------------------------- looping kernel
-
-template <int W>
-__device__ __forceinline__ float block_sum(float v, float *red)
-{
-    v = wave_sum(v);
-    if constexpr (W > 1) {
-        const int wave = threadIdx.x / kWave;
-        if (threadIdx.x % kWave == 0)
-            red[wave] = v;
-        __syncthreads();
-        v = red[0];
-#pragma unroll
-        for (int i = 1; i < W; ++i)
-            v += red[i];
-    }
-    return v;
-}
-
-template <typename T, int E, int W, int U>
-__global__ __launch_bounds__(W *kWave) void layernorm_gelu_loop(
-    const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
-    T *__restrict__ y, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
-{
-    constexpr int NT = W * kWave;
-    __shared__ float red[2][W];
-    const int64_t row = blockIdx.x;
-    const T *xr = x + row * ldx;
-    T *yr = y + row * ldy;
-    const RowSplit<E> rs(N);
-    const int nv = rs.count();
-    const int tid = static_cast<int>(threadIdx.x);
-
-    float s = 0.0f;
-    for (int base = 0; base < nv; base += NT * U) {
-        float v[U][E];
-        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                s += v[u][e];
-    }
-    const float mean = block_sum<W>(s, red[0]) * inv_n;
-
-    float q = 0.0f;
-    for (int base = 0; base < nv; base += NT * U) {
-        float v[U][E];
-        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int col = (base + tid + u * NT) * E + e;  // < N: a true column
-                const float d = col < N ? v[u][e] - mean : 0.0f;
-                q = fmaf(d, d, q);
-            }
-    }
-    const float rstd = __builtin_amdgcn_rsqf(fmaf(block_sum<W>(q, red[1]), inv_n, eps));
-
-    for (int base = 0; base < nv; base += NT * U) {
-        float v[U][E], wv[U][E], bv[U][E];
-        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
-        load_row<T, E, U, NT, kCached>(w, base + tid, nv, rs, 0.0f, wv);
-        load_row<T, E, U, NT, kCached>(b, base + tid, nv, rs, 0.0f, bv);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                v[u][e] = gelu_tanh(fmaf((v[u][e] - mean) * rstd, wv[u][e], bv[u][e]));
-        store_row<T, E, U, NT>(yr, base + tid, nv, rs, v);
-    }
-}
-
-namespace {
-constexpr int kLoopW = 4;
-constexpr int kLoopU = 4;
-
-template <typename T, int E>
-hipError_t loop_run(const RowProblem &p)
-{
-    return launch(layernorm_gelu_loop<T, E, kLoopW, kLoopU>, dim3(static_cast<unsigned>(p.M)),
-                  dim3(kLoopW * kWave), p.stream, static_cast<const T *>(p.x),
-                  static_cast<const T *>(p.w), static_cast<const T *>(p.b), static_cast<T *>(p.y),
-                  p.N, p.ldx, p.ldy, static_cast<float>(1.0 / p.N), p.eps);
-}
-}  // namespace
-
-hipError_t layernorm_gelu_loop_run(const RowProblem &p, bool vectorized)
-{
-    if (p.dtype == RK_F32)
-        return vectorized ? loop_run<float, 4>(p) : loop_run<float, 1>(p);
-    return vectorized ? loop_run<bf16_t, 8>(p) : loop_run<bf16_t, 1>(p);
 }
 
 }  // namespace rk

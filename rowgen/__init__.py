@@ -13,6 +13,9 @@ Recipes (one per named workload; seeds are ``1000 + k``):
 * ``online_f32_64x262144`` x = 3 N(0,1) [64,262144]
 * ``bf16_16384x4096``      x = bf16(N(0,1)) [16384,4096]; softmax input 8 x (exact in
   bf16); w, b as above rounded to bf16
+* ``ln_long_f32_64x262144`` LayerNorm on rows too long for registers: x = N(0,1)
+  [64,262144] fp32, rows i % 8 == 0 get +100 (a mean far from zero, where
+  one-pass E[x^2] - E[x]^2 in fp32 would lose the variance); w, b as above
 
 Draw order is always x, then w, then b.  bf16 values are produced by torch's
 round-to-nearest-even cast of the fp32 draw.
@@ -55,6 +58,8 @@ WORKLOADS = {
                                      ("online_softmax",), x_scale=3.0),
     "bf16_16384x4096": Workload("bf16_16384x4096", 1005, 16384, 4096, torch.bfloat16,
                                 ("softmax", "layernorm_gelu"), softmax_scale=8.0),
+    "ln_long_f32_64x262144": Workload("ln_long_f32_64x262144", 1006, 64, 262144, torch.float32,
+                                      ("layernorm_gelu",), offset_every=8, offset=100.0),
 }
 
 
