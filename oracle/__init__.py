@@ -25,7 +25,7 @@ __all__ = [
     "build", "Oracle", "default", "softmax", "softmax_stats", "online_softmax", "online_stats",
     "merge", "split_stats", "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
     "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf", "chunk_moments",
-    "chan_merge", "split_moments", "layernorm_gelu_ex",
+    "chan_merge", "split_moments", "layernorm_gelu_ex", "row_sum", "row_max",
 ]
 
 
@@ -63,6 +63,8 @@ def _signatures():
         "oracle_chan_merge": [d, d, d, d, d, d, P, P, P],
         "oracle_split_moments": [P, i64, i64, P, P, P, P, P],
         "oracle_layernorm_gelu_ex": [P, P, P, P, i64, i64, d, ctypes.c_int, i64],
+        "oracle_row_sum": [P, P, i64, i64],
+        "oracle_row_max": [P, P, i64, i64],
     }
 
 
@@ -255,6 +257,20 @@ class Oracle:
                                           float(eps), kind, int(splits))
         return y
 
+    def row_sum(self, x) -> np.ndarray:
+        """sum_j x[i, j] of a [M, N] array, in double."""
+        x = _rows(x)
+        out = np.empty(x.shape[0])
+        self.lib.oracle_row_sum(_p(x), _p(out), x.shape[0], x.shape[1])
+        return out
+
+    def row_max(self, x) -> np.ndarray:
+        """max_j x[i, j] of a [M, N] array (NaN if the row holds a NaN)."""
+        x = _rows(x)
+        out = np.empty(x.shape[0])
+        self.lib.oracle_row_max(_p(x), _p(out), x.shape[0], x.shape[1])
+        return out
+
 
 _default = None
 
@@ -278,6 +294,7 @@ def _forward(name):
 for _n in ["softmax", "softmax_stats", "online_stats", "merge", "split_stats", "online_softmax",
            "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
            "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf",
-           "chunk_moments", "chan_merge", "split_moments", "layernorm_gelu_ex"]:
+           "chunk_moments", "chan_merge", "split_moments", "layernorm_gelu_ex", "row_sum",
+           "row_max"]:
     globals()[_n] = _forward(_n)
 del _n

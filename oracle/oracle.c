@@ -405,3 +405,24 @@ void oracle_layernorm_gelu_ex(const double *x, const double *w, const double *b,
         }
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Row-wise sum and max: [TKE] §2.2 "Row-wise Sum" (out[i] = sum_j x[i,j])  */
+/* and §2.3 "Row-wise Max" (out[i] = max_j x[i,j], padding must be -inf). */
+/* ---------------------------------------------------------------------- */
+void oracle_row_sum(const double *x, double *out, int64_t M, int64_t N)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        double s = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            s += x[i * N + j];
+        out[i] = s;
+    }
+}
+
+/* NaN anywhere in a row makes its max NaN (as row_max above). */
+void oracle_row_max(const double *x, double *out, int64_t M, int64_t N)
+{
+    for (int64_t i = 0; i < M; ++i)
+        out[i] = row_max(x + i * N, N);
+}

@@ -40,6 +40,10 @@ What pins what (citations are to the pages' titles and sections):
   split statistics of any chunk count equal the whole row's; LayerNorm + GeLU
   on them equals the whole-row version, and with erf equals torch's
   layer_norm followed by the exact gelu.
+* row sum and row max, same page §2.2 and §2.3: the sum against math.fsum
+  (correctly rounded) and closed forms (arithmetic progressions, exact
+  cancellation); the max against numpy, invariant under permutation, NaN
+  propagating, -inf for an all -inf row.
 """
 from __future__ import annotations
 
@@ -499,6 +503,41 @@ def check_layernorm_gelu_ex(orc):
     assert np.max(np.abs(orc.layernorm_gelu_ex(x, w, b, EPS, "erf", 0) - base)) > 1e-4
 
 
+# ------------------------------------------------------ row sum and max
+
+
+def check_row_sum(orc):
+    r = _rng(83)
+    for n in (1, 2, 7, 1000, 262144):
+        x = r.standard_normal((3, n)) * np.array([[1.0], [1e3], [1e-3]])
+        s = orc.row_sum(x)
+        for i in range(3):
+            ref = math.fsum(x[i])
+            assert abs(s[i] - ref) <= 1e-15 * np.abs(x[i]).sum() + 1e-300, (n, i)
+    for n in (1, 10, 4097):
+        ap = np.arange(n, dtype=np.float64)
+        assert orc.row_sum(ap)[0] == n * (n - 1) / 2
+    x = np.concatenate([np.full(500, 0.25), np.full(500, -0.25)])[None, :]
+    assert orc.row_sum(x)[0] == 0.0
+    assert orc.row_sum(np.array([[3.5]]))[0] == 3.5
+
+
+def check_row_max(orc):
+    r = _rng(89)
+    for n in (1, 3, 1000, 65537):
+        x = 5.0 * r.standard_normal((4, n))
+        m = orc.row_max(x)
+        assert np.array_equal(m, x.max(axis=1)), n
+        perm = r.permutation(n)
+        assert np.array_equal(orc.row_max(x[:, perm]), m)
+    x = r.standard_normal((3, 100))
+    x[0, 50] = np.nan
+    x[1, :] = -np.inf
+    x[2, 99] = np.inf
+    m = orc.row_max(x)
+    assert np.isnan(m[0]) and m[1] == -np.inf and m[2] == np.inf
+
+
 PINS = [
     check_softmax_sums_to_one,
     check_softmax_shift_invariance,
@@ -528,4 +567,6 @@ PINS = [
     check_chan_merge_algebra,
     check_split_moments_match_whole_row,
     check_layernorm_gelu_ex,
+    check_row_sum,
+    check_row_max,
 ]

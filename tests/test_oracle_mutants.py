@@ -50,6 +50,9 @@ MUTANTS = {
     "chan_identity_swapped": ("*n_out = n2, *mean_out = mean2, *m2_out = m2_2;", "*n_out = n1, *mean_out = mean1, *m2_out = m2_1;"),
     "split_var_divisor": ("rstd = 1.0 / sqrt(m2 / (double)N + eps);", "rstd = 1.0 / sqrt(m2 / (double)(N - 1) + eps);"),
     "ex_gelu_kind_ignored": ("yr[j] = gelu ? oracle_gelu_erf(z) : oracle_gelu_tanh(z);", "yr[j] = oracle_gelu_tanh(z);"),
+    "row_sum_drops_last": ("        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];", "        for (int64_t j = 0; j + 1 < N; ++j)\n            s += x[i * N + j];"),
+    "row_sum_first_twice": ("        double s = 0.0;\n        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];", "        double s = x[i * N];\n        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];"),
+    "row_max_ignores_nan": ("        if (isnan(x[j]))\n            return NAN;\n", ""),
     "split_moments_chunk_floor": ("    int64_t C = (N + S - 1) / S;\n    double n = 0.0", "    int64_t C = N / S;\n    if (C < 1)\n        C = 1;\n    double n = 0.0"),
 }
 
