@@ -73,6 +73,9 @@ class Case:
             self.bytes = 3 * M * N * es + 2 * N * es
             if self.splits > 1:
                 self.bytes += 2 * M * self.splits * 8
+        elif self.op in ("row_sum", "row_max"):
+            self.bytes = M * N * es + M * es  # one read of x, M results
+            footprint = M * N * es
         elif self.op == "rmsnorm":
             self.bytes = io + N * es  # x, y, and w once
         elif self.op == "residual_rmsnorm":
@@ -119,6 +122,15 @@ class Case:
             wb = self.ws.numel() if self.ws is not None else 0
             self.args = [(xx.data_ptr(), self.w.data_ptr(), self.b.data_ptr(), yy.data_ptr(), M,
                           N, N, N, fp, self.dtype_code, 0, self.splits, wp, wb, stream)
+                         for xx, yy in zip(self.xs, self.ys)]
+        elif self.op in ("row_sum", "row_max"):
+            fn = getattr(lib, "rk_" + self.op)
+            self.ys = [torch.empty(M, dtype=x.dtype, device=dev) for _ in range(self.R)]
+            self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, self.dtype_code, stream)
+                         for xx, yy in zip(self.xs, self.ys)]
+        elif self.op == "gelu":
+            fn = lib.rk_gelu
+            self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, N, self.dtype_code, 0, stream)
                          for xx, yy in zip(self.xs, self.ys)]
         elif self.op == "rmsnorm":
             fn = lib.rk_rmsnorm
@@ -196,6 +208,11 @@ def all_cases():
              splits=64),
         Case("ln_gelu_auto_f32_64x262144", "layernorm_gelu_ex", "ln_long_f32_64x262144",
              splits=0),
+        Case("row_sum_f32_8192x1000", "row_sum", "softmax_f32_8192x1000"),
+        Case("row_max_f32_8192x1000", "row_max", "softmax_f32_8192x1000"),
+        Case("row_sum_f32_64x262144", "row_sum", "online_f32_64x262144"),
+        Case("row_sum_bf16_16384x4096", "row_sum", "bf16_16384x4096"),
+        Case("gelu_bf16_16384x4096", "gelu", "bf16_16384x4096"),
         Case("rmsnorm_f32_4096x768", "rmsnorm", "ln_gelu_f32_4096x768"),
         Case("residual_rmsnorm_f32_4096x768", "residual_rmsnorm", "ln_gelu_f32_4096x768"),
         Case("rmsnorm_bf16_16384x4096", "rmsnorm", "bf16_16384x4096"),

@@ -51,11 +51,11 @@ typedef enum rk_dtype {
     RK_BF16 = 1, /* bfloat16 storage, fp32 arithmetic */
 } rk_dtype;
 
-/* GeLU of the LayerNorm epilogue ([TKE] §3.4 gives both forms). */
-typedef enum rk_gelu {
+/* GeLU form ([TKE] §3.4 gives both): the LayerNorm epilogue and rk_gelu. */
+typedef enum rk_gelu_kind {
     RK_GELU_TANH = 0, /* 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
     RK_GELU_ERF = 1,  /* 0.5 z (1 + erf(z / sqrt(2))), the exact form */
-} rk_gelu;
+} rk_gelu_kind;
 
 typedef enum rk_status {
     RK_OK = 0,
@@ -179,7 +179,7 @@ rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias,
  */
 rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, const void *bias, void *y,
                                int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
-                               rk_dtype dtype, rk_gelu gelu, int32_t num_splits,
+                               rk_dtype dtype, rk_gelu_kind gelu, int32_t num_splits,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes rk_layernorm_gelu_ex needs: M * S * 8 for S > 1 (S the
@@ -230,6 +230,36 @@ rk_status rk_residual_rmsnorm(const void *x, const void *residual, const void *w
                               void *residual_out, int64_t M, int64_t N, int64_t ldx,
                               int64_t ldr, int64_t ldy, int64_t ldo, float eps, rk_dtype dtype,
                               hipStream_t stream);
+
+/*
+ * Row-wise sum and max ([TKE] §2.2 "Row-wise Sum", §2.3 "Row-wise Max"):
+ *     out[i] = sum_j x[i, j]   (fp32 accumulation, rounded to `dtype`),
+ *     out[i] = max_j x[i, j]   (exact; NaN if the row holds a NaN).
+ *
+ * x [M][ldx] and out [M] (contiguous), both of `dtype`.  One HBM read per
+ * element.  A row goes to one wave (up to 1024 16-byte vectors), four waves
+ * (up to 8192) or sixteen.  The sum's order of addition is fixed: results
+ * are reproducible bit for bit.
+ *
+ * Returns RK_ERR_INVALID_ARG for an unknown dtype, M < 0, N < 1, ldx < N, a
+ * NULL or misaligned pointer with M > 0, or out overlapping x;
+ * RK_ERR_UNSUPPORTED if N > 2^30.
+ */
+rk_status rk_row_sum(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                     rk_dtype dtype, hipStream_t stream);
+rk_status rk_row_max(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                     rk_dtype dtype, hipStream_t stream);
+
+/*
+ * Elementwise GeLU ([TKE] §3.4; [KTN] "Triton GeLU"): y = GeLU(x), the tanh
+ * approximation or the exact erf form, fp32 arithmetic.
+ *
+ * x [M][ldx], y [M][ldy] of `dtype`; a contiguous, 16-byte aligned buffer is
+ * processed as one flat array.  Arguments, aliasing and errors as in
+ * rk_softmax, plus RK_ERR_INVALID_ARG for an unknown gelu.
+ */
+rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
+                  rk_dtype dtype, rk_gelu_kind gelu, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status ("unknown status" for an
  * unknown value). */

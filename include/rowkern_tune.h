@@ -68,7 +68,7 @@ rk_status rk__softmax_variant(int32_t index, const void *x, void *y, int64_t M, 
 rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, const void *weight,
                                      const void *bias, void *y, int64_t M, int64_t N,
                                      int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
-                                     rk_gelu gelu, hipStream_t stream);
+                                     rk_gelu_kind gelu, hipStream_t stream);
 
 /* rk_rmsnorm / rk_residual_rmsnorm forced onto one path, as above (index -1:
  * the two-pass looping kernel). */

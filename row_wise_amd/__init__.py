@@ -13,6 +13,7 @@ Functions carry the C entry points' names:
 * ``rk_layernorm_gelu_ex(x, weight, bias, eps=1e-5, gelu="tanh", num_splits=1, out=None,
   workspace=None)``, ``rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype)``,
   ``rk_layernorm_gelu_auto_splits(M, N, dtype)``
+* ``rk_row_sum(x, out=None)``, ``rk_row_max(x, out=None)``, ``rk_gelu(x, gelu="tanh", out=None)``
 * ``rk_rmsnorm(x, weight, eps=1e-5, out=None)``
 * ``rk_residual_rmsnorm(x, residual, weight, eps=1e-5, out=None, residual_out=None)``
 * ``rk_online_softmax_workspace_bytes(M, N, num_splits)``,
@@ -37,7 +38,7 @@ __all__ = [
     "RK_OP_LAYERNORM_GELU", "rk_rmsnorm", "rk_residual_rmsnorm", "rk__rmsnorm_variant",
     "rk__residual_rmsnorm_variant", "RK_OP_RMSNORM", "RK_OP_RESIDUAL_RMSNORM",
     "rk_layernorm_gelu_ex", "rk_layernorm_gelu_workspace_bytes", "rk_layernorm_gelu_auto_splits",
-    "RK_GELU_TANH", "RK_GELU_ERF",
+    "RK_GELU_TANH", "RK_GELU_ERF", "rk_row_sum", "rk_row_max", "rk_gelu",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.so")
@@ -91,6 +92,9 @@ def load():
                                        sz, vp]),
         "rk_layernorm_gelu_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "rk_layernorm_gelu_auto_splits": (i32, [i64, i64, i32]),
+        "rk_row_sum": (i32, [vp, vp, i64, i64, i64, i32, vp]),
+        "rk_row_max": (i32, [vp, vp, i64, i64, i64, i32, vp]),
+        "rk_gelu": (i32, [vp, vp, i64, i64, i64, i64, i32, i32, vp]),
         "rk_rmsnorm": (i32, [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
         "rk_residual_rmsnorm": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32,
                                       vp]),
@@ -265,6 +269,40 @@ def rk_layernorm_gelu_ex(x, weight, bias, eps: float = 1e-5, gelu: str = "tanh",
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _call("rk_layernorm_gelu_ex", v.data_ptr(), weight.data_ptr(), bias.data_ptr(), o.data_ptr(),
           M, N, ldx, ldy, float(eps), dt, _GELU[gelu], int(num_splits), wptr, wbytes, _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def _row_reduce(name, x, out):
+    torch = _torch()
+    _check_device(x)
+    v, M, N, ldx = _as_rows(x)
+    shape = x.shape[:-1] if x.dim() > 1 else ()
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif out.shape != shape or out.dtype != x.dtype or out.device != x.device \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of the input's rows, dtype and device")
+    _call(name, v.data_ptr(), out.data_ptr(), M, N, ldx, _dtype_code(x), _stream(x))
+    return out
+
+
+def rk_row_sum(x, out=None):
+    """sum over the last dimension (fp32 accumulation, result in x's dtype)."""
+    return _row_reduce("rk_row_sum", x, out)
+
+
+def rk_row_max(x, out=None):
+    """max over the last dimension (NaN if a row holds a NaN)."""
+    return _row_reduce("rk_row_max", x, out)
+
+
+def rk_gelu(x, gelu: str = "tanh", out=None):
+    """Elementwise GeLU ("tanh" approximation or exact "erf")."""
+    _check_device(x)
+    v, M, N, ldx = _as_rows(x)
+    o, ldy = _out_like(x, v, out)
+    _call("rk_gelu", v.data_ptr(), o.data_ptr(), M, N, ldx, ldy, _dtype_code(x), _GELU[gelu],
+          _stream(x))
     return o.reshape(x.shape) if out is None else out
 
 

@@ -154,7 +154,7 @@ rk_status layernorm_generic(const RowProblem &p, bool aligned)
     return hip_status(layernorm_stream_run(p, aligned));
 }
 
-bool valid_gelu(rk_gelu g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
+bool valid_gelu(rk_gelu_kind g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
 
 // Largest N a LayerNorm register tile holds for `dtype`.
 int64_t layernorm_tile_cap(rk_dtype dtype)
@@ -423,7 +423,7 @@ RK_EXPORT size_t rk_layernorm_gelu_workspace_bytes(int64_t M, int64_t N, int32_t
 
 RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, const void *bias,
                                          void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
-                                         float eps, rk_dtype dtype, rk_gelu gelu,
+                                         float eps, rk_dtype dtype, rk_gelu_kind gelu,
                                          int32_t num_splits, void *workspace,
                                          size_t workspace_bytes, hipStream_t stream)
 {
@@ -492,6 +492,83 @@ RK_EXPORT rk_status rk_residual_rmsnorm(const void *x, const void *residual, con
     p.ldr = ldr;
     p.ldo = ldo;
     return rmsnorm_dispatch(p, true, 0, false);
+}
+
+// ------------------------------------------------- standalone primitives
+
+namespace {
+
+rk_status check_reduce(const void *x, const void *out, int64_t M, int64_t N, int64_t ldx,
+                       rk_dtype dtype)
+{
+    if (!valid_dtype(dtype))
+        return RK_ERR_INVALID_ARG;
+    if (M < 0 || N < 1 || N > INT32_MAX || ldx < N)
+        return RK_ERR_INVALID_ARG;
+    if (N > kMaxN)
+        return RK_ERR_UNSUPPORTED;
+    if (M == 0)
+        return RK_OK;
+    const int es = elem_size(dtype);
+    if (x == nullptr || out == nullptr || !elem_aligned(x, es) || !elem_aligned(out, es))
+        return RK_ERR_INVALID_ARG;
+    if (!extent_ok(M, N, ldx, es) || M > INT64_MAX / es)
+        return RK_ERR_INVALID_ARG;
+    // the results are written while other rows are still read: no overlap
+    if (overlaps(matrix_span(x, M, N, ldx, es), matrix_span(out, 1, M, M, es)))
+        return RK_ERR_INVALID_ARG;
+    return RK_OK;
+}
+
+rk_status row_reduce_entry(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                           rk_dtype dtype, int op, hipStream_t stream)
+{
+    rk_status st = check_reduce(x, out, M, N, ldx, dtype);
+    if (st != RK_OK || M == 0)
+        return st;
+    const int es = elem_size(dtype);
+    const bool aligned = aligned16(x) && (ldx * es) % 16 == 0;
+    int threads = 0;
+    if (!grid_ok(row_reduce_blocks(M, N, dtype, aligned, &threads), threads))
+        return RK_ERR_UNSUPPORTED;
+    const RowProblem p = make_problem(x, out, nullptr, nullptr, M, N, ldx, 1, 0.0f, dtype, stream);
+    return hip_status(row_reduce_run(p, op, aligned));
+}
+
+}  // namespace
+
+RK_EXPORT rk_status rk_row_sum(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                               rk_dtype dtype, hipStream_t stream)
+{
+    return row_reduce_entry(x, out, M, N, ldx, dtype, RK_REDUCE_SUM, stream);
+}
+
+RK_EXPORT rk_status rk_row_max(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                               rk_dtype dtype, hipStream_t stream)
+{
+    return row_reduce_entry(x, out, M, N, ldx, dtype, RK_REDUCE_MAX, stream);
+}
+
+RK_EXPORT rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_t ldx,
+                            int64_t ldy, rk_dtype dtype, rk_gelu_kind gelu, hipStream_t stream)
+{
+    rk_status st = check_rows(x, y, M, N, ldx, ldy, dtype);
+    if (st != RK_OK)
+        return st;
+    if (!valid_gelu(gelu))
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
+    p.gelu = gelu;
+    const int es = elem_size(dtype);
+    const bool contiguous = M == 1 || (ldx == N && ldy == N);
+    const bool flat = contiguous && aligned16(x) && aligned16(y);
+    if (flat)
+        return hip_status(gelu_run(p, true, true));
+    if (!grid_ok(M, 256))
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(gelu_run(p, false, rows_aligned(x, y, ldx, ldy, es)));
 }
 
 RK_EXPORT const char *rk_status_string(rk_status status)
@@ -590,7 +667,7 @@ RK_EXPORT rk_status rk__softmax_variant(int32_t index, const void *x, void *y, i
 RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, const void *weight,
                                                const void *bias, void *y, int64_t M, int64_t N,
                                                int64_t ldx, int64_t ldy, float eps, rk_dtype dtype,
-                                               rk_gelu gelu, hipStream_t stream)
+                                               rk_gelu_kind gelu, hipStream_t stream)
 {
     rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
     if (st != RK_OK)

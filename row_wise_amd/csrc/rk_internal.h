@@ -49,7 +49,7 @@ struct RowProblem {
     const void *r = nullptr;  // residual RMSNorm: residual input
     void *ro = nullptr;       // residual RMSNorm: residual output
     int64_t ldr = 0, ldo = 0;
-    rk_gelu gelu = RK_GELU_TANH;  // LayerNorm: activation
+    rk_gelu_kind gelu = RK_GELU_TANH;  // LayerNorm, GeLU: activation
 };
 
 // A compiled register-resident kernel shape.
@@ -80,6 +80,12 @@ hipError_t layernorm_stream_run(const RowProblem &p, bool vectorized);
 hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
                                bool vectorized);
 hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, bool vectorized);
+enum { RK_REDUCE_SUM = 0, RK_REDUCE_MAX = 1 };
+hipError_t row_reduce_run(const RowProblem &p, int op, bool vectorized);
+// Workgroups (and threads per workgroup) row_reduce_run launches.
+int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, bool vectorized, int *threads);
+// flat: x and y contiguous and 16-byte aligned, processed as one buffer.
+hipError_t gelu_run(const RowProblem &p, bool flat, bool vectorized);
 hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
                           hipStream_t stream);
 

@@ -182,6 +182,33 @@ def test_layernorm_ex_workspace_and_splits(lib):
                                     None) == 0
 
 
+@pytest.mark.parametrize("fn", ["rk_row_sum", "rk_row_max"])
+def test_row_reduce_rejects(lib, fn):
+    f = getattr(lib, fn)
+    assert f(None, B, 4, 8, 8, F32, None) == INVALID
+    assert f(A, None, 4, 8, 8, F32, None) == INVALID
+    assert f(A, B, -1, 8, 8, F32, None) == INVALID
+    assert f(A, B, 4, 0, 8, F32, None) == INVALID
+    assert f(A, B, 4, 8, 7, F32, None) == INVALID
+    assert f(A, B, 4, 8, 8, 5, None) == INVALID
+    assert f(A + 2, B, 4, 8, 8, F32, None) == INVALID
+    assert f(A, B + 1, 4, 8, 8, BF16, None) == INVALID
+    assert f(A, A + 64, 4, 8, 8, F32, None) == INVALID  # out inside x
+    assert f(A, A - 8, 4, 8, 8, F32, None) == INVALID  # out overlaps x's start
+    assert f(None, None, 0, 8, 8, F32, None) == 0
+    assert f(A, B, 1, 2**30 + 1, 2**30 + 1, F32, None) == UNSUPPORTED
+
+
+def test_gelu_rejects(lib):
+    g = lib.rk_gelu
+    assert g(A, B, 4, 8, 8, 8, F32, 2, None) == INVALID
+    assert g(A, B, 4, 8, 8, 8, F32, -1, None) == INVALID
+    assert g(A, A + 16, 4, 8, 8, 8, F32, 0, None) == INVALID
+    assert g(None, B, 4, 8, 8, 8, F32, 0, None) == INVALID
+    assert g(A, B, 4, 8, 8, 7, F32, 1, None) == INVALID
+    assert g(None, None, 0, 8, 8, 8, F32, 0, None) == 0
+
+
 def online(lib, x=A, y=B, M=4, N=4096, S=64, ws=A + 0x400000, wb=4 * 64 * 8, dt=F32):
     return lib.rk_online_softmax(x, y, M, N, N, N, dt, S, ws, wb, None)
 

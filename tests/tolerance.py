@@ -15,6 +15,11 @@ softmax.  y = v * inv_rms * w is a product with no cancellation, and
 residual_out = x + residual is one correctly rounded addition; an exact zero
 reference (v = 0) demands an exact zero.
 
+Row sums: max_i |y_i - r_i| / sum_j |x_ij|, the error relative to the row's
+scale.  A sum may cancel to near zero, where no fp32 summation has a small
+relative error; the bound of any summation order is proportional to
+sum |x|.  Row max: bit-exact (the max is one of the inputs).
+
 Tolerances: 1e-5 for fp32 input/output, 1e-2 for bf16 storage with fp32
 arithmetic.
 """
@@ -65,3 +70,19 @@ def rel_err_floor1(y, ref, floor: float = 1.0) -> float:
 def rel_err(y, ref) -> float:
     """max |y - r| / |r| (zero references require exact zeros)."""
     return rel_err_softmax(y, ref)
+
+
+def rel_err_sum(y, ref, x) -> float:
+    """max_i |y_i - r_i| / sum_j |x_ij| over the rows of x."""
+    y, ref, x = _arr(y).ravel(), _arr(ref).ravel(), _arr(x)
+    if y.shape != ref.shape or x.shape[0] != y.size:
+        raise ValueError("shape mismatch")
+    if y.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    scale = np.abs(x).sum(axis=1)
+    num = np.abs(y - ref)
+    if np.any(num[scale == 0] != 0):
+        return float("inf")
+    return float(np.max(np.where(scale == 0, 0.0, num / np.where(scale == 0, 1.0, scale))))
