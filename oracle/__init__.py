@@ -25,7 +25,8 @@ __all__ = [
     "build", "Oracle", "default", "softmax", "softmax_stats", "online_softmax", "online_stats",
     "merge", "split_stats", "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
     "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf", "chunk_moments",
-    "chan_merge", "split_moments", "layernorm_gelu_ex", "row_sum", "row_max",
+    "chan_merge", "split_moments", "layernorm_gelu_ex", "row_sum", "row_max", "attention",
+    "flash_attention",
 ]
 
 
@@ -65,6 +66,8 @@ def _signatures():
         "oracle_layernorm_gelu_ex": [P, P, P, P, i64, i64, d, ctypes.c_int, i64],
         "oracle_row_sum": [P, P, i64, i64],
         "oracle_row_max": [P, P, i64, i64],
+        "oracle_attention": [P, P, P, P, i64, i64, i64, ctypes.c_int, d],
+        "oracle_flash_attention": [P, P, P, P, i64, i64, i64, ctypes.c_int, d, i64, i64],
     }
 
 
@@ -271,6 +274,36 @@ class Oracle:
         self.lib.oracle_row_max(_p(x), _p(out), x.shape[0], x.shape[1])
         return out
 
+    @staticmethod
+    def _qkv(q, k, v):
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim < 2 or q.shape != k.shape or q.shape != v.shape:
+            raise ValueError("q, k, v must share one shape [..., T, d]")
+        return q, k, v
+
+    def attention(self, q, k, v, causal: bool = False, scale: float | None = None):
+        """softmax(q k^T * scale) v over the last two dimensions [..., T, d]
+        (scale defaults to 1/sqrt(d)); causal: query i sees keys j <= i."""
+        q, k, v = self._qkv(q, k, v)
+        T, d = q.shape[-2:]
+        BH = q.size // (T * d) if T * d else 0
+        sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+        o = np.empty_like(q)
+        self.lib.oracle_attention(_p(q), _p(k), _p(v), _p(o), BH, T, d, int(causal), sc)
+        return o
+
+    def flash_attention(self, q, k, v, causal: bool = False, scale: float | None = None,
+                        block_q: int = 16, block_kv: int = 16):
+        """The tiled online-softmax form with the given block sizes."""
+        q, k, v = self._qkv(q, k, v)
+        T, d = q.shape[-2:]
+        BH = q.size // (T * d) if T * d else 0
+        sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+        o = np.empty_like(q)
+        self.lib.oracle_flash_attention(_p(q), _p(k), _p(v), _p(o), BH, T, d, int(causal), sc,
+                                        int(block_q), int(block_kv))
+        return o
+
 
 _default = None
 
@@ -295,6 +328,6 @@ for _n in ["softmax", "softmax_stats", "online_stats", "merge", "split_stats", "
            "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
            "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf",
            "chunk_moments", "chan_merge", "split_moments", "layernorm_gelu_ex", "row_sum",
-           "row_max"]:
+           "row_max", "attention", "flash_attention"]:
     globals()[_n] = _forward(_n)
 del _n

@@ -25,6 +25,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* ---------------------------------------------------------------------- */
 /* Stable softmax: [TKE] §2.4 "Softmax" (stable version m = max(x),        */
@@ -425,4 +426,112 @@ void oracle_row_max(const double *x, double *out, int64_t M, int64_t N)
 {
     for (int64_t i = 0; i < M; ++i)
         out[i] = row_max(x + i * N, N);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Attention: [TKE] §5.1 "Naive Attention" and §5.2 "FlashAttention-style  */
+/* Forward"; [L6] §7.1-7.3.  Per (batch, head), with q, k, v, o of shape  */
+/* [T][d] (contiguous, one block of T*d per (batch, head)):                */
+/*   S = q k^T * scale;  causal: query i sees keys j <= i only;            */
+/*   P = softmax(S) over keys;  o = P v.                                   */
+/* ---------------------------------------------------------------------- */
+
+/* The definition, row by row: scores of the visible keys, their max, the
+ * exp-weights and their sum, then the weighted sum of value rows. */
+void oracle_attention(const double *q, const double *k, const double *v, double *o, int64_t BH,
+                      int64_t T, int64_t d, int causal, double scale)
+{
+    double *s = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int64_t h = 0; h < BH; ++h) {
+        const double *qh = q + h * T * d, *kh = k + h * T * d, *vh = v + h * T * d;
+        double *oh = o + h * T * d;
+        for (int64_t i = 0; i < T; ++i) {
+            int64_t n = causal ? i + 1 : T;  /* visible keys 0 .. n-1 */
+            for (int64_t j = 0; j < n; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += qh[i * d + c] * kh[j * d + c];
+                s[j] = dot * scale;
+            }
+            double m = row_max(s, n);
+            double den = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                den += exp(s[j] - m);
+            for (int64_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < n; ++j)
+                    acc += exp(s[j] - m) * vh[j * d + c];
+                oh[i * d + c] = acc / den;
+            }
+        }
+    }
+    free(s);
+}
+
+/* The tiled form ([L6] §7.3, [TKE] §5.2): query blocks of Br rows; for each,
+ * key/value blocks of Bc rows are scanned with a per-row state m (max so
+ * far), l (sum of exp so far) and acc (exp-weighted sum of value rows so
+ * far):  m_new = max(m, rowmax(S_blk)), alpha = exp(m - m_new),
+ * P = exp(S_blk - m_new), l = alpha l + rowsum(P), acc = alpha acc + P V_blk;
+ * finally o = acc / l.  Causal masking sets the scores of keys j > i to
+ * -inf; a block a row cannot see at all leaves its state unchanged. */
+void oracle_flash_attention(const double *q, const double *k, const double *v, double *o,
+                            int64_t BH, int64_t T, int64_t d, int causal, double scale,
+                            int64_t Br, int64_t Bc)
+{
+    double *acc = malloc(sizeof(double) * (size_t)(Br * d));
+    double *m = malloc(sizeof(double) * (size_t)Br);
+    double *l = malloc(sizeof(double) * (size_t)Br);
+    double *sblk = malloc(sizeof(double) * (size_t)Bc);
+    for (int64_t h = 0; h < BH; ++h) {
+        const double *qh = q + h * T * d, *kh = k + h * T * d, *vh = v + h * T * d;
+        double *oh = o + h * T * d;
+        for (int64_t i0 = 0; i0 < T; i0 += Br) {
+            int64_t rows = T - i0 < Br ? T - i0 : Br;
+            for (int64_t r = 0; r < rows; ++r) {
+                m[r] = -INFINITY;
+                l[r] = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    acc[r * d + c] = 0.0;
+            }
+            for (int64_t j0 = 0; j0 < T; j0 += Bc) {
+                int64_t cols = T - j0 < Bc ? T - j0 : Bc;
+                for (int64_t r = 0; r < rows; ++r) {
+                    int64_t i = i0 + r;
+                    double bmax = -INFINITY;
+                    for (int64_t t = 0; t < cols; ++t) {
+                        int64_t j = j0 + t;
+                        double dot = 0.0;
+                        for (int64_t c = 0; c < d; ++c)
+                            dot += qh[i * d + c] * kh[j * d + c];
+                        sblk[t] = (causal && j > i) ? -INFINITY : dot * scale;
+                        if (sblk[t] > bmax)
+                            bmax = sblk[t];
+                    }
+                    if (bmax == -INFINITY)
+                        continue; /* nothing visible in this block */
+                    double m_new = m[r] > bmax ? m[r] : bmax;
+                    double alpha = m[r] == -INFINITY ? 0.0 : exp(m[r] - m_new);
+                    double psum = 0.0;
+                    for (int64_t c = 0; c < d; ++c)
+                        acc[r * d + c] *= alpha;
+                    for (int64_t t = 0; t < cols; ++t) {
+                        double p = exp(sblk[t] - m_new);
+                        psum += p;
+                        for (int64_t c = 0; c < d; ++c)
+                            acc[r * d + c] += p * vh[(j0 + t) * d + c];
+                    }
+                    l[r] = alpha * l[r] + psum;
+                    m[r] = m_new;
+                }
+            }
+            for (int64_t r = 0; r < rows; ++r)
+                for (int64_t c = 0; c < d; ++c)
+                    oh[(i0 + r) * d + c] = acc[r * d + c] / l[r];
+        }
+    }
+    free(acc);
+    free(m);
+    free(l);
+    free(sblk);
 }

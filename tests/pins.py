@@ -44,6 +44,13 @@ What pins what (citations are to the pages' titles and sections):
   (correctly rounded) and closed forms (arithmetic progressions, exact
   cancellation); the max against numpy, invariant under permutation, NaN
   propagating, -inf for an all -inf row.
+* attention, same page §5.1-5.2 and "第 6 讲" §7: torch's
+  scaled_dot_product_attention in float64 (causal and not); closed forms
+  (equal value rows give that row; q = 0 averages the visible value rows;
+  T = 1 returns v; the first causal row returns v[0]; a dominant score picks
+  its value row); invariance of non-causal attention under a joint
+  permutation of keys and values; the definition at 50 digits on tiny
+  shapes; the tiled online form equals the definition for every block size.
 """
 from __future__ import annotations
 
@@ -538,6 +545,100 @@ def check_row_max(orc):
     assert np.isnan(m[0]) and m[1] == -np.inf and m[2] == np.inf
 
 
+# ------------------------------------------------------------- attention
+
+
+def _sdpa(q, k, v, causal, scale=None):
+    import torch
+    import torch.nn.functional as F
+
+    t = [torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v)]
+    return F.scaled_dot_product_attention(*t, is_causal=causal, scale=scale).numpy()
+
+
+def check_attention_torch(orc):
+    r = _rng(107)
+    for T, d in ((1, 8), (7, 16), (64, 64), (130, 128)):
+        q, k, v = (r.standard_normal((2, 3, T, d)) for _ in range(3))
+        for causal in (False, True):
+            o = orc.attention(q, k, v, causal)
+            ref = _sdpa(q, k, v, causal)
+            assert np.max(np.abs(o - ref)) <= 1e-13, (T, d, causal)
+    q, k, v = (3.0 * r.standard_normal((1, 2, 33, 32)) for _ in range(3))
+    o = orc.attention(q, k, v, True, scale=0.3)
+    assert np.max(np.abs(o - _sdpa(q, k, v, True, 0.3))) <= 1e-13
+
+
+def check_attention_closed_forms(orc):
+    r = _rng(109)
+    T, d = 40, 16
+    q, k = r.standard_normal((1, T, d)), r.standard_normal((1, T, d))
+    c = r.standard_normal(d)
+    v = np.tile(c, (1, T, 1))
+    for causal in (False, True):
+        assert np.max(np.abs(orc.attention(q, k, v, causal) - c)) <= 1e-14
+    v = r.standard_normal((1, T, d))
+    z = np.zeros((1, T, d))
+    o = orc.attention(z, k, v, False)
+    assert np.max(np.abs(o[0] - v[0].mean(axis=0))) <= 1e-14
+    o = orc.attention(z, k, v, True)
+    prefix = np.cumsum(v[0], axis=0) / np.arange(1, T + 1)[:, None]
+    assert np.max(np.abs(o[0] - prefix)) <= 1e-14
+    o = orc.attention(q, k, v, True)
+    assert np.array_equal(o[0, 0], v[0, 0])
+    o1 = orc.attention(q[:, :1], k[:, :1], v[:, :1], False)
+    assert np.array_equal(o1, v[:, :1])
+    # a dominant score: query 5 aligned with key 11 at large scale
+    qd = np.zeros((1, T, d))
+    kd = 0.01 * r.standard_normal((1, T, d))
+    qd[0, 5, 0] = 1.0
+    kd[0, 11, 0] = 1.0
+    o = orc.attention(qd, kd, v, False, scale=200.0)
+    assert np.max(np.abs(o[0, 5] - v[0, 11])) <= 1e-12
+
+
+def check_attention_permutation(orc):
+    r = _rng(113)
+    q, k, v = (r.standard_normal((2, 50, 8)) for _ in range(3))
+    perm = r.permutation(50)
+    o = orc.attention(q, k, v, False)
+    op = orc.attention(q, k[:, perm], v[:, perm], False)
+    assert np.max(np.abs(o - op)) <= 1e-14
+    # a permutation of keys changes the causal result (the mask is positional)
+    assert np.max(np.abs(orc.attention(q, k, v, True) - orc.attention(q, k[:, perm], v[:, perm],
+                                                                      True))) > 1e-3
+
+
+def check_attention_brute_force(orc):
+    import mpmath
+
+    mpmath.mp.dps = 50
+    r = _rng(127)
+    for T, d, causal in ((3, 2, False), (4, 3, True), (5, 1, True)):
+        q, k, v = (2.0 * r.standard_normal((1, T, d)) for _ in range(3))
+        o = orc.attention(q, k, v, causal)
+        sc = mpmath.mpf(1) / mpmath.sqrt(d)
+        for i in range(T):
+            n = i + 1 if causal else T
+            w = [mpmath.exp(sc * mpmath.fsum(mpmath.mpf(float(q[0, i, c])) * float(k[0, j, c])
+                                             for c in range(d))) for j in range(n)]
+            den = mpmath.fsum(w)
+            for c in range(d):
+                ref = mpmath.fsum(w[j] * float(v[0, j, c]) for j in range(n)) / den
+                assert abs(o[0, i, c] - float(ref)) <= 4e-15 * max(1.0, abs(float(ref)))
+
+
+def check_flash_attention_tiled(orc):
+    r = _rng(131)
+    for T, d in ((1, 4), (37, 16), (100, 32)):
+        q, k, v = (2.0 * r.standard_normal((2, T, d)) for _ in range(3))
+        for causal in (False, True):
+            ref = orc.attention(q, k, v, causal)
+            for br, bc in ((1, 1), (3, 5), (16, 16), (T, T), (T + 5, 7), (64, 3)):
+                o = orc.flash_attention(q, k, v, causal, block_q=br, block_kv=bc)
+                assert np.max(np.abs(o - ref)) <= 1e-13, (T, causal, br, bc)
+
+
 PINS = [
     check_softmax_sums_to_one,
     check_softmax_shift_invariance,
@@ -569,4 +670,9 @@ PINS = [
     check_layernorm_gelu_ex,
     check_row_sum,
     check_row_max,
+    check_attention_torch,
+    check_attention_closed_forms,
+    check_attention_permutation,
+    check_attention_brute_force,
+    check_flash_attention_tiled,
 ]

@@ -53,6 +53,16 @@ MUTANTS = {
     "row_sum_drops_last": ("        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];", "        for (int64_t j = 0; j + 1 < N; ++j)\n            s += x[i * N + j];"),
     "row_sum_first_twice": ("        double s = 0.0;\n        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];", "        double s = x[i * N];\n        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];"),
     "row_max_ignores_nan": ("        if (isnan(x[j]))\n            return NAN;\n", ""),
+    "attn_scale_dropped": ("                s[j] = dot * scale;", "                s[j] = dot;"),
+    "attn_causal_off_by_one": ("int64_t n = causal ? i + 1 : T;", "int64_t n = causal ? (i > 0 ? i : 1) : T;"),
+    "attn_causal_ignored": ("int64_t n = causal ? i + 1 : T;", "int64_t n = T;"),
+    "attn_no_max_shift": ("                den += exp(s[j] - m);\n", "                den += exp(s[j]);\n"),
+    "attn_unnormalized": ("                oh[i * d + c] = acc / den;", "                oh[i * d + c] = acc;"),
+    "attn_key_index": ("dot += qh[i * d + c] * kh[j * d + c];\n                s[j]", "dot += qh[i * d + c] * kh[i * d + c];\n                s[j]"),
+    "flash_acc_not_rescaled": ("                        acc[r * d + c] *= alpha;", ""),
+    "flash_l_not_rescaled": ("l[r] = alpha * l[r] + psum;", "l[r] = l[r] + psum;"),
+    "flash_causal_strict": ("sblk[t] = (causal && j > i) ? -INFINITY", "sblk[t] = (causal && j >= i && j > 0) ? -INFINITY"),
+    "flash_alpha_inverted": ("double alpha = m[r] == -INFINITY ? 0.0 : exp(m[r] - m_new);", "double alpha = m[r] == -INFINITY ? 0.0 : exp(m_new - m[r]);"),
     "split_moments_chunk_floor": ("    int64_t C = (N + S - 1) / S;\n    double n = 0.0", "    int64_t C = N / S;\n    if (C < 1)\n        C = 1;\n    double n = 0.0"),
 }
 
