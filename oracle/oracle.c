@@ -442,6 +442,7 @@ void oracle_attention(const double *q, const double *k, const double *v, double 
                       int64_t T, int64_t d, int causal, double scale)
 {
     double *s = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double *w = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
     for (int64_t h = 0; h < BH; ++h) {
         const double *qh = q + h * T * d, *kh = k + h * T * d, *vh = v + h * T * d;
         double *oh = o + h * T * d;
@@ -455,17 +456,20 @@ void oracle_attention(const double *q, const double *k, const double *v, double 
             }
             double m = row_max(s, n);
             double den = 0.0;
-            for (int64_t j = 0; j < n; ++j)
-                den += exp(s[j] - m);
+            for (int64_t j = 0; j < n; ++j) {
+                w[j] = exp(s[j] - m);
+                den += w[j];
+            }
             for (int64_t c = 0; c < d; ++c) {
                 double acc = 0.0;
                 for (int64_t j = 0; j < n; ++j)
-                    acc += exp(s[j] - m) * vh[j * d + c];
+                    acc += w[j] * vh[j * d + c];
                 oh[i * d + c] = acc / den;
             }
         }
     }
     free(s);
+    free(w);
 }
 
 /* The tiled form ([L6] §7.3, [TKE] §5.2): query blocks of Br rows; for each,

@@ -597,6 +597,16 @@ def check_attention_closed_forms(orc):
     assert np.max(np.abs(o[0, 5] - v[0, 11])) <= 1e-12
 
 
+def check_attention_large_scores(orc):
+    # scores in the thousands: exp without the max shift overflows
+    r = _rng(137)
+    q, k, v = (r.standard_normal((1, 2, 48, 16)) for _ in range(3))
+    for causal in (False, True):
+        o = orc.attention(q, k, v, causal, scale=500.0)
+        assert np.all(np.isfinite(o))
+        assert np.max(np.abs(o - _sdpa(q, k, v, causal, 500.0))) <= 1e-12, causal
+
+
 def check_attention_permutation(orc):
     r = _rng(113)
     q, k, v = (r.standard_normal((2, 50, 8)) for _ in range(3))
@@ -672,6 +682,7 @@ PINS = [
     check_row_max,
     check_attention_torch,
     check_attention_closed_forms,
+    check_attention_large_scores,
     check_attention_permutation,
     check_attention_brute_force,
     check_flash_attention_tiled,

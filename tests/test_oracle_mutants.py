@@ -56,7 +56,7 @@ MUTANTS = {
     "attn_scale_dropped": ("                s[j] = dot * scale;", "                s[j] = dot;"),
     "attn_causal_off_by_one": ("int64_t n = causal ? i + 1 : T;", "int64_t n = causal ? (i > 0 ? i : 1) : T;"),
     "attn_causal_ignored": ("int64_t n = causal ? i + 1 : T;", "int64_t n = T;"),
-    "attn_no_max_shift": ("                den += exp(s[j] - m);\n", "                den += exp(s[j]);\n"),
+    "attn_no_max_shift": ("                w[j] = exp(s[j] - m);\n", "                w[j] = exp(s[j]);\n"),
     "attn_unnormalized": ("                oh[i * d + c] = acc / den;", "                oh[i * d + c] = acc;"),
     "attn_key_index": ("dot += qh[i * d + c] * kh[j * d + c];\n                s[j]", "dot += qh[i * d + c] * kh[i * d + c];\n                s[j]"),
     "flash_acc_not_rescaled": ("                        acc[r * d + c] *= alpha;", ""),
