@@ -49,6 +49,7 @@ extern "C" {
 typedef enum rk_dtype {
     RK_F32 = 0,  /* IEEE binary32 */
     RK_BF16 = 1, /* bfloat16 storage, fp32 arithmetic */
+    RK_F16 = 2,  /* IEEE binary16 storage (rk_flash_attention only) */
 } rk_dtype;
 
 /* GeLU form ([TKE] §3.4 gives both): the LayerNorm epilogue and rk_gelu. */
@@ -260,6 +261,38 @@ rk_status rk_row_max(const void *x, void *out, int64_t M, int64_t N, int64_t ldx
  */
 rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
                   rk_dtype dtype, rk_gelu_kind gelu, hipStream_t stream);
+
+/*
+ * Attention forward with the online softmax fused into the value product
+ * ([TKE] §5.2 "FlashAttention-style Forward"; [L6] §7.2-7.3 and §8):
+ *     o[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:] . k[b,h,j,:]) v[b,h,j,:]
+ * over keys j < T, or j <= i when `causal` is nonzero.  Neither the T x T
+ * scores nor the probabilities are written anywhere: keys and values are
+ * scanned in blocks with a running max, sum and output per query row.
+ *
+ * q, k, v, o  [B][H][T][d] of `dtype` (RK_BF16 or RK_F16), unit stride along
+ *             d; `*_strides` = {batch, head, seq} element strides of each, or
+ *             NULL for the contiguous layout {H*T*d, T*d, d}.  Base pointers
+ *             16-byte aligned and every stride a multiple of 8 elements.
+ * d           head dimension, 64 or 128.
+ * scale       multiplies the scores (finite; usually 1 / sqrt(d)).
+ * Arithmetic  products on the matrix cores with fp32 accumulation; the
+ *             probabilities are rounded to `dtype` for the value product (as
+ *             the pages' kernel casts them to the value type); softmax state
+ *             and accumulators in fp32; o rounded to nearest even.
+ *
+ * Returns RK_ERR_INVALID_ARG for negative sizes, d < 1, a NULL pointer with
+ * B*H*T > 0, a non-finite scale, causal outside {0, 1}, an unknown dtype, a
+ * seq stride below d, o overlapping q, k or v, or o's rows overlapping one
+ * another; RK_ERR_UNSUPPORTED for RK_F32, d other than 64 or 128,
+ * misaligned pointers or strides, or sizes beyond the launch limits.
+ * B*H*T == 0 is a no-op.
+ */
+rk_status rk_flash_attention(const void *q, const void *k, const void *v, void *o, int64_t B,
+                             int64_t H, int64_t T, int64_t d, const int64_t *q_strides,
+                             const int64_t *k_strides, const int64_t *v_strides,
+                             const int64_t *o_strides, float scale, int32_t causal,
+                             rk_dtype dtype, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status ("unknown status" for an
  * unknown value). */

@@ -14,6 +14,7 @@ Functions carry the C entry points' names:
   workspace=None)``, ``rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype)``,
   ``rk_layernorm_gelu_auto_splits(M, N, dtype)``
 * ``rk_row_sum(x, out=None)``, ``rk_row_max(x, out=None)``, ``rk_gelu(x, gelu="tanh", out=None)``
+* ``rk_flash_attention(q, k, v, causal=False, scale=None, out=None)``
 * ``rk_rmsnorm(x, weight, eps=1e-5, out=None)``
 * ``rk_residual_rmsnorm(x, residual, weight, eps=1e-5, out=None, residual_out=None)``
 * ``rk_online_softmax_workspace_bytes(M, N, num_splits)``,
@@ -38,12 +39,13 @@ __all__ = [
     "RK_OP_LAYERNORM_GELU", "rk_rmsnorm", "rk_residual_rmsnorm", "rk__rmsnorm_variant",
     "rk__residual_rmsnorm_variant", "RK_OP_RMSNORM", "RK_OP_RESIDUAL_RMSNORM",
     "rk_layernorm_gelu_ex", "rk_layernorm_gelu_workspace_bytes", "rk_layernorm_gelu_auto_splits",
-    "RK_GELU_TANH", "RK_GELU_ERF", "rk_row_sum", "rk_row_max", "rk_gelu",
+    "RK_GELU_TANH", "RK_GELU_ERF", "rk_row_sum", "rk_row_max", "rk_gelu", "rk_flash_attention",
+    "RK_F16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.so")
 
-RK_F32, RK_BF16 = 0, 1
+RK_F32, RK_BF16, RK_F16 = 0, 1, 2
 RK_OP_SOFTMAX, RK_OP_LAYERNORM_GELU, RK_OP_RMSNORM, RK_OP_RESIDUAL_RMSNORM = 0, 1, 2, 3
 RK_GELU_TANH, RK_GELU_ERF = 0, 1
 _GELU = {"tanh": RK_GELU_TANH, "erf": RK_GELU_ERF}
@@ -93,6 +95,8 @@ def load():
         "rk_layernorm_gelu_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "rk_layernorm_gelu_auto_splits": (i32, [i64, i64, i32]),
         "rk_row_sum": (i32, [vp, vp, i64, i64, i64, i32, vp]),
+        "rk_flash_attention": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, f32, i32,
+                                     i32, vp]),
         "rk_row_max": (i32, [vp, vp, i64, i64, i64, i32, vp]),
         "rk_gelu": (i32, [vp, vp, i64, i64, i64, i64, i32, i32, vp]),
         "rk_rmsnorm": (i32, [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
@@ -304,6 +308,38 @@ def rk_gelu(x, gelu: str = "tanh", out=None):
     _call("rk_gelu", v.data_ptr(), o.data_ptr(), M, N, ldx, ldy, _dtype_code(x), _GELU[gelu],
           _stream(x))
     return o.reshape(x.shape) if out is None else out
+
+
+def rk_flash_attention(q, k, v, causal: bool = False, scale=None, out=None):
+    """softmax(q k^T * scale) v for [B, H, T, d] tensors (bf16 or fp16, unit
+    stride along d); scale defaults to 1 / sqrt(d)."""
+    torch = _torch()
+    _check_device(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, T, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    B, H, T, d = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must match q")
+    for t in (q, k, v, out):
+        if T > 0 and d > 1 and t.stride(3) != 1:
+            raise ValueError("the head dimension must have unit stride")
+    code = {torch.bfloat16: RK_BF16, torch.float16: RK_F16, torch.float32: RK_F32}.get(q.dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    sc = 1.0 / (d ** 0.5) if scale is None else float(scale)
+
+    def strides(t):
+        return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+    arrs = [strides(t) for t in (q, k, v, out)]  # alive for the call
+    sq, sk, sv, so = (ctypes.cast(a, ctypes.c_void_p) for a in arrs)
+    _call("rk_flash_attention", q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H,
+          T, d, sq, sk, sv, so, sc, int(bool(causal)), code, _stream(q))
+    return out
 
 
 def _check_weight(weight, x, N):

@@ -571,6 +571,109 @@ RK_EXPORT rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_
     return hip_status(gelu_run(p, false, rows_aligned(x, y, ldx, ldy, es)));
 }
 
+// ------------------------------------------------------------ attention
+
+namespace {
+
+// Span of a [B][H][T][d] tensor with element strides s; false on overflow.
+bool attn_span(const void *p, int64_t B, int64_t H, int64_t T, int64_t d, const int64_t *s,
+               int es, Span *out)
+{
+    int64_t e = d, t;
+    const int64_t n[3] = {B, H, T};
+    for (int i = 0; i < 3; ++i) {
+        if (__builtin_mul_overflow(n[i] - 1, s[i], &t) || __builtin_add_overflow(e, t, &e))
+            return false;
+    }
+    if (__builtin_mul_overflow(e, int64_t{es}, &t))
+        return false;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    *out = Span{lo, lo + static_cast<uintptr_t>(t)};
+    return true;
+}
+
+// Rows of o (d elements each) are pairwise disjoint when the dimensions,
+// ordered by stride, nest: each stride at least the extent of those inside it.
+bool attn_rows_disjoint(int64_t B, int64_t H, int64_t T, int64_t d, const int64_t *s)
+{
+    int64_t n[3] = {B, H, T}, st[3] = {s[0], s[1], s[2]};
+    // sort the dimensions by stride (size-1 dimensions never collide)
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (st[j] < st[i]) {
+                int64_t a = st[i], b = n[i];
+                st[i] = st[j], n[i] = n[j];
+                st[j] = a, n[j] = b;
+            }
+    int64_t extent = d;
+    for (int i = 0; i < 3; ++i) {
+        if (n[i] <= 1)
+            continue;
+        if (st[i] < extent)
+            return false;
+        int64_t t;
+        if (__builtin_mul_overflow(n[i] - 1, st[i], &t) || __builtin_add_overflow(extent, t, &extent))
+            return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+RK_EXPORT rk_status rk_flash_attention(const void *q, const void *k, const void *v, void *o,
+                                       int64_t B, int64_t H, int64_t T, int64_t d,
+                                       const int64_t *q_strides, const int64_t *k_strides,
+                                       const int64_t *v_strides, const int64_t *o_strides,
+                                       float scale, int32_t causal, rk_dtype dtype,
+                                       hipStream_t stream)
+{
+    if (dtype != RK_BF16 && dtype != RK_F16 && dtype != RK_F32)
+        return RK_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || T < 0 || d < 1 || !std::isfinite(scale) || (causal != 0 && causal != 1))
+        return RK_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || T == 0)
+        return RK_OK;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+        return RK_ERR_INVALID_ARG;
+    const int64_t dense[3] = {H * T * d, T * d, d};
+    if (H > INT64_MAX / T || H * T > INT64_MAX / d || B > INT64_MAX / (H * T * d))
+        return RK_ERR_INVALID_ARG;
+    const int64_t *st[4] = {q_strides ? q_strides : dense, k_strides ? k_strides : dense,
+                            v_strides ? v_strides : dense, o_strides ? o_strides : dense};
+    const void *base[4] = {q, k, v, o};
+    Span span[4];
+    for (int i = 0; i < 4; ++i) {
+        if (st[i][0] < 0 || st[i][1] < 0 || st[i][2] < d)
+            return RK_ERR_INVALID_ARG;
+        if (!attn_span(base[i], B, H, T, d, st[i], 2, &span[i]))
+            return RK_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(span[3], span[i]))
+            return RK_ERR_INVALID_ARG;
+    if (!attn_rows_disjoint(B, H, T, d, st[3]))
+        return RK_ERR_INVALID_ARG;
+    if (dtype == RK_F32 || (d != 64 && d != 128))
+        return RK_ERR_UNSUPPORTED;
+    for (int i = 0; i < 4; ++i) {
+        if (!aligned16(base[i]) || st[i][0] % 8 || st[i][1] % 8 || st[i][2] % 8)
+            return RK_ERR_UNSUPPORTED;
+    }
+    const int64_t bm = attention_block_rows();
+    const int64_t nqb = (T + bm - 1) / bm;
+    if (T > INT32_MAX || B * H > INT32_MAX || B * H > INT64_MAX / nqb ||
+        !grid_ok(B * H * nqb, 256))
+        return RK_ERR_UNSUPPORTED;
+    AttentionProblem p{q, k, v, o, B, H, T, d, {}, {}, {}, {}, scale, causal != 0, dtype, stream};
+    for (int j = 0; j < 3; ++j) {
+        p.sq[j] = st[0][j];
+        p.sk[j] = st[1][j];
+        p.sv[j] = st[2][j];
+        p.so[j] = st[3][j];
+    }
+    return hip_status(flash_attention_run(p));
+}
+
 RK_EXPORT const char *rk_status_string(rk_status status)
 {
     switch (status) {

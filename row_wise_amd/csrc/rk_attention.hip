@@ -1,0 +1,397 @@
+// Attention forward with the online softmax fused into the value product
+// ("Triton Kernel 实现练习" §5.2 "FlashAttention-style Forward"; "第 6 讲：GPU
+// Kernels 与 Triton" §7.2-7.3 and §8).
+//
+// Per (batch, head) and query row i: S_ij = scale q_i . k_j (causal: keys
+// j <= i only), o_i = sum_j softmax(S_i)_j v_j.  Key/value blocks are scanned
+// with a per-row state m (max so far), l (sum of exp so far) and acc (the
+// exp-weighted sum of value rows so far); a new block moves the state by
+// alpha = exp(m - m_new): l = alpha l + sum p, acc = alpha acc + p V.  At the
+// end o = acc / l.  Scores and probabilities live only in registers.
+//
+// CDNA4 mapping (16x16x32 MFMA, bf16 or fp16 operands, fp32 accumulation):
+//   a workgroup of 4 waves owns BM = 128 query rows of one (batch, head);
+//   each wave owns 32 of them as two 16-row tiles, with its Q fragments in
+//   registers for the whole kernel.  Per step of BN = 64 keys the workgroup
+//   stages K (row-major) and V (transposed) in LDS; every wave then forms
+//   S^T = K Q^T (keys x queries, so that each lane holds one query's scores
+//   for 16 of the keys), the row max across the four 16-lane groups
+//   (permlane16/32 swaps), p = exp2(S log2e scale - m), and O^T += V^T P^T,
+//   where P^T is the S^T fragments rounded to the operand type in place (the
+//   key order inside each 32-key step is permuted identically in V^T).
+//   The next block's K/V are loaded into registers while this one is used.
+#include "rk_device.h"
+#include "rk_internal.h"
+
+namespace rk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Operand traits: DT = RK_BF16 or RK_F16 (both 16-bit storage).
+template <int DT>
+struct Operand;
+
+template <>
+struct Operand<RK_BF16> {
+    typedef bf16x8_t vec;
+    __device__ static __forceinline__ f32x4v_t mfma(vec a, vec b, f32x4v_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // two fp32 -> two packed 16-bit values, round to nearest even
+    __device__ static __forceinline__ uint32_t pack2(float a, float b)
+    {
+        f32x2_t f = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    }
+};
+
+template <>
+struct Operand<RK_F16> {
+    typedef f16x8_t vec;
+    __device__ static __forceinline__ f32x4v_t mfma(vec a, vec b, f32x4v_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ uint32_t pack2(float a, float b)
+    {
+        f32x2_t f = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+    }
+};
+
+// Value of lane l and of lane l ^ 16 (in the order even row, odd row of the
+// pair of 16-lane rows, identical in both lanes).
+__device__ __forceinline__ u32x2_t swap16(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return u32x2_t{r[0], r[1]};
+}
+__device__ __forceinline__ u32x2_t swap32(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return u32x2_t{r[0], r[1]};
+}
+// max / sum over the four lanes l, l^16, l^32, l^48 (same bits in all four)
+__device__ __forceinline__ float group4_max(float v)
+{
+    u32x2_t a = swap16(v);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    u32x2_t b = swap32(v);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float v)
+{
+    u32x2_t a = swap16(v);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    u32x2_t b = swap32(v);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnBM = 32 * kAttnWaves;  // query rows per workgroup
+constexpr int kAttnBN = 64;              // keys per step
+
+template <int D>
+struct AttnLds {
+    static constexpr int kKStride = D + 8;       // K row pitch (elements): 16 B of padding
+    static constexpr int kVStride = kAttnBN + 4; // V^T row pitch (elements): 8 B of padding
+    uint16_t k[kAttnBN * kKStride];
+    uint16_t vt[D * kVStride];
+};
+
+// Strides in elements; the head_dim stride is 1.
+struct AttnStrides {
+    int64_t b, h, t;
+};
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kAttnWaves *kWave) void flash_attention_fwd(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, uint16_t *__restrict__ o, int H, int T, int nqb, int BH,
+    AttnStrides sq, AttnStrides sk, AttnStrides sv, AttnStrides so, float scale_log2e)
+{
+    typedef Operand<DT> Op;
+    typedef typename Op::vec vec;
+    constexpr int DS = D / 32;   // 32-wide d steps of S
+    constexpr int DT16 = D / 16; // 16-wide d tiles of O
+    constexpr int NKT = kAttnBN / 16;
+    constexpr int NKS = kAttnBN / 32;
+    constexpr int CH = D / 8;    // 16-byte chunks per K/V row
+    constexpr int LOADS = kAttnBN * CH / (kAttnWaves * kWave);  // K chunks per thread
+    static_assert(LOADS * kAttnWaves * kWave == kAttnBN * CH, "whole K block per workgroup");
+    static_assert(kAttnBN == 64 && (D == 64 || D == 128), "shapes of this kernel");
+    __shared__ AttnLds<D> lds;
+
+    // heaviest query blocks first (causal), and every query block of one
+    // (batch, head) on the same XCD when BH is a multiple of 8
+    const int rank = static_cast<int>(blockIdx.x) / BH;
+    const int bh = static_cast<int>(blockIdx.x) % BH;
+    const int qb = nqb - 1 - rank;
+    const int b = bh / H, h = bh % H;
+    const uint16_t *qh = q + b * sq.b + h * sq.h;
+    const uint16_t *kh = k + b * sk.b + h * sk.h;
+    const uint16_t *vh = v + b * sv.b + h * sv.h;
+    uint16_t *oh = o + b * so.b + h * so.h;
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int l16 = lane % 16;
+    const int g = lane / 16;
+    const int q0 = qb * kAttnBM;
+    const int qw = q0 + 32 * wave;  // first query row of this wave
+
+    // Q fragments (B operand of S^T = K Q^T): query qw + 16 qt + l16,
+    // d = 32 ds + 8 g .. + 8.  Rows past T read row T - 1 (never stored).
+    vec qf[2][DS];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        int row = qw + 16 * qt + l16;
+        row = row < T ? row : T - 1;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+            qf[qt][ds] = *reinterpret_cast<const vec *>(qh + row * sq.t + 32 * ds + 8 * g);
+    }
+
+    f32x4v_t acc[2][DT16];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt)
+            acc[qt][dt] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m[2] = {-INFINITY, -INFINITY};
+    float lsum[2] = {0.0f, 0.0f};  // this lane's part of the row sums
+
+    // K/V staging: K chunk i of this thread is key (tid + 256 i) / CH,
+    // column 8 ((tid + 256 i) % CH); V: keys 4 kq .. 4 kq + 3 at column
+    // 8 cv, kq = tid / CH (LOADS keys per group of 4), so that the four keys
+    // of one column pack into one 8-byte V^T write.
+    u32x4_t kreg[LOADS], vreg[LOADS];
+    auto load_block = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int idx = tid + kAttnWaves * kWave * i;
+            const int key = kb + idx / CH;
+            const int col = 8 * (idx % CH);
+            kreg[i] = key < T ? *reinterpret_cast<const u32x4_t *>(kh + key * sk.t + col)
+                              : u32x4_t{0, 0, 0, 0};
+        }
+        const int cv = tid % CH;
+        const int kq = tid / CH;  // 0 .. 256 / CH - 1
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int key = kb + LOADS * kq + i;
+            vreg[i] = key < T ? *reinterpret_cast<const u32x4_t *>(vh + key * sv.t + 8 * cv)
+                              : u32x4_t{0, 0, 0, 0};
+        }
+    };
+    auto store_block = [&]() {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int idx = tid + kAttnWaves * kWave * i;
+            *reinterpret_cast<u32x4_t *>(&lds.k[(idx / CH) * AttnLds<D>::kKStride +
+                                                8 * (idx % CH)]) = kreg[i];
+        }
+        const int cv = tid % CH;
+        const int kq = tid / CH;
+        // V^T[d][keys LOADS kq .. + LOADS]: LOADS (= 2 or 4) keys per write
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint16_t vals[LOADS];
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i)
+                vals[i] = static_cast<uint16_t>(vreg[i][e / 2] >> (16 * (e % 2)));
+            uint16_t *dst = &lds.vt[(8 * cv + e) * AttnLds<D>::kVStride + LOADS * kq];
+            if constexpr (LOADS == 4) {
+                const uint32_t lo = vals[0] | (uint32_t{vals[1]} << 16);
+                const uint32_t hi = vals[2] | (uint32_t{vals[3]} << 16);
+                *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{lo, hi};
+            } else {
+                *reinterpret_cast<uint32_t *>(dst) = vals[0] | (uint32_t{vals[1]} << 16);
+            }
+        }
+    };
+
+    const int kend = CAUSAL ? (q0 + kAttnBM < T ? q0 + kAttnBM : T) : T;
+    load_block(0);
+    store_block();
+    __syncthreads();
+
+    for (int kb = 0; kb < kend; kb += kAttnBN) {
+        const bool more = kb + kAttnBN < kend;
+        if (more)
+            load_block(kb + kAttnBN);
+
+        // S^T tiles: s[qt][kt] holds, in lane (g, l16), query qw + 16 qt + l16
+        // and keys kb + 16 kt + 4 g + r.
+        f32x4v_t s[2][NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+                s[qt][kt] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const vec a = *reinterpret_cast<const vec *>(
+                    &lds.k[(16 * kt + l16) * AttnLds<D>::kKStride + 32 * ds + 8 * g]);
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+                    s[qt][kt] = Op::mfma(a, qf[qt][ds], s[qt][kt]);
+            }
+        }
+
+        // scale (in log2 units) and mask: keys past T, and (causal) keys
+        // after the query
+        const bool edge = kb + kAttnBN > T || (CAUSAL && kb + kAttnBN - 1 > qw);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            const int qi = qw + 16 * qt + l16;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float t = s[qt][kt][r] * scale_log2e;
+                    if (edge) {
+                        const int key = kb + 16 * kt + 4 * g + r;
+                        if (key >= T || (CAUSAL && key > qi))
+                            t = -INFINITY;
+                    }
+                    s[qt][kt][r] = t;
+                }
+        }
+
+        // online softmax state per query row
+        uint32_t pk[2][NKS][4];  // P^T operand words
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    mx = fmaxf(mx, s[qt][kt][r]);
+            mx = group4_max(mx);
+            const float m_new = fmaxf(m[qt], mx);
+            // a row that has seen no key yet keeps m = -inf: shift by 0 so that
+            // its (all -inf) scores give p = 0 rather than NaN
+            const float shift = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = m[qt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[qt] - shift);
+            m[qt] = m_new;
+            float ps = 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(s[qt][kt][r] - shift);
+                    s[qt][kt][r] = p;
+                    ps += p;
+                }
+            lsum[qt] = fmaf(alpha, lsum[qt], ps);
+#pragma unroll
+            for (int dt = 0; dt < DT16; ++dt)
+                acc[qt][dt] *= alpha;
+            // 32-key step ks: slots 0..3 are keys 32 ks + 4 g + r (tile 2 ks),
+            // slots 4..7 keys 32 ks + 16 + 4 g + r (tile 2 ks + 1)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                pk[qt][ks][0] = Op::pack2(s[qt][2 * ks][0], s[qt][2 * ks][1]);
+                pk[qt][ks][1] = Op::pack2(s[qt][2 * ks][2], s[qt][2 * ks][3]);
+                pk[qt][ks][2] = Op::pack2(s[qt][2 * ks + 1][0], s[qt][2 * ks + 1][1]);
+                pk[qt][ks][3] = Op::pack2(s[qt][2 * ks + 1][2], s[qt][2 * ks + 1][3]);
+            }
+        }
+
+        // O^T += V^T P^T: A = V^T rows d = 16 dt + l16 at the same permuted
+        // keys (two 8-byte reads), B = P^T of the lane's query
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            vec bq[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                u32x4_t w = {pk[qt][ks][0], pk[qt][ks][1], pk[qt][ks][2], pk[qt][ks][3]};
+                bq[qt] = __builtin_bit_cast(vec, w);
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT16; ++dt) {
+                const uint16_t *row = &lds.vt[(16 * dt + l16) * AttnLds<D>::kVStride + 32 * ks];
+                const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(row + 4 * g);
+                const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(row + 16 + 4 * g);
+                const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+                const vec a = __builtin_bit_cast(vec, w);
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+                    acc[qt][dt] = Op::mfma(a, bq[qt], acc[qt][dt]);
+            }
+        }
+
+        __syncthreads();  // every wave is done with this block's K and V^T
+        if (more) {
+            store_block();
+            __syncthreads();
+        }
+    }
+
+    // o = acc / l; lane (g, l16) holds query qw + 16 qt + l16, d = 16 dt + 4 g + r
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int qi = qw + 16 * qt + l16;
+        const float inv = 1.0f / group4_sum(lsum[qt]);
+        if (qi < T) {
+            uint16_t *orow = oh + qi * so.t;
+#pragma unroll
+            for (int dt = 0; dt < DT16; ++dt) {
+                const f32x4v_t a = acc[qt][dt];
+                const u32x2_t w = {Op::pack2(a[0] * inv, a[1] * inv), Op::pack2(a[2] * inv, a[3] * inv)};
+                *reinterpret_cast<u32x2_t *>(orow + 16 * dt + 4 * g) = w;
+            }
+        }
+    }
+}
+
+namespace {
+
+AttnStrides strides_of(const int64_t *s) { return AttnStrides{s[0], s[1], s[2]}; }
+
+template <int DT, int D, bool CAUSAL>
+hipError_t attn_launch(const AttentionProblem &p)
+{
+    const int nqb = static_cast<int>((p.T + kAttnBM - 1) / kAttnBM);
+    const int BH = static_cast<int>(p.B * p.H);
+    const float scale_log2e = p.scale * 1.4426950408889634f;
+    return launch(flash_attention_fwd<DT, D, CAUSAL>,
+                  dim3(static_cast<unsigned>(int64_t{nqb} * BH)), dim3(kAttnWaves * kWave),
+                  p.stream, static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                  static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o),
+                  static_cast<int>(p.H), static_cast<int>(p.T), nqb, BH, strides_of(p.sq),
+                  strides_of(p.sk), strides_of(p.sv), strides_of(p.so), scale_log2e);
+}
+
+template <int DT, int D>
+hipError_t attn_causal(const AttentionProblem &p)
+{
+    return p.causal ? attn_launch<DT, D, true>(p) : attn_launch<DT, D, false>(p);
+}
+
+template <int DT>
+hipError_t attn_dim(const AttentionProblem &p)
+{
+    return p.d == 64 ? attn_causal<DT, 64>(p) : attn_causal<DT, 128>(p);
+}
+
+}  // namespace
+
+int attention_block_rows() { return kAttnBM; }
+
+hipError_t flash_attention_run(const AttentionProblem &p)
+{
+    return p.dtype == RK_BF16 ? attn_dim<RK_BF16>(p) : attn_dim<RK_F16>(p);
+}
+
+}  // namespace rk

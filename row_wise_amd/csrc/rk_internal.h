@@ -52,6 +52,19 @@ struct RowProblem {
     rk_gelu_kind gelu = RK_GELU_TANH;  // LayerNorm, GeLU: activation
 };
 
+// One attention problem as validated by the ABI layer: q, k, v, o of shape
+// [B][H][T][d] with element strides (batch, head, seq) and unit d stride.
+struct AttentionProblem {
+    const void *q, *k, *v;
+    void *o;
+    int64_t B, H, T, d;
+    int64_t sq[3], sk[3], sv[3], so[3];
+    float scale;
+    bool causal;
+    rk_dtype dtype;
+    hipStream_t stream;
+};
+
 // A compiled register-resident kernel shape.
 struct TileVariant {
     int waves_per_row;    // G: waves cooperating on a row
@@ -86,6 +99,9 @@ hipError_t row_reduce_run(const RowProblem &p, int op, bool vectorized);
 int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, bool vectorized, int *threads);
 // flat: x and y contiguous and 16-byte aligned, processed as one buffer.
 hipError_t gelu_run(const RowProblem &p, bool flat, bool vectorized);
+// Query rows per workgroup of the attention kernel.
+int attention_block_rows();
+hipError_t flash_attention_run(const AttentionProblem &p);
 hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
                           hipStream_t stream);
 

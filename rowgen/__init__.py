@@ -20,6 +20,10 @@ Recipes (one per named workload; seeds are ``1000 + k``):
 Draw order is always x, then w, then b.  bf16 values are produced by torch's
 round-to-nearest-even cast of the fp32 draw.
 
+Attention inputs (``attention_qkv``): q, k, v ~ N(0,1) of shape [B, H, T, d],
+drawn in that order in fp32 and rounded to bf16 or fp16, seed given; the
+pages benchmark B = 4, H = 32, d = 128, T = 128 ... 4096 in fp16.
+
 RMSNorm runs on the same workloads: its input is ``x``, its weight ``w``; the
 fused residual variant adds ``residual(name)``, an independent N(0,1) draw of
 the workload's shape and dtype from seed ``seed + 100``.
@@ -30,7 +34,8 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make", "randn", "ln_params", "bf16_round", "residual"]
+__all__ = ["Workload", "WORKLOADS", "make", "randn", "ln_params", "bf16_round", "residual",
+           "attention_qkv"]
 
 
 @dataclass(frozen=True)
@@ -122,3 +127,10 @@ def residual(name: str, rows: int | None = None) -> torch.Tensor:
     wl = WORKLOADS[name]
     r = randn(wl.M, wl.N, seed=wl.seed + 100, dtype=wl.dtype)
     return r if rows is None else r[:rows].contiguous()
+
+
+def attention_qkv(B: int, H: int, T: int, d: int, dtype=torch.bfloat16, seed: int = 2001):
+    """q, k, v ~ N(0,1) [B, H, T, d], drawn q, k, v in fp32, cast to dtype."""
+    g = _gen(seed)
+    return tuple(torch.randn((B, H, T, d), generator=g, dtype=torch.float32).to(dtype)
+                 for _ in range(3))

@@ -209,6 +209,40 @@ def test_gelu_rejects(lib):
     assert g(None, None, 0, 8, 8, 8, F32, 0, None) == 0
 
 
+def attn(lib, q=A, k=B, v=0x2000000, o=0x3000000, Bn=2, H=3, T=100, d=128, st=None, scale=0.1,
+         causal=0, dt=BF16):
+    arr = None
+    if st is not None:
+        arr = (ctypes.c_int64 * 3)(*st)
+    sp = ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None
+    return lib.rk_flash_attention(q, k, v, o, Bn, H, T, d, None, None, None, sp, scale, causal,
+                                  dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), INVALID), (dict(Bn=-1), INVALID), (dict(d=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(causal=2), INVALID), (dict(q=None), INVALID), (dict(o=None), INVALID),
+    (dict(o=A + 4096), INVALID),  # o overlaps q
+    (dict(o=0x2000000 - 64), INVALID),  # o overlaps v
+    (dict(st=(3 * 100 * 128, 100 * 128, 64)), INVALID),  # seq stride < d
+    (dict(st=(3 * 100 * 128, 0, 128)), INVALID),  # heads of o on top of each other
+    (dict(st=(0, 100 * 128, 128)), INVALID),  # batches of o on top of each other
+    (dict(dt=F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(q=A + 2), UNSUPPORTED), (dict(st=(3 * 100 * 136, 100 * 136, 132)), UNSUPPORTED),
+    (dict(Bn=0), 0), (dict(T=0, q=None, k=None, v=None, o=None), 0),
+])
+def test_attention_rejects(lib, kw, status):
+    assert attn(lib, **kw) == status
+
+
+def test_attention_layouts_accepted_by_validation(lib):
+    # a [B, T, H, d] output layout nests (no overlap): only alignment or launch
+    # can stop it, and M = 0 style no-ops need no pointers
+    assert lib.rk_flash_attention(None, None, None, None, 2, 0, 100, 128, None, None, None,
+                                  None, 0.1, 1, BF16, None) == 0
+
+
 def online(lib, x=A, y=B, M=4, N=4096, S=64, ws=A + 0x400000, wb=4 * 64 * 8, dt=F32):
     return lib.rk_online_softmax(x, y, M, N, N, N, dt, S, ws, wb, None)
 

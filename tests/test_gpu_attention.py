@@ -1,0 +1,121 @@
+"""Parity of rk_flash_attention with the CPU oracle's attention (by
+definition) on seeded inputs ("Triton Kernel 实现练习" §5.2; "第 6 讲" §7-8).
+
+Error measure: max |o - r| / max(|r|, 1) (outputs are convex combinations
+of N(0,1) value rows), 1e-2 for bf16 and fp16 I/O with fp32 accumulation.
+Full-size shapes are checked on sampled (batch, head) pairs, each against
+the oracle over its whole T x T problem.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import row_wise_amd as rk
+import rowgen
+from tolerance import rel_err_floor1
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-2
+DTYPES = [torch.bfloat16, torch.float16]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rk.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def key(dtype):
+    return {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check(o, q, k, v, causal, scale=None, heads=None, what=""):
+    """o (GPU) against the oracle, on all heads or on the listed (b, h)."""
+    oc = o.cpu()
+    if heads is None:
+        ref = oracle.attention(q, k, v, causal, scale)
+        err = rel_err_floor1(oc, ref)
+    else:
+        err = 0.0
+        for b, h in heads:
+            ref = oracle.attention(q[b, h], k[b, h], v[b, h], causal, scale)
+            err = max(err, rel_err_floor1(oc[b, h], ref))
+    assert err <= TOL, (what, err)
+    return err
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("T", [128, 1024, 4096])
+def test_pages_benchmark_shapes(dtype, causal, T):
+    q, k, v = rowgen.attention_qkv(4, 32, T, 128, dtype, seed=2000 + T)
+    o = rk.rk_flash_attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    heads = [(0, 0), (3, 31)] if T >= 1024 else [(0, 0), (1, 7), (3, 31)]
+    if T == 4096 and not causal:
+        heads = [(3, 31)]  # the oracle takes ~9 s per head here
+    err = check(o, q, k, v, causal, heads=heads, what=(T, causal))
+    say(f"attention {key(dtype)} 4x32x{T}x128 causal={causal} err={err:.3e}")
+
+
+EDGE_T = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 200, 257]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", EDGE_T)
+def test_edge_lengths(dtype, d, T):
+    q, k, v = rowgen.attention_qkv(2, 3, T, d, dtype, seed=T * 7 + d)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for causal in (False, True):
+        say(f"attention {key(dtype)} T={T} d={d} causal={causal}")
+        o = rk.rk_flash_attention(qd, kd, vd, causal=causal)
+        check(o, q, k, v, causal, what=(T, d, causal))
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+def test_strided_layouts_and_scale(dtype):
+    # [B, T, H, d] storage viewed as [B, H, T, d]; output into a padded buffer
+    B, H, T, d = 2, 4, 300, 128
+    q, k, v = rowgen.attention_qkv(B, H, T, d, dtype, seed=211)
+    qs = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    ks = k.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    vd = v.to(DEV)
+    buf = torch.full((B, H, T, d + 64), -7.0, dtype=dtype, device=DEV)
+    out = buf[..., :d]
+    for causal in (False, True):
+        rk.rk_flash_attention(qs, ks, vd, causal=causal, scale=0.05, out=out)
+        check(out, q, k, v, causal, scale=0.05, what=("strided", causal))
+        assert torch.all(buf[..., d:] == -7.0)
+
+
+def test_large_scores_and_constant_values():
+    # scores of several hundred: the running max moves often and far
+    B, H, T, d = 1, 2, 513, 64
+    q, k, v = rowgen.attention_qkv(B, H, T, d, torch.bfloat16, seed=223)
+    q = (q.float() * 8).to(torch.bfloat16)
+    o = rk.rk_flash_attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=1.0)
+    check(o, q, k, v, True, scale=1.0, what="large scores")
+    # equal value rows: every output row is that row
+    c = torch.randn(d).to(torch.bfloat16)
+    vc = c.expand(B, H, T, d).contiguous()
+    o = rk.rk_flash_attention(q.to(DEV), k.to(DEV), vc.to(DEV), causal=False, scale=1.0).cpu()
+    assert torch.max((o.float() - c.float()).abs()).item() <= 2e-2 * max(1.0, c.abs().max().item())
+
+
+def test_causal_first_row_and_determinism():
+    q, k, v = rowgen.attention_qkv(2, 2, 256, 128, torch.float16, seed=227)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = rk.rk_flash_attention(qd, kd, vd, causal=True)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])  # sees only key 0: o = v[0] exactly
+    o2 = rk.rk_flash_attention(qd, kd, vd, causal=True)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    e = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device=DEV)
+    assert rk.rk_flash_attention(e, e, e).shape == e.shape
