@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix cores, published
 ROTATE_BYTES = 1 << 30
 EPS = 1e-5
 METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s for softmax & LayerNorm+GeLU"
@@ -164,6 +165,43 @@ class Case:
         self.rs = self.ros = None
 
 
+class AttnCase:
+    """rk_flash_attention on [B, H, T, d] inputs: MFMA-bound, reported in
+    TFLOP/s (4 B H T^2 d flops, about half of that causal: 2 B H T (T+1) d)."""
+
+    def __init__(self, name, B, H, T, d, dtype, causal):
+        self.name, self.B, self.H, self.T, self.d = name, B, H, T, d
+        self.dtype_name, self.causal = dtype, causal
+
+    def setup(self, torch, rk, rowgen):
+        dt = {"bf16": torch.bfloat16, "f16": torch.float16}[self.dtype_name]
+        B, H, T, d = self.B, self.H, self.T, self.d
+        q, k, v = rowgen.attention_qkv(B, H, T, d, dt, seed=3000 + T)
+        dev = torch.device("cuda")
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.o = torch.empty_like(self.q)
+        self.M = None
+        self.flops = (2.0 * B * H * T * (T + 1) * d if self.causal else 4.0 * B * H * T * T * d)
+        self.bytes = 4 * B * H * T * d * q.element_size()  # q, k, v read once, o written
+        self.R = 1  # compute-bound: no buffer rotation needed
+        lib = rk.load()
+        self.fn = lib.rk_flash_attention
+        code = rk.RK_BF16 if dt == torch.bfloat16 else rk.RK_F16
+        stream = torch.cuda.current_stream().cuda_stream
+        self.args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                     B, H, T, d, None, None, None, None, ctypes.c_float(1.0 / math.sqrt(d)),
+                     int(self.causal), code, stream)
+        return self
+
+    def launch(self, i):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"{self.name}: status {st}")
+
+    def free(self):
+        self.q = self.k = self.v = self.o = self.args = None
+
+
 class CopyCase:
     """The 16-byte copy kernel: achievable read+write bandwidth."""
 
@@ -217,6 +255,10 @@ def all_cases():
         Case("residual_rmsnorm_f32_4096x768", "residual_rmsnorm", "ln_gelu_f32_4096x768"),
         Case("rmsnorm_bf16_16384x4096", "rmsnorm", "bf16_16384x4096"),
         Case("residual_rmsnorm_bf16_16384x4096", "residual_rmsnorm", "bf16_16384x4096"),
+        AttnCase("attn_bf16_4x32x1024x128", 4, 32, 1024, 128, "bf16", False),
+        AttnCase("attn_bf16_4x32x4096x128", 4, 32, 4096, 128, "bf16", False),
+        AttnCase("attn_causal_bf16_4x32x4096x128", 4, 32, 4096, 128, "bf16", True),
+        AttnCase("attn_f16_4x32x4096x128", 4, 32, 4096, 128, "f16", False),
         CopyCase("copy_256MiB", 256 << 20),
         # copies of the same total traffic as the small workloads: the
         # achievable ceiling at that size (launch and latency included)
@@ -393,13 +435,20 @@ def main():
                "GB_per_s": round(c.bytes / t / 1e9, 1),
                "pct_hbm_peak": round(100 * c.bytes / t / 1e9 / HBM_PEAK_GBS, 1),
                "bytes_per_call": c.bytes, "rotation_sets": c.R}
+        if getattr(c, "flops", None):
+            rec["TFLOP_per_s"] = round(c.flops / t / 1e12, 1)
+            rec["pct_mfma_peak"] = round(100 * c.flops / t / 1e12 / MFMA_PEAK_TFLOPS, 1)
         if c.M is not None:
             rec["rows_per_s"] = round(c.M / t, 1)
         if getattr(c, "splits", None):
             rec["splits"] = c.splits
         detail.append(rec)
-        log(f"case {c.name}: {rec['us_per_call']} us  {rec['GB_per_s']} GB/s "
-            f"({rec['pct_hbm_peak']}% of 8 TB/s)")
+        if "TFLOP_per_s" in rec:
+            log(f"case {c.name}: {rec['us_per_call']} us  {rec['TFLOP_per_s']} TFLOP/s "
+                f"({rec['pct_mfma_peak']}% of 2.5 PFLOP/s)")
+        else:
+            log(f"case {c.name}: {rec['us_per_call']} us  {rec['GB_per_s']} GB/s "
+                f"({rec['pct_hbm_peak']}% of 8 TB/s)")
         c.free()
         torch.cuda.empty_cache()
 

@@ -275,14 +275,15 @@ rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_t ldx, int
  *             NULL for the contiguous layout {H*T*d, T*d, d}.  Base pointers
  *             16-byte aligned and every stride a multiple of 8 elements.
  * d           head dimension, 64 or 128.
- * scale       multiplies the scores (finite; usually 1 / sqrt(d)).
+ * scale       multiplies the scores (finite and > 0; usually 1 / sqrt(d)).
  * Arithmetic  products on the matrix cores with fp32 accumulation; the
  *             probabilities are rounded to `dtype` for the value product (as
  *             the pages' kernel casts them to the value type); softmax state
  *             and accumulators in fp32; o rounded to nearest even.
  *
  * Returns RK_ERR_INVALID_ARG for negative sizes, d < 1, a NULL pointer with
- * B*H*T > 0, a non-finite scale, causal outside {0, 1}, an unknown dtype, a
+ * B*H*T > 0, a scale that is not finite and > 0, causal outside {0, 1}, an
+ * unknown dtype, a
  * seq stride below d, o overlapping q, k or v, or o's rows overlapping one
  * another; RK_ERR_UNSUPPORTED for RK_F32, d other than 64 or 128,
  * misaligned pointers or strides, or sizes beyond the launch limits.

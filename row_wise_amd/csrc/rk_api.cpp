@@ -629,7 +629,8 @@ RK_EXPORT rk_status rk_flash_attention(const void *q, const void *k, const void 
 {
     if (dtype != RK_BF16 && dtype != RK_F16 && dtype != RK_F32)
         return RK_ERR_INVALID_ARG;
-    if (B < 0 || H < 0 || T < 0 || d < 1 || !std::isfinite(scale) || (causal != 0 && causal != 1))
+    if (B < 0 || H < 0 || T < 0 || d < 1 || !std::isfinite(scale) || !(scale > 0.0f) ||
+        (causal != 0 && causal != 1))
         return RK_ERR_INVALID_ARG;
     if (B == 0 || H == 0 || T == 0)
         return RK_OK;

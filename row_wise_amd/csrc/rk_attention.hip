@@ -112,7 +112,8 @@ struct AttnStrides {
 };
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kAttnWaves *kWave) void flash_attention_fwd(
+__global__ __launch_bounds__(kAttnWaves *kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void flash_attention_fwd(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, int H, int T, int nqb, int BH,
     AttnStrides sq, AttnStrides sk, AttnStrides sv, AttnStrides so, float scale_log2e)
@@ -247,24 +248,22 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void flash_attention_fwd(
             }
         }
 
-        // scale (in log2 units) and mask: keys past T, and (causal) keys
-        // after the query
+        // mask keys past T and (causal) keys after the query, on the raw
+        // scores (scale > 0: the max commutes with it)
         const bool edge = kb + kAttnBN > T || (CAUSAL && kb + kAttnBN - 1 > qw);
+        if (edge) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const int qi = qw + 16 * qt + l16;
+            for (int qt = 0; qt < 2; ++qt) {
+                const int qi = qw + 16 * qt + l16;
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float t = s[qt][kt][r] * scale_log2e;
-                    if (edge) {
+                    for (int r = 0; r < 4; ++r) {
                         const int key = kb + 16 * kt + 4 * g + r;
                         if (key >= T || (CAUSAL && key > qi))
-                            t = -INFINITY;
+                            s[qt][kt][r] = -INFINITY;
                     }
-                    s[qt][kt][r] = t;
-                }
+            }
         }
 
         // online softmax state per query row
@@ -278,25 +277,30 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void flash_attention_fwd(
                 for (int r = 0; r < 4; ++r)
                     mx = fmaxf(mx, s[qt][kt][r]);
             mx = group4_max(mx);
-            const float m_new = fmaxf(m[qt], mx);
-            // a row that has seen no key yet keeps m = -inf: shift by 0 so that
-            // its (all -inf) scores give p = 0 rather than NaN
-            const float shift = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = m[qt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[qt] - shift);
+            const float m_new = fmaxf(m[qt], mx);  // raw (unscaled) score units
+            // p = exp(scale (s - m)) = exp2(s c - m c), c = scale log2(e).  A
+            // row that has seen no key yet keeps m = -inf: shift by 0 so that
+            // its (all -inf) scores give p = 0 rather than NaN.
+            const float shift = m_new == -INFINITY ? 0.0f : m_new * scale_log2e;
+            const float alpha =
+                m[qt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(m[qt], scale_log2e, -shift));
             m[qt] = m_new;
             float ps = 0.0f;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(s[qt][kt][r] - shift);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][r], scale_log2e, -shift));
                     s[qt][kt][r] = p;
                     ps += p;
                 }
             lsum[qt] = fmaf(alpha, lsum[qt], ps);
+            // rescale the output only when some row's max moved (alpha < 1)
+            if (!__all(alpha == 1.0f)) {
 #pragma unroll
-            for (int dt = 0; dt < DT16; ++dt)
-                acc[qt][dt] *= alpha;
+                for (int dt = 0; dt < DT16; ++dt)
+                    acc[qt][dt] *= alpha;
+            }
             // 32-key step ks: slots 0..3 are keys 32 ks + 4 g + r (tile 2 ks),
             // slots 4..7 keys 32 ks + 16 + 4 g + r (tile 2 ks + 1)
 #pragma unroll

@@ -222,6 +222,7 @@ def attn(lib, q=A, k=B, v=0x2000000, o=0x3000000, Bn=2, H=3, T=100, d=128, st=No
 @pytest.mark.parametrize("kw,status", [
     (dict(dt=7), INVALID), (dict(Bn=-1), INVALID), (dict(d=0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-0.5), INVALID),
     (dict(causal=2), INVALID), (dict(q=None), INVALID), (dict(o=None), INVALID),
     (dict(o=A + 4096), INVALID),  # o overlaps q
     (dict(o=0x2000000 - 64), INVALID),  # o overlaps v
