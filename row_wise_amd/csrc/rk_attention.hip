@@ -101,7 +101,10 @@ constexpr int kAttnBN = 64;              // keys per step
 template <int D>
 struct AttnLds {
     static constexpr int kKStride = D + 8;       // K row pitch (elements): 16 B of padding
-    static constexpr int kVStride = kAttnBN + 4; // V^T row pitch (elements): 8 B of padding
+    // V^T row pitch: 68 elements (34 words), so that the 16 rows an MFMA
+    // operand load reads together fall on distinct banks (measured: a pitch
+    // of 72 triples the bank conflicts)
+    static constexpr int kVStride = kAttnBN + 4;
     uint16_t k[kAttnBN * kKStride];
     uint16_t vt[D * kVStride];
 };
@@ -128,7 +131,9 @@ void flash_attention_fwd(
     constexpr int LOADS = kAttnBN * CH / (kAttnWaves * kWave);  // K chunks per thread
     static_assert(LOADS * kAttnWaves * kWave == kAttnBN * CH, "whole K block per workgroup");
     static_assert(kAttnBN == 64 && (D == 64 || D == 128), "shapes of this kernel");
-    __shared__ AttnLds<D> lds;
+    // two buffers: block j is read from buffer j % 2 while block j + 1 is
+    // written to the other, with one barrier per block
+    __shared__ AttnLds<D> lds[2];
 
     // heaviest query blocks first (causal), and every query block of one
     // (batch, head) on the same XCD when BH is a multiple of 8
@@ -171,37 +176,55 @@ void flash_attention_fwd(
     float lsum[2] = {0.0f, 0.0f};  // this lane's part of the row sums
 
     // K/V staging: K chunk i of this thread is key (tid + 256 i) / CH,
-    // column 8 ((tid + 256 i) % CH); V: keys 4 kq .. 4 kq + 3 at column
-    // 8 cv, kq = tid / CH (LOADS keys per group of 4), so that the four keys
-    // of one column pack into one 8-byte V^T write.
+    // column 8 ((tid + 256 i) % CH).  V: keys LOADS kq .. LOADS kq + LOADS - 1
+    // at columns 8 cv .. 8 cv + 7, so that the LOADS keys of one column pack
+    // into one V^T write; kq runs fastest across the lanes, so that the lanes
+    // writing together fill one contiguous V^T row segment (no bank
+    // conflicts), while each key row is still read 64 bytes at a time.
+    constexpr int NKQ = kAttnBN / LOADS;  // key groups
     u32x4_t kreg[LOADS], vreg[LOADS];
     auto load_block = [&](int kb) {
+        const int kq = tid % NKQ;
+        const int cv = tid / NKQ;  // 0 .. CH - 1
+        if (kb + kAttnBN <= T) {  // the whole block is in range: no guards
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int idx = tid + kAttnWaves * kWave * i;
+                kreg[i] = *reinterpret_cast<const u32x4_t *>(kh + (kb + idx / CH) * sk.t +
+                                                             8 * (idx % CH));
+            }
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i)
+                vreg[i] = *reinterpret_cast<const u32x4_t *>(vh + (kb + LOADS * kq + i) * sv.t +
+                                                             8 * cv);
+            return;
+        }
+        // keys past T: read row T - 1 (in bounds) and zero the data
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int idx = tid + kAttnWaves * kWave * i;
             const int key = kb + idx / CH;
-            const int col = 8 * (idx % CH);
-            kreg[i] = key < T ? *reinterpret_cast<const u32x4_t *>(kh + key * sk.t + col)
-                              : u32x4_t{0, 0, 0, 0};
+            const u32x4_t val = *reinterpret_cast<const u32x4_t *>(
+                kh + (key < T ? key : T - 1) * sk.t + 8 * (idx % CH));
+            kreg[i] = key < T ? val : u32x4_t{0, 0, 0, 0};
         }
-        const int cv = tid % CH;
-        const int kq = tid / CH;  // 0 .. 256 / CH - 1
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int key = kb + LOADS * kq + i;
-            vreg[i] = key < T ? *reinterpret_cast<const u32x4_t *>(vh + key * sv.t + 8 * cv)
-                              : u32x4_t{0, 0, 0, 0};
+            const u32x4_t val = *reinterpret_cast<const u32x4_t *>(
+                vh + (key < T ? key : T - 1) * sv.t + 8 * cv);
+            vreg[i] = key < T ? val : u32x4_t{0, 0, 0, 0};
         }
     };
-    auto store_block = [&]() {
+    auto store_block = [&](AttnLds<D> &buf) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int idx = tid + kAttnWaves * kWave * i;
-            *reinterpret_cast<u32x4_t *>(&lds.k[(idx / CH) * AttnLds<D>::kKStride +
+            *reinterpret_cast<u32x4_t *>(&buf.k[(idx / CH) * AttnLds<D>::kKStride +
                                                 8 * (idx % CH)]) = kreg[i];
         }
-        const int cv = tid % CH;
-        const int kq = tid / CH;
+        const int kq = tid % NKQ;
+        const int cv = tid / NKQ;
         // V^T[d][keys LOADS kq .. + LOADS]: LOADS (= 2 or 4) keys per write
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -209,7 +232,7 @@ void flash_attention_fwd(
 #pragma unroll
             for (int i = 0; i < LOADS; ++i)
                 vals[i] = static_cast<uint16_t>(vreg[i][e / 2] >> (16 * (e % 2)));
-            uint16_t *dst = &lds.vt[(8 * cv + e) * AttnLds<D>::kVStride + LOADS * kq];
+            uint16_t *dst = &buf.vt[(8 * cv + e) * AttnLds<D>::kVStride + LOADS * kq];
             if constexpr (LOADS == 4) {
                 const uint32_t lo = vals[0] | (uint32_t{vals[1]} << 16);
                 const uint32_t hi = vals[2] | (uint32_t{vals[3]} << 16);
@@ -222,11 +245,12 @@ void flash_attention_fwd(
 
     const int kend = CAUSAL ? (q0 + kAttnBM < T ? q0 + kAttnBM : T) : T;
     load_block(0);
-    store_block();
+    store_block(lds[0]);
     __syncthreads();
 
-    for (int kb = 0; kb < kend; kb += kAttnBN) {
+    for (int kb = 0, it = 0; kb < kend; kb += kAttnBN, ++it) {
         const bool more = kb + kAttnBN < kend;
+        const AttnLds<D> &cur = lds[it & 1];
         if (more)
             load_block(kb + kAttnBN);
 
@@ -241,7 +265,7 @@ void flash_attention_fwd(
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
                 const vec a = *reinterpret_cast<const vec *>(
-                    &lds.k[(16 * kt + l16) * AttnLds<D>::kKStride + 32 * ds + 8 * g]);
+                    &cur.k[(16 * kt + l16) * AttnLds<D>::kKStride + 32 * ds + 8 * g]);
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
                     s[qt][kt] = Op::mfma(a, qf[qt][ds], s[qt][kt]);
@@ -324,7 +348,7 @@ void flash_attention_fwd(
             }
 #pragma unroll
             for (int dt = 0; dt < DT16; ++dt) {
-                const uint16_t *row = &lds.vt[(16 * dt + l16) * AttnLds<D>::kVStride + 32 * ks];
+                const uint16_t *row = &cur.vt[(16 * dt + l16) * AttnLds<D>::kVStride + 32 * ks];
                 const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(row + 4 * g);
                 const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(row + 16 + 4 * g);
                 const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
@@ -335,11 +359,11 @@ void flash_attention_fwd(
             }
         }
 
-        __syncthreads();  // every wave is done with this block's K and V^T
-        if (more) {
-            store_block();
-            __syncthreads();
-        }
+        // The other buffer was last read in the previous step, which every
+        // wave finished before the barrier ending that step.
+        if (more)
+            store_block(lds[(it + 1) & 1]);
+        __syncthreads();  // the next block is visible; this one is free
     }
 
     // o = acc / l; lane (g, l16) holds query qw + 16 qt + l16, d = 16 dt + 4 g + r
