@@ -301,13 +301,21 @@ void flash_attention_fwd(
                 for (int r = 0; r < 4; ++r)
                     mx = fmaxf(mx, s[qt][kt][r]);
             mx = group4_max(mx);
-            const float m_new = fmaxf(m[qt], mx);  // raw (unscaled) score units
-            // p = exp(scale (s - m)) = exp2(s c - m c), c = scale log2(e).  A
-            // row that has seen no key yet keeps m = -inf: shift by 0 so that
-            // its (all -inf) scores give p = 0 rather than NaN.
+            // m is the reference max of the row in raw score units, and
+            // p = exp(scale (s - m)) = exp2(s c - m c), c = scale log2(e).
+            // Softmax does not depend on the reference as long as l and acc
+            // share it, so m moves only when this block's max exceeds it by
+            // more than 2^8 in p (p stays <= 256, far inside the operand
+            // range); a moved m rescales l and acc by alpha.  A row that has
+            // seen no key keeps m = -inf (the comparison with NaN is false)
+            // and shifts by 0, so that its -inf scores give p = 0.
+            const bool bump = (mx - m[qt]) * scale_log2e > 8.0f;
+            const float m_new = bump ? mx : m[qt];
             const float shift = m_new == -INFINITY ? 0.0f : m_new * scale_log2e;
             const float alpha =
-                m[qt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(m[qt], scale_log2e, -shift));
+                !bump ? 1.0f
+                      : (m[qt] == -INFINITY ? 0.0f
+                                            : __builtin_amdgcn_exp2f(fmaf(m[qt], scale_log2e, -shift)));
             m[qt] = m_new;
             float ps = 0.0f;
 #pragma unroll
@@ -319,7 +327,7 @@ void flash_attention_fwd(
                     ps += p;
                 }
             lsum[qt] = fmaf(alpha, lsum[qt], ps);
-            // rescale the output only when some row's max moved (alpha < 1)
+            // rescale the output only when some row's reference moved
             if (!__all(alpha == 1.0f)) {
 #pragma unroll
                 for (int dt = 0; dt < DT16; ++dt)
