@@ -659,6 +659,9 @@ RK_EXPORT rk_status rk_flash_attention(const void *q, const void *k, const void 
     for (int i = 0; i < 4; ++i) {
         if (!aligned16(base[i]) || st[i][0] % 8 || st[i][1] % 8 || st[i][2] % 8)
             return RK_ERR_UNSUPPORTED;
+        // the kernel addresses a 64-key block with 32-bit byte offsets
+        if (st[i][2] > ((int64_t{1} << 30) - d) / 64)
+            return RK_ERR_UNSUPPORTED;
     }
     const int64_t bm = attention_block_rows();
     const int64_t nqb = (T + bm - 1) / bm;

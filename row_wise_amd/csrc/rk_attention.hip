@@ -10,13 +10,13 @@
 // end o = acc / l.  Scores and probabilities live only in registers.
 //
 // CDNA4 mapping (16x16x32 MFMA, bf16 or fp16 operands, fp32 accumulation):
-//   a workgroup of 4 waves owns BM = 128 query rows of one (batch, head);
-//   each wave owns 32 of them as two 16-row tiles, with its Q fragments in
+//   a workgroup of W waves owns BM = 16 QT W query rows of one (batch, head);
+//   each wave owns 16 QT of them as QT 16-row tiles, with its Q fragments in
 //   registers for the whole kernel.  Per step of BN = 64 keys the workgroup
 //   stages K (row-major) and V (transposed) in LDS; every wave then forms
 //   S^T = K Q^T (keys x queries, so that each lane holds one query's scores
 //   for 16 of the keys), the row max across the four 16-lane groups
-//   (permlane16/32 swaps), p = exp2(S log2e scale - m), and O^T += V^T P^T,
+//   (permlane16/32 swaps), p = exp2((S - m) scale log2e), and O^T += V^T P^T,
 //   where P^T is the S^T fragments rounded to the operand type in place (the
 //   key order inside each 32-key step is permuted identically in V^T).
 //   The next block's K/V are loaded into registers while this one is used.
@@ -94,9 +94,7 @@ __device__ __forceinline__ float group4_sum(float v)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-constexpr int kAttnWaves = 4;
-constexpr int kAttnBM = 32 * kAttnWaves;  // query rows per workgroup
-constexpr int kAttnBN = 64;              // keys per step
+constexpr int kAttnBN = 64;  // keys per step
 
 template <int D>
 struct AttnLds {
@@ -114,8 +112,9 @@ struct AttnStrides {
     int64_t b, h, t;
 };
 
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kAttnWaves *kWave) __attribute__((amdgpu_waves_per_eu(2)))
+// W waves per workgroup, each owning QT tiles of 16 query rows.
+template <int DT, int D, bool CAUSAL, int W, int QT>
+__global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 4 : (QT == 2 ? 2 : 1))))
 void flash_attention_fwd(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, int H, int T, int nqb, int BH,
@@ -128,8 +127,10 @@ void flash_attention_fwd(
     constexpr int NKT = kAttnBN / 16;
     constexpr int NKS = kAttnBN / 32;
     constexpr int CH = D / 8;    // 16-byte chunks per K/V row
-    constexpr int LOADS = kAttnBN * CH / (kAttnWaves * kWave);  // K chunks per thread
-    static_assert(LOADS * kAttnWaves * kWave == kAttnBN * CH, "whole K block per workgroup");
+    constexpr int NT = W * kWave;
+    constexpr int BM = 16 * QT * W;  // query rows per workgroup
+    constexpr int LOADS = kAttnBN * CH / NT;  // K chunks per thread
+    static_assert(LOADS >= 1 && LOADS * NT == kAttnBN * CH, "whole K block per workgroup");
     static_assert(kAttnBN == 64 && (D == 64 || D == 128), "shapes of this kernel");
     // two buffers: block j is read from buffer j % 2 while block j + 1 is
     // written to the other, with one barrier per block
@@ -151,14 +152,14 @@ void flash_attention_fwd(
     const int lane = tid % kWave;
     const int l16 = lane % 16;
     const int g = lane / 16;
-    const int q0 = qb * kAttnBM;
-    const int qw = q0 + 32 * wave;  // first query row of this wave
+    const int q0 = qb * BM;
+    const int qw = q0 + 16 * QT * wave;  // first query row of this wave
 
     // Q fragments (B operand of S^T = K Q^T): query qw + 16 qt + l16,
     // d = 32 ds + 8 g .. + 8.  Rows past T read row T - 1 (never stored).
-    vec qf[2][DS];
+    vec qf[QT][DS];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
         int row = qw + 16 * qt + l16;
         row = row < T ? row : T - 1;
 #pragma unroll
@@ -166,14 +167,18 @@ void flash_attention_fwd(
             qf[qt][ds] = *reinterpret_cast<const vec *>(qh + row * sq.t + 32 * ds + 8 * g);
     }
 
-    f32x4v_t acc[2][DT16];
+    f32x4v_t acc[QT][DT16];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt)
             acc[qt][dt] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.0f, 0.0f};  // this lane's part of the row sums
+    float m[QT], lsum[QT];  // reference max; this lane's part of the row sum
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        m[qt] = -INFINITY;
+        lsum[qt] = 0.0f;
+    }
 
     // K/V staging: K chunk i of this thread is key (tid + 256 i) / CH,
     // column 8 ((tid + 256 i) % CH).  V: keys LOADS kq .. LOADS kq + LOADS - 1
@@ -183,26 +188,37 @@ void flash_attention_fwd(
     // conflicts), while each key row is still read 64 bytes at a time.
     constexpr int NKQ = kAttnBN / LOADS;  // key groups
     u32x4_t kreg[LOADS], vreg[LOADS];
+    // byte offsets of this thread's loads from the block's first key row
+    // (32-bit: the host keeps 64 seq strides + d below 2^30 elements)
+    uint32_t koff[LOADS], voff[LOADS];
+    {
+        const int kq = tid % NKQ;
+        const int cv = tid / NKQ;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int idx = tid + NT * i;
+            koff[i] = static_cast<uint32_t>(((idx / CH) * sk.t + 8 * (idx % CH)) * 2);
+            voff[i] = static_cast<uint32_t>(((LOADS * kq + i) * sv.t + 8 * cv) * 2);
+        }
+    }
     auto load_block = [&](int kb) {
         const int kq = tid % NKQ;
         const int cv = tid / NKQ;  // 0 .. CH - 1
         if (kb + kAttnBN <= T) {  // the whole block is in range: no guards
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int idx = tid + kAttnWaves * kWave * i;
-                kreg[i] = *reinterpret_cast<const u32x4_t *>(kh + (kb + idx / CH) * sk.t +
-                                                             8 * (idx % CH));
-            }
+            const char *kbase = reinterpret_cast<const char *>(kh + kb * sk.t);
+            const char *vbase = reinterpret_cast<const char *>(vh + kb * sv.t);
 #pragma unroll
             for (int i = 0; i < LOADS; ++i)
-                vreg[i] = *reinterpret_cast<const u32x4_t *>(vh + (kb + LOADS * kq + i) * sv.t +
-                                                             8 * cv);
+                kreg[i] = *reinterpret_cast<const u32x4_t *>(kbase + koff[i]);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i)
+                vreg[i] = *reinterpret_cast<const u32x4_t *>(vbase + voff[i]);
             return;
         }
         // keys past T: read row T - 1 (in bounds) and zero the data
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int idx = tid + kAttnWaves * kWave * i;
+            const int idx = tid + NT * i;
             const int key = kb + idx / CH;
             const u32x4_t val = *reinterpret_cast<const u32x4_t *>(
                 kh + (key < T ? key : T - 1) * sk.t + 8 * (idx % CH));
@@ -219,7 +235,7 @@ void flash_attention_fwd(
     auto store_block = [&](AttnLds<D> &buf) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int idx = tid + kAttnWaves * kWave * i;
+            const int idx = tid + NT * i;
             *reinterpret_cast<u32x4_t *>(&buf.k[(idx / CH) * AttnLds<D>::kKStride +
                                                 8 * (idx % CH)]) = kreg[i];
         }
@@ -237,13 +253,15 @@ void flash_attention_fwd(
                 const uint32_t lo = vals[0] | (uint32_t{vals[1]} << 16);
                 const uint32_t hi = vals[2] | (uint32_t{vals[3]} << 16);
                 *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{lo, hi};
-            } else {
+            } else if constexpr (LOADS == 2) {
                 *reinterpret_cast<uint32_t *>(dst) = vals[0] | (uint32_t{vals[1]} << 16);
+            } else {
+                *dst = vals[0];
             }
         }
     };
 
-    const int kend = CAUSAL ? (q0 + kAttnBM < T ? q0 + kAttnBM : T) : T;
+    const int kend = CAUSAL ? (q0 + BM < T ? q0 + BM : T) : T;
     load_block(0);
     store_block(lds[0]);
     __syncthreads();
@@ -256,18 +274,18 @@ void flash_attention_fwd(
 
         // S^T tiles: s[qt][kt] holds, in lane (g, l16), query qw + 16 qt + l16
         // and keys kb + 16 kt + 4 g + r.
-        f32x4v_t s[2][NKT];
+        f32x4v_t s[QT][NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+            for (int qt = 0; qt < QT; ++qt)
                 s[qt][kt] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
                 const vec a = *reinterpret_cast<const vec *>(
                     &cur.k[(16 * kt + l16) * AttnLds<D>::kKStride + 32 * ds + 8 * g]);
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
+                for (int qt = 0; qt < QT; ++qt)
                     s[qt][kt] = Op::mfma(a, qf[qt][ds], s[qt][kt]);
             }
         }
@@ -277,7 +295,7 @@ void flash_attention_fwd(
         const bool edge = kb + kAttnBN > T || (CAUSAL && kb + kAttnBN - 1 > qw);
         if (edge) {
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
+            for (int qt = 0; qt < QT; ++qt) {
                 const int qi = qw + 16 * qt + l16;
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt)
@@ -291,9 +309,9 @@ void flash_attention_fwd(
         }
 
         // online softmax state per query row
-        uint32_t pk[2][NKS][4];  // P^T operand words
+        uint32_t pk[QT][NKS][4];  // P^T operand words
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < QT; ++qt) {
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
@@ -348,9 +366,9 @@ void flash_attention_fwd(
         // keys (two 8-byte reads), B = P^T of the lane's query
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            vec bq[2];
+            vec bq[QT];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
+            for (int qt = 0; qt < QT; ++qt) {
                 u32x4_t w = {pk[qt][ks][0], pk[qt][ks][1], pk[qt][ks][2], pk[qt][ks][3]};
                 bq[qt] = __builtin_bit_cast(vec, w);
             }
@@ -362,7 +380,7 @@ void flash_attention_fwd(
                 const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
                 const vec a = __builtin_bit_cast(vec, w);
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
+                for (int qt = 0; qt < QT; ++qt)
                     acc[qt][dt] = Op::mfma(a, bq[qt], acc[qt][dt]);
             }
         }
@@ -376,7 +394,7 @@ void flash_attention_fwd(
 
     // o = acc / l; lane (g, l16) holds query qw + 16 qt + l16, d = 16 dt + 4 g + r
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
         const int qi = qw + 16 * qt + l16;
         const float inv = 1.0f / group4_sum(lsum[qt]);
         if (qi < T) {
@@ -395,14 +413,22 @@ namespace {
 
 AttnStrides strides_of(const int64_t *s) { return AttnStrides{s[0], s[1], s[2]}; }
 
+// Launch shape: kLaunchW waves of kLaunchQT query tiles each.  Measured on
+// 4 x 32 x 4096 x 128 bf16: 8 x 2 (256 rows, two waves per SIMD) 900 TFLOP/s;
+// 4 x 2: 845; 8 x 1 (four waves per SIMD, twice the LDS reads per MFMA):
+// 700; 4 x 4 (one wave per SIMD, spills): 490.
+constexpr int kLaunchW = 8;
+constexpr int kLaunchQT = 2;
+constexpr int kLaunchBM = 16 * kLaunchQT * kLaunchW;
+
 template <int DT, int D, bool CAUSAL>
 hipError_t attn_launch(const AttentionProblem &p)
 {
-    const int nqb = static_cast<int>((p.T + kAttnBM - 1) / kAttnBM);
+    const int nqb = static_cast<int>((p.T + kLaunchBM - 1) / kLaunchBM);
     const int BH = static_cast<int>(p.B * p.H);
     const float scale_log2e = p.scale * 1.4426950408889634f;
-    return launch(flash_attention_fwd<DT, D, CAUSAL>,
-                  dim3(static_cast<unsigned>(int64_t{nqb} * BH)), dim3(kAttnWaves * kWave),
+    return launch(flash_attention_fwd<DT, D, CAUSAL, kLaunchW, kLaunchQT>,
+                  dim3(static_cast<unsigned>(int64_t{nqb} * BH)), dim3(kLaunchW * kWave),
                   p.stream, static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                   static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o),
                   static_cast<int>(p.H), static_cast<int>(p.T), nqb, BH, strides_of(p.sq),
@@ -423,7 +449,7 @@ hipError_t attn_dim(const AttentionProblem &p)
 
 }  // namespace
 
-int attention_block_rows() { return kAttnBM; }
+int attention_block_rows() { return kLaunchBM; }
 
 hipError_t flash_attention_run(const AttentionProblem &p)
 {
