@@ -13,8 +13,10 @@ bracketed by device synchronizations.  `roofline.achieved` divides the same
 bytes by the kernel's average duration from HIP events on its stream.
 `detail` holds the same measurement for every other workload (softmax fp32
 8192x1000, online softmax fp32 64x262144 streaming and split-row, bf16
-16384x4096 LayerNorm+GeLU and softmax, RMSNorm and fused residual RMSNorm on
-the fp32 4096x768 and bf16 16384x4096 inputs) and the 16-byte copy ceiling.
+16384x4096 LayerNorm+GeLU and softmax, long-row LayerNorm streaming and split,
+row sum and max, elementwise GeLU, RMSNorm and fused residual RMSNorm, and the
+flash-attention forward in TFLOP/s against the 2.5 PFLOP/s matrix-core peak)
+and the 16-byte copy ceiling.
 `cpu_baseline` is the CPU oracle timed on this host on repeated full batches.
 """
 from __future__ import annotations
