@@ -274,20 +274,31 @@ void flash_attention_fwd(
 
         // S^T tiles: s[qt][kt] holds, in lane (g, l16), query qw + 16 qt + l16
         // and keys kb + 16 kt + 4 g + r.
+        // The K fragments of d-step ds + 1 are read while the MFMAs of d-step
+        // ds run; consecutive MFMAs on one accumulator are NKT * QT apart.
         f32x4v_t s[QT][NKT];
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
                 s[qt][kt] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
+        vec ka[2][NKT];
+        auto read_k = [&](int ds, vec(&dst)[NKT]) {
 #pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-                const vec a = *reinterpret_cast<const vec *>(
+            for (int kt = 0; kt < NKT; ++kt)
+                dst[kt] = *reinterpret_cast<const vec *>(
                     &cur.k[(16 * kt + l16) * AttnLds<D>::kKStride + 32 * ds + 8 * g]);
+        };
+        read_k(0, ka[0]);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            if (ds + 1 < DS)
+                read_k(ds + 1, ka[(ds + 1) & 1]);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
-                    s[qt][kt] = Op::mfma(a, qf[qt][ds], s[qt][kt]);
-            }
+                    s[qt][kt] = Op::mfma(ka[ds & 1][kt], qf[qt][ds], s[qt][kt]);
         }
 
         // mask keys past T and (causal) keys after the query, on the raw
@@ -372,16 +383,24 @@ void flash_attention_fwd(
                 u32x4_t w = {pk[qt][ks][0], pk[qt][ks][1], pk[qt][ks][2], pk[qt][ks][3]};
                 bq[qt] = __builtin_bit_cast(vec, w);
             }
-#pragma unroll
-            for (int dt = 0; dt < DT16; ++dt) {
+            // V^T fragments are read two d-tiles ahead of their MFMAs
+            auto read_v = [&](int dt) {
                 const uint16_t *row = &cur.vt[(16 * dt + l16) * AttnLds<D>::kVStride + 32 * ks];
                 const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(row + 4 * g);
                 const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(row + 16 + 4 * g);
                 const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-                const vec a = __builtin_bit_cast(vec, w);
+                return __builtin_bit_cast(vec, w);
+            };
+            vec va[3];
+            va[0] = read_v(0);
+            va[1] = read_v(1);
+#pragma unroll
+            for (int dt = 0; dt < DT16; ++dt) {
+                if (dt + 2 < DT16)
+                    va[(dt + 2) % 3] = read_v(dt + 2);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
-                    acc[qt][dt] = Op::mfma(a, bq[qt], acc[qt][dt]);
+                    acc[qt][dt] = Op::mfma(va[dt % 3], bq[qt], acc[qt][dt]);
             }
         }
 
