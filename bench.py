@@ -273,8 +273,9 @@ def all_cases():
 # --------------------------------------------------------------- timing
 
 
-def event_time(torch, case, K, W, reps=3):
-    """Median over `reps` of (elapsed of K back-to-back launches) / K, in s."""
+def event_time(torch, case, K, W, reps=3, spread=None):
+    """Median over `reps` of (elapsed of K back-to-back launches) / K, in s
+    (`spread`, if a dict, receives the minimum and maximum)."""
     for i in range(W):
         case.launch(i)
     torch.cuda.synchronize()
@@ -288,6 +289,8 @@ def event_time(torch, case, K, W, reps=3):
         e.record()
         e.synchronize()
         out.append(s.elapsed_time(e) * 1e-3 / K)
+    if spread is not None:
+        spread["min"], spread["max"] = min(out), max(out)
     return statistics.median(out)
 
 
@@ -353,15 +356,31 @@ def cpu_baseline(seconds):
     M, N = x.shape
     nbytes = 2 * M * N * 4 + 2 * N * 4
     orc = oracle.default()
-    orc.layernorm_gelu(x[:16], w, b, float(np.float32(EPS)))  # load / warm
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.layernorm_gelu(x, w, b, float(np.float32(EPS)))
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    eps = float(np.float32(EPS))
+    orc.layernorm_gelu(x[:16], w, b, eps)  # load / warm
+
+    def timed(fn, budget):
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return passes, el
+
+    # one thread on whole batches
+    passes, el = timed(lambda: orc.layernorm_gelu(x, w, b, eps), seconds)
+    # the same oracle on every core of this process's affinity mask, one row
+    # block per thread (the C call releases the interpreter lock)
+    from concurrent.futures import ThreadPoolExecutor
+
+    # (at most 16 threads: the CPU share that one GPU's host process gets)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    blocks = [x[i * M // cores:(i + 1) * M // cores] for i in range(cores)]
+    with ThreadPoolExecutor(cores) as pool:
+        def batch():
+            list(pool.map(lambda blk: orc.layernorm_gelu(blk, w, b, eps), blocks))
+        p_n, el_n = timed(batch, seconds / 2)
     return {
         "value": round(passes * nbytes / el / 1e9, 4),
         "unit": "GB/s",
@@ -370,6 +389,10 @@ def cpu_baseline(seconds):
         "kind": "oracle",
         "sample": f"full {M}x{N} fp32 batch, {passes} passes in {el:.1f} s, single thread, "
                   f"double precision",
+        "all_cores": {"value": round(p_n * nbytes / el_n / 1e9, 4), "unit": "GB/s",
+                      "rows_per_s": round(p_n * M / el_n, 1), "cores": cores,
+                      "sample": f"{p_n} full batches in {el_n:.1f} s, {cores} threads over row "
+                                f"blocks"},
         "cpu": cpu_model(),
     }
 
@@ -426,13 +449,14 @@ def main():
     for c in cases:
         log(f"case {c.name}: setup")
         c.setup(torch, rk, rowgen)
+        spread = {}
         if c.name == HEADLINE:
             wall, evt = wall_time(torch, c, K, W)
             t_evt = event_time(torch, c, K, W)
             head = (c, wall, evt, t_evt)
             t = t_evt
         else:
-            t = event_time(torch, c, K, W)
+            t = event_time(torch, c, K, W, spread=spread)
         rec = {"case": c.name, "us_per_call": round(t * 1e6, 3),
                "GB_per_s": round(c.bytes / t / 1e9, 1),
                "pct_hbm_peak": round(100 * c.bytes / t / 1e9 / HBM_PEAK_GBS, 1),
@@ -444,6 +468,11 @@ def main():
             rec["rows_per_s"] = round(c.M / t, 1)
         if getattr(c, "splits", None):
             rec["splits"] = c.splits
+        if c.name != HEADLINE and spread:
+            rec["us_min_max"] = [round(spread["min"] * 1e6, 3), round(spread["max"] * 1e6, 3)]
+        if getattr(c, "op", None) in ("online", "layernorm_gelu_ex"):
+            # against the one-read-one-write minimum (the row cannot stay on chip)
+            rec["GB_per_s_1R1W"] = round(2 * c.M * c.N * (4 if c.dtype_code == 0 else 2) / t / 1e9, 1)
         detail.append(rec)
         if "TFLOP_per_s" in rec:
             log(f"case {c.name}: {rec['us_per_call']} us  {rec['TFLOP_per_s']} TFLOP/s "
