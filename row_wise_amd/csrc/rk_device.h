@@ -477,6 +477,17 @@ struct RowLoad {
         }
     }
 
+    // Vector k alone (finish() unpacks all V; this keeps the rest packed).
+    __device__ __forceinline__ void finish_one(int k, float (&v)[E], RowSplit<E> rs) const
+    {
+        unpack<T, E>(q[k], v);
+        if (has_tail(rs) && vi0 + k * STRIDE == rs.nfull) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[e] = tl[e];
+        }
+    }
+
     __device__ __forceinline__ void finish(float (&v)[V][E], RowSplit<E> rs) const
     {
 #pragma unroll

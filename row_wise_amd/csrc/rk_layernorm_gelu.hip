@@ -61,7 +61,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     RowLoad<T, E, V, L, kCached> wl, bl;
     wl.issue(w, li, nv, rs, 0.0f, slots_full);
     bl.issue(b, li, nv, rs, 0.0f, slots_full);
-    float wv[V][E], bv[V][E];
+    float wv[R > 1 ? V : 1][E], bv[R > 1 ? V : 1][E];
 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -127,15 +127,30 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         // hardware reciprocal square root (1 ulp), once per row
         const float rstd = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
 
-        if (r == 0) {
-            wl.finish(wv, rs);
-            bl.finish(bv, rs);
+        if constexpr (R > 1) {
+            // weight and bias serve R rows: unpack them once
+            if (r == 0) {
+                wl.finish(wv, rs);
+                bl.finish(bv, rs);
+            }
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v[k][e] = gelu<GK>(fmaf(v[k][e] * rstd, wv[k][e], bv[k][e]));
+        } else {
+            // one row: unpack weight and bias a vector at a time, so that they
+            // stay packed (half the registers for bf16) until used
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                float wk[E], bk[E];
+                wl.finish_one(k, wk, rs);
+                bl.finish_one(k, bk, rs);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v[k][e] = gelu<GK>(fmaf(v[k][e] * rstd, wk[e], bk[e]));
+            }
         }
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                v[k][e] = gelu<GK>(fmaf(v[k][e] * rstd, wv[k][e], bv[k][e]));
         if (EXACT) {
             if (row_ok)
                 store_row<T, E, V, L>(yr, li, vend, rs, v, true);
