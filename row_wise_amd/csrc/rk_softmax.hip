@@ -160,6 +160,9 @@ static const TileVariant kSoftmaxF32[] = {
     tile<float, 4, 1, 4>(),
     tile<float, 2, 8, 4>(),
     exact<float, 1, 4, 4>(),
+    exact<float, 8, 8, 8>(),   // large-row alternatives: fewer waves per row
+    tile<float, 8, 8, 8>(),
+    exact<float, 4, 8, 4>(),
 };
 
 static const TileVariant kSoftmaxBF16[] = {
@@ -183,6 +186,9 @@ static const TileVariant kSoftmaxBF16[] = {
     exact<bf16_t, 1, 8, 4>(),
     exact<bf16_t, 2, 4, 4>(),
     exact<bf16_t, 8, 1, 8>(),
+    exact<bf16_t, 8, 8, 8>(),   // large-row alternatives: fewer waves per row
+    tile<bf16_t, 8, 8, 8>(),
+    exact<bf16_t, 8, 4, 8>(),
 };
 
 const TileVariant *softmax_variants(rk_dtype dtype, int *count)
