@@ -1,0 +1,102 @@
+"""The C ABI under HIP graph capture and from several host threads and
+streams: results must equal the eager single-stream results bit for bit
+(every kernel here is deterministic)."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import row_wise_amd as rk
+import rowgen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+EPS = float(np.float32(1e-5))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rk.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def test_graph_capture_and_replay():
+    d = rowgen.make("ln_gelu_f32_4096x768")
+    x = d["x"].to(DEV)
+    w, b = d["w"].to(DEV), d["b"].to(DEV)
+    xs = rowgen.randn(64, 20000, seed=301).to(DEV)
+    res = rowgen.residual("ln_gelu_f32_4096x768").to(DEV)
+    q, k, v = (t.to(DEV) for t in rowgen.attention_qkv(1, 4, 300, 128, torch.bfloat16, seed=302))
+    ws = torch.empty(rk.rk_online_softmax_workspace_bytes(64, 20000, 4), dtype=torch.uint8,
+                     device=DEV)
+    outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn")}
+
+    def step():
+        outs["ln"] = rk.rk_layernorm_gelu(x, w, b, EPS, out=outs["ln"])
+        outs["sm"] = rk.rk_online_softmax(xs, num_splits=4, out=outs["sm"], workspace=ws)
+        y, r = rk.rk_residual_rmsnorm(x, res, w, EPS, out=outs["rms"], residual_out=outs["ro"])
+        outs["rms"], outs["ro"] = y, r
+        outs["attn"] = rk.rk_flash_attention(q, k, v, causal=True, out=outs["attn"])
+
+    step()  # allocates the outputs, eagerly
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        step()  # warm the side stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        # new inputs each time, written by eager work between replays
+        x.copy_(rowgen.randn(4096, 768, seed=310 + rep).to(DEV))
+        xs.copy_(rowgen.randn(64, 20000, seed=320 + rep).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {n: t.clone() for n, t in outs.items()}
+        step()  # eager, same buffers
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(bits(got[n]), bits(outs[n])), (rep, n)
+
+
+def test_threads_and_streams():
+    inputs = [rowgen.randn(2048, 1000 + 37 * i, seed=400 + i).to(DEV) for i in range(4)]
+    ws = [torch.ones(x.shape[1], device=DEV) for x in inputs]
+    bs = [torch.zeros(x.shape[1], device=DEV) for x in inputs]
+    ref = [(rk.rk_softmax(x), rk.rk_layernorm_gelu(x, w, b, EPS))
+           for x, w, b in zip(inputs, ws, bs)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    a = rk.rk_softmax(inputs[i])
+                    c = rk.rk_layernorm_gelu(inputs[i], ws[i], bs[i], EPS)
+                s.synchronize()
+                if not (torch.equal(bits(a), bits(ref[i][0])) and
+                        torch.equal(bits(c), bits(ref[i][1]))):
+                    errors.append(i)
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
