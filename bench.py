@@ -345,6 +345,19 @@ def load_traffic(case_name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def profiled_duration(case_name):
+    """(avg, median) per-dispatch duration in us of the case's kernel in the
+    committed rocprofv3 kernel trace, or None."""
+    path = os.path.join(ROOT, "profiles", "kernel_trace_all_cases.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 12 and f[0] == case_name:
+            return float(f[8]), float(f[9])
+    return None
+
+
 def cpu_baseline(seconds):
     import numpy as np
 
@@ -520,6 +533,13 @@ def main():
         },
         "detail": detail,
     }
+    prof = profiled_duration(c.name)
+    if prof is not None:
+        # the committed rocprofv3 trace of the same kernel: per-dispatch
+        # duration under the profiler (which serializes dispatches), and the
+        # rate it implies
+        out["roofline"]["profile_us_avg_median"] = list(prof)
+        out["roofline"]["achieved_at_profile_median"] = round(c.bytes / (prof[1] * 1e-6) / 1e9, 2)
     if not args.no_cpu:
         log("cpu baseline: oracle on the host")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
