@@ -120,7 +120,7 @@ int64_t tile_blocks(const TileVariant &v, int64_t M)
     return (M + rows_per_block - 1) / rows_per_block;
 }
 
-constexpr int kStreamThreads = 1024;  // online_stream workgroup size
+constexpr int kStreamThreads = 1024;  // largest streaming workgroup (16 waves)
 constexpr int kSplitThreads = 256;    // online_partials / online_finish
 constexpr int kLoopThreads = 256;     // rmsnorm_loop
 constexpr int32_t kMaxSplits = 65536;

@@ -108,6 +108,19 @@ hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
 inline int elem_size(rk_dtype dt) { return dt == RK_F32 ? 4 : 2; }
 inline int vec_elems(rk_dtype dt) { return 16 / elem_size(dt); }
 
+// Waves per workgroup of a one-workgroup-per-row streaming kernel for a row of
+// nvec vectors processed U per thread per step: the largest of 16, 4 and 1
+// that still gives every thread at least two steps, so that short rows do
+// not leave most of a 1024-thread workgroup idle.
+inline int stream_waves(int64_t nvec, int U)
+{
+    if (nvec >= int64_t{16} * 64 * U * 2)
+        return 16;
+    if (nvec >= int64_t{4} * 64 * U * 2)
+        return 4;
+    return 1;
+}
+
 // Chunk length (elements) of the split-row variant: ceil(N / S) rounded up to
 // whole 16-byte vectors when the vector path is used.
 inline int64_t split_chunk(int64_t N, int64_t S, int vec)

@@ -18,9 +18,11 @@
 // output centres the same way, z = ((x - K) - mean_K) rstd w + b, so the
 // row mean itself is never rounded.
 //
-// layernorm_stream    one workgroup per row.  Pass 1 gathers the moments
-//                     (cached loads, so that pass 2 finds the row in L2 or
-//                     the memory-side cache); pass 2 writes GeLU(z).
+// layernorm_stream    1, 4 or 16 waves per row by the row's length (four
+//                     one-wave rows share a workgroup, otherwise one row
+//                     each).  Pass 1 gathers the moments (cached loads,
+//                     so that pass 2 finds the row in L2 or the
+//                     memory-side cache); pass 2 writes GeLU(z).
 //                     2 reads + 1 write per element.
 // layernorm_partials  split-row, first kernel: one workgroup per
 //                     (row, chunk) writes the chunk's (mean, M2).
@@ -92,7 +94,7 @@ __device__ __forceinline__ Moments scan_moments(const T *__restrict__ xr, RowSpl
                                                 int vbeg, int vend, float K)
 {
     constexpr int NT = W * kWave;
-    const int tid = static_cast<int>(threadIdx.x);
+    const int tid = static_cast<int>(threadIdx.x % NT);
     const int lim = vend < rs.nfull ? vend : rs.nfull;
     Moments st{0.0f, 0.0f, 0.0f};
     // padding loads as K (an element of the row, exact in T): 0 once shifted
@@ -146,7 +148,7 @@ __device__ __forceinline__ void ln_write_range(const T *__restrict__ xr,
                                                int vend, float K, float mean_k, float rstd)
 {
     constexpr int NT = W * kWave;
-    const int tid = static_cast<int>(threadIdx.x);
+    const int tid = static_cast<int>(threadIdx.x % NT);
     const int lim = vend < rs.nfull ? vend : rs.nfull;
     RowLoad<T, E, U, NT> cur;
     cur.issue(xr, vbeg + tid, vend, rs, 0.0f, vbeg + NT * U <= lim);
@@ -173,13 +175,18 @@ __device__ __forceinline__ void ln_write_range(const T *__restrict__ xr,
     }
 }
 
-template <typename T, int E, int W, int U, int GK>
-__global__ __launch_bounds__(W *kWave) void layernorm_stream(
+// RB rows per workgroup, W waves each; several rows only for W == 1, where
+// no barrier is taken and a wave past the last row may leave at once.
+template <typename T, int E, int W, int U, int GK, int RB>
+__global__ __launch_bounds__(W *kWave *RB) void layernorm_stream(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
-    T *__restrict__ y, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
+    T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
 {
+    static_assert(RB == 1 || W == 1, "several rows per workgroup only with one wave each");
     __shared__ float sn[W], sm[W], sq[W];
-    const int64_t row = blockIdx.x;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RB + threadIdx.x / (W * kWave);
+    if (RB > 1 && row >= M)
+        return;
     const T *xr = x + row * ldx;
     const RowSplit<E> rs(N);
     const int nv = rs.count();
@@ -253,7 +260,6 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
 
 namespace {
 
-constexpr int kStreamW = 16;  // 1024 threads per row
 constexpr int kSplitW = 4;    // 256 threads per chunk
 
 // Vectors per thread per step: 64 bytes of row per thread (four fp32 or two
@@ -261,16 +267,32 @@ constexpr int kSplitW = 4;    // 256 threads per chunk
 // 128 VGPRs of a 1024-thread workgroup.
 constexpr int step_vectors(int E) { return E == 8 ? 2 : 4; }
 
+template <typename T, int E, int W>
+hipError_t stream_launch(const RowProblem &p)
+{
+    constexpr int U = step_vectors(E);
+    // one-wave rows go four to a workgroup
+    constexpr int RB = W == 1 ? 4 : 1;
+    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_stream<T, E, W, U, 1, RB>
+                                        : layernorm_stream<T, E, W, U, 0, RB>;
+    return launch(kernel, dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB),
+                  p.stream, static_cast<const T *>(p.x), static_cast<const T *>(p.w),
+                  static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,
+                  static_cast<float>(1.0 / p.N), p.eps);
+}
+
+// One workgroup per row, 1 to 16 waves by the row's length.
 template <typename T, int E>
 hipError_t stream_run(const RowProblem &p)
 {
-    constexpr int U = step_vectors(E);
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_stream<T, E, kStreamW, U, 1>
-                                        : layernorm_stream<T, E, kStreamW, U, 0>;
-    return launch(kernel, dim3(static_cast<unsigned>(p.M)), dim3(kStreamW * kWave), p.stream,
-                  static_cast<const T *>(p.x), static_cast<const T *>(p.w),
-                  static_cast<const T *>(p.b), static_cast<T *>(p.y), p.N, p.ldx, p.ldy,
-                  static_cast<float>(1.0 / p.N), p.eps);
+    switch (stream_waves((p.N + E - 1) / E, step_vectors(E))) {
+    case 16:
+        return stream_launch<T, E, 16>(p);
+    case 4:
+        return stream_launch<T, E, 4>(p);
+    default:
+        return stream_launch<T, E, 1>(p);
+    }
 }
 
 template <typename T, int E>

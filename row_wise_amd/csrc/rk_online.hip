@@ -6,9 +6,10 @@
 // d' = d exp(m - m') + sum exp(block - m').  Two partial states of disjoint
 // parts merge with the same rescaling (rk::merge).
 //
-// online_stream    one workgroup per row.  Pass 1: every lane folds the
-//                  blocks it loads into its own state; lanes merge through
-//                  DPP, waves through LDS.  Pass 2 re-reads the row and
+// online_stream    1, 4 or 16 waves per row by the row's length (four
+//                  one-wave rows share a workgroup, otherwise one row each).  Pass 1: every lane folds the blocks it loads
+//                  into its own state; lanes merge through DPP, waves
+//                  through LDS.  Pass 2 re-reads the row and
 //                  writes exp(x - m) / d.  2 reads + 1 write per element.
 // online_partials  split-row, first kernel: one workgroup per (row, chunk)
 //                  writes the chunk's (m_s, d_s) to the workspace.
@@ -95,7 +96,7 @@ __device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xr, Row
                                                    int vbeg, int vend)
 {
     constexpr int NT = W * kWave;
-    const int tid = static_cast<int>(threadIdx.x);
+    const int tid = static_cast<int>(threadIdx.x % NT);
     SoftmaxState st{-INFINITY, 0.0f};
     // software pipeline: the next step's loads are in flight while this
     // step's values are folded
@@ -122,7 +123,7 @@ __device__ __forceinline__ void write_range(const T *__restrict__ xr, T *__restr
                                             RowSplit<E> rs, int vbeg, int vend, SoftmaxState st)
 {
     constexpr int NT = W * kWave;
-    const int tid = static_cast<int>(threadIdx.x);
+    const int tid = static_cast<int>(threadIdx.x % NT);
     const float inv = 1.0f / st.d;
     const float mL = st.m * 1.4426950408889634f;
     const int lim = vend < rs.nfull ? vend : rs.nfull;
@@ -145,13 +146,18 @@ __device__ __forceinline__ void write_range(const T *__restrict__ xr, T *__restr
     }
 }
 
-template <typename T, int E, int W, int U>
-__global__ __launch_bounds__(W *kWave) void online_stream(const T *__restrict__ x,
-                                                           T *__restrict__ y, int N, int64_t ldx,
-                                                           int64_t ldy)
+// RB rows per workgroup, W waves each; several rows only for W == 1, where
+// no barrier is taken and a wave past the last row may leave at once.
+template <typename T, int E, int W, int U, int RB>
+__global__ __launch_bounds__(W *kWave *RB) void online_stream(const T *__restrict__ x,
+                                                               T *__restrict__ y, int64_t M,
+                                                               int N, int64_t ldx, int64_t ldy)
 {
+    static_assert(RB == 1 || W == 1, "several rows per workgroup only with one wave each");
     __shared__ float sm[W], sd[W];
-    const int64_t row = blockIdx.x;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RB + threadIdx.x / (W * kWave);
+    if (RB > 1 && row >= M)
+        return;
     const T *xr = x + row * ldx;
     T *yr = y + row * ldy;
     const RowSplit<E> rs(N);
@@ -219,17 +225,32 @@ __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ 
 
 namespace {
 
-constexpr int kStreamW = 16;  // 1024 threads per row
 constexpr int kStreamU = 4;
 constexpr int kSplitW = 4;    // 256 threads per chunk
 constexpr int kSplitU = 4;
 
+template <typename T, int E, int W>
+hipError_t stream_launch(const RowProblem &p)
+{
+    // one-wave rows go four to a workgroup
+    constexpr int RB = W == 1 ? 4 : 1;
+    return launch(online_stream<T, E, W, kStreamU, RB>,
+                  dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB), p.stream, static_cast<const T *>(p.x),
+                  static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy);
+}
+
+// One workgroup per row, 1 to 16 waves by the row's length.
 template <typename T, int E>
 hipError_t stream_run(const RowProblem &p)
 {
-    return launch(online_stream<T, E, kStreamW, kStreamU>, dim3(static_cast<unsigned>(p.M)),
-                  dim3(kStreamW * kWave), p.stream, static_cast<const T *>(p.x),
-                  static_cast<T *>(p.y), p.N, p.ldx, p.ldy);
+    switch (stream_waves((p.N + E - 1) / E, kStreamU)) {
+    case 16:
+        return stream_launch<T, E, 16>(p);
+    case 4:
+        return stream_launch<T, E, 4>(p);
+    default:
+        return stream_launch<T, E, 1>(p);
+    }
 }
 
 template <typename T, int E>

@@ -227,6 +227,33 @@ def test_generic_paths_forced(dtype):
     assert rel_err_floor1(y, oracle.layernorm_gelu(x, w, b, EPS)) <= tol_of(dtype)
 
 
+STREAM_N = [1, 5, 300, 1000, 3000, 9000, 40000, 100003]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+@pytest.mark.parametrize("N", STREAM_N)
+def test_stream_widths(dtype, N):
+    """The one-workgroup-per-row kernels take 1, 4 or 16 waves per row by N,
+    and pack one-wave rows four to a workgroup: row counts that are not a
+    multiple of four, on the vector (aligned) and element (misaligned) paths."""
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(N), dtype)
+    wd, bd = w.to(DEV), b.to(DEV)
+    for M in (1, 3, 70):
+        flat = rowgen.randn(1, M * N + 1, seed=M + N, scale=3.0, dtype=dtype)[0]
+        x = flat[1:].view(M, N)
+        ref_s = oracle.softmax(x)
+        ref_l = oracle.layernorm_gelu(x, w, b, EPS)
+        aligned = x.contiguous().to(DEV)
+        misaligned = flat.to(DEV)[1:].view(M, N)  # one element off 16-byte alignment
+        for name, xd in (("aligned", aligned), ("misaligned", misaligned)):
+            say(f"stream {key(dtype)} M={M} N={N} {name}")
+            y = rk.rk__softmax_variant(-1, xd) if name == "aligned" else rk.rk_softmax(xd)
+            assert rel_err_softmax(y, ref_s) <= tol_of(dtype), name
+            y = (rk.rk__layernorm_gelu_variant(-1, xd, wd, bd, EPS) if name == "aligned"
+                 else rk.rk_layernorm_gelu(xd, wd, bd, EPS))
+            assert rel_err_floor1(y, ref_l) <= tol_of(dtype), name
+
+
 def test_in_place():
     M, N = 64, 768
     d = rowgen.make("tiny_f32_64x768")
