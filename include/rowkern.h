@@ -139,10 +139,12 @@ int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N);
  *     y_j = 0.5 z_j (1 + tanh(sqrt(2/pi) (z_j + 0.044715 z_j^3))).
  *
  * x [M][ldx], y [M][ldy], weight [N], bias [N] (contiguous), all of `dtype`.
- * Rows up to 16384 (fp32) / 32768 (bf16) columns with 16-byte alignment stay
- * in registers (one HBM read and write per element); other rows take one
- * workgroup per row that reads the row twice (statistics by parts merged as
- * in rk_layernorm_gelu_ex, then the output).  Same as rk_layernorm_gelu_ex
+ * 16-byte aligned rows of up to 14336 (fp32) / 20480 (bf16) columns, and of
+ * exactly 16384 (fp32) / 32768 (bf16), stay in registers (one HBM read and
+ * write per element); other rows take one workgroup per row that reads the
+ * row twice (statistics by parts merged as in rk_layernorm_gelu_ex, then the
+ * output), which measured faster than a register tile filled well below its
+ * capacity.  Same as rk_layernorm_gelu_ex
  * with RK_GELU_TANH and num_splits = 1.
  *
  * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight or bias is NULL
@@ -189,7 +191,7 @@ size_t rk_layernorm_gelu_workspace_bytes(int64_t M, int64_t N, int32_t num_split
                                          rk_dtype dtype);
 
 /* The split count rk_layernorm_gelu_ex uses for num_splits == 0: 1 when a
- * register tile holds the row (N up to 16384 fp32 / 32768 bf16) or M >= 512,
+ * register tile takes the row (as listed under rk_layernorm_gelu) or M >= 512,
  * else enough chunks of >= 2048 elements to give about 2048 workgroups. */
 int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
 

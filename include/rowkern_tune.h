@@ -43,17 +43,19 @@ int32_t rk__variant_count(rk_op op, rk_dtype dtype);
 /*
  * Geometry of tile variant `index`: waves cooperating on one row, 16-byte
  * vectors held per lane, waves per workgroup, rows each row-group handles in
- * sequence, the largest N it accepts, and whether it is compiled for
- * N == max_n only (every register slot a column: no masks, no padding).  Any
- * output pointer may be NULL.
+ * sequence, the largest N it accepts, whether it is compiled for N == max_n
+ * only (every register slot a column: no masks, no padding), and whether it
+ * is an alternative (run by index only, never picked).  Any output pointer
+ * may be NULL.
  */
 rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index, int32_t *waves_per_row,
                            int32_t *vecs_per_lane, int32_t *waves_per_block,
-                           int32_t *rows_per_group, int64_t *max_n, int32_t *exact);
+                           int32_t *rows_per_group, int64_t *max_n, int32_t *exact,
+                           int32_t *alternative);
 
-/* Index of the variant rk_softmax / rk_layernorm_gelu pick for N: the first
- * exact variant with max_n == N, else the first general one that holds N
- * (-1 when N is beyond every tile variant and the generic path runs). */
+/* Index of the variant the entry points pick for N: the first exact variant
+ * with max_n == N, else the first general one that holds N, alternatives
+ * skipped (-1 when none does and the rows-in-memory path runs). */
 int32_t rk__variant_pick(rk_op op, rk_dtype dtype, int64_t N);
 
 /*

@@ -85,7 +85,8 @@ def load():
         "rk__variant_count": (i32, [i32, i32]),
         "rk__variant_info": (i32, [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(i32),
-                                   ctypes.POINTER(i64), ctypes.POINTER(i32)]),
+                                   ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32)]),
         "rk__variant_pick": (i32, [i32, i32, i64]),
         "rk__softmax_variant": (i32, [i32, vp, vp, i64, i64, i64, i64, i32, vp]),
         "rk__layernorm_gelu_variant": (i32, [i32, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32,
@@ -395,15 +396,16 @@ def variants(op: int, dtype: int) -> list[dict]:
     lib = load()
     out = []
     for i in range(lib.rk__variant_count(op, dtype)):
-        g, v, w, r, ex = (ctypes.c_int32() for _ in range(5))
+        g, v, w, r, ex, alt = (ctypes.c_int32() for _ in range(6))
         n = ctypes.c_int64()
         st = lib.rk__variant_info(op, dtype, i, ctypes.byref(g), ctypes.byref(v), ctypes.byref(w),
-                                  ctypes.byref(r), ctypes.byref(n), ctypes.byref(ex))
+                                  ctypes.byref(r), ctypes.byref(n), ctypes.byref(ex),
+                                  ctypes.byref(alt))
         if st != RK_OK:
             raise RowKernError("rk__variant_info", st)
         out.append({"index": i, "waves_per_row": g.value, "vecs_per_lane": v.value,
                     "waves_per_block": w.value, "rows_per_group": r.value, "max_n": n.value,
-                    "exact": bool(ex.value)})
+                    "exact": bool(ex.value), "alternative": bool(alt.value)})
     return out
 
 

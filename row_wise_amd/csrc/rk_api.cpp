@@ -106,6 +106,8 @@ int pick_variant(rk_op op, rk_dtype dtype, int64_t N)
     const TileVariant *v = variants(op, dtype, &count);
     int general = -1;
     for (int i = 0; i < count; ++i) {
+        if (v[i].alternative)
+            continue;
         if (v[i].exact && N == v[i].max_n)
             return i;
         if (!v[i].exact && general < 0 && N <= v[i].max_n)
@@ -156,21 +158,10 @@ rk_status layernorm_generic(const RowProblem &p, bool aligned)
 
 bool valid_gelu(rk_gelu_kind g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
 
-// Largest N a LayerNorm register tile holds for `dtype`.
-int64_t layernorm_tile_cap(rk_dtype dtype)
-{
-    int count = 0;
-    const TileVariant *v = layernorm_gelu_variants(dtype, &count);
-    int64_t cap = 0;
-    for (int i = 0; i < count; ++i)
-        cap = v[i].max_n > cap ? v[i].max_n : cap;
-    return cap;
-}
-
 int32_t layernorm_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
 {
-    // rows a register tile holds are read once there: no split
-    if (N <= layernorm_tile_cap(dtype))
+    // rows a register tile takes are read once there: no split
+    if (pick_variant(RK_OP_LAYERNORM_GELU, dtype, N) >= 0)
         return 1;
     return auto_splits(M, N);
 }
@@ -723,7 +714,7 @@ RK_EXPORT int32_t rk__variant_count(rk_op op, rk_dtype dtype)
 RK_EXPORT rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index,
                                      int32_t *waves_per_row, int32_t *vecs_per_lane,
                                      int32_t *waves_per_block, int32_t *rows_per_group,
-                                     int64_t *max_n, int32_t *exact)
+                                     int64_t *max_n, int32_t *exact, int32_t *alternative)
 {
     int count = 0;
     const TileVariant *v = variants(op, dtype, &count);
@@ -741,6 +732,8 @@ RK_EXPORT rk_status rk__variant_info(rk_op op, rk_dtype dtype, int32_t index,
         *max_n = v[index].max_n;
     if (exact)
         *exact = v[index].exact ? 1 : 0;
+    if (alternative)
+        *alternative = v[index].alternative ? 1 : 0;
     return RK_OK;
 }
 

@@ -74,13 +74,23 @@ struct TileVariant {
     int max_n;            // largest N the variant holds
     bool exact;           // compiled for N == max_n only: no masks, no padding
     hipError_t (*run)(const RowProblem &);
+    bool alternative = false;  // reachable by index only, never dispatched
 
     bool accepts(int64_t n) const { return exact ? n == max_n : n <= max_n; }
 };
 
+// Marks a table entry as an alternative: run by index (tuning, tests), never
+// chosen by the dispatcher.
+constexpr TileVariant alt(TileVariant v)
+{
+    v.alternative = true;
+    return v;
+}
+
 // Variant tables (defined next to the kernels), in order of preference: the
 // dispatcher takes the first exact variant with max_n == N, else the first
-// general variant whose max_n covers N.
+// general variant whose max_n covers N, skipping alternatives.  An N that no
+// dispatched entry takes goes to the kernels that keep the row in memory.
 const TileVariant *softmax_variants(rk_dtype dtype, int *count);
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count);
 const TileVariant *rmsnorm_variants(rk_dtype dtype, bool residual, int *count);

@@ -187,7 +187,13 @@ constexpr TileVariant exact()
 }
 
 // Preference order as for softmax: first exact entry with max_n == N, else
-// the first general entry that holds N; the rest are alternatives.
+// the first general entry that holds N.  General entries ascend in capacity
+// so that a row takes the smallest tile that holds it: a tile's time per row
+// follows its capacity (every register slot is loaded, reduced and passed
+// through the epilogue), and the 16-wave tiles, one workgroup per CU at their
+// register count, measured slower below capacity than the streaming kernel,
+// which therefore takes the N between the last general entry and the exact
+// 16384 (fp32) / 32768 (bf16).  alt(): run by index only.
 static const TileVariant kLayerNormF32[] = {
     exact<float, 1, 1, 4>(),    // N = 256
     exact<float, 1, 2, 4>(),    // N = 512
@@ -204,14 +210,16 @@ static const TileVariant kLayerNormF32[] = {
     tile<float, 1, 8, 4>(),     // N <= 2048
     tile<float, 4, 4, 4>(),     // N <= 4096
     tile<float, 8, 4, 8>(),     // N <= 8192
-    tile<float, 16, 4, 16>(),   // N <= 16384
-    tile<float, 1, 3, 4, 2>(),  // alternatives
-    tile<float, 2, 2, 4>(),
-    exact<float, 1, 3, 4, 2>(),
-    exact<float, 1, 3, 4, 4>(),
-    exact<float, 8, 4, 8>(),
-    exact<float, 16, 4, 16>(),
-    tile<float, 8, 8, 8>(),
+    tile<float, 8, 6, 8>(),     // N <= 12288 (N = 12000: 51 us vs 65 us for 16 x 4)
+    tile<float, 8, 7, 8>(),     // N <= 14336
+    alt(tile<float, 16, 4, 16>()),
+    alt(tile<float, 8, 8, 8>()),
+    alt(tile<float, 1, 3, 4, 2>()),
+    alt(tile<float, 2, 2, 4>()),
+    alt(exact<float, 1, 3, 4, 2>()),
+    alt(exact<float, 1, 3, 4, 4>()),
+    alt(exact<float, 8, 4, 8>()),
+    alt(exact<float, 16, 4, 16>()),
 };
 
 static const TileVariant kLayerNormBF16[] = {
@@ -225,20 +233,24 @@ static const TileVariant kLayerNormBF16[] = {
     tile<bf16_t, 1, 1, 4>(),    // N <= 512
     tile<bf16_t, 1, 2, 4>(),    // N <= 1024
     tile<bf16_t, 1, 4, 4>(),    // N <= 2048
-    tile<bf16_t, 2, 4, 4>(),    // N <= 4096
+    tile<bf16_t, 4, 2, 4>(),    // N <= 4096 (N = 3000: 59 us vs 65 us for 2 x 4)
+    tile<bf16_t, 4, 3, 4>(),    // N <= 6144
     tile<bf16_t, 8, 2, 8>(),    // N <= 8192
-    tile<bf16_t, 16, 2, 16>(),  // N <= 16384
-    tile<bf16_t, 16, 4, 16>(),  // N <= 32768
-    tile<bf16_t, 4, 2, 4>(),    // alternatives
-    tile<bf16_t, 1, 8, 4>(),
-    exact<bf16_t, 4, 2, 4>(),
-    exact<bf16_t, 2, 4, 4>(),
-    exact<bf16_t, 1, 8, 4>(),
-    exact<bf16_t, 2, 4, 4, 2>(),
-    exact<bf16_t, 16, 2, 16>(),
-    exact<bf16_t, 8, 8, 8>(),
-    tile<bf16_t, 8, 8, 8>(),
-    exact<bf16_t, 4, 8, 4>(),
+    tile<bf16_t, 8, 3, 8>(),    // N <= 12288
+    tile<bf16_t, 8, 4, 8>(),    // N <= 16384 (N = 14000: 60 us vs 87 us for 16 x 2)
+    tile<bf16_t, 8, 5, 8>(),    // N <= 20480
+    alt(tile<bf16_t, 2, 4, 4>()),
+    alt(tile<bf16_t, 16, 2, 16>()),
+    alt(tile<bf16_t, 16, 4, 16>()),
+    alt(tile<bf16_t, 8, 8, 8>()),
+    alt(tile<bf16_t, 1, 8, 4>()),
+    alt(exact<bf16_t, 4, 2, 4>()),
+    alt(exact<bf16_t, 2, 4, 4>()),
+    alt(exact<bf16_t, 1, 8, 4>()),
+    alt(exact<bf16_t, 2, 4, 4, 2>()),
+    alt(exact<bf16_t, 16, 2, 16>()),
+    alt(exact<bf16_t, 8, 8, 8>()),
+    alt(exact<bf16_t, 4, 8, 4>()),
 };
 
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count)

@@ -137,8 +137,8 @@ constexpr TileVariant exact()
 }
 
 // Preference order: the dispatcher takes the first exact entry whose max_n is
-// N, else the first general entry whose max_n covers N.  General entries after
-// the largest one are alternatives reachable by index.
+// N, else the first general entry whose max_n covers N (general entries in
+// ascending capacity).  alt(): run by index only, never picked.
 static const TileVariant kSoftmaxF32[] = {
     exact<float, 1, 1, 4>(),   // N = 256
     exact<float, 1, 2, 4>(),   // N = 512
@@ -156,13 +156,13 @@ static const TileVariant kSoftmaxF32[] = {
     tile<float, 4, 4, 4>(),    // N <= 4096
     tile<float, 8, 4, 8>(),    // N <= 8192
     tile<float, 16, 4, 16>(),  // N <= 16384
-    tile<float, 1, 4, 4>(),    // alternatives
-    tile<float, 4, 1, 4>(),
-    tile<float, 2, 8, 4>(),
-    exact<float, 1, 4, 4>(),
-    exact<float, 8, 8, 8>(),   // large-row alternatives: fewer waves per row
-    tile<float, 8, 8, 8>(),
-    exact<float, 4, 8, 4>(),
+    alt(tile<float, 1, 4, 4>()),
+    alt(tile<float, 4, 1, 4>()),
+    alt(tile<float, 2, 8, 4>()),
+    alt(exact<float, 1, 4, 4>()),
+    alt(exact<float, 8, 8, 8>()),  // large rows with fewer waves per row
+    alt(tile<float, 8, 8, 8>()),
+    alt(exact<float, 4, 8, 4>()),
 };
 
 static const TileVariant kSoftmaxBF16[] = {
@@ -180,15 +180,15 @@ static const TileVariant kSoftmaxBF16[] = {
     tile<bf16_t, 8, 2, 8>(),    // N <= 8192
     tile<bf16_t, 16, 2, 16>(),  // N <= 16384
     tile<bf16_t, 16, 4, 16>(),  // N <= 32768
-    tile<bf16_t, 1, 8, 4>(),    // alternatives
-    tile<bf16_t, 2, 4, 4>(),
-    tile<bf16_t, 8, 1, 8>(),
-    exact<bf16_t, 1, 8, 4>(),
-    exact<bf16_t, 2, 4, 4>(),
-    exact<bf16_t, 8, 1, 8>(),
-    exact<bf16_t, 8, 8, 8>(),   // large-row alternatives: fewer waves per row
-    tile<bf16_t, 8, 8, 8>(),
-    exact<bf16_t, 8, 4, 8>(),
+    alt(tile<bf16_t, 1, 8, 4>()),
+    alt(tile<bf16_t, 2, 4, 4>()),
+    alt(tile<bf16_t, 8, 1, 8>()),
+    alt(exact<bf16_t, 1, 8, 4>()),
+    alt(exact<bf16_t, 2, 4, 4>()),
+    alt(exact<bf16_t, 8, 1, 8>()),
+    alt(exact<bf16_t, 8, 8, 8>()),  // large rows with fewer waves per row
+    alt(tile<bf16_t, 8, 8, 8>()),
+    alt(exact<bf16_t, 8, 4, 8>()),
 };
 
 const TileVariant *softmax_variants(rk_dtype dtype, int *count)

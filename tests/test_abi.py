@@ -290,23 +290,37 @@ def test_variant_tables():
                 assert v["waves_per_block"] % v["waves_per_row"] == 0
                 assert v["waves_per_block"] * 64 <= 1024
             assert max(v["max_n"] for v in vs) == cap
-            for N in (1, 7, 255, 256, 257, 768, 1000, 4096, cap):
+            picked = [v for v in vs if not v["alternative"]]
+            # the dispatched general entries cover 1..reach in ascending caps
+            general = [v["max_n"] for v in picked if not v["exact"]]
+            assert general == sorted(general)
+            reach = general[-1]
+            for N in (1, 7, 255, 256, 257, 768, 1000, 4096, reach, cap):
                 i = rk.variant_pick(op, dt, N)
-                assert i >= 0
+                assert i >= 0 and not vs[i]["alternative"]
                 assert vs[i]["max_n"] == N if vs[i]["exact"] else vs[i]["max_n"] >= N
+                if not vs[i]["exact"]:  # the smallest general tile that holds N
+                    assert vs[i]["max_n"] == min(c for c in general if c >= N)
             assert rk.variant_pick(op, dt, cap + 1) == -1
-            # every N has a general variant; exact ones are preferred when they fit
+            if reach < cap:  # between the two, rows stay in memory
+                assert rk.variant_pick(op, dt, reach + 1) == -1
+                assert rk.variant_pick(op, dt, cap - 1) == -1
+            # exact entries are taken when they fit, and have a general twin
             caps = {v["max_n"] for v in vs if not v["exact"]}
-            for v in vs:
+            for v in picked:
                 if v["exact"]:
                     assert v["max_n"] in caps
                     assert vs[rk.variant_pick(op, dt, v["max_n"])]["exact"]
+            # an alternative is never picked
+            for v in vs:
+                if v["alternative"]:
+                    assert rk.variant_pick(op, dt, v["max_n"]) != v["index"]
 
 
 def test_variant_entry_points_reject(lib):
     n = lib.rk__variant_count(0, F32)
     assert lib.rk__variant_count(5, F32) == 0 and lib.rk__variant_count(0, 9) == 0
-    assert lib.rk__variant_info(0, F32, n, None, None, None, None, None, None) == INVALID
+    assert lib.rk__variant_info(0, F32, n, None, None, None, None, None, None, None) == INVALID
     assert lib.rk__softmax_variant(n, A, B, 4, 8, 8, 8, F32, None) == INVALID
     assert lib.rk__softmax_variant(-2, A, B, 4, 8, 8, 8, F32, None) == INVALID
     assert lib.rk__layernorm_gelu_variant(0, A, A + 0x80000, A + 0x90000, B, 4, 8, 8, 8, 0.0,
