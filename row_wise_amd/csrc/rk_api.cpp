@@ -69,6 +69,15 @@ bool rows_aligned(const void *x, const void *y, int64_t ldx, int64_t ldy, int es
     return aligned16(x) && aligned16(y) && (ldx * es) % 16 == 0 && (ldy * es) % 16 == 0;
 }
 
+// The row-in-memory kernels read each row as aligned 16-byte vectors from
+// the row's own offset past a 16-byte boundary; the matrices they read or
+// write by row must share that offset, row for row, for all M rows.
+bool same_phase(const void *a, int64_t lda, const void *b, int64_t ldb, int es)
+{
+    return (reinterpret_cast<uintptr_t>(a) - reinterpret_cast<uintptr_t>(b)) % 16 == 0 &&
+           ((lda - ldb) * es) % 16 == 0;
+}
+
 // gridDim.x * blockDim.x must stay below 2^32 work-items.
 bool grid_ok(int64_t blocks, int threads)
 {
@@ -116,6 +125,18 @@ int pick_variant(rk_op op, rk_dtype dtype, int64_t N)
     return general;
 }
 
+// The general tile whose phased form takes rows of N at any offset: the first
+// dispatched general entry with room for N + E - 1 columns, or -1.
+int pick_phased(rk_op op, rk_dtype dtype, int64_t N)
+{
+    int count = 0;
+    const TileVariant *v = variants(op, dtype, &count);
+    for (int i = 0; i < count; ++i)
+        if (!v[i].alternative && !v[i].exact && v[i].accepts_phased(N, vec_elems(dtype)))
+            return i;
+    return -1;
+}
+
 int64_t tile_blocks(const TileVariant &v, int64_t M)
 {
     const int64_t rows_per_block = int64_t{v.waves_per_block} / v.waves_per_row * v.rows_per_group;
@@ -124,7 +145,7 @@ int64_t tile_blocks(const TileVariant &v, int64_t M)
 
 constexpr int kStreamThreads = 1024;  // largest streaming workgroup (16 waves)
 constexpr int kSplitThreads = 256;    // online_partials / online_finish
-constexpr int kLoopThreads = 256;     // rmsnorm_loop
+constexpr int kLoopThreads = 1024;    // largest rmsnorm_loop workgroup
 constexpr int32_t kMaxSplits = 65536;
 
 int32_t auto_splits(int64_t M, int64_t N)
@@ -142,18 +163,29 @@ int32_t auto_splits(int64_t M, int64_t N)
     return static_cast<int32_t>(s < 1 ? 1 : s);
 }
 
-rk_status softmax_generic(const RowProblem &p, bool aligned)
+bool softmax_vectorized(const RowProblem &p)
 {
-    if (!grid_ok(p.M, kStreamThreads))
-        return RK_ERR_UNSUPPORTED;
-    return hip_status(online_stream_run(p, aligned));
+    return same_phase(p.x, p.ldx, p.y, p.ldy, elem_size(p.dtype));
 }
 
-rk_status layernorm_generic(const RowProblem &p, bool aligned)
+// Weight and bias are shifted into each row's phase from 16-byte alignment.
+bool layernorm_vectorized(const RowProblem &p)
+{
+    return softmax_vectorized(p) && aligned16(p.w) && aligned16(p.b);
+}
+
+rk_status softmax_generic(const RowProblem &p)
 {
     if (!grid_ok(p.M, kStreamThreads))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(layernorm_stream_run(p, aligned));
+    return hip_status(online_stream_run(p, softmax_vectorized(p)));
+}
+
+rk_status layernorm_generic(const RowProblem &p)
+{
+    if (!grid_ok(p.M, kStreamThreads))
+        return RK_ERR_UNSUPPORTED;
+    return hip_status(layernorm_stream_run(p, layernorm_vectorized(p)));
 }
 
 bool valid_gelu(rk_gelu_kind g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
@@ -196,12 +228,24 @@ rk_status check_workspace(void *workspace, size_t workspace_bytes, size_t need, 
     return RK_OK;
 }
 
-rk_status run_tile(const TileVariant &v, const RowProblem &p)
+rk_status run_tile(const TileVariant &v, const RowProblem &p, bool phased = false)
 {
     const int64_t blocks = tile_blocks(v, p.M);
     if (!grid_ok(blocks, v.waves_per_block * 64))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(v.run(p));
+    return hip_status(phased ? v.run_phased(p) : v.run(p));
+}
+
+// A tile forced by index: aligned rows run it as compiled; rows that share
+// their offsets with the output (and, where given, weight and bias are
+// aligned) run its phased form if it has one that holds them.
+rk_status run_forced(const TileVariant &v, const RowProblem &p, bool aligned, bool vectorized)
+{
+    if (aligned && v.accepts(p.N))
+        return run_tile(v, p);
+    if (!aligned && vectorized && v.accepts_phased(p.N, vec_elems(p.dtype)))
+        return run_tile(v, p, true);
+    return RK_ERR_UNSUPPORTED;
 }
 
 rk_status check_layernorm(const void *x, const void *w, const void *b, const void *y, int64_t M,
@@ -305,11 +349,20 @@ bool rmsnorm_aligned(const RowProblem &p, bool residual)
     return ok;
 }
 
-rk_status rmsnorm_generic(const RowProblem &p, bool residual, bool aligned)
+bool rmsnorm_vectorized(const RowProblem &p, bool residual)
+{
+    const int es = elem_size(p.dtype);
+    bool ok = same_phase(p.x, p.ldx, p.y, p.ldy, es) && aligned16(p.w);
+    if (residual)
+        ok = ok && same_phase(p.x, p.ldx, p.r, p.ldr, es) && same_phase(p.x, p.ldx, p.ro, p.ldo, es);
+    return ok;
+}
+
+rk_status rmsnorm_generic(const RowProblem &p, bool residual)
 {
     if (!grid_ok(p.M, kLoopThreads))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(rmsnorm_loop_run(p, residual, aligned));
+    return hip_status(rmsnorm_loop_run(p, residual, rmsnorm_vectorized(p, residual)));
 }
 
 rk_status rmsnorm_dispatch(const RowProblem &p, bool residual, int32_t index, bool forced)
@@ -321,15 +374,19 @@ rk_status rmsnorm_dispatch(const RowProblem &p, bool residual, int32_t index, bo
         if (index < -1 || index >= count)
             return RK_ERR_INVALID_ARG;
         if (index == -1)
-            return rmsnorm_generic(p, residual, aligned);
-        if (!aligned || !v[index].accepts(p.N))
-            return RK_ERR_UNSUPPORTED;
-        return run_tile(v[index], p);
+            return rmsnorm_generic(p, residual);
+        return run_forced(v[index], p, aligned, rmsnorm_vectorized(p, residual));
     }
-    const int idx = pick_variant(residual ? RK_OP_RESIDUAL_RMSNORM : RK_OP_RMSNORM, p.dtype, p.N);
+    const rk_op op = residual ? RK_OP_RESIDUAL_RMSNORM : RK_OP_RMSNORM;
+    const int idx = pick_variant(op, p.dtype, p.N);
     if (aligned && idx >= 0)
         return run_tile(v[idx], p);
-    return rmsnorm_generic(p, residual, aligned);
+    if (!aligned && rmsnorm_vectorized(p, residual)) {
+        const int ph = pick_phased(op, p.dtype, p.N);
+        if (ph >= 0)
+            return run_tile(v[ph], p, true);
+    }
+    return rmsnorm_generic(p, residual);
 }
 
 }  // namespace
@@ -344,12 +401,17 @@ RK_EXPORT rk_status rk_softmax(const void *x, void *y, int64_t M, int64_t N, int
         return st;
     const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
     const bool aligned = rows_aligned(x, y, ldx, ldy, elem_size(dtype));
+    int count = 0;
+    const TileVariant *v = softmax_variants(dtype, &count);
     const int idx = pick_variant(RK_OP_SOFTMAX, dtype, N);
-    if (aligned && idx >= 0) {
-        int count = 0;
-        return run_tile(softmax_variants(dtype, &count)[idx], p);
+    if (aligned && idx >= 0)
+        return run_tile(v[idx], p);
+    if (!aligned && softmax_vectorized(p)) {
+        const int ph = pick_phased(RK_OP_SOFTMAX, dtype, N);
+        if (ph >= 0)
+            return run_tile(v[ph], p, true);
     }
-    return softmax_generic(p, aligned);
+    return softmax_generic(p);
 }
 
 RK_EXPORT int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N)
@@ -379,20 +441,20 @@ RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t
     if (M == 0)
         return RK_OK;
     const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
-    const bool aligned = rows_aligned(x, y, ldx, ldy, elem_size(dtype));
     const int32_t S = num_splits == 0 ? auto_splits(M, N) : num_splits;
     if (S <= 1)
-        return softmax_generic(p, aligned);
+        return softmax_generic(p);
+    const bool vec = softmax_vectorized(p);
 
     const int es = elem_size(dtype);
     st = check_workspace(workspace, workspace_bytes, rk_online_softmax_workspace_bytes(M, N, S), M,
                          S, {matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es)});
     if (st != RK_OK)
         return st;
-    const int64_t chunk = split_chunk(N, S, aligned ? vec_elems(dtype) : 1);
+    const int64_t chunk = split_chunk(N, S, vec ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
-    return hip_status(online_split_run(p, S, static_cast<int>(chunk), workspace, aligned));
+    return hip_status(online_split_run(p, S, static_cast<int>(chunk), workspace, vec));
 }
 
 RK_EXPORT int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
@@ -430,12 +492,17 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
     const bool aligned = layernorm_aligned(p);
     const int32_t S = num_splits == 0 ? layernorm_auto_splits(M, N, dtype) : num_splits;
     if (S <= 1) {
+        int count = 0;
+        const TileVariant *v = layernorm_gelu_variants(dtype, &count);
         const int idx = pick_variant(RK_OP_LAYERNORM_GELU, dtype, N);
-        if (aligned && idx >= 0) {
-            int count = 0;
-            return run_tile(layernorm_gelu_variants(dtype, &count)[idx], p);
+        if (aligned && idx >= 0)
+            return run_tile(v[idx], p);
+        if (!aligned && layernorm_vectorized(p)) {
+            const int ph = pick_phased(RK_OP_LAYERNORM_GELU, dtype, N);
+            if (ph >= 0)
+                return run_tile(v[ph], p, true);
         }
-        return layernorm_generic(p, aligned);
+        return layernorm_generic(p);
     }
     const int es = elem_size(dtype);
     st = check_workspace(workspace, workspace_bytes, split_workspace_bytes(M, S), M, S,
@@ -443,10 +510,11 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
                           matrix_span(weight, 1, N, N, es), matrix_span(bias, 1, N, N, es)});
     if (st != RK_OK)
         return st;
-    const int64_t chunk = split_chunk(N, S, aligned ? vec_elems(dtype) : 1);
+    const bool vec = layernorm_vectorized(p);
+    const int64_t chunk = split_chunk(N, S, vec ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
-    return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), workspace, aligned));
+    return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), workspace, vec));
 }
 
 RK_EXPORT rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias, void *y,
@@ -758,10 +826,8 @@ RK_EXPORT rk_status rk__softmax_variant(int32_t index, const void *x, void *y, i
     const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
     const bool aligned = rows_aligned(x, y, ldx, ldy, elem_size(dtype));
     if (index == -1)
-        return softmax_generic(p, aligned);
-    if (!aligned || !v[index].accepts(N))
-        return RK_ERR_UNSUPPORTED;
-    return run_tile(v[index], p);
+        return softmax_generic(p);
+    return run_forced(v[index], p, aligned, softmax_vectorized(p));
 }
 
 RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, const void *weight,
@@ -784,10 +850,8 @@ RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, con
     p.gelu = gelu;
     const bool aligned = layernorm_aligned(p);
     if (index == -1)
-        return layernorm_generic(p, aligned);
-    if (!aligned || !v[index].accepts(N))
-        return RK_ERR_UNSUPPORTED;
-    return run_tile(v[index], p);
+        return layernorm_generic(p);
+    return run_forced(v[index], p, aligned, layernorm_vectorized(p));
 }
 
 RK_EXPORT rk_status rk__rmsnorm_variant(int32_t index, const void *x, const void *weight, void *y,

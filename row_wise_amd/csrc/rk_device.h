@@ -549,4 +549,206 @@ __device__ __forceinline__ void store_row(T *__restrict__ row, int vi0, int vend
     }
 }
 
+// ------------------------------------------- rows at any element offset
+//
+// A row that starts h elements (0 <= h < E) past a 16-byte boundary is read
+// and written as the aligned vectors of base = row - h: vector j holds
+// columns j*E - h .. j*E - h + E - 1, of which those in [0, N) are the row's.
+// Only the first and the last vector can hold other columns.  The load of
+// such a vector stays inside a 16-byte block that also holds an element of
+// the row, hence inside that element's page, so it cannot fault; its
+// outside values are replaced by a pad value, and its stores go element by
+// element.  A row whose output (and any other operand read by row) has the
+// same phase uses the same vector indices for all of them.
+template <int E>
+struct RowSpan {
+    int h;  // phase: elements from the aligned base to the row's first element
+    int n;  // row length
+
+    __device__ __forceinline__ int count() const { return (h + n + E - 1) / E; }
+    // vectors [full_begin(), full_end()) hold row elements only
+    __device__ __forceinline__ int full_begin() const { return h != 0 ? 1 : 0; }
+    __device__ __forceinline__ int full_end() const { return (h + n) / E; }
+    __device__ __forceinline__ bool valid(int j, int e) const
+    {
+        return static_cast<unsigned>(j * E + e - h) < static_cast<unsigned>(n);
+    }
+};
+
+// Phase of a row's first element.  The same for every lane of a wave (a
+// wave works on one row), so it is read into a scalar register.
+template <typename T, int E>
+__device__ __forceinline__ int row_phase(const T *row)
+{
+    if constexpr (E == 1)
+        return 0;
+    else
+        return __builtin_amdgcn_readfirstlane(
+            static_cast<int>((reinterpret_cast<uintptr_t>(row) % 16) / sizeof(T)));
+}
+
+// Vector range [jbeg, jend) of chunk s of S when a row is split into chunks
+// of C phased positions (C a multiple of E): positions [s C, s C + C), the
+// last chunk running to the row's end.
+template <int E>
+__device__ __forceinline__ void chunk_span(RowSpan<E> sp, int s, int S, int C, int &jbeg,
+                                           int &jend)
+{
+    const int nv = sp.count();
+    const int64_t c0 = static_cast<int64_t>(s) * C;
+    const int64_t len = static_cast<int64_t>(sp.h) + sp.n;
+    jbeg = static_cast<int>(c0 < len ? c0 / E : nv);
+    jend = static_cast<int>(s == S - 1 || c0 + C >= len ? nv : (c0 + C) / E);
+}
+
+// U vectors of a row in flight: vector k of this lane is j0 + k * STRIDE.
+// issue() starts the loads of the vectors below jend (all of them, unmasked,
+// when `full`) and never waits; finish() unpacks to fp32 and replaces
+// elements outside the row or at or past jend by `pad`.
+template <typename T, int E, int U, int STRIDE, int CP = kStreaming>
+struct SpanLoad {
+    typedef typename RawVec<T, E>::type R;
+    R q[U];
+    int j0;
+
+    __device__ __forceinline__ void issue(const T *__restrict__ base, int j0_, int jend, bool full)
+    {
+        j0 = j0_;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int j = j0 + k * STRIDE;
+            if (full) {
+                q[k] = ld<CP>(reinterpret_cast<const R *>(base + static_cast<int64_t>(j) * E));
+            } else {
+                q[k] = R{};
+                if (j < jend)
+                    q[k] = ld<CP>(reinterpret_cast<const R *>(base + static_cast<int64_t>(j) * E));
+            }
+        }
+    }
+
+    __device__ __forceinline__ void finish(float (&v)[U][E], RowSpan<E> sp, int jend, float pad,
+                                           bool full) const
+    {
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            unpack<T, E>(q[k], v[k]);
+        if (!full) {
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int j = j0 + k * STRIDE;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (!(j < jend && sp.valid(j, e)))
+                        v[k][e] = pad;
+            }
+        }
+    }
+};
+
+// Store the row elements of the vectors a SpanLoad covered below jend.
+template <typename T, int E, int U, int STRIDE, int CP = kStreaming>
+__device__ __forceinline__ void store_span(T *__restrict__ base, int j0, int jend, RowSpan<E> sp,
+                                           const float (&v)[U][E], bool full)
+{
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            store_vec<T, E, CP>(base + static_cast<int64_t>(j0 + k * STRIDE) * E, v[k]);
+        return;
+    }
+    const int fb = sp.full_begin();
+    const int fe = sp.full_end();
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int j = j0 + k * STRIDE;
+        if (j >= jend)
+            continue;
+        if (j >= fb && j < fe) {
+            store_vec<T, E, CP>(base + static_cast<int64_t>(j) * E, v[k]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (sp.valid(j, e))
+                    base[static_cast<int64_t>(j) * E + e] = Elem<T>::from_f32(v[k][e]);
+        }
+    }
+}
+
+// out = the E elements that start H elements before hi[0]: the last H of lo,
+// then the first E - H of hi (H < E; other H never occur and copy hi).
+template <int H, int E>
+__device__ __forceinline__ void shift_in(const float (&lo)[E], const float (&hi)[E],
+                                         float (&out)[E])
+{
+    if constexpr (H > 0 && H < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            out[e] = e < H ? lo[E - H + e] : hi[e - H];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            out[e] = hi[e];
+    }
+}
+
+// The E elements of a per-column parameter p[n] (16-byte aligned, cached)
+// that meet vector j of a row at phase h: p[j*E - h + e], 0 outside [0, n).
+// Two aligned loads straddle the shift; each reads a 16-byte block that
+// holds an element of p.
+// `full` promises that vector j holds row elements only: no checks then.
+template <typename T, int E>
+__device__ __forceinline__ void load_param(const T *__restrict__ p, int j, int h, int n,
+                                           float (&out)[E], bool full)
+{
+    typedef typename RawVec<T, E>::type R;
+    const R *pv = reinterpret_cast<const R *>(p);
+    float hi[E], lo[E];
+    R qh = R{}, ql = R{};
+    // a block is read only if it holds an element of p (lanes of a masked
+    // step may sit past the row)
+    if (full || j * E < n)
+        qh = pv[j];
+    if (h != 0 && (full || (j >= 1 && (j - 1) * E < n)))
+        ql = pv[j - 1];
+    unpack<T, E>(qh, hi);
+    unpack<T, E>(ql, lo);
+    // element e comes from lo[E - h + e] (e < h) or hi[e - h]; h is uniform
+    // over the wave, so one case runs
+    switch (h) {
+    case 1:
+        shift_in<1>(lo, hi, out);
+        break;
+    case 2:
+        shift_in<2>(lo, hi, out);
+        break;
+    case 3:
+        shift_in<3>(lo, hi, out);
+        break;
+    case 4:
+        shift_in<4>(lo, hi, out);
+        break;
+    case 5:
+        shift_in<5>(lo, hi, out);
+        break;
+    case 6:
+        shift_in<6>(lo, hi, out);
+        break;
+    case 7:
+        shift_in<7>(lo, hi, out);
+        break;
+    default:
+        shift_in<0>(lo, hi, out);
+        break;
+    }
+    // columns outside [0, n) read as 0 (the elements of a block that are
+    // not p's, or a block that was not loaded)
+    if (!full) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (static_cast<unsigned>(j * E + e - h) >= static_cast<unsigned>(n))
+                out[e] = 0.0f;
+    }
+}
+
 }  // namespace rk

@@ -75,8 +75,17 @@ struct TileVariant {
     bool exact;           // compiled for N == max_n only: no masks, no padding
     hipError_t (*run)(const RowProblem &);
     bool alternative = false;  // reachable by index only, never dispatched
+    // The same tile for rows at any offset past a 16-byte boundary (shared
+    // by the row's input and output): general, one row per row group; a row
+    // at offset h takes h + N register slots.  Null where not compiled.
+    hipError_t (*run_phased)(const RowProblem &) = nullptr;
 
     bool accepts(int64_t n) const { return exact ? n == max_n : n <= max_n; }
+    // every offset h < vec fits
+    bool accepts_phased(int64_t n, int vec) const
+    {
+        return run_phased != nullptr && n + vec - 1 <= max_n;
+    }
 };
 
 // Marks a table entry as an alternative: run by index (tuning, tests), never
@@ -130,6 +139,11 @@ inline int stream_waves(int64_t nvec, int U)
         return 4;
     return 1;
 }
+
+// Rows of at most this many vectors take one wave and one vector per lane
+// per step: with U vectors per step, most of a short row's step would be
+// masked padding.
+constexpr int64_t kShortRowVectors = 128;
 
 // Chunk length (elements) of the split-row variant: ceil(N / S) rounded up to
 // whole 16-byte vectors when the vector path is used.

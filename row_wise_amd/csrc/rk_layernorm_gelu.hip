@@ -22,11 +22,16 @@ namespace rk {
 // EXACT: compiled for N == V * L * E, i.e. every register slot of a row group
 // is a column of its row: no masks, no padding, no excluded columns.  Rows
 // past M (the last workgroup) then read row 0 and store nothing.
-template <typename T, int G, int V, int W, int R, bool EXACT, int GK>
+// PH: rows at any offset past a 16-byte boundary (the output's rows at the
+// same offset), read and written as the aligned vectors that cover them
+// (RowSpan), their ends masked; weight and bias are shifted into each row's
+// offset as they are used.  One row per row group.
+template <typename T, int G, int V, int W, int R, bool EXACT, int GK, bool PH>
 __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
     T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
 {
+    static_assert(!PH || (!EXACT && R == 1), "phased rows: general tiles, one row per group");
     constexpr int E = Elem<T>::kVec;
     constexpr int RG = W / G;
     constexpr int L = G * kWave;
@@ -52,15 +57,27 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     // and bias (shared by all R rows).  Each later row is issued while the
     // previous one is reduced.
     RowLoad<T, E, V, L> xl;
-    {
+    SpanLoad<T, E, V, L> xs;  // PH
+    RowSpan<E> sp{0, N};
+    int jend = 0;
+    if constexpr (PH) {
+        const int64_t row = row_of(0);
+        const bool ok = row < M;
+        const T *xr = x + (ok ? row : 0) * ldx;
+        sp.h = row_phase<T, E>(xr);
+        jend = ok ? sp.count() : 0;
+        xs.issue(xr - sp.h, li, jend, false);
+    } else {
         const int64_t row = row_of(0);
         const bool ok = row < M;
         xl.issue(x + (ok ? row : 0) * ldx, li, ok ? nv : 0, rs, 0.0f,
                  EXACT || (ok && slots_full));
     }
     RowLoad<T, E, V, L, kCached> wl, bl;
-    wl.issue(w, li, nv, rs, 0.0f, slots_full);
-    bl.issue(b, li, nv, rs, 0.0f, slots_full);
+    if constexpr (!PH) {
+        wl.issue(w, li, nv, rs, 0.0f, slots_full);
+        bl.issue(b, li, nv, rs, 0.0f, slots_full);
+    }
     float wv[R > 1 ? V : 1][E], bv[R > 1 ? V : 1][E];
 
 #pragma unroll
@@ -74,7 +91,10 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         const int buf = r & 1;
 
         float v[V][E];
-        xl.finish(v, rs);
+        if constexpr (PH)
+            xs.finish(v, sp, jend, 0.0f, false);
+        else
+            xl.finish(v, rs);
         if (r + 1 < R) {
             const int64_t nrow = row_of(r + 1);
             const bool nok = nrow < M;
@@ -108,7 +128,9 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
             const int vi = k * L + li;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const bool valid = EXACT || vi < rs.nfull || (vi == rs.nfull && e < rs.tail);
+                const bool valid =
+                    PH ? vi < jend && sp.valid(vi, e)
+                       : EXACT || vi < rs.nfull || (vi == rs.nfull && e < rs.tail);
                 const float d = valid ? v[k][e] - mean : 0.0f;
                 v[k][e] = d;
                 q = fmaf(d, d, q);
@@ -144,14 +166,21 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
 #pragma unroll
             for (int k = 0; k < V; ++k) {
                 float wk[E], bk[E];
-                wl.finish_one(k, wk, rs);
-                bl.finish_one(k, bk, rs);
+                if constexpr (PH) {
+                    load_param<T, E>(w, k * L + li, sp.h, N, wk, false);
+                    load_param<T, E>(b, k * L + li, sp.h, N, bk, false);
+                } else {
+                    wl.finish_one(k, wk, rs);
+                    bl.finish_one(k, bk, rs);
+                }
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     v[k][e] = gelu<GK>(fmaf(v[k][e] * rstd, wk[e], bk[e]));
             }
         }
-        if (EXACT) {
+        if constexpr (PH) {
+            store_span<T, E, V, L>(yr - sp.h, li, jend, sp, v, false);
+        } else if (EXACT) {
             if (row_ok)
                 store_row<T, E, V, L>(yr, li, vend, rs, v, true);
         } else {
@@ -160,25 +189,36 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     }
 }
 
-template <typename T, int G, int V, int W, int R, bool EXACT>
+template <typename T, int G, int V, int W, int R, bool EXACT, bool PH>
 static hipError_t layernorm_gelu_tile_run(const RowProblem &p)
 {
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG * R - 1) / (RG * R);
     const float inv_n = static_cast<float>(1.0 / p.N);
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 1>
-                                        : layernorm_gelu_tile<T, G, V, W, R, EXACT, 0>;
+    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 1, PH>
+                                        : layernorm_gelu_tile<T, G, V, W, R, EXACT, 0, PH>;
     return launch(kernel, dim3(static_cast<unsigned>(blocks)), dim3(W * kWave), p.stream,
                   static_cast<const T *>(p.x), static_cast<const T *>(p.w),
                   static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,
                   inv_n, p.eps);
 }
 
+// The phased form of a general one-row-per-group tile (null for others).
+template <typename T, int G, int V, int W, int R, bool EXACT>
+constexpr hipError_t (*phased_run())(const RowProblem &)
+{
+    if constexpr (!EXACT && R == 1)
+        return &layernorm_gelu_tile_run<T, G, V, W, 1, false, true>;
+    else
+        return nullptr;
+}
+
 template <typename T, int G, int V, int W, int R = 1, bool EXACT = false>
 constexpr TileVariant tile()
 {
     return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec, EXACT,
-                       &layernorm_gelu_tile_run<T, G, V, W, R, EXACT>};
+                       &layernorm_gelu_tile_run<T, G, V, W, R, EXACT, false>, false,
+                       phased_run<T, G, V, W, R, EXACT>()};
 }
 template <typename T, int G, int V, int W, int R = 1>
 constexpr TileVariant exact()

@@ -29,18 +29,21 @@
 // layernorm_finish    split-row, second kernel: one workgroup per
 //                     (row, chunk) merges the row's S summaries (each lane a
 //                     subset, then DPP) and writes its chunk.
+// Rows are read and written as aligned 16-byte vectors from whatever offset
+// they start at (RowSpan), when input and output rows share that offset;
+// weight and bias, aligned at column 0, are shifted into each row's phase
+// (load_param).  E = 1 (one element per access) serves the rest.
 #include "rk_device.h"
 #include "rk_internal.h"
 
 namespace rk {
 
-// Summary of one step: v holds U vectors of E elements (already shifted) at
-// vector indices vi0 + u * STRIDE; only elements of the row that are below
-// vend count (padding is 0 after the shift).  `full` promises that all of
-// them count.
+// Summary of one step: v holds U vectors of E elements (already shifted,
+// padding 0) at vector indices j0 + u * STRIDE; only row elements below jend
+// count.  `full` promises that all of them count.
 template <int E, int U, int STRIDE>
-__device__ __forceinline__ Moments step_moments(const float (&v)[U][E], int vi0, int vend,
-                                                RowSplit<E> rs, bool full)
+__device__ __forceinline__ Moments step_moments(const float (&v)[U][E], int j0, int jend,
+                                                RowSpan<E> sp, bool full)
 {
     float s = 0.0f;
 #pragma unroll
@@ -64,10 +67,10 @@ __device__ __forceinline__ Moments step_moments(const float (&v)[U][E], int vi0,
     bool valid[U][E];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int vi = vi0 + u * STRIDE;
+        const int j = j0 + u * STRIDE;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            valid[u][e] = vi < vend && (vi < rs.nfull || (vi == rs.nfull && e < rs.tail));
+            valid[u][e] = j < jend && sp.valid(j, e);
             cnt += valid[u][e] ? 1 : 0;
         }
     }
@@ -86,33 +89,36 @@ __device__ __forceinline__ Moments step_moments(const float (&v)[U][E], int vi0,
     return Moments{n, mean, q};
 }
 
-// Moments of vectors [vbeg, vend) of a row, U vectors per thread per step,
-// software-pipelined (the next step's loads are in flight while this step is
-// summarised).  Returns the thread's own summary.
+// Moments of vectors [jbeg, jend) of a row (aligned base xb), U vectors per
+// thread per step, software-pipelined (the next step's loads are in flight
+// while this step is summarised).  Returns the thread's own summary.
 template <typename T, int E, int W, int U, int CP>
-__device__ __forceinline__ Moments scan_moments(const T *__restrict__ xr, RowSplit<E> rs,
-                                                int vbeg, int vend, float K)
+__device__ __forceinline__ Moments scan_moments(const T *__restrict__ xb, RowSpan<E> sp,
+                                                int jbeg, int jend, float K)
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
-    const int lim = vend < rs.nfull ? vend : rs.nfull;
+    const int fb = sp.full_begin();
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
     Moments st{0.0f, 0.0f, 0.0f};
-    // padding loads as K (an element of the row, exact in T): 0 once shifted
-    RowLoad<T, E, U, NT, CP> cur;
-    cur.issue(xr, vbeg + tid, vend, rs, K, vbeg + NT * U <= lim);
-    for (int base = vbeg; base < vend; base += NT * U) {
-        RowLoad<T, E, U, NT, CP> nxt;
+    SpanLoad<T, E, U, NT, CP> cur;
+    cur.issue(xb, jbeg + tid, jend, full(jbeg));
+    for (int base = jbeg; base < jend; base += NT * U) {
+        SpanLoad<T, E, U, NT, CP> nxt;
         const int next = base + NT * U;
-        if (next < vend)
-            nxt.issue(xr, next + tid, vend, rs, K, next + NT * U <= lim);
+        if (next < jend)
+            nxt.issue(xb, next + tid, jend, full(next));
+        const bool f = full(base);
+        // padding reads as K (an element of the row, exact in T): 0 once shifted
         float v[U][E];
-        cur.finish(v, rs);
+        cur.finish(v, sp, jend, K, f);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[u][e] -= K;
-        st = merge(st, step_moments<E, U, NT>(v, base + tid, vend, rs, base + NT * U <= lim));
+        st = merge(st, step_moments<E, U, NT>(v, base + tid, jend, sp, f));
         cur = nxt;
     }
     return st;
@@ -140,37 +146,41 @@ __device__ __forceinline__ Moments ln_block_merge(Moments st, float *sn, float *
     return st;
 }
 
-// y = GeLU(((x - K) - mean_K) rstd w + b) for vectors [vbeg, vend) of a row.
+// y = GeLU(((x - K) - mean_K) rstd w + b) for vectors [jbeg, jend) of a row
+// (aligned bases xb, yb; w and b by column).
 template <typename T, int E, int W, int U, int GK>
-__device__ __forceinline__ void ln_write_range(const T *__restrict__ xr,
+__device__ __forceinline__ void ln_write_range(const T *__restrict__ xb,
                                                const T *__restrict__ w, const T *__restrict__ b,
-                                               T *__restrict__ yr, RowSplit<E> rs, int vbeg,
-                                               int vend, float K, float mean_k, float rstd)
+                                               T *__restrict__ yb, RowSpan<E> sp, int jbeg,
+                                               int jend, float K, float mean_k, float rstd)
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
-    const int lim = vend < rs.nfull ? vend : rs.nfull;
-    RowLoad<T, E, U, NT> cur;
-    cur.issue(xr, vbeg + tid, vend, rs, 0.0f, vbeg + NT * U <= lim);
-    for (int base = vbeg; base < vend; base += NT * U) {
-        const bool full = base + NT * U <= lim;
-        RowLoad<T, E, U, NT, kCached> wl, bl;
-        wl.issue(w, base + tid, vend, rs, 0.0f, full);
-        bl.issue(b, base + tid, vend, rs, 0.0f, full);
-        RowLoad<T, E, U, NT> nxt;
+    const int fb = sp.full_begin();
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    SpanLoad<T, E, U, NT> cur;
+    cur.issue(xb, jbeg + tid, jend, full(jbeg));
+    for (int base = jbeg; base < jend; base += NT * U) {
+        const bool f = full(base);
+        float wv[U][E], bv[U][E];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            load_param<T, E>(w, base + tid + u * NT, sp.h, sp.n, wv[u], f);
+            load_param<T, E>(b, base + tid + u * NT, sp.h, sp.n, bv[u], f);
+        }
+        SpanLoad<T, E, U, NT> nxt;
         const int next = base + NT * U;
-        if (next < vend)
-            nxt.issue(xr, next + tid, vend, rs, 0.0f, next + NT * U <= lim);
-        float v[U][E], wv[U][E], bv[U][E];
-        cur.finish(v, rs);
-        wl.finish(wv, rs);
-        bl.finish(bv, rs);
+        if (next < jend)
+            nxt.issue(xb, next + tid, jend, full(next));
+        float v[U][E];
+        cur.finish(v, sp, jend, 0.0f, f);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[u][e] = gelu<GK>(fmaf(((v[u][e] - K) - mean_k) * rstd, wv[u][e], bv[u][e]));
-        store_row<T, E, U, NT>(yr, base + tid, vend, rs, v, full);
+        store_span<T, E, U, NT>(yb, base + tid, jend, sp, v, f);
         cur = nxt;
     }
 }
@@ -188,22 +198,14 @@ __global__ __launch_bounds__(W *kWave *RB) void layernorm_stream(
     if (RB > 1 && row >= M)
         return;
     const T *xr = x + row * ldx;
-    const RowSplit<E> rs(N);
-    const int nv = rs.count();
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const T *xb = xr - sp.h;
+    const int nv = sp.count();
     const float K = Elem<T>::to_f32(xr[0]);
-    Moments st = scan_moments<T, E, W, U, kCached>(xr, rs, 0, nv, K);
+    Moments st = scan_moments<T, E, W, U, kCached>(xb, sp, 0, nv, K);
     st = ln_block_merge<W>(st, sn, sm, sq);
     const float rstd = __builtin_amdgcn_rsqf(fmaf(st.m2, inv_n, eps));
-    ln_write_range<T, E, W, U, GK>(xr, w, b, y + row * ldy, rs, 0, nv, K, st.mean, rstd);
-}
-
-// Vector range [vbeg, vend) of chunk s (C elements, a multiple of E).
-template <int E>
-__device__ __forceinline__ void chunk_range(int N, int s, int C, int nv, int &vbeg, int &vend)
-{
-    const int64_t c0 = static_cast<int64_t>(s) * C;
-    vbeg = static_cast<int>(c0 < N ? c0 / E : nv);
-    vend = static_cast<int>(c0 + C < N ? (c0 + C) / E : nv);
+    ln_write_range<T, E, W, U, GK>(xb, w, b, y + row * ldy - sp.h, sp, 0, nv, K, st.mean, rstd);
 }
 
 template <typename T, int E, int W, int U>
@@ -214,13 +216,14 @@ __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restri
     __shared__ float sn[W], sm[W], sq[W];
     const int64_t row = blockIdx.x / S;
     const int s = static_cast<int>(blockIdx.x % S);
-    const RowSplit<E> rs(N);
-    int vbeg, vend;
-    chunk_range<E>(N, s, C, rs.count(), vbeg, vend);
+    const T *xr = x + row * ldx;
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
     // cached: the second kernel reads the chunk again.  Every chunk of a row
     // shifts by the same K, the row's first element.
-    const T *xr = x + row * ldx;
-    Moments st = scan_moments<T, E, W, U, kCached>(xr, rs, vbeg, vend, Elem<T>::to_f32(xr[0]));
+    Moments st = scan_moments<T, E, W, U, kCached>(xr - sp.h, sp, jbeg, jend,
+                                                   Elem<T>::to_f32(xr[0]));
     st = ln_block_merge<W>(st, sn, sm, sq);
     if (threadIdx.x == 0)
         ws[blockIdx.x] = make_float2(st.mean, st.m2);
@@ -234,25 +237,28 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
 {
     const int64_t row = blockIdx.x / S;
     const int s = static_cast<int>(blockIdx.x % S);
+    const T *xr = x + row * ldx;
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
     // Every wave merges the row's S summaries on its own (lane l takes
     // summaries l, l + 64, ...): no LDS, no barrier, and every workgroup of
-    // the row forms the same bits.  A chunk's count follows from N, S and C.
+    // the row forms the same bits.  A chunk's count is that of the row
+    // columns its vectors hold.
     Moments st{0.0f, 0.0f, 0.0f};
     const float2 *wr = ws + row * S;
     for (int i = static_cast<int>(threadIdx.x % kWave); i < S; i += kWave) {
-        const int64_t c0 = static_cast<int64_t>(i) * C;
-        const int64_t cn = c0 >= N ? 0 : (N - c0 < C ? N - c0 : C);
+        int jb, je;
+        chunk_span<E>(sp, i, S, C, jb, je);
+        const int lo = jb * E - sp.h > 0 ? jb * E - sp.h : 0;
+        const int hi = je * E - sp.h < N ? je * E - sp.h : N;
         const float2 p = wr[i];
-        st = merge(st, Moments{static_cast<float>(cn), p.x, p.y});
+        st = merge(st, Moments{static_cast<float>(hi > lo ? hi - lo : 0), p.x, p.y});
     }
     st = wave_merge(st);
     const float rstd = __builtin_amdgcn_rsqf(fmaf(st.m2, inv_n, eps));
 
-    const RowSplit<E> rs(N);
-    int vbeg, vend;
-    chunk_range<E>(N, s, C, rs.count(), vbeg, vend);
-    const T *xr = x + row * ldx;
-    ln_write_range<T, E, W, U, GK>(xr, w, b, y + row * ldy, rs, vbeg, vend,
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
+    ln_write_range<T, E, W, U, GK>(xr - sp.h, w, b, y + row * ldy - sp.h, sp, jbeg, jend,
                                    Elem<T>::to_f32(xr[0]), st.mean, rstd);
 }
 
@@ -267,10 +273,9 @@ constexpr int kSplitW = 4;    // 256 threads per chunk
 // 128 VGPRs of a 1024-thread workgroup.
 constexpr int step_vectors(int E) { return E == 8 ? 2 : 4; }
 
-template <typename T, int E, int W>
+template <typename T, int E, int W, int U = step_vectors(E)>
 hipError_t stream_launch(const RowProblem &p)
 {
-    constexpr int U = step_vectors(E);
     // one-wave rows go four to a workgroup
     constexpr int RB = W == 1 ? 4 : 1;
     auto kernel = p.gelu == RK_GELU_ERF ? layernorm_stream<T, E, W, U, 1, RB>
@@ -285,7 +290,10 @@ hipError_t stream_launch(const RowProblem &p)
 template <typename T, int E>
 hipError_t stream_run(const RowProblem &p)
 {
-    switch (stream_waves((p.N + E - 1) / E, step_vectors(E))) {
+    const int64_t nvec = (p.N + 2 * E - 2) / E;
+    if (nvec <= kShortRowVectors)
+        return stream_launch<T, E, 1, 1>(p);
+    switch (stream_waves(nvec, step_vectors(E))) {
     case 16:
         return stream_launch<T, E, 16>(p);
     case 4:

@@ -7,15 +7,19 @@
 // parts merge with the same rescaling (rk::merge).
 //
 // online_stream    1, 4 or 16 waves per row by the row's length (four
-//                  one-wave rows share a workgroup, otherwise one row each).  Pass 1: every lane folds the blocks it loads
-//                  into its own state; lanes merge through DPP, waves
-//                  through LDS.  Pass 2 re-reads the row and
-//                  writes exp(x - m) / d.  2 reads + 1 write per element.
+//                  one-wave rows share a workgroup, otherwise one row
+//                  each).  Pass 1: every lane folds the blocks it loads into
+//                  its own state; lanes merge through DPP, waves through
+//                  LDS.  Pass 2 re-reads the row and writes exp(x - m) / d.
+//                  2 reads + 1 write per element.
 // online_partials  split-row, first kernel: one workgroup per (row, chunk)
 //                  writes the chunk's (m_s, d_s) to the workspace.
 // online_finish    split-row, second kernel: one workgroup per (row, chunk)
 //                  merges the row's S partials (each lane a subset, then
 //                  DPP) and writes its chunk.
+// Rows are read and written as aligned 16-byte vectors from whatever offset
+// they start at (RowSpan), when input and output rows share that offset;
+// E = 1 (one element per access) serves the rest.
 #include "rk_device.h"
 #include "rk_internal.h"
 
@@ -88,60 +92,67 @@ __device__ __forceinline__ SoftmaxState block_merge(SoftmaxState st, float *sm, 
     return st;
 }
 
-// Vectors [vbeg, vend) of a row (vector index space of RowSplit<E>), U
-// vectors per thread per step, folded into the thread's state.  The scan's
-// loads are cached (CP = kCached) when the same data is read again soon.
+// Vectors [jbeg, jend) of a row (the aligned vectors of RowSpan<E>, base xb),
+// U vectors per thread per step, folded into the thread's state.  The
+// scan's loads are cached (CP = kCached) when the same data is read again
+// soon.
 template <typename T, int E, int W, int U, int CP>
-__device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xr, RowSplit<E> rs,
-                                                   int vbeg, int vend)
+__device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xb, RowSpan<E> sp,
+                                                   int jbeg, int jend)
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
     SoftmaxState st{-INFINITY, 0.0f};
+    // a step is full when all its vectors hold row elements only and lie
+    // below jend: no masks then
+    const int fb = sp.full_begin();
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
     // software pipeline: the next step's loads are in flight while this
     // step's values are folded
-    // a step is full when all its vectors are complete and in range
-    const int lim = vend < rs.nfull ? vend : rs.nfull;
-    RowLoad<T, E, U, NT, CP> cur;
-    cur.issue(xr, vbeg + tid, vend, rs, -INFINITY, vbeg + NT * U <= lim);
-    for (int base = vbeg; base < vend; base += NT * U) {
-        RowLoad<T, E, U, NT, CP> nxt;
+    SpanLoad<T, E, U, NT, CP> cur;
+    cur.issue(xb, jbeg + tid, jend, full(jbeg));
+    for (int base = jbeg; base < jend; base += NT * U) {
+        SpanLoad<T, E, U, NT, CP> nxt;
         const int next = base + NT * U;
-        if (next < vend)
-            nxt.issue(xr, next + tid, vend, rs, -INFINITY, next + NT * U <= lim);
+        if (next < jend)
+            nxt.issue(xb, next + tid, jend, full(next));
         float v[U][E];
-        cur.finish(v, rs);
+        cur.finish(v, sp, jend, -INFINITY, full(base));
         st = fold<T, U, E>(st, v);
         cur = nxt;
     }
     return st;
 }
 
-// Write exp(x - m) / d for vectors [vbeg, vend) of a row.
+// Write exp(x - m) / d for vectors [jbeg, jend) of a row (bases xb, yb).
 template <typename T, int E, int W, int U>
-__device__ __forceinline__ void write_range(const T *__restrict__ xr, T *__restrict__ yr,
-                                            RowSplit<E> rs, int vbeg, int vend, SoftmaxState st)
+__device__ __forceinline__ void write_range(const T *__restrict__ xb, T *__restrict__ yb,
+                                            RowSpan<E> sp, int jbeg, int jend, SoftmaxState st)
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
     const float inv = 1.0f / st.d;
     const float mL = st.m * 1.4426950408889634f;
-    const int lim = vend < rs.nfull ? vend : rs.nfull;
-    RowLoad<T, E, U, NT> cur;
-    cur.issue(xr, vbeg + tid, vend, rs, -INFINITY, vbeg + NT * U <= lim);
-    for (int base = vbeg; base < vend; base += NT * U) {
-        RowLoad<T, E, U, NT> nxt;
+    const int fb = sp.full_begin();
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    SpanLoad<T, E, U, NT> cur;
+    cur.issue(xb, jbeg + tid, jend, full(jbeg));
+    for (int base = jbeg; base < jend; base += NT * U) {
+        SpanLoad<T, E, U, NT> nxt;
         const int next = base + NT * U;
-        if (next < vend)
-            nxt.issue(xr, next + tid, vend, rs, -INFINITY, next + NT * U <= lim);
+        if (next < jend)
+            nxt.issue(xb, next + tid, jend, full(next));
+        const bool f = full(base);
         float v[U][E];
-        cur.finish(v, rs);
+        cur.finish(v, sp, jend, -INFINITY, f);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[u][e] = softmax_exp<T>(v[u][e], st.m, mL) * inv;
-        store_row<T, E, U, NT>(yr, base + tid, vend, rs, v, base + NT * U <= lim);
+        store_span<T, E, U, NT>(yb, base + tid, jend, sp, v, f);
         cur = nxt;
     }
 }
@@ -159,17 +170,17 @@ __global__ __launch_bounds__(W *kWave *RB) void online_stream(const T *__restric
     if (RB > 1 && row >= M)
         return;
     const T *xr = x + row * ldx;
-    T *yr = y + row * ldy;
-    const RowSplit<E> rs(N);
-    const int nv = rs.count();
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const T *xb = xr - sp.h;
+    T *yb = y + row * ldy - sp.h;
+    const int nv = sp.count();
     // pass 1 leaves the row in the caches for pass 2
-    SoftmaxState st = scan_range<T, E, W, U, kCached>(xr, rs, 0, nv);
+    SoftmaxState st = scan_range<T, E, W, U, kCached>(xb, sp, 0, nv);
     st = block_merge<W>(st, sm, sd);
-    write_range<T, E, W, U>(xr, yr, rs, 0, nv, st);
+    write_range<T, E, W, U>(xb, yb, sp, 0, nv, st);
 }
 
-// Partials of chunk s = blockIdx.x % S of row blockIdx.x / S; chunk length C
-// elements (a multiple of E).
+// Partials of chunk s = blockIdx.x % S of row blockIdx.x / S.
 template <typename T, int E, int W, int U>
 __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict__ x, int N,
                                                              int64_t ldx, int S, int C,
@@ -179,14 +190,12 @@ __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict_
     const int64_t row = blockIdx.x / S;
     const int s = static_cast<int>(blockIdx.x % S);
     const T *xr = x + row * ldx;
-    const RowSplit<E> rs(N);
-    const int nv = rs.count();
-    const int64_t c0 = static_cast<int64_t>(s) * C;
-    const int vbeg = static_cast<int>(c0 < N ? c0 / E : nv);
-    const int vend = static_cast<int>(c0 + C < N ? (c0 + C) / E : nv);
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
     // cached: the second kernel reads the chunk again (measured: 15% faster
     // than non-temporal loads here)
-    SoftmaxState st = scan_range<T, E, W, U, kCached>(xr, rs, vbeg, vend);
+    SoftmaxState st = scan_range<T, E, W, U, kCached>(xr - sp.h, sp, jbeg, jend);
     st = block_merge<W>(st, sm, sd);
     if (threadIdx.x == 0)
         ws[blockIdx.x] = make_float2(st.m, st.d);
@@ -212,13 +221,10 @@ __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ 
     st = wave_merge(st);
 
     const T *xr = x + row * ldx;
-    T *yr = y + row * ldy;
-    const RowSplit<E> rs(N);
-    const int nv = rs.count();
-    const int64_t c0 = static_cast<int64_t>(s) * C;
-    const int vbeg = static_cast<int>(c0 < N ? c0 / E : nv);
-    const int vend = static_cast<int>(c0 + C < N ? (c0 + C) / E : nv);
-    write_range<T, E, W, U>(xr, yr, rs, vbeg, vend, st);
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
+    write_range<T, E, W, U>(xr - sp.h, y + row * ldy - sp.h, sp, jbeg, jend, st);
 }
 
 // ------------------------------------------------------------------ host
@@ -229,12 +235,12 @@ constexpr int kStreamU = 4;
 constexpr int kSplitW = 4;    // 256 threads per chunk
 constexpr int kSplitU = 4;
 
-template <typename T, int E, int W>
+template <typename T, int E, int W, int U = kStreamU>
 hipError_t stream_launch(const RowProblem &p)
 {
     // one-wave rows go four to a workgroup
     constexpr int RB = W == 1 ? 4 : 1;
-    return launch(online_stream<T, E, W, kStreamU, RB>,
+    return launch(online_stream<T, E, W, U, RB>,
                   dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB), p.stream, static_cast<const T *>(p.x),
                   static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy);
 }
@@ -243,7 +249,10 @@ hipError_t stream_launch(const RowProblem &p)
 template <typename T, int E>
 hipError_t stream_run(const RowProblem &p)
 {
-    switch (stream_waves((p.N + E - 1) / E, kStreamU)) {
+    const int64_t nvec = (p.N + 2 * E - 2) / E;
+    if (nvec <= kShortRowVectors)
+        return stream_launch<T, E, 1, 1>(p);
+    switch (stream_waves(nvec, kStreamU)) {
     case 16:
         return stream_launch<T, E, 16>(p);
     case 4:

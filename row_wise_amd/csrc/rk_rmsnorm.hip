@@ -11,8 +11,8 @@
 // rmsnorm_tile  the row stays in VGPRs: one HBM read of each input and one
 //               write of each output per element; weight is loaded once per
 //               row group for its R rows.
-// rmsnorm_loop  one workgroup per row, two passes over the row in memory;
-//               any N, any alignment.
+// rmsnorm_loop  1, 4 or 16 waves per row by its length, two passes over the
+//               row in memory; any N, any alignment.
 #include "rk_device.h"
 #include "rk_internal.h"
 
@@ -46,12 +46,17 @@ __device__ __forceinline__ void add_rounded(float (&v)[V][E], const float (&u)[V
     }
 }
 
-template <typename T, int G, int V, int W, int R, bool EXACT, bool RES>
+// PH: rows at any offset past a 16-byte boundary (residual, y and
+// residual_out rows at the same offset), read and written as the aligned
+// vectors that cover them (RowSpan), their ends masked; the weight is shifted
+// into each row's offset as it is used.  One row per row group.
+template <typename T, int G, int V, int W, int R, bool EXACT, bool RES, bool PH>
 __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
     const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w,
     T *__restrict__ y, T *__restrict__ ro, int64_t M, int N, int64_t ldx, int64_t ldr,
     int64_t ldy, int64_t ldo, float inv_n, float eps)
 {
+    static_assert(!PH || (!EXACT && R == 1), "phased rows: general tiles, one row per group");
     constexpr int E = Elem<T>::kVec;
     constexpr int RG = W / G;
     constexpr int L = G * kWave;
@@ -69,18 +74,30 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
     auto row_of = [&](int r) { return (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp; };
 
     RowLoad<T, E, V, L> xl, rl;
+    SpanLoad<T, E, V, L> xs, rsl;  // PH
+    RowSpan<E> sp{0, N};
+    int jend = 0;
     auto issue_row = [&](int r) {
         const int64_t row = row_of(r);
         const bool ok = row < M;
         const int64_t rr = ok ? row : 0;
-        const bool full = EXACT || (ok && slots_full);
-        xl.issue(x + rr * ldx, li, ok ? nv : 0, rs, 0.0f, full);
-        if constexpr (RES)
-            rl.issue(res + rr * ldr, li, ok ? nv : 0, rs, 0.0f, full);
+        if constexpr (PH) {
+            sp.h = row_phase<T, E>(x + rr * ldx);
+            jend = ok ? sp.count() : 0;
+            xs.issue(x + rr * ldx - sp.h, li, jend, false);
+            if constexpr (RES)
+                rsl.issue(res + rr * ldr - sp.h, li, jend, false);
+        } else {
+            const bool full = EXACT || (ok && slots_full);
+            xl.issue(x + rr * ldx, li, ok ? nv : 0, rs, 0.0f, full);
+            if constexpr (RES)
+                rl.issue(res + rr * ldr, li, ok ? nv : 0, rs, 0.0f, full);
+        }
     };
     issue_row(0);
     RowLoad<T, E, V, L, kCached> wl;
-    wl.issue(w, li, nv, rs, 0.0f, slots_full);
+    if constexpr (!PH)
+        wl.issue(w, li, nv, rs, 0.0f, slots_full);
     float wv[V][E];
 
 #pragma unroll
@@ -92,16 +109,24 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
         const bool store_full = EXACT || (row_ok && slots_full);
 
         float v[V][E];
-        xl.finish(v, rs);
+        if constexpr (PH)
+            xs.finish(v, sp, jend, 0.0f, false);
+        else
+            xl.finish(v, rs);
         if constexpr (RES) {
             float u[V][E];
-            rl.finish(u, rs);
+            if constexpr (PH)
+                rsl.finish(u, sp, jend, 0.0f, false);
+            else
+                rl.finish(u, rs);
             add_rounded<T>(v, u);
         }
         if (r + 1 < R)
             issue_row(r + 1);
         if constexpr (RES) {
-            if (!EXACT || row_ok)
+            if constexpr (PH)
+                store_span<T, E, V, L>(ro + rr * ldo - sp.h, li, jend, sp, v, false);
+            else if (!EXACT || row_ok)
                 store_row<T, E, V, L>(ro + rr * ldo, li, vend, rs, v, store_full);
         }
 
@@ -124,36 +149,55 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
         }
         const float inv = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
 
-        if (r == 0)
+        if constexpr (PH) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                load_param<T, E>(w, k * L + li, sp.h, N, wv[k], false);
+        } else if (r == 0) {
             wl.finish(wv, rs);
+        }
 #pragma unroll
         for (int k = 0; k < V; ++k)
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[k][e] = v[k][e] * inv * wv[k][e];
-        if (!EXACT || row_ok)
+        if constexpr (PH)
+            store_span<T, E, V, L>(y + rr * ldy - sp.h, li, jend, sp, v, false);
+        else if (!EXACT || row_ok)
             store_row<T, E, V, L>(y + rr * ldy, li, vend, rs, v, store_full);
     }
 }
 
-template <typename T, int G, int V, int W, int R, bool EXACT, bool RES>
+template <typename T, int G, int V, int W, int R, bool EXACT, bool RES, bool PH>
 static hipError_t rmsnorm_tile_run(const RowProblem &p)
 {
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG * R - 1) / (RG * R);
     const float inv_n = static_cast<float>(1.0 / p.N);
-    return launch(rmsnorm_tile<T, G, V, W, R, EXACT, RES>, dim3(static_cast<unsigned>(blocks)),
+    return launch(rmsnorm_tile<T, G, V, W, R, EXACT, RES, PH>,
+                  dim3(static_cast<unsigned>(blocks)),
                   dim3(W * kWave), p.stream, static_cast<const T *>(p.x),
                   static_cast<const T *>(p.r), static_cast<const T *>(p.w),
                   static_cast<T *>(p.y), static_cast<T *>(p.ro), p.M, p.N, p.ldx, p.ldr, p.ldy,
                   p.ldo, inv_n, p.eps);
 }
 
+// The phased form of a general one-row-per-group tile (null for others).
+template <typename T, bool RES, int G, int V, int W, int R, bool EXACT>
+constexpr hipError_t (*phased_run())(const RowProblem &)
+{
+    if constexpr (!EXACT && R == 1)
+        return &rmsnorm_tile_run<T, G, V, W, 1, false, RES, true>;
+    else
+        return nullptr;
+}
+
 template <typename T, bool RES, int G, int V, int W, int R = 1, bool EXACT = false>
 constexpr TileVariant tile()
 {
     return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec, EXACT,
-                       &rmsnorm_tile_run<T, G, V, W, R, EXACT, RES>};
+                       &rmsnorm_tile_run<T, G, V, W, R, EXACT, RES, false>, false,
+                       phased_run<T, RES, G, V, W, R, EXACT>()};
 }
 template <typename T, bool RES, int G, int V, int W, int R = 1>
 constexpr TileVariant exact()
@@ -212,40 +256,82 @@ const TileVariant *rmsnorm_variants(rk_dtype dtype, bool residual, int *count)
 
 // ------------------------------------------------------- looping kernel
 
-template <typename T, int E, int W, int U, bool RES>
-__global__ __launch_bounds__(W *kWave) void rmsnorm_loop(
-    const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w,
-    T *__restrict__ y, T *__restrict__ ro, int N, int64_t ldx, int64_t ldr, int64_t ldy,
-    int64_t ldo, float inv_n, float eps)
-{
-    constexpr int NT = W * kWave;
-    __shared__ float red[W];
-    const int64_t row = blockIdx.x;
-    const T *xr = x + row * ldx;
-    const T *rr = RES ? res + row * ldr : nullptr;
-    const RowSplit<E> rs(N);
-    const int nv = rs.count();
-    const int tid = static_cast<int>(threadIdx.x);
+// Row v = x (or x + residual, rounded) for U vectors per thread: the loads
+// of one step, in flight together (x, and the residual with RES).
+template <typename T, int E, int U, int NT, int CP, bool RES>
+struct RmsStep {
+    SpanLoad<T, E, U, NT, CP> xl, rl;
 
-    float q = 0.0f;
-    for (int base = 0; base < nv; base += NT * U) {
-        float v[U][E];
-        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
+    __device__ __forceinline__ void issue(const T *__restrict__ xb, const T *__restrict__ rb,
+                                          int j0, int jend, bool full)
+    {
+        xl.issue(xb, j0, jend, full);
+        if constexpr (RES)
+            rl.issue(rb, j0, jend, full);
+    }
+
+    __device__ __forceinline__ void finish(float (&v)[U][E], RowSpan<E> sp, int jend,
+                                           bool full) const
+    {
+        xl.finish(v, sp, jend, 0.0f, full);
         if constexpr (RES) {
             float u[U][E];
-            load_row<T, E, U, NT>(rr, base + tid, nv, rs, 0.0f, u);
-            add_rounded<T>(v, u);
+            rl.finish(u, sp, jend, 0.0f, full);
+            add_rounded<T>(v, u);  // padding stays 0
         }
+    }
+};
+
+// One row per W waves, RB rows per workgroup (several only for W == 1,
+// where no barrier is taken).  Pass 1 (cached loads) sums v^2; pass 2
+// re-reads the row, stores residual_out (RES) and y = v inv w.  Rows are
+// read as aligned vectors from their own phase (RowSpan): x, residual, y and
+// residual_out share it, the weight is shifted into it.
+template <typename T, int E, int W, int U, bool RES, int RB>
+__global__ __launch_bounds__(W *kWave *RB) void rmsnorm_loop(
+    const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w,
+    T *__restrict__ y, T *__restrict__ ro, int64_t M, int N, int64_t ldx, int64_t ldr,
+    int64_t ldy, int64_t ldo, float inv_n, float eps)
+{
+    static_assert(RB == 1 || W == 1, "several rows per workgroup only with one wave each");
+    constexpr int NT = W * kWave;
+    __shared__ float red[W];
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RB + threadIdx.x / NT;
+    if (RB > 1 && row >= M)
+        return;
+    const T *xr = x + row * ldx;
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const T *xb = xr - sp.h;
+    const T *rb = RES ? res + row * ldr - sp.h : nullptr;
+    const int nv = sp.count();
+    const int tid = static_cast<int>(threadIdx.x % NT);
+    const int fb = sp.full_begin();
+    const int fe = sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+
+    float q = 0.0f;
+    {
+        RmsStep<T, E, U, NT, kCached, RES> cur;
+        cur.issue(xb, rb, tid, nv, full(0));
+        for (int base = 0; base < nv; base += NT * U) {
+            RmsStep<T, E, U, NT, kCached, RES> nxt;
+            const int next = base + NT * U;
+            if (next < nv)
+                nxt.issue(xb, rb, next + tid, nv, full(next));
+            float v[U][E];
+            cur.finish(v, sp, nv, full(base));
 #pragma unroll
-        for (int i = 0; i < U; ++i)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                q = fmaf(v[i][e], v[i][e], q);
+                for (int e = 0; e < E; ++e)
+                    q = fmaf(v[u][e], v[u][e], q);
+            cur = nxt;
+        }
     }
     q = wave_sum(q);
     if constexpr (W > 1) {
-        if (tid % kWave == 0)
-            red[tid / kWave] = q;
+        if (threadIdx.x % kWave == 0)
+            red[threadIdx.x / kWave] = q;
         __syncthreads();
         q = red[0];
 #pragma unroll
@@ -254,37 +340,66 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_loop(
     }
     const float inv = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
 
+    T *yb = y + row * ldy - sp.h;
+    T *ob = RES ? ro + row * ldo - sp.h : nullptr;
+    RmsStep<T, E, U, NT, kStreaming, RES> cur;
+    cur.issue(xb, rb, tid, nv, full(0));
     for (int base = 0; base < nv; base += NT * U) {
-        float v[U][E], wv[U][E];
-        load_row<T, E, U, NT>(xr, base + tid, nv, rs, 0.0f, v);
-        if constexpr (RES) {
-            float u[U][E];
-            load_row<T, E, U, NT>(rr, base + tid, nv, rs, 0.0f, u);
-            add_rounded<T>(v, u);
-            store_row<T, E, U, NT>(ro + row * ldo, base + tid, nv, rs, v);
-        }
-        load_row<T, E, U, NT, kCached>(w, base + tid, nv, rs, 0.0f, wv);
+        const bool f = full(base);
+        float wv[U][E];
 #pragma unroll
-        for (int i = 0; i < U; ++i)
+        for (int u = 0; u < U; ++u)
+            load_param<T, E>(w, base + tid + u * NT, sp.h, N, wv[u], f);
+        RmsStep<T, E, U, NT, kStreaming, RES> nxt;
+        const int next = base + NT * U;
+        if (next < nv)
+            nxt.issue(xb, rb, next + tid, nv, full(next));
+        float v[U][E];
+        cur.finish(v, sp, nv, f);
+        if constexpr (RES)
+            store_span<T, E, U, NT>(ob, base + tid, nv, sp, v, f);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                v[i][e] = v[i][e] * inv * wv[i][e];
-        store_row<T, E, U, NT>(y + row * ldy, base + tid, nv, rs, v);
+                v[u][e] = v[u][e] * inv * wv[u][e];
+        store_span<T, E, U, NT>(yb, base + tid, nv, sp, v, f);
+        cur = nxt;
     }
 }
 
 namespace {
-constexpr int kLoopW = 4;
-constexpr int kLoopU = 4;
 
+// Vectors per thread per step: 64 bytes of row (two bf16 vectors), as in
+// the LayerNorm streaming kernel.
+constexpr int loop_vectors(int E) { return E == 8 ? 2 : 4; }
+
+template <typename T, int E, bool RES, int W, int U = loop_vectors(E)>
+hipError_t loop_launch(const RowProblem &p)
+{
+    constexpr int RB = W == 1 ? 4 : 1;  // one-wave rows go four to a workgroup
+    return launch(rmsnorm_loop<T, E, W, U, RES, RB>,
+                  dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB),
+                  p.stream, static_cast<const T *>(p.x), static_cast<const T *>(p.r),
+                  static_cast<const T *>(p.w), static_cast<T *>(p.y), static_cast<T *>(p.ro),
+                  p.M, p.N, p.ldx, p.ldr, p.ldy, p.ldo, static_cast<float>(1.0 / p.N), p.eps);
+}
+
+// 1, 4 or 16 waves per row by the row's length.
 template <typename T, int E, bool RES>
 hipError_t loop_run(const RowProblem &p)
 {
-    return launch(rmsnorm_loop<T, E, kLoopW, kLoopU, RES>, dim3(static_cast<unsigned>(p.M)),
-                  dim3(kLoopW * kWave), p.stream, static_cast<const T *>(p.x),
-                  static_cast<const T *>(p.r), static_cast<const T *>(p.w),
-                  static_cast<T *>(p.y), static_cast<T *>(p.ro), p.N, p.ldx, p.ldr, p.ldy, p.ldo,
-                  static_cast<float>(1.0 / p.N), p.eps);
+    const int64_t nvec = (p.N + 2 * E - 2) / E;
+    if (nvec <= kShortRowVectors)
+        return loop_launch<T, E, RES, 1, 1>(p);
+    switch (stream_waves(nvec, loop_vectors(E))) {
+    case 16:
+        return loop_launch<T, E, RES, 16>(p);
+    case 4:
+        return loop_launch<T, E, RES, 4>(p);
+    default:
+        return loop_launch<T, E, RES, 1>(p);
+    }
 }
 
 template <bool RES>
@@ -294,6 +409,7 @@ hipError_t loop_dispatch(const RowProblem &p, bool vectorized)
         return vectorized ? loop_run<float, 4, RES>(p) : loop_run<float, 1, RES>(p);
     return vectorized ? loop_run<bf16_t, 8, RES>(p) : loop_run<bf16_t, 1, RES>(p);
 }
+
 }  // namespace
 
 hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, bool vectorized)

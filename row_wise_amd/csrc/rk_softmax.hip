@@ -18,11 +18,15 @@ namespace rk {
 // is a column of its row: loads and stores need no masks and nothing is
 // padded.  Rows past M (the last workgroup) then read row 0 and store
 // nothing.
-template <typename T, int G, int V, int W, bool EXACT>
+// PH: rows at any offset past a 16-byte boundary (the output's rows at the
+// same offset), read and written as the aligned vectors that cover them
+// (RowSpan), their ends masked.
+template <typename T, int G, int V, int W, bool EXACT, bool PH>
 __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x,
                                                           T *__restrict__ y, int64_t M, int N,
                                                           int64_t ldx, int64_t ldy)
 {
+    static_assert(!(EXACT && PH), "a phased row is never an exact fit");
     constexpr int E = Elem<T>::kVec;
     constexpr int RG = W / G;    // row groups per workgroup
     constexpr int L = G * kWave; // lanes per row
@@ -47,7 +51,17 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
     const bool full = EXACT || (row_ok && V * L <= rs.nfull);
 
     float v[V][E];
-    load_row<T, E, V, L>(xr, li, vend, rs, -INFINITY, v, full);
+    RowSpan<E> sp{0, N};
+    int jend = 0;
+    if constexpr (PH) {
+        sp.h = row_phase<T, E>(xr);
+        jend = row_ok ? sp.count() : 0;
+        SpanLoad<T, E, V, L> l;
+        l.issue(xr - sp.h, li, jend, false);
+        l.finish(v, sp, jend, -INFINITY, false);
+    } else {
+        load_row<T, E, V, L>(xr, li, vend, rs, -INFINITY, v, full);
+    }
 
     float m = -INFINITY;
 #pragma unroll
@@ -104,7 +118,9 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
 #pragma unroll
         for (int e = 0; e < E; ++e)
             v[k][e] *= inv;
-    if (EXACT) {
+    if constexpr (PH) {
+        store_span<T, E, V, L>(yr - sp.h, li, jend, sp, v, false);
+    } else if (EXACT) {
         if (row_ok)
             store_row<T, E, V, L>(yr, li, vend, rs, v, true);
     } else {
@@ -112,23 +128,34 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
     }
 }
 
-template <typename T, int G, int V, int W, bool EXACT>
+template <typename T, int G, int V, int W, bool EXACT, bool PH>
 static hipError_t softmax_tile_run(const RowProblem &p)
 {
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG - 1) / RG;
-    return launch(softmax_tile<T, G, V, W, EXACT>, dim3(static_cast<unsigned>(blocks)),
+    return launch(softmax_tile<T, G, V, W, EXACT, PH>, dim3(static_cast<unsigned>(blocks)),
                   dim3(W * kWave), p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y),
                   p.M, p.N, p.ldx, p.ldy);
 }
 
-// A general variant (any N up to its capacity) and an exact one (N equal to
-// its capacity).
+// A general variant (any N up to its capacity, and rows at any offset up to
+// capacity - E + 1) and an exact one (N equal to its capacity).
+// The phased form of a general tile (null for an exact one).
+template <typename T, int G, int V, int W, bool EXACT>
+constexpr hipError_t (*phased_run())(const RowProblem &)
+{
+    if constexpr (!EXACT)
+        return &softmax_tile_run<T, G, V, W, false, true>;
+    else
+        return nullptr;
+}
+
 template <typename T, int G, int V, int W, bool EXACT = false>
 constexpr TileVariant tile()
 {
     return TileVariant{G, V, W, 1, G * V * kWave * Elem<T>::kVec, EXACT,
-                       &softmax_tile_run<T, G, V, W, EXACT>};
+                       &softmax_tile_run<T, G, V, W, EXACT, false>, false,
+                       phased_run<T, G, V, W, EXACT>()};
 }
 template <typename T, int G, int V, int W>
 constexpr TileVariant exact()

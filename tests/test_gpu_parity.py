@@ -154,6 +154,44 @@ def test_layernorm_gelu_variant(dtype, index, N):
     assert rel_err_floor1(y, oracle.layernorm_gelu(base[:, :N], w, b, EPS)) <= tol_of(dtype)
 
 
+def _phased_cases(op):
+    """General one-row-per-group tiles on rows at every offset: odd N, so row
+    r starts r N elements into an aligned buffer; N + E - 1 fits the tile."""
+    cases = []
+    for dtype, code in ((torch.float32, rk.RK_F32), (torch.bfloat16, rk.RK_BF16)):
+        E = 4 if code == rk.RK_F32 else 8
+        for v in rk.variants(op, code):
+            if v["exact"] or v["rows_per_group"] != 1:
+                continue
+            cap = v["max_n"]
+            for N in sorted({cap - E + 1, (cap // 2 + 1) | 1, 3}):
+                cases.append((dtype, v["index"], N))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,index,N", _phased_cases(rk.RK_OP_SOFTMAX),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_softmax_variant_phased(dtype, index, N):
+    M = 37
+    x = rowgen.randn(M, N, seed=N * 13 + index, scale=4.0, dtype=dtype)
+    y = rk.rk__softmax_variant(index, x.to(DEV))
+    assert rel_err_softmax(y, oracle.softmax(x)) <= tol_of(dtype)
+
+
+@pytest.mark.parametrize("dtype,index,N", _phased_cases(rk.RK_OP_LAYERNORM_GELU),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_layernorm_gelu_variant_phased(dtype, index, N):
+    M = 37
+    g = torch.Generator().manual_seed(N * 19 + index)
+    x = (torch.randn(M, N, generator=g) + 5.0).to(dtype)
+    w, b = rowgen.ln_params(N, g, dtype)
+    for gelu in ("tanh", "erf"):
+        y = rk.rk__layernorm_gelu_variant(index, x.to(DEV), w.to(DEV), b.to(DEV), EPS, gelu=gelu)
+        ref = (oracle.layernorm_gelu(x, w, b, EPS) if gelu == "tanh"
+               else oracle.layernorm_gelu_ex(x, w, b, EPS, "erf"))
+        assert rel_err_floor1(y, ref) <= tol_of(dtype), gelu
+
+
 # ------------------------------------------------------ shapes and layouts
 
 EDGE_N = [1, 2, 3, 63, 64, 65, 767, 769, 1000, 1025, 4095, 4097, 16384, 16385, 40000]
@@ -252,6 +290,69 @@ def test_stream_widths(dtype, N):
             y = (rk.rk__layernorm_gelu_variant(-1, xd, wd, bd, EPS) if name == "aligned"
                  else rk.rk_layernorm_gelu(xd, wd, bd, EPS))
             assert rel_err_floor1(y, ref_l) <= tol_of(dtype), name
+
+
+PHASE_N = [1, 3, 5, 301, 1001, 3001, 12001, 40001, 100001]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+@pytest.mark.parametrize("N", PHASE_N)
+def test_phased_rows(dtype, N):
+    """Odd N: row r starts r N elements into an aligned buffer, so each row
+    sits at its own offset past a 16-byte boundary; input and output share it
+    row for row, and the rows-in-memory kernels read and write them as aligned
+    vectors with masked ends (streaming and split)."""
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(N + 1), dtype)
+    wd, bd = w.to(DEV), b.to(DEV)
+    for M in (1, 3, 70):
+        x = rowgen.randn(M, N, seed=M * 7 + N, scale=3.0, dtype=dtype)
+        x[::2] += 30.0  # LayerNorm rows far from zero
+        xd = x.to(DEV)
+        ref_s = oracle.softmax(x)
+        ref_l = oracle.layernorm_gelu(x, w, b, EPS)
+        say(f"phased {key(dtype)} M={M} N={N}")
+        assert rel_err_softmax(rk.rk_softmax(xd), ref_s) <= tol_of(dtype)
+        assert rel_err_floor1(rk.rk_layernorm_gelu(xd, wd, bd, EPS), ref_l) <= tol_of(dtype)
+        for S in (2, 3, 0):
+            y = rk.rk_online_softmax(xd, num_splits=S)
+            assert rel_err_softmax(y, ref_s) <= tol_of(dtype), S
+            y = rk.rk_layernorm_gelu_ex(xd, wd, bd, EPS, num_splits=S)
+            assert rel_err_floor1(y, ref_l) <= tol_of(dtype), S
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+@pytest.mark.parametrize("off", [1, 3])
+def test_shared_offset_and_in_place(dtype, off):
+    """Every row at the same non-zero offset (input and output views `off`
+    elements into their buffers, aligned pitch), then in place over odd N."""
+    M, N = 37, 4096
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(off), dtype)
+    wd, bd = w.to(DEV), b.to(DEV)
+    flat = rowgen.randn(1, M * N + off, seed=off + 50, scale=2.0, dtype=dtype)[0]
+    x = flat[off:].view(M, N)
+    xd = flat.to(DEV)[off:].view(M, N)
+    canary = -7.0
+    obuf = torch.full((M * N + off + 8,), canary, dtype=dtype, device=DEV)
+    out = obuf[off:off + M * N].view(M, N)
+    rk.rk_softmax(xd, out=out)
+    assert rel_err_softmax(out, oracle.softmax(x)) <= tol_of(dtype)
+    rk.rk_layernorm_gelu_ex(xd, wd, bd, EPS, num_splits=4, out=out)
+    assert rel_err_floor1(out, oracle.layernorm_gelu(x, w, b, EPS)) <= tol_of(dtype)
+    host = obuf.cpu()
+    assert torch.all(host[:off] == canary) and torch.all(host[off + M * N:] == canary)
+    # in place, odd N
+    M, N = 33, 2999
+    x = rowgen.randn(M, N, seed=off + 60, scale=2.0, dtype=dtype)
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(off + 1), dtype)
+    xd = x.to(DEV)
+    rk.rk_softmax(xd, out=xd)
+    assert rel_err_softmax(xd, oracle.softmax(x)) <= tol_of(dtype)
+    xd = x.to(DEV)
+    rk.rk_layernorm_gelu(xd, w.to(DEV), b.to(DEV), EPS, out=xd)
+    assert rel_err_floor1(xd, oracle.layernorm_gelu(x, w, b, EPS)) <= tol_of(dtype)
+    xd = x.to(DEV)
+    rk.rk_online_softmax(xd, num_splits=5, out=xd)
+    assert rel_err_softmax(xd, oracle.softmax(x)) <= tol_of(dtype)
 
 
 def test_in_place():

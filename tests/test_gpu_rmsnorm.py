@@ -138,6 +138,39 @@ def test_residual_rmsnorm_variant(dtype, index, N):
     check_residual(y, ro, base[:, :N], rbase[:, :N], w, dtype)
 
 
+def _phased_cases(op):
+    """General one-row-per-group tiles on rows at every offset (odd N)."""
+    cases = []
+    for dtype, code in ((torch.float32, rk.RK_F32), (torch.bfloat16, rk.RK_BF16)):
+        E = 4 if code == rk.RK_F32 else 8
+        for v in rk.variants(op, code):
+            if v["exact"] or v["rows_per_group"] != 1:
+                continue
+            cap = v["max_n"]
+            for N in sorted({cap - E + 1, (cap // 2 + 1) | 1, 3}):
+                cases.append((dtype, v["index"], N))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,index,N", _phased_cases(rk.RK_OP_RMSNORM), ids=_ids)
+def test_rmsnorm_variant_phased(dtype, index, N):
+    M = 37
+    x = rowgen.randn(M, N, seed=N * 11 + index, scale=2.0, dtype=dtype)
+    w = weight(N, N + index + 1, dtype)
+    y = rk.rk__rmsnorm_variant(index, x.to(DEV), w.to(DEV), EPS)
+    assert rel_err(y, oracle.rmsnorm(x, w, EPS)) <= tol_of(dtype)
+
+
+@pytest.mark.parametrize("dtype,index,N", _phased_cases(rk.RK_OP_RESIDUAL_RMSNORM), ids=_ids)
+def test_residual_rmsnorm_variant_phased(dtype, index, N):
+    M = 37
+    x = rowgen.randn(M, N, seed=N * 7 + index, dtype=dtype)
+    res = rowgen.randn(M, N, seed=N * 7 + index + 1, dtype=dtype)
+    w = weight(N, N + index + 2, dtype)
+    y, ro = rk.rk__residual_rmsnorm_variant(index, x.to(DEV), res.to(DEV), w.to(DEV), EPS)
+    check_residual(y, ro, x, res, w, dtype, ("phased", index, N))
+
+
 # ------------------------------------------------------ shapes and layouts
 
 EDGE_N = [1, 2, 3, 63, 64, 65, 767, 769, 1000, 1025, 4095, 4097, 16384, 16385, 40000]
@@ -212,7 +245,53 @@ def test_misaligned_and_forced_generic(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=key)
-@pytest.mark.parametrize("N", [768, 4096, 1000, 40000])
+@pytest.mark.parametrize("N", [1, 3, 5, 301, 1001, 3001, 12001, 40001, 100001])
+def test_phased_rows(dtype, N):
+    """Odd N: every row at its own offset past a 16-byte boundary, shared by
+    x, residual, y and residual_out row for row: the looping kernel reads
+    and writes aligned vectors with masked ends and shifts the weight into
+    each row's offset."""
+    w = weight(N, N + 2, dtype)
+    wd = w.to(DEV)
+    for M in (1, 3, 70):
+        x = rowgen.randn(M, N, seed=M * 5 + N, scale=2.0, dtype=dtype)
+        res = rowgen.randn(M, N, seed=M * 5 + N + 1, dtype=dtype)
+        say(f"rms phased {key(dtype)} M={M} N={N}")
+        assert rel_err(rk.rk_rmsnorm(x.to(DEV), wd, EPS), oracle.rmsnorm(x, w, EPS)) <= tol_of(dtype)
+        y, ro = rk.rk_residual_rmsnorm(x.to(DEV), res.to(DEV), wd, EPS)
+        check_residual(y, ro, x, res, w, dtype, ("phased", M, N))
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+def test_shared_offset(dtype):
+    """All four matrices viewed 3 elements into their buffers (aligned pitch):
+    every row at the same non-zero offset; the buffers' ends stay untouched."""
+    M, N, off = 29, 2048, 3
+    w = weight(N, 91, dtype)
+    canary = -5.0
+
+    def at_offset(t):
+        buf = torch.full((M * N + off + 8,), canary, dtype=dtype, device=DEV)
+        buf[off:off + M * N] = t.reshape(-1).to(DEV)
+        return buf, buf[off:off + M * N].view(M, N)
+
+    x = rowgen.randn(M, N, seed=92, dtype=dtype)
+    res = rowgen.randn(M, N, seed=93, dtype=dtype)
+    _, xd = at_offset(x)
+    _, rd = at_offset(res)
+    ybuf, yd = at_offset(torch.zeros(M, N, dtype=dtype))
+    obuf, od = at_offset(torch.zeros(M, N, dtype=dtype))
+    rk.rk_rmsnorm(xd, w.to(DEV), EPS, out=yd)
+    assert rel_err(yd, oracle.rmsnorm(x, w, EPS)) <= tol_of(dtype)
+    rk.rk_residual_rmsnorm(xd, rd, w.to(DEV), EPS, out=yd, residual_out=od)
+    check_residual(yd, od, x, res, w, dtype, "offset")
+    for buf in (ybuf, obuf):
+        host = buf.cpu()
+        assert torch.all(host[:off] == canary) and torch.all(host[off + M * N:] == canary)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("N", [768, 4096, 1000, 40000, 3001])
 def test_in_place(dtype, N):
     M = 64
     x = rowgen.randn(M, N, seed=N + 7, dtype=dtype)
