@@ -695,60 +695,79 @@ __device__ __forceinline__ void shift_in(const float (&lo)[E], const float (&hi)
 // The E elements of a per-column parameter p[n] (16-byte aligned, cached)
 // that meet vector j of a row at phase h: p[j*E - h + e], 0 outside [0, n).
 // Two aligned loads straddle the shift; each reads a 16-byte block that
-// holds an element of p.
-// `full` promises that vector j holds row elements only: no checks then.
+// holds an element of p.  issue() starts the loads, finish() waits, unpacks
+// and shifts.  `full` promises that vector j holds row elements only: no
+// checks then.
+template <typename T, int E>
+struct ParamLoad {
+    typedef typename RawVec<T, E>::type R;
+    R qh, ql;
+
+    // The block at column j*E and the one before it.  A block is read only
+    // if it holds an element of p: lanes of a masked step may sit past the
+    // row.
+    __device__ __forceinline__ void issue(const T *__restrict__ p, int j, int h, int n, bool full)
+    {
+        const R *pv = reinterpret_cast<const R *>(p);
+        qh = R{};
+        ql = R{};
+        if (full || j * E < n)
+            qh = pv[j];
+        if (h != 0 && (full || (j >= 1 && (j - 1) * E < n)))
+            ql = pv[j - 1];
+    }
+
+    __device__ __forceinline__ void finish(float (&out)[E], int j, int h, int n, bool full) const
+    {
+        float hi[E], lo[E];
+        unpack<T, E>(qh, hi);
+        unpack<T, E>(ql, lo);
+        // element e comes from lo[E - h + e] (e < h) or hi[e - h]; h is
+        // uniform over the wave, so one case runs
+        switch (h) {
+        case 1:
+            shift_in<1>(lo, hi, out);
+            break;
+        case 2:
+            shift_in<2>(lo, hi, out);
+            break;
+        case 3:
+            shift_in<3>(lo, hi, out);
+            break;
+        case 4:
+            shift_in<4>(lo, hi, out);
+            break;
+        case 5:
+            shift_in<5>(lo, hi, out);
+            break;
+        case 6:
+            shift_in<6>(lo, hi, out);
+            break;
+        case 7:
+            shift_in<7>(lo, hi, out);
+            break;
+        default:
+            shift_in<0>(lo, hi, out);
+            break;
+        }
+        // columns outside [0, n) read as 0 (the elements of a block that are
+        // not p's, or a block that was not loaded)
+        if (!full) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (static_cast<unsigned>(j * E + e - h) >= static_cast<unsigned>(n))
+                    out[e] = 0.0f;
+        }
+    }
+};
+
 template <typename T, int E>
 __device__ __forceinline__ void load_param(const T *__restrict__ p, int j, int h, int n,
                                            float (&out)[E], bool full)
 {
-    typedef typename RawVec<T, E>::type R;
-    const R *pv = reinterpret_cast<const R *>(p);
-    float hi[E], lo[E];
-    R qh = R{}, ql = R{};
-    // a block is read only if it holds an element of p (lanes of a masked
-    // step may sit past the row)
-    if (full || j * E < n)
-        qh = pv[j];
-    if (h != 0 && (full || (j >= 1 && (j - 1) * E < n)))
-        ql = pv[j - 1];
-    unpack<T, E>(qh, hi);
-    unpack<T, E>(ql, lo);
-    // element e comes from lo[E - h + e] (e < h) or hi[e - h]; h is uniform
-    // over the wave, so one case runs
-    switch (h) {
-    case 1:
-        shift_in<1>(lo, hi, out);
-        break;
-    case 2:
-        shift_in<2>(lo, hi, out);
-        break;
-    case 3:
-        shift_in<3>(lo, hi, out);
-        break;
-    case 4:
-        shift_in<4>(lo, hi, out);
-        break;
-    case 5:
-        shift_in<5>(lo, hi, out);
-        break;
-    case 6:
-        shift_in<6>(lo, hi, out);
-        break;
-    case 7:
-        shift_in<7>(lo, hi, out);
-        break;
-    default:
-        shift_in<0>(lo, hi, out);
-        break;
-    }
-    // columns outside [0, n) read as 0 (the elements of a block that are
-    // not p's, or a block that was not loaded)
-    if (!full) {
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (static_cast<unsigned>(j * E + e - h) >= static_cast<unsigned>(n))
-                out[e] = 0.0f;
-    }
+    ParamLoad<T, E> l;
+    l.issue(p, j, h, n, full);
+    l.finish(out, j, h, n, full);
 }
 
 }  // namespace rk

@@ -58,6 +58,12 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     // previous one is reduced.
     RowLoad<T, E, V, L> xl;
     SpanLoad<T, E, V, L> xs;  // PH
+    // PH: the weight and bias blocks of small tiles are loaded with the row
+    // (two blocks each per vector); larger tiles load them as they are used
+    // (measured: loading them early there costs more in registers than it
+    // saves in latency)
+    constexpr bool kParamAhead = PH && V <= 2;
+    ParamLoad<T, E> wp[kParamAhead ? V : 1], bp[kParamAhead ? V : 1];
     RowSpan<E> sp{0, N};
     int jend = 0;
     if constexpr (PH) {
@@ -67,6 +73,13 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         sp.h = row_phase<T, E>(xr);
         jend = ok ? sp.count() : 0;
         xs.issue(xr - sp.h, li, jend, false);
+        if constexpr (kParamAhead) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                wp[k].issue(w, k * L + li, sp.h, N, false);
+                bp[k].issue(b, k * L + li, sp.h, N, false);
+            }
+        }
     } else {
         const int64_t row = row_of(0);
         const bool ok = row < M;
@@ -166,7 +179,10 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
 #pragma unroll
             for (int k = 0; k < V; ++k) {
                 float wk[E], bk[E];
-                if constexpr (PH) {
+                if constexpr (kParamAhead) {
+                    wp[k].finish(wk, k * L + li, sp.h, N, false);
+                    bp[k].finish(bk, k * L + li, sp.h, N, false);
+                } else if constexpr (PH) {
                     load_param<T, E>(w, k * L + li, sp.h, N, wk, false);
                     load_param<T, E>(b, k * L + li, sp.h, N, bk, false);
                 } else {

@@ -96,8 +96,17 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
     };
     issue_row(0);
     RowLoad<T, E, V, L, kCached> wl;
-    if constexpr (!PH)
+    // PH: the weight blocks of small tiles are loaded with the row (two per
+    // vector); larger tiles load them as they are used
+    constexpr bool kParamAhead = PH && V <= 2;
+    ParamLoad<T, E> wp[kParamAhead ? V : 1];
+    if constexpr (kParamAhead) {
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            wp[k].issue(w, k * L + li, sp.h, N, false);
+    } else if constexpr (!PH) {
         wl.issue(w, li, nv, rs, 0.0f, slots_full);
+    }
     float wv[V][E];
 
 #pragma unroll
@@ -149,7 +158,11 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
         }
         const float inv = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
 
-        if constexpr (PH) {
+        if constexpr (kParamAhead) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                wp[k].finish(wv[k], k * L + li, sp.h, N, false);
+        } else if constexpr (PH) {
 #pragma unroll
             for (int k = 0; k < V; ++k)
                 load_param<T, E>(w, k * L + li, sp.h, N, wv[k], false);
