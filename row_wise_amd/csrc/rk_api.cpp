@@ -585,13 +585,11 @@ rk_status row_reduce_entry(const void *x, void *out, int64_t M, int64_t N, int64
     rk_status st = check_reduce(x, out, M, N, ldx, dtype);
     if (st != RK_OK || M == 0)
         return st;
-    const int es = elem_size(dtype);
-    const bool aligned = aligned16(x) && (ldx * es) % 16 == 0;
     int threads = 0;
-    if (!grid_ok(row_reduce_blocks(M, N, dtype, aligned, &threads), threads))
+    if (!grid_ok(row_reduce_blocks(M, N, dtype, &threads), threads))
         return RK_ERR_UNSUPPORTED;
     const RowProblem p = make_problem(x, out, nullptr, nullptr, M, N, ldx, 1, 0.0f, dtype, stream);
-    return hip_status(row_reduce_run(p, op, aligned));
+    return hip_status(row_reduce_run(p, op));
 }
 
 }  // namespace
@@ -621,13 +619,16 @@ RK_EXPORT rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_
     RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
     p.gelu = gelu;
     const int es = elem_size(dtype);
+    // a contiguous buffer is one flat array, read as aligned vectors from
+    // its offset when the output shares it
     const bool contiguous = M == 1 || (ldx == N && ldy == N);
-    const bool flat = contiguous && aligned16(x) && aligned16(y);
-    if (flat)
+    const bool same_base_phase =
+        (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 == 0;
+    if (contiguous && same_base_phase)
         return hip_status(gelu_run(p, true, true));
     if (!grid_ok(M, 256))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(gelu_run(p, false, rows_aligned(x, y, ldx, ldy, es)));
+    return hip_status(gelu_run(p, false, same_phase(x, ldx, y, ldy, es)));
 }
 
 // ------------------------------------------------------------ attention

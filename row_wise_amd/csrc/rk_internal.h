@@ -113,9 +113,9 @@ hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, void 
                                bool vectorized);
 hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, bool vectorized);
 enum { RK_REDUCE_SUM = 0, RK_REDUCE_MAX = 1 };
-hipError_t row_reduce_run(const RowProblem &p, int op, bool vectorized);
+hipError_t row_reduce_run(const RowProblem &p, int op);
 // Workgroups (and threads per workgroup) row_reduce_run launches.
-int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, bool vectorized, int *threads);
+int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, int *threads);
 // flat: x and y contiguous and 16-byte aligned, processed as one buffer.
 hipError_t gelu_run(const RowProblem &p, bool flat, bool vectorized);
 // Query rows per workgroup of the attention kernel.

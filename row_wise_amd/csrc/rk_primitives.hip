@@ -7,9 +7,12 @@
 //             A row group of G waves loops over the row with U vectors per
 //             lane in flight, keeps U partial results per lane, then reduces
 //             them, the wave (DPP) and the G waves (LDS).  One HBM read per
-//             element; the M results are the only writes.
+//             element; the M results are the only writes.  A row at any
+//             offset is read as the aligned 16-byte vectors that cover it
+//             (RowSpan), its ends masked.
 // gelu_flat   y = GeLU(x) elementwise over a contiguous buffer: 16-byte
-//             vectors, U per thread per step.
+//             vectors, U per thread per step, from whatever offset the
+//             buffer starts at (the output at the same offset).
 // gelu_rows   the same for rows with a pitch: one workgroup per row.
 #include "rk_device.h"
 #include "rk_internal.h"
@@ -42,9 +45,13 @@ __global__ __launch_bounds__(W *kWave) void row_reduce(const T *__restrict__ x, 
     const int64_t row = static_cast<int64_t>(blockIdx.x) * RG + grp;
     const bool ok = row < M;
     const T *xr = x + (ok ? row : 0) * ldx;
-    const RowSplit<E> rs(N);
-    const int vend = ok ? rs.count() : 0;
-    const int lim = vend < rs.nfull ? vend : rs.nfull;
+    // the row as the aligned vectors that cover it, whatever its offset
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const T *xb = xr - sp.h;
+    const int jend = ok ? sp.count() : 0;
+    const int fb = sp.full_begin();
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + L * U <= fe; };
 
     float acc[U];
 #pragma unroll
@@ -52,15 +59,15 @@ __global__ __launch_bounds__(W *kWave) void row_reduce(const T *__restrict__ x, 
         acc[u] = kPad;
     // software pipeline: the next step's loads are in flight while this step
     // is reduced
-    RowLoad<T, E, U, L> cur;
-    cur.issue(xr, li, vend, rs, kPad, L * U <= lim);
-    for (int base = 0; base < vend; base += L * U) {
-        RowLoad<T, E, U, L> nxt;
+    SpanLoad<T, E, U, L> cur;
+    cur.issue(xb, li, jend, full(0));
+    for (int base = 0; base < jend; base += L * U) {
+        SpanLoad<T, E, U, L> nxt;
         const int next = base + L * U;
-        if (next < vend)
-            nxt.issue(xr, next + li, vend, rs, kPad, next + L * U <= lim);
+        if (next < jend)
+            nxt.issue(xb, next + li, jend, full(next));
         float v[U][E];
-        cur.finish(v, rs);
+        cur.finish(v, sp, jend, kPad, full(base));
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -99,41 +106,46 @@ static hipError_t reduce_launch(const RowProblem &p)
                   p.M, p.N, p.ldx);
 }
 
-// Row-group size by row length in vectors: one wave per row up to 1024
-// vectors (16 per lane), four waves up to 8192, sixteen beyond.
-template <typename T, int E, int OP>
+// Row-group size by row length in vectors (phase included): one wave per
+// row up to 1024 vectors (16 per lane), four waves up to 8192, sixteen
+// beyond.
+constexpr int64_t kReduceWave1 = 1024;
+constexpr int64_t kReduceWave4 = 8192;
+
+inline int64_t reduce_vectors(int64_t N, int E) { return (N + 2 * E - 2) / E; }
+
+template <typename T, int OP>
 static hipError_t reduce_dispatch(const RowProblem &p)
 {
+    constexpr int E = Elem<T>::kVec;
     constexpr int U = 16 / E > 4 ? 4 : (16 / E < 2 ? 2 : 16 / E);
-    const int64_t nv = (p.N + E - 1) / E;
-    if (nv <= 1024)
+    const int64_t nv = reduce_vectors(p.N, E);
+    if (nv <= kReduceWave1)
         return reduce_launch<T, E, 1, 4, U, OP>(p);
-    if (nv <= 8192)
+    if (nv <= kReduceWave4)
         return reduce_launch<T, E, 4, 4, U, OP>(p);
     return reduce_launch<T, E, 16, 16, U, OP>(p);
 }
 
-int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, bool vectorized, int *threads)
+int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, int *threads)
 {
-    const int E = vectorized ? vec_elems(dtype) : 1;
-    const int64_t nv = (N + E - 1) / E;
-    const int rows_per_block = nv <= 1024 ? 4 : 1;
-    *threads = nv <= 8192 ? 256 : 1024;
+    const int64_t nv = reduce_vectors(N, vec_elems(dtype));
+    const int rows_per_block = nv <= kReduceWave1 ? 4 : 1;
+    *threads = nv <= kReduceWave4 ? 256 : 1024;
     return (M + rows_per_block - 1) / rows_per_block;
 }
 
 template <int OP>
-static hipError_t reduce_run(const RowProblem &p, bool vectorized)
+static hipError_t reduce_run(const RowProblem &p)
 {
     if (p.dtype == RK_F32)
-        return vectorized ? reduce_dispatch<float, 4, OP>(p) : reduce_dispatch<float, 1, OP>(p);
-    return vectorized ? reduce_dispatch<bf16_t, 8, OP>(p) : reduce_dispatch<bf16_t, 1, OP>(p);
+        return reduce_dispatch<float, OP>(p);
+    return reduce_dispatch<bf16_t, OP>(p);
 }
 
-hipError_t row_reduce_run(const RowProblem &p, int op, bool vectorized)
+hipError_t row_reduce_run(const RowProblem &p, int op)
 {
-    return op == RK_REDUCE_SUM ? reduce_run<RK_REDUCE_SUM>(p, vectorized)
-                               : reduce_run<RK_REDUCE_MAX>(p, vectorized);
+    return op == RK_REDUCE_SUM ? reduce_run<RK_REDUCE_SUM>(p) : reduce_run<RK_REDUCE_MAX>(p);
 }
 
 // ----------------------------------------------------------- elementwise
@@ -141,13 +153,22 @@ hipError_t row_reduce_run(const RowProblem &p, int op, bool vectorized)
 constexpr int kGeluThreads = 256;
 constexpr int kGeluU = 4;
 
+// y = GeLU(x) over n contiguous elements whose first sits h elements past a
+// 16-byte boundary, y at the same offset: the aligned vectors of x - h, U per
+// thread per step, grid-stride.  Only the first and the last vector can hold
+// elements outside the buffer; their loads stay in a block that holds one of
+// its elements, and their stores go element by element.
 template <typename T, int GK>
 __global__ __launch_bounds__(kGeluThreads) void gelu_flat(const T *__restrict__ x,
-                                                          T *__restrict__ y, int64_t n)
+                                                          T *__restrict__ y, int64_t n, int h)
 {
     constexpr int E = Elem<T>::kVec;
     typedef typename RawVec<T, E>::type R;
-    const int64_t nvec = n / E;
+    const T *xb = x - h;
+    T *yb = y - h;
+    const int64_t nvec = (h + n + E - 1) / E;
+    const int64_t full_lo = h != 0 ? 1 : 0;
+    const int64_t full_hi = (h + n) / E;
     const int64_t step = static_cast<int64_t>(gridDim.x) * kGeluThreads * kGeluU;
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * kGeluThreads * kGeluU + threadIdx.x;
          base < nvec; base += step) {
@@ -156,7 +177,7 @@ __global__ __launch_bounds__(kGeluThreads) void gelu_flat(const T *__restrict__ 
         for (int u = 0; u < kGeluU; ++u) {
             const int64_t i = base + u * kGeluThreads;
             if (i < nvec)
-                q[u] = ld<kStreaming>(reinterpret_cast<const R *>(x) + i);
+                q[u] = ld<kStreaming>(reinterpret_cast<const R *>(xb + i * E));
         }
 #pragma unroll
         for (int u = 0; u < kGeluU; ++u) {
@@ -167,39 +188,51 @@ __global__ __launch_bounds__(kGeluThreads) void gelu_flat(const T *__restrict__ 
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     v[e] = gelu<GK>(v[e]);
-                store_vec<T, E, kStreaming>(y + i * E, v);
+                if (i >= full_lo && i < full_hi) {
+                    store_vec<T, E, kStreaming>(yb + i * E, v);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int64_t c = i * E + e - h;
+                        if (c >= 0 && c < n)
+                            y[c] = Elem<T>::from_f32(v[e]);
+                    }
+                }
             }
         }
     }
-    // the last n % E elements
-    const int64_t t = nvec * E + static_cast<int64_t>(blockIdx.x) * kGeluThreads + threadIdx.x;
-    if (t < n && blockIdx.x == 0)
-        y[t] = Elem<T>::from_f32(gelu<GK>(Elem<T>::to_f32(x[t])));
 }
 
+// The same for rows with a pitch: one workgroup per row, each row read and
+// written as the aligned vectors that cover it (RowSpan; output rows at the
+// same offsets), or element by element (E = 1).
 template <typename T, int E, int GK>
 __global__ __launch_bounds__(kGeluThreads) void gelu_rows(const T *__restrict__ x,
                                                           T *__restrict__ y, int N, int64_t ldx,
                                                           int64_t ldy)
 {
+    constexpr int NT = kGeluThreads;
     const int64_t row = blockIdx.x;
     const T *xr = x + row * ldx;
-    T *yr = y + row * ldy;
-    const RowSplit<E> rs(N);
-    const int nv = rs.count();
-    const int lim = rs.nfull;
-    for (int base = 0; base < nv; base += kGeluThreads * kGeluU) {
-        const bool full = base + kGeluThreads * kGeluU <= lim;
+    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const T *xb = xr - sp.h;
+    T *yb = y + row * ldy - sp.h;
+    const int nv = sp.count();
+    const int fb = sp.full_begin();
+    const int fe = sp.full_end();
+    const int tid = static_cast<int>(threadIdx.x);
+    for (int base = 0; base < nv; base += NT * kGeluU) {
+        const bool full = base >= fb && base + NT * kGeluU <= fe;
+        SpanLoad<T, E, kGeluU, NT> l;
+        l.issue(xb, base + tid, nv, full);
         float v[kGeluU][E];
-        load_row<T, E, kGeluU, kGeluThreads>(xr, base + static_cast<int>(threadIdx.x), nv, rs,
-                                              0.0f, v, full);
+        l.finish(v, sp, nv, 0.0f, full);
 #pragma unroll
         for (int u = 0; u < kGeluU; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[u][e] = gelu<GK>(v[u][e]);
-        store_row<T, E, kGeluU, kGeluThreads>(yr, base + static_cast<int>(threadIdx.x), nv, rs, v,
-                                              full);
+        store_span<T, E, kGeluU, NT>(yb, base + tid, nv, sp, v, full);
     }
 }
 
@@ -209,14 +242,13 @@ template <typename T, int GK>
 hipError_t flat_run(const RowProblem &p, int64_t n)
 {
     constexpr int E = Elem<T>::kVec;
+    const int h = static_cast<int>((reinterpret_cast<uintptr_t>(p.x) % 16) / sizeof(T));
     const int64_t per_block = int64_t{kGeluThreads} * kGeluU;
-    int64_t blocks = (n / E + per_block - 1) / per_block;
-    if (blocks < 1)
-        blocks = 1;  // the tail
+    int64_t blocks = ((h + n + E - 1) / E + per_block - 1) / per_block;
     if (blocks > 65536)
         blocks = 65536;  // grid-stride beyond
     return launch(gelu_flat<T, GK>, dim3(static_cast<unsigned>(blocks)), dim3(kGeluThreads),
-                  p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), n);
+                  p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), n, h);
 }
 
 template <typename T, int E, int GK>

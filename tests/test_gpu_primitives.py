@@ -132,6 +132,39 @@ def test_gelu_flat_and_rows(dtype, gelu):
     assert rel_err_floor1(xi, ref_fn(xb.double().numpy())) <= tol_of(dtype)
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("off", [1, 3, 5])
+def test_gelu_shared_offset(dtype, off):
+    """Input and output `off` elements into their buffers: the flat kernel
+    (contiguous) and the row kernel (odd pitch) read and write aligned
+    vectors from that offset; the bytes around the output stay untouched."""
+    canary = -12288.0
+    for M, N, ld in ((1, 7, 7), (5, 1001, 1001), (1, 100003, 100003), (37, 999, 1003)):
+        x = rowgen.randn(M, ld, seed=off * 100 + N, scale=4.0, dtype=dtype)
+        xbuf = torch.zeros(M * ld + off + 8, dtype=dtype, device=DEV)
+        xbuf[off:off + M * ld] = x.reshape(-1).to(DEV)
+        xd = xbuf[off:off + M * ld].view(M, ld)[:, :N]
+        ybuf = torch.full((M * ld + off + 8,), canary, dtype=dtype, device=DEV)
+        yd = ybuf[off:off + M * ld].view(M, ld)[:, :N]
+        say(f"gelu offset {off} {key(dtype)} M={M} N={N} ld={ld}")
+        rk.rk_gelu(xd, out=yd)
+        assert rel_err_floor1(yd, oracle.gelu_tanh(x[:, :N].double().numpy())) <= tol_of(dtype)
+        host = ybuf.cpu().float()
+        assert torch.all(host[:off] == canary) and torch.all(host[off + M * ld:] == canary)
+        assert torch.all(host[off:off + M * ld].view(M, ld)[:, N:] == canary)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("off", [0, 1, 3, 7])
+def test_reductions_at_offsets(dtype, off):
+    """Rows at every offset (odd N, and a view `off` elements into its
+    buffer): loads as aligned vectors with masked ends."""
+    for M, N in ((1, 1), (9, 3), (70, 301), (33, 4097), (5, 70001)):
+        flat = rowgen.randn(1, M * N + off, seed=off * 7 + N, dtype=dtype)[0]
+        check_reductions(flat[off:].view(M, N), flat.to(DEV)[off:].view(M, N), dtype,
+                         ("offset", off, M, N))
+
+
 def test_gelu_extremes():
     z = torch.tensor([[0.0, -0.0, 1e-30, -1e-30, 10.0, 20.0, 80.0, -10.0, -30.0, -80.0, 3e38,
                        -3e38]], dtype=torch.float32)
