@@ -174,18 +174,33 @@ bool layernorm_vectorized(const RowProblem &p)
     return softmax_vectorized(p) && aligned16(p.w) && aligned16(p.b);
 }
 
+// Access mode of the kernels that keep rows in memory.
+RowIo softmax_io(const RowProblem &p)
+{
+    if (rows_aligned(p.x, p.y, p.ldx, p.ldy, elem_size(p.dtype)))
+        return kIoAligned;
+    return softmax_vectorized(p) ? kIoPhased : kIoElement;
+}
+
+RowIo layernorm_io(const RowProblem &p)
+{
+    if (!aligned16(p.w) || !aligned16(p.b))
+        return kIoElement;
+    return softmax_io(p);
+}
+
 rk_status softmax_generic(const RowProblem &p)
 {
     if (!grid_ok(p.M, kStreamThreads))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(online_stream_run(p, softmax_vectorized(p)));
+    return hip_status(online_stream_run(p, softmax_io(p)));
 }
 
 rk_status layernorm_generic(const RowProblem &p)
 {
     if (!grid_ok(p.M, kStreamThreads))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(layernorm_stream_run(p, layernorm_vectorized(p)));
+    return hip_status(layernorm_stream_run(p, layernorm_io(p)));
 }
 
 bool valid_gelu(rk_gelu_kind g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
@@ -358,11 +373,18 @@ bool rmsnorm_vectorized(const RowProblem &p, bool residual)
     return ok;
 }
 
+RowIo rmsnorm_io(const RowProblem &p, bool residual)
+{
+    if (rmsnorm_aligned(p, residual))
+        return kIoAligned;
+    return rmsnorm_vectorized(p, residual) ? kIoPhased : kIoElement;
+}
+
 rk_status rmsnorm_generic(const RowProblem &p, bool residual)
 {
     if (!grid_ok(p.M, kLoopThreads))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(rmsnorm_loop_run(p, residual, rmsnorm_vectorized(p, residual)));
+    return hip_status(rmsnorm_loop_run(p, residual, rmsnorm_io(p, residual)));
 }
 
 rk_status rmsnorm_dispatch(const RowProblem &p, bool residual, int32_t index, bool forced)
@@ -444,7 +466,8 @@ RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t
     const int32_t S = num_splits == 0 ? auto_splits(M, N) : num_splits;
     if (S <= 1)
         return softmax_generic(p);
-    const bool vec = softmax_vectorized(p);
+    const RowIo io = softmax_io(p);
+    const bool vec = io != kIoElement;
 
     const int es = elem_size(dtype);
     st = check_workspace(workspace, workspace_bytes, rk_online_softmax_workspace_bytes(M, N, S), M,
@@ -454,7 +477,7 @@ RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t
     const int64_t chunk = split_chunk(N, S, vec ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
-    return hip_status(online_split_run(p, S, static_cast<int>(chunk), workspace, vec));
+    return hip_status(online_split_run(p, S, static_cast<int>(chunk), workspace, io));
 }
 
 RK_EXPORT int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
@@ -510,11 +533,12 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
                           matrix_span(weight, 1, N, N, es), matrix_span(bias, 1, N, N, es)});
     if (st != RK_OK)
         return st;
-    const bool vec = layernorm_vectorized(p);
+    const RowIo io = layernorm_io(p);
+    const bool vec = io != kIoElement;
     const int64_t chunk = split_chunk(N, S, vec ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
-    return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), workspace, vec));
+    return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), workspace, io));
 }
 
 RK_EXPORT rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias, void *y,
@@ -625,10 +649,15 @@ RK_EXPORT rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_
     const bool same_base_phase =
         (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 == 0;
     if (contiguous && same_base_phase)
-        return hip_status(gelu_run(p, true, true));
+        return hip_status(gelu_run(p, true, kIoAligned));
     if (!grid_ok(M, 256))
         return RK_ERR_UNSUPPORTED;
-    return hip_status(gelu_run(p, false, same_phase(x, ldx, y, ldy, es)));
+    RowIo io = kIoElement;
+    if (rows_aligned(x, y, ldx, ldy, es))
+        io = kIoAligned;
+    else if (same_phase(x, ldx, y, ldy, es))
+        io = kIoPhased;
+    return hip_status(gelu_run(p, false, io));
 }
 
 // ------------------------------------------------------------ attention

@@ -576,11 +576,13 @@ struct RowSpan {
 };
 
 // Phase of a row's first element.  The same for every lane of a wave (a
-// wave works on one row), so it is read into a scalar register.
-template <typename T, int E>
+// wave works on one row), so it is read into a scalar register.  PH = false
+// promises aligned rows: the phase is then the constant 0 and the code that
+// handles other phases folds away.
+template <typename T, int E, bool PH = true>
 __device__ __forceinline__ int row_phase(const T *row)
 {
-    if constexpr (E == 1)
+    if constexpr (E == 1 || !PH)
         return 0;
     else
         return __builtin_amdgcn_readfirstlane(

@@ -104,20 +104,26 @@ const TileVariant *softmax_variants(rk_dtype dtype, int *count);
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count);
 const TileVariant *rmsnorm_variants(rk_dtype dtype, bool residual, int *count);
 
+// How the kernels that keep rows in memory access them: aligned 16-byte
+// vectors (every row starts on a 16-byte boundary), aligned vectors from each
+// row's own offset (rows and outputs share their offsets; RowSpan), or one
+// element at a time.
+enum RowIo { kIoElement = 0, kIoAligned = 1, kIoPhased = 2 };
+
 // Generic paths (any alignment, any N).
-hipError_t online_stream_run(const RowProblem &p, bool vectorized);
+hipError_t online_stream_run(const RowProblem &p, RowIo io);
 hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
-                            bool vectorized);
-hipError_t layernorm_stream_run(const RowProblem &p, bool vectorized);
+                            RowIo io);
+hipError_t layernorm_stream_run(const RowProblem &p, RowIo io);
 hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
-                               bool vectorized);
-hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, bool vectorized);
+                               RowIo io);
+hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, RowIo io);
 enum { RK_REDUCE_SUM = 0, RK_REDUCE_MAX = 1 };
 hipError_t row_reduce_run(const RowProblem &p, int op);
 // Workgroups (and threads per workgroup) row_reduce_run launches.
 int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, int *threads);
 // flat: x and y contiguous and 16-byte aligned, processed as one buffer.
-hipError_t gelu_run(const RowProblem &p, bool flat, bool vectorized);
+hipError_t gelu_run(const RowProblem &p, bool flat, RowIo io);
 // Query rows per workgroup of the attention kernel.
 int attention_block_rows();
 hipError_t flash_attention_run(const AttentionProblem &p);

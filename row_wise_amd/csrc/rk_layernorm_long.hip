@@ -163,18 +163,25 @@ __device__ __forceinline__ void ln_write_range(const T *__restrict__ xb,
     cur.issue(xb, jbeg + tid, jend, full(jbeg));
     for (int base = jbeg; base < jend; base += NT * U) {
         const bool f = full(base);
-        float wv[U][E], bv[U][E];
+        // weight and bias, the next step's row and this step's row are all in
+        // flight before the first wait
+        ParamLoad<T, E> wl[U], bl[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            load_param<T, E>(w, base + tid + u * NT, sp.h, sp.n, wv[u], f);
-            load_param<T, E>(b, base + tid + u * NT, sp.h, sp.n, bv[u], f);
+            wl[u].issue(w, base + tid + u * NT, sp.h, sp.n, f);
+            bl[u].issue(b, base + tid + u * NT, sp.h, sp.n, f);
         }
         SpanLoad<T, E, U, NT> nxt;
         const int next = base + NT * U;
         if (next < jend)
             nxt.issue(xb, next + tid, jend, full(next));
-        float v[U][E];
+        float v[U][E], wv[U][E], bv[U][E];
         cur.finish(v, sp, jend, 0.0f, f);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wl[u].finish(wv[u], base + tid + u * NT, sp.h, sp.n, f);
+            bl[u].finish(bv[u], base + tid + u * NT, sp.h, sp.n, f);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -186,8 +193,9 @@ __device__ __forceinline__ void ln_write_range(const T *__restrict__ xb,
 }
 
 // RB rows per workgroup, W waves each; several rows only for W == 1, where
-// no barrier is taken and a wave past the last row may leave at once.
-template <typename T, int E, int W, int U, int GK, int RB>
+// no barrier is taken and a wave past the last row may leave at once.  PH:
+// rows at any offset (else every row starts on a 16-byte boundary).
+template <typename T, int E, int W, int U, int GK, int RB, bool PH>
 __global__ __launch_bounds__(W *kWave *RB) void layernorm_stream(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
     T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(W *kWave *RB) void layernorm_stream(
     if (RB > 1 && row >= M)
         return;
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     const T *xb = xr - sp.h;
     const int nv = sp.count();
     const float K = Elem<T>::to_f32(xr[0]);
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(W *kWave *RB) void layernorm_stream(
     ln_write_range<T, E, W, U, GK>(xb, w, b, y + row * ldy - sp.h, sp, 0, nv, K, st.mean, rstd);
 }
 
-template <typename T, int E, int W, int U>
+template <typename T, int E, int W, int U, bool PH>
 __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restrict__ x, int N,
                                                                 int64_t ldx, int S, int C,
                                                                 float2 *__restrict__ ws)
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restri
     const int64_t row = blockIdx.x / S;
     const int s = static_cast<int>(blockIdx.x % S);
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
     // cached: the second kernel reads the chunk again.  Every chunk of a row
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restri
         ws[blockIdx.x] = make_float2(st.mean, st.m2);
 }
 
-template <typename T, int E, int W, int U, int GK>
+template <typename T, int E, int W, int U, int GK, bool PH>
 __global__ __launch_bounds__(W *kWave) void layernorm_finish(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
     T *__restrict__ y, int N, int64_t ldx, int64_t ldy, int S, int C, float inv_n, float eps,
@@ -238,7 +246,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
     const int64_t row = blockIdx.x / S;
     const int s = static_cast<int>(blockIdx.x % S);
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     // Every wave merges the row's S summaries on its own (lane l takes
     // summaries l, l + 64, ...): no LDS, no barrier, and every workgroup of
     // the row forms the same bits.  A chunk's count is that of the row
@@ -273,13 +281,13 @@ constexpr int kSplitW = 4;    // 256 threads per chunk
 // 128 VGPRs of a 1024-thread workgroup.
 constexpr int step_vectors(int E) { return E == 8 ? 2 : 4; }
 
-template <typename T, int E, int W, int U = step_vectors(E)>
+template <typename T, int E, bool PH, int W, int U = step_vectors(E)>
 hipError_t stream_launch(const RowProblem &p)
 {
     // one-wave rows go four to a workgroup
     constexpr int RB = W == 1 ? 4 : 1;
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_stream<T, E, W, U, 1, RB>
-                                        : layernorm_stream<T, E, W, U, 0, RB>;
+    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_stream<T, E, W, U, 1, RB, PH>
+                                        : layernorm_stream<T, E, W, U, 0, RB, PH>;
     return launch(kernel, dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB),
                   p.stream, static_cast<const T *>(p.x), static_cast<const T *>(p.w),
                   static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,
@@ -287,57 +295,79 @@ hipError_t stream_launch(const RowProblem &p)
 }
 
 // One workgroup per row, 1 to 16 waves by the row's length.
-template <typename T, int E>
+template <typename T, int E, bool PH>
 hipError_t stream_run(const RowProblem &p)
 {
     const int64_t nvec = (p.N + 2 * E - 2) / E;
     if (nvec <= kShortRowVectors)
-        return stream_launch<T, E, 1, 1>(p);
+        return stream_launch<T, E, PH, 1, 1>(p);
     switch (stream_waves(nvec, step_vectors(E))) {
     case 16:
-        return stream_launch<T, E, 16>(p);
+        return stream_launch<T, E, PH, 16>(p);
     case 4:
-        return stream_launch<T, E, 4>(p);
+        return stream_launch<T, E, PH, 4>(p);
     default:
-        return stream_launch<T, E, 1>(p);
+        return stream_launch<T, E, PH, 1>(p);
     }
 }
 
-template <typename T, int E>
+// Split chunks: two vectors per thread per step for both formats (fp32 at
+// four measured 12% slower on 64 rows of 262144: the 256-thread workgroups
+// then hold more registers than they gain in loads in flight).
+constexpr int split_vectors(int E) { return E == 1 ? 4 : 2; }
+
+template <typename T, int E, bool PH>
 hipError_t split_run(const RowProblem &p, int S, int C, void *ws)
 {
-    constexpr int U = step_vectors(E);
+    constexpr int U = split_vectors(E);
     const dim3 grid(static_cast<unsigned>(p.M * S));
-    hipError_t err = launch(layernorm_partials<T, E, kSplitW, U>, grid,
+    hipError_t err = launch(layernorm_partials<T, E, kSplitW, U, PH>, grid,
                             dim3(kSplitW * kWave), p.stream, static_cast<const T *>(p.x), p.N,
                             p.ldx, S, C, static_cast<float2 *>(ws));
     if (err != hipSuccess)
         return err;
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_finish<T, E, kSplitW, U, 1>
-                                        : layernorm_finish<T, E, kSplitW, U, 0>;
+    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_finish<T, E, kSplitW, U, 1, PH>
+                                        : layernorm_finish<T, E, kSplitW, U, 0, PH>;
     return launch(kernel, grid, dim3(kSplitW * kWave), p.stream, static_cast<const T *>(p.x),
                   static_cast<const T *>(p.w), static_cast<const T *>(p.b),
                   static_cast<T *>(p.y), p.N, p.ldx, p.ldy, S, C, static_cast<float>(1.0 / p.N),
                   p.eps, static_cast<const float2 *>(ws));
 }
 
+template <typename T>
+hipError_t stream_io(const RowProblem &p, RowIo io)
+{
+    constexpr int E = Elem<T>::kVec;
+    if (io == kIoAligned)
+        return stream_run<T, E, false>(p);
+    if (io == kIoPhased)
+        return stream_run<T, E, true>(p);
+    return stream_run<T, 1, false>(p);
+}
+
+template <typename T>
+hipError_t split_io(const RowProblem &p, int S, int C, void *ws, RowIo io)
+{
+    constexpr int E = Elem<T>::kVec;
+    if (io == kIoAligned)
+        return split_run<T, E, false>(p, S, C, ws);
+    if (io == kIoPhased)
+        return split_run<T, E, true>(p, S, C, ws);
+    return split_run<T, 1, false>(p, S, C, ws);
+}
+
 }  // namespace
 
-hipError_t layernorm_stream_run(const RowProblem &p, bool vectorized)
+hipError_t layernorm_stream_run(const RowProblem &p, RowIo io)
 {
-    if (p.dtype == RK_F32)
-        return vectorized ? stream_run<float, 4>(p) : stream_run<float, 1>(p);
-    return vectorized ? stream_run<bf16_t, 8>(p) : stream_run<bf16_t, 1>(p);
+    return p.dtype == RK_F32 ? stream_io<float>(p, io) : stream_io<bf16_t>(p, io);
 }
 
 hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
-                               bool vectorized)
+                               RowIo io)
 {
-    if (p.dtype == RK_F32)
-        return vectorized ? split_run<float, 4>(p, splits, chunk, workspace)
-                          : split_run<float, 1>(p, splits, chunk, workspace);
-    return vectorized ? split_run<bf16_t, 8>(p, splits, chunk, workspace)
-                      : split_run<bf16_t, 1>(p, splits, chunk, workspace);
+    return p.dtype == RK_F32 ? split_io<float>(p, splits, chunk, workspace, io)
+                             : split_io<bf16_t>(p, splits, chunk, workspace, io);
 }
 
 }  // namespace rk

@@ -158,8 +158,9 @@ __device__ __forceinline__ void write_range(const T *__restrict__ xb, T *__restr
 }
 
 // RB rows per workgroup, W waves each; several rows only for W == 1, where
-// no barrier is taken and a wave past the last row may leave at once.
-template <typename T, int E, int W, int U, int RB>
+// no barrier is taken and a wave past the last row may leave at once.  PH:
+// rows at any offset (else every row starts on a 16-byte boundary).
+template <typename T, int E, int W, int U, int RB, bool PH>
 __global__ __launch_bounds__(W *kWave *RB) void online_stream(const T *__restrict__ x,
                                                                T *__restrict__ y, int64_t M,
                                                                int N, int64_t ldx, int64_t ldy)
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(W *kWave *RB) void online_stream(const T *__restric
     if (RB > 1 && row >= M)
         return;
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     const T *xb = xr - sp.h;
     T *yb = y + row * ldy - sp.h;
     const int nv = sp.count();
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(W *kWave *RB) void online_stream(const T *__restric
 }
 
 // Partials of chunk s = blockIdx.x % S of row blockIdx.x / S.
-template <typename T, int E, int W, int U>
+template <typename T, int E, int W, int U, bool PH>
 __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict__ x, int N,
                                                              int64_t ldx, int S, int C,
                                                              float2 *__restrict__ ws)
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict_
     const int64_t row = blockIdx.x / S;
     const int s = static_cast<int>(blockIdx.x % S);
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
     // cached: the second kernel reads the chunk again (measured: 15% faster
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict_
         ws[blockIdx.x] = make_float2(st.m, st.d);
 }
 
-template <typename T, int E, int W, int U>
+template <typename T, int E, int W, int U, bool PH>
 __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ x,
                                                            T *__restrict__ y, int N, int64_t ldx,
                                                            int64_t ldy, int S, int C,
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ 
     st = wave_merge(st);
 
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
     write_range<T, E, W, U>(xr - sp.h, y + row * ldy - sp.h, sp, jbeg, jend, st);
@@ -235,64 +236,80 @@ constexpr int kStreamU = 4;
 constexpr int kSplitW = 4;    // 256 threads per chunk
 constexpr int kSplitU = 4;
 
-template <typename T, int E, int W, int U = kStreamU>
+template <typename T, int E, bool PH, int W, int U = kStreamU>
 hipError_t stream_launch(const RowProblem &p)
 {
     // one-wave rows go four to a workgroup
     constexpr int RB = W == 1 ? 4 : 1;
-    return launch(online_stream<T, E, W, U, RB>,
+    return launch(online_stream<T, E, W, U, RB, PH>,
                   dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB), p.stream, static_cast<const T *>(p.x),
                   static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy);
 }
 
 // One workgroup per row, 1 to 16 waves by the row's length.
-template <typename T, int E>
+template <typename T, int E, bool PH>
 hipError_t stream_run(const RowProblem &p)
 {
     const int64_t nvec = (p.N + 2 * E - 2) / E;
     if (nvec <= kShortRowVectors)
-        return stream_launch<T, E, 1, 1>(p);
+        return stream_launch<T, E, PH, 1, 1>(p);
     switch (stream_waves(nvec, kStreamU)) {
     case 16:
-        return stream_launch<T, E, 16>(p);
+        return stream_launch<T, E, PH, 16>(p);
     case 4:
-        return stream_launch<T, E, 4>(p);
+        return stream_launch<T, E, PH, 4>(p);
     default:
-        return stream_launch<T, E, 1>(p);
+        return stream_launch<T, E, PH, 1>(p);
     }
 }
 
-template <typename T, int E>
+template <typename T, int E, bool PH>
 hipError_t split_run(const RowProblem &p, int S, int C, void *ws)
 {
     const dim3 grid(static_cast<unsigned>(p.M * S));
-    hipError_t err = launch(online_partials<T, E, kSplitW, kSplitU>, grid, dim3(kSplitW * kWave),
-                            p.stream, static_cast<const T *>(p.x), p.N, p.ldx, S, C,
-                            static_cast<float2 *>(ws));
+    hipError_t err = launch(online_partials<T, E, kSplitW, kSplitU, PH>, grid,
+                            dim3(kSplitW * kWave), p.stream, static_cast<const T *>(p.x), p.N,
+                            p.ldx, S, C, static_cast<float2 *>(ws));
     if (err != hipSuccess)
         return err;
-    return launch(online_finish<T, E, kSplitW, kSplitU>, grid, dim3(kSplitW * kWave), p.stream,
-                  static_cast<const T *>(p.x), static_cast<T *>(p.y), p.N, p.ldx, p.ldy, S, C,
-                  static_cast<const float2 *>(ws));
+    return launch(online_finish<T, E, kSplitW, kSplitU, PH>, grid, dim3(kSplitW * kWave),
+                  p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), p.N, p.ldx, p.ldy,
+                  S, C, static_cast<const float2 *>(ws));
+}
+
+template <typename T>
+hipError_t stream_io(const RowProblem &p, RowIo io)
+{
+    constexpr int E = Elem<T>::kVec;
+    if (io == kIoAligned)
+        return stream_run<T, E, false>(p);
+    if (io == kIoPhased)
+        return stream_run<T, E, true>(p);
+    return stream_run<T, 1, false>(p);
+}
+
+template <typename T>
+hipError_t split_io(const RowProblem &p, int S, int C, void *ws, RowIo io)
+{
+    constexpr int E = Elem<T>::kVec;
+    if (io == kIoAligned)
+        return split_run<T, E, false>(p, S, C, ws);
+    if (io == kIoPhased)
+        return split_run<T, E, true>(p, S, C, ws);
+    return split_run<T, 1, false>(p, S, C, ws);
 }
 
 }  // namespace
 
-hipError_t online_stream_run(const RowProblem &p, bool vectorized)
+hipError_t online_stream_run(const RowProblem &p, RowIo io)
 {
-    if (p.dtype == RK_F32)
-        return vectorized ? stream_run<float, 4>(p) : stream_run<float, 1>(p);
-    return vectorized ? stream_run<bf16_t, 8>(p) : stream_run<bf16_t, 1>(p);
+    return p.dtype == RK_F32 ? stream_io<float>(p, io) : stream_io<bf16_t>(p, io);
 }
 
-hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
-                            bool vectorized)
+hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace, RowIo io)
 {
-    if (p.dtype == RK_F32)
-        return vectorized ? split_run<float, 4>(p, splits, chunk, workspace)
-                          : split_run<float, 1>(p, splits, chunk, workspace);
-    return vectorized ? split_run<bf16_t, 8>(p, splits, chunk, workspace)
-                      : split_run<bf16_t, 1>(p, splits, chunk, workspace);
+    return p.dtype == RK_F32 ? split_io<float>(p, splits, chunk, workspace, io)
+                             : split_io<bf16_t>(p, splits, chunk, workspace, io);
 }
 
 }  // namespace rk

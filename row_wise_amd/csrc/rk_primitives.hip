@@ -28,7 +28,7 @@ __device__ __forceinline__ float reduce_op(float a, float b)
         return nanmax(a, b);
 }
 
-template <typename T, int E, int G, int W, int U, int OP>
+template <typename T, int E, int G, int W, int U, int OP, bool PH>
 __global__ __launch_bounds__(W *kWave) void row_reduce(const T *__restrict__ x, T *__restrict__ out,
                                                        int64_t M, int N, int64_t ldx)
 {
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(W *kWave) void row_reduce(const T *__restrict__ x, 
     const bool ok = row < M;
     const T *xr = x + (ok ? row : 0) * ldx;
     // the row as the aligned vectors that cover it, whatever its offset
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     const T *xb = xr - sp.h;
     const int jend = ok ? sp.count() : 0;
     const int fb = sp.full_begin();
@@ -96,12 +96,12 @@ __global__ __launch_bounds__(W *kWave) void row_reduce(const T *__restrict__ x, 
         out[row] = Elem<T>::from_f32(a);
 }
 
-template <typename T, int E, int G, int W, int U, int OP>
+template <typename T, int E, int G, int W, int U, int OP, bool PH>
 static hipError_t reduce_launch(const RowProblem &p)
 {
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG - 1) / RG;
-    return launch(row_reduce<T, E, G, W, U, OP>, dim3(static_cast<unsigned>(blocks)),
+    return launch(row_reduce<T, E, G, W, U, OP, PH>, dim3(static_cast<unsigned>(blocks)),
                   dim3(W * kWave), p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y),
                   p.M, p.N, p.ldx);
 }
@@ -114,17 +114,17 @@ constexpr int64_t kReduceWave4 = 8192;
 
 inline int64_t reduce_vectors(int64_t N, int E) { return (N + 2 * E - 2) / E; }
 
-template <typename T, int OP>
+template <typename T, int OP, bool PH>
 static hipError_t reduce_dispatch(const RowProblem &p)
 {
     constexpr int E = Elem<T>::kVec;
     constexpr int U = 16 / E > 4 ? 4 : (16 / E < 2 ? 2 : 16 / E);
     const int64_t nv = reduce_vectors(p.N, E);
     if (nv <= kReduceWave1)
-        return reduce_launch<T, E, 1, 4, U, OP>(p);
+        return reduce_launch<T, E, 1, 4, U, OP, PH>(p);
     if (nv <= kReduceWave4)
-        return reduce_launch<T, E, 4, 4, U, OP>(p);
-    return reduce_launch<T, E, 16, 16, U, OP>(p);
+        return reduce_launch<T, E, 4, 4, U, OP, PH>(p);
+    return reduce_launch<T, E, 16, 16, U, OP, PH>(p);
 }
 
 int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, int *threads)
@@ -135,12 +135,16 @@ int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, int *threads)
     return (M + rows_per_block - 1) / rows_per_block;
 }
 
+// Rows that all start on 16-byte boundaries take the kernel compiled for
+// that; others read each row from its own offset.
 template <int OP>
 static hipError_t reduce_run(const RowProblem &p)
 {
+    const int es = elem_size(p.dtype);
+    const bool aligned = reinterpret_cast<uintptr_t>(p.x) % 16 == 0 && (p.ldx * es) % 16 == 0;
     if (p.dtype == RK_F32)
-        return reduce_dispatch<float, OP>(p);
-    return reduce_dispatch<bf16_t, OP>(p);
+        return aligned ? reduce_dispatch<float, OP, false>(p) : reduce_dispatch<float, OP, true>(p);
+    return aligned ? reduce_dispatch<bf16_t, OP, false>(p) : reduce_dispatch<bf16_t, OP, true>(p);
 }
 
 hipError_t row_reduce_run(const RowProblem &p, int op)
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(kGeluThreads) void gelu_flat(const T *__restrict__ 
 // The same for rows with a pitch: one workgroup per row, each row read and
 // written as the aligned vectors that cover it (RowSpan; output rows at the
 // same offsets), or element by element (E = 1).
-template <typename T, int E, int GK>
+template <typename T, int E, int GK, bool PH>
 __global__ __launch_bounds__(kGeluThreads) void gelu_rows(const T *__restrict__ x,
                                                           T *__restrict__ y, int N, int64_t ldx,
                                                           int64_t ldy)
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(kGeluThreads) void gelu_rows(const T *__restrict__ 
     constexpr int NT = kGeluThreads;
     const int64_t row = blockIdx.x;
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     const T *xb = xr - sp.h;
     T *yb = y + row * ldy - sp.h;
     const int nv = sp.count();
@@ -251,32 +255,40 @@ hipError_t flat_run(const RowProblem &p, int64_t n)
                   p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), n, h);
 }
 
-template <typename T, int E, int GK>
+template <typename T, int E, int GK, bool PH>
 hipError_t rows_run(const RowProblem &p)
 {
-    return launch(gelu_rows<T, E, GK>, dim3(static_cast<unsigned>(p.M)), dim3(kGeluThreads),
+    return launch(gelu_rows<T, E, GK, PH>, dim3(static_cast<unsigned>(p.M)), dim3(kGeluThreads),
                   p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), p.N, p.ldx,
                   p.ldy);
 }
 
+template <typename T, int GK>
+hipError_t rows_io(const RowProblem &p, RowIo io)
+{
+    constexpr int E = Elem<T>::kVec;
+    if (io == kIoAligned)
+        return rows_run<T, E, GK, false>(p);
+    if (io == kIoPhased)
+        return rows_run<T, E, GK, true>(p);
+    return rows_run<T, 1, GK, false>(p);
+}
+
 template <int GK>
-hipError_t gelu_dispatch(const RowProblem &p, bool flat, bool vectorized)
+hipError_t gelu_dispatch(const RowProblem &p, bool flat, RowIo io)
 {
     if (flat) {
         const int64_t n = p.M * p.N;
         return p.dtype == RK_F32 ? flat_run<float, GK>(p, n) : flat_run<bf16_t, GK>(p, n);
     }
-    if (p.dtype == RK_F32)
-        return vectorized ? rows_run<float, 4, GK>(p) : rows_run<float, 1, GK>(p);
-    return vectorized ? rows_run<bf16_t, 8, GK>(p) : rows_run<bf16_t, 1, GK>(p);
+    return p.dtype == RK_F32 ? rows_io<float, GK>(p, io) : rows_io<bf16_t, GK>(p, io);
 }
 
 }  // namespace
 
-hipError_t gelu_run(const RowProblem &p, bool flat, bool vectorized)
+hipError_t gelu_run(const RowProblem &p, bool flat, RowIo io)
 {
-    return p.gelu == RK_GELU_ERF ? gelu_dispatch<1>(p, flat, vectorized)
-                                 : gelu_dispatch<0>(p, flat, vectorized);
+    return p.gelu == RK_GELU_ERF ? gelu_dispatch<1>(p, flat, io) : gelu_dispatch<0>(p, flat, io);
 }
 
 }  // namespace rk

@@ -300,7 +300,7 @@ struct RmsStep {
 // re-reads the row, stores residual_out (RES) and y = v inv w.  Rows are
 // read as aligned vectors from their own phase (RowSpan): x, residual, y and
 // residual_out share it, the weight is shifted into it.
-template <typename T, int E, int W, int U, bool RES, int RB>
+template <typename T, int E, int W, int U, bool RES, int RB, bool PH>
 __global__ __launch_bounds__(W *kWave *RB) void rmsnorm_loop(
     const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w,
     T *__restrict__ y, T *__restrict__ ro, int64_t M, int N, int64_t ldx, int64_t ldr,
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(W *kWave *RB) void rmsnorm_loop(
     if (RB > 1 && row >= M)
         return;
     const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E>(xr), N};
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     const T *xb = xr - sp.h;
     const T *rb = RES ? res + row * ldr - sp.h : nullptr;
     const int nv = sp.count();
@@ -359,16 +359,21 @@ __global__ __launch_bounds__(W *kWave *RB) void rmsnorm_loop(
     cur.issue(xb, rb, tid, nv, full(0));
     for (int base = 0; base < nv; base += NT * U) {
         const bool f = full(base);
-        float wv[U][E];
+        // the weight, the next step's row and this step's row are all in
+        // flight before the first wait
+        ParamLoad<T, E> wl[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            load_param<T, E>(w, base + tid + u * NT, sp.h, N, wv[u], f);
+            wl[u].issue(w, base + tid + u * NT, sp.h, N, f);
         RmsStep<T, E, U, NT, kStreaming, RES> nxt;
         const int next = base + NT * U;
         if (next < nv)
             nxt.issue(xb, rb, next + tid, nv, full(next));
-        float v[U][E];
+        float v[U][E], wv[U][E];
         cur.finish(v, sp, nv, f);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            wl[u].finish(wv[u], base + tid + u * NT, sp.h, N, f);
         if constexpr (RES)
             store_span<T, E, U, NT>(ob, base + tid, nv, sp, v, f);
 #pragma unroll
@@ -387,11 +392,11 @@ namespace {
 // the LayerNorm streaming kernel.
 constexpr int loop_vectors(int E) { return E == 8 ? 2 : 4; }
 
-template <typename T, int E, bool RES, int W, int U = loop_vectors(E)>
+template <typename T, int E, bool RES, bool PH, int W, int U = loop_vectors(E)>
 hipError_t loop_launch(const RowProblem &p)
 {
     constexpr int RB = W == 1 ? 4 : 1;  // one-wave rows go four to a workgroup
-    return launch(rmsnorm_loop<T, E, W, U, RES, RB>,
+    return launch(rmsnorm_loop<T, E, W, U, RES, RB, PH>,
                   dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB),
                   p.stream, static_cast<const T *>(p.x), static_cast<const T *>(p.r),
                   static_cast<const T *>(p.w), static_cast<T *>(p.y), static_cast<T *>(p.ro),
@@ -399,35 +404,44 @@ hipError_t loop_launch(const RowProblem &p)
 }
 
 // 1, 4 or 16 waves per row by the row's length.
-template <typename T, int E, bool RES>
+template <typename T, int E, bool RES, bool PH>
 hipError_t loop_run(const RowProblem &p)
 {
     const int64_t nvec = (p.N + 2 * E - 2) / E;
     if (nvec <= kShortRowVectors)
-        return loop_launch<T, E, RES, 1, 1>(p);
+        return loop_launch<T, E, RES, PH, 1, 1>(p);
     switch (stream_waves(nvec, loop_vectors(E))) {
     case 16:
-        return loop_launch<T, E, RES, 16>(p);
+        return loop_launch<T, E, RES, PH, 16>(p);
     case 4:
-        return loop_launch<T, E, RES, 4>(p);
+        return loop_launch<T, E, RES, PH, 4>(p);
     default:
-        return loop_launch<T, E, RES, 1>(p);
+        return loop_launch<T, E, RES, PH, 1>(p);
     }
 }
 
-template <bool RES>
-hipError_t loop_dispatch(const RowProblem &p, bool vectorized)
+template <typename T, bool RES>
+hipError_t loop_io(const RowProblem &p, RowIo io)
 {
-    if (p.dtype == RK_F32)
-        return vectorized ? loop_run<float, 4, RES>(p) : loop_run<float, 1, RES>(p);
-    return vectorized ? loop_run<bf16_t, 8, RES>(p) : loop_run<bf16_t, 1, RES>(p);
+    constexpr int E = Elem<T>::kVec;
+    if (io == kIoAligned)
+        return loop_run<T, E, RES, false>(p);
+    if (io == kIoPhased)
+        return loop_run<T, E, RES, true>(p);
+    return loop_run<T, 1, RES, false>(p);
+}
+
+template <bool RES>
+hipError_t loop_dispatch(const RowProblem &p, RowIo io)
+{
+    return p.dtype == RK_F32 ? loop_io<float, RES>(p, io) : loop_io<bf16_t, RES>(p, io);
 }
 
 }  // namespace
 
-hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, bool vectorized)
+hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, RowIo io)
 {
-    return residual ? loop_dispatch<true>(p, vectorized) : loop_dispatch<false>(p, vectorized);
+    return residual ? loop_dispatch<true>(p, io) : loop_dispatch<false>(p, io);
 }
 
 }  // namespace rk
