@@ -17,8 +17,10 @@
 //   S^T = K Q^T (keys x queries, so that each lane holds one query's scores
 //   for 16 of the keys), the row max across the four 16-lane groups
 //   (permlane16/32 swaps), p = exp2((S - m) scale log2e), and O^T += V^T P^T,
-//   where P^T is the S^T fragments rounded to the operand type in place (the
-//   key order inside each 32-key step is permuted identically in V^T).
+//   where P^T is the S^T fragments rounded to the operand type in place.  K
+//   rows are staged in a permuted order (k_slot) that leaves each lane 8
+//   consecutive keys per 32-key step, so that its V^T operand is one 16-byte
+//   read of the key-ordered V^T.
 //   The next block's K/V are loaded into registers while this one is used.
 #include "rk_device.h"
 #include "rk_internal.h"
@@ -99,13 +101,25 @@ constexpr int kAttnBN = 64;  // keys per step
 template <int D>
 struct AttnLds {
     static constexpr int kKStride = D + 8;       // K row pitch (elements): 16 B of padding
-    // V^T row pitch: 68 elements (34 words), so that the 16 rows an MFMA
-    // operand load reads together fall on distinct banks (measured: a pitch
-    // of 72 triples the bank conflicts)
-    static constexpr int kVStride = kAttnBN + 4;
+    // V^T row pitch: 72 elements (36 words).  Rows stay 16-byte aligned for
+    // the 16-byte operand reads; the 16 rows one read serves start on banks
+    // 36 r mod 64, distinct multiples of 4, and the V^T writes of a wave (rows
+    // 8 apart, 288 words) fall on the other half of the banks.
+    static constexpr int kVStride = kAttnBN + 8;
     uint16_t k[kAttnBN * kKStride];
     uint16_t vt[D * kVStride];
 };
+
+// LDS row of key j (0..63) of a K block.  The S^T tile kt = 2 ks + t reads
+// rows 16 kt .. 16 kt + 15 in order, and its row 4 g + r (the rows that lane
+// group g's accumulators hold) is key 32 ks + 8 g + 4 t + r: each lane then
+// ends with 8 consecutive keys of every 32-key step (4 from each tile), which
+// its P^T operand takes in that order, so that V^T, staged in key order,
+// gives the matching operand in one 16-byte read.
+__device__ __forceinline__ int k_slot(int j)
+{
+    return 32 * (j / 32) + 16 * ((j % 8) / 4) + 4 * ((j % 32) / 8) + j % 4;
+}
 
 // Strides in elements; the head_dim stride is 1.
 struct AttnStrides {
@@ -236,7 +250,7 @@ void flash_attention_fwd(
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int idx = tid + NT * i;
-            *reinterpret_cast<u32x4_t *>(&buf.k[(idx / CH) * AttnLds<D>::kKStride +
+            *reinterpret_cast<u32x4_t *>(&buf.k[k_slot(idx / CH) * AttnLds<D>::kKStride +
                                                 8 * (idx % CH)]) = kreg[i];
         }
         const int kq = tid % NKQ;
@@ -262,21 +276,14 @@ void flash_attention_fwd(
     };
 
     const int kend = CAUSAL ? (q0 + BM < T ? q0 + BM : T) : T;
-    load_block(0);
-    store_block(lds[0]);
-    __syncthreads();
 
-    for (int kb = 0, it = 0; kb < kend; kb += kAttnBN, ++it) {
-        const bool more = kb + kAttnBN < kend;
-        const AttnLds<D> &cur = lds[it & 1];
-        if (more)
-            load_block(kb + kAttnBN);
-
-        // S^T tiles: s[qt][kt] holds, in lane (g, l16), query qw + 16 qt + l16
-        // and keys kb + 16 kt + 4 g + r.
+    // S^T of the block at key kb (K in buf): s[qt][kt] holds, in lane
+    // (g, l16), query qw + 16 qt + l16 and keys kb + 32 (kt / 2) + 8 g +
+    // 4 (kt % 2) + r (k_slot); keys past T and (causal) keys after the query
+    // are masked.
+    auto scores = [&](const AttnLds<D> &buf, int kb, f32x4v_t(&s)[QT][NKT]) {
         // The K fragments of d-step ds + 1 are read while the MFMAs of d-step
         // ds run; consecutive MFMAs on one accumulator are NKT * QT apart.
-        f32x4v_t s[QT][NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -287,7 +294,7 @@ void flash_attention_fwd(
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
                 dst[kt] = *reinterpret_cast<const vec *>(
-                    &cur.k[(16 * kt + l16) * AttnLds<D>::kKStride + 32 * ds + 8 * g]);
+                    &buf.k[(16 * kt + l16) * AttnLds<D>::kKStride + 32 * ds + 8 * g]);
         };
         read_k(0, ka[0]);
 #pragma unroll
@@ -312,15 +319,18 @@ void flash_attention_fwd(
                 for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int key = kb + 16 * kt + 4 * g + r;
+                        const int key = kb + 32 * (kt / 2) + 8 * g + 4 * (kt % 2) + r;
                         if (key >= T || (CAUSAL && key > qi))
                             s[qt][kt][r] = -INFINITY;
                     }
             }
         }
 
-        // online softmax state per query row
-        uint32_t pk[QT][NKS][4];  // P^T operand words
+    };
+
+    // The online softmax update of one block: p = exp2(...) into s, the
+    // state m, l and acc moved, P^T packed into pk.
+    auto softmax_step = [&](f32x4v_t(&s)[QT][NKT], uint32_t(&pk)[QT][NKS][4]) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             float mx = -INFINITY;
@@ -362,8 +372,8 @@ void flash_attention_fwd(
                 for (int dt = 0; dt < DT16; ++dt)
                     acc[qt][dt] *= alpha;
             }
-            // 32-key step ks: slots 0..3 are keys 32 ks + 4 g + r (tile 2 ks),
-            // slots 4..7 keys 32 ks + 16 + 4 g + r (tile 2 ks + 1)
+            // 32-key step ks: slots 0..3 are keys 32 ks + 8 g + r (tile 2 ks),
+            // slots 4..7 keys 32 ks + 8 g + 4 + r (tile 2 ks + 1)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 pk[qt][ks][0] = Op::pack2(s[qt][2 * ks][0], s[qt][2 * ks][1]);
@@ -373,8 +383,12 @@ void flash_attention_fwd(
             }
         }
 
-        // O^T += V^T P^T: A = V^T rows d = 16 dt + l16 at the same permuted
-        // keys (two 8-byte reads), B = P^T of the lane's query
+    };
+
+    // O^T += V^T P^T for one block (V^T in buf).
+    auto value_step = [&](const AttnLds<D> &buf, const uint32_t(&pk)[QT][NKS][4]) {
+        // O^T += V^T P^T: A = V^T rows d = 16 dt + l16 at the lane's 8 keys of
+        // the step (one 16-byte read), B = P^T of the lane's query
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             vec bq[QT];
@@ -383,13 +397,11 @@ void flash_attention_fwd(
                 u32x4_t w = {pk[qt][ks][0], pk[qt][ks][1], pk[qt][ks][2], pk[qt][ks][3]};
                 bq[qt] = __builtin_bit_cast(vec, w);
             }
-            // V^T fragments are read two d-tiles ahead of their MFMAs
+            // V^T fragments (keys 32 ks + 8 g .. + 8 of d row 16 dt + l16, one
+            // 16-byte read) are read two d-tiles ahead of their MFMAs
             auto read_v = [&](int dt) {
-                const uint16_t *row = &cur.vt[(16 * dt + l16) * AttnLds<D>::kVStride + 32 * ks];
-                const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(row + 4 * g);
-                const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(row + 16 + 4 * g);
-                const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-                return __builtin_bit_cast(vec, w);
+                const uint16_t *row = &buf.vt[(16 * dt + l16) * AttnLds<D>::kVStride + 32 * ks];
+                return *reinterpret_cast<const vec *>(row + 8 * g);
             };
             vec va[3];
             va[0] = read_v(0);
@@ -404,6 +416,22 @@ void flash_attention_fwd(
             }
         }
 
+    };
+
+    load_block(0);
+    store_block(lds[0]);
+    __syncthreads();
+
+    f32x4v_t s[QT][NKT];
+    uint32_t pk[QT][NKS][4];  // P^T operand words
+    for (int kb = 0, it = 0; kb < kend; kb += kAttnBN, ++it) {
+        const bool more = kb + kAttnBN < kend;
+        const AttnLds<D> &cur = lds[it & 1];
+        if (more)
+            load_block(kb + kAttnBN);
+        scores(cur, kb, s);
+        softmax_step(s, pk);
+        value_step(cur, pk);
         // The other buffer was last read in the previous step, which every
         // wave finished before the barrier ending that step.
         if (more)
@@ -435,7 +463,9 @@ AttnStrides strides_of(const int64_t *s) { return AttnStrides{s[0], s[1], s[2]};
 // Launch shape: kLaunchW waves of kLaunchQT query tiles each.  Measured on
 // 4 x 32 x 4096 x 128 bf16: 8 x 2 (256 rows, two waves per SIMD) 900 TFLOP/s;
 // 4 x 2: 845; 8 x 1 (four waves per SIMD, twice the LDS reads per MFMA):
-// 700; 4 x 4 (one wave per SIMD, spills): 490.
+// 700; 4 x 4 (one wave per SIMD, spills): 490.  Waves 0-3 and 4-7 run half
+// a step apart (one softmax overlapping the other group's MFMAs, two
+// barriers per step): the same speed as 8 x 2 in step, so not kept.
 constexpr int kLaunchW = 8;
 constexpr int kLaunchQT = 2;
 constexpr int kLaunchBM = 16 * kLaunchQT * kLaunchW;
