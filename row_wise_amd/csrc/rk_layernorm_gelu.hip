@@ -58,11 +58,11 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     // previous one is reduced.
     RowLoad<T, E, V, L> xl;
     SpanLoad<T, E, V, L> xs;  // PH
-    // PH: the weight and bias blocks of small tiles are loaded with the row
-    // (two blocks each per vector); larger tiles load them as they are used
-    // (measured: loading them early there costs more in registers than it
-    // saves in latency)
-    constexpr bool kParamAhead = PH && V <= 2;
+    // PH: the weight and bias blocks of tiles of up to three vectors per lane
+    // are loaded with the row (two blocks each per vector); larger tiles load
+    // them as they are used (measured: loading them early there costs more in
+    // registers than it saves in latency)
+    constexpr bool kParamAhead = PH && V <= 3;
     ParamLoad<T, E> wp[kParamAhead ? V : 1], bp[kParamAhead ? V : 1];
     RowSpan<E> sp{0, N};
     int jend = 0;
