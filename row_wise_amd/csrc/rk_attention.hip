@@ -429,9 +429,13 @@ void flash_attention_fwd(
         const AttnLds<D> &cur = lds[it & 1];
         if (more)
             load_block(kb + kAttnBN);
-        scores(cur, kb, s);
-        softmax_step(s, pk);
-        value_step(cur, pk);
+        // causal: a block whose keys all follow this wave's last query row
+        // adds nothing (every p would be 0); the wave still stages and waits
+        if (!CAUSAL || kb <= qw + 16 * QT - 1) {
+            scores(cur, kb, s);
+            softmax_step(s, pk);
+            value_step(cur, pk);
+        }
         // The other buffer was last read in the previous step, which every
         // wave finished before the barrier ending that step.
         if (more)
