@@ -21,9 +21,16 @@
  *               current device and the call returns without synchronizing.
  *               Multi-kernel operations are ordered by the stream alone.
  *   Alignment   Any element-aligned pointer and any ld >= N are accepted.
- *               16-byte vector loads and stores are used when the base
- *               pointers and the row pitches (ld * element size) are 16-byte
- *               aligned; other rows take a slower element-wise path.
+ *               Rows are read and written with 16-byte vector accesses when
+ *               every row of every row operand starts on a 16-byte boundary
+ *               (base pointers and row pitches 16-byte aligned), and also
+ *               when rows start at other offsets that the input and output
+ *               (and residual operands) share row for row: the row is then
+ *               covered by aligned vectors whose first and last are masked
+ *               (such a load stays inside a 16-byte block that holds an
+ *               element of the row).  Weight and bias must be 16-byte
+ *               aligned for this.  Other layouts take a slower element-wise
+ *               path with the same results.
  *   Aliasing    y may be x exactly (same pointer and same ld: in place);
  *               any other overlap of an output with an input is rejected.
  *   Errors      Arguments are validated before any HIP call; a rejected call
@@ -72,9 +79,10 @@ typedef enum rk_status {
  *     m_i = max_j x_ij,   y_ij = exp(x_ij - m_i) / sum_k exp(x_ik - m_i).
  *
  * x  [M][ldx] input, y [M][ldy] output, both of `dtype`.
- * Rows that fit on chip (N <= 16384 for fp32, N <= 32768 for bf16, 16-byte
- * aligned) are held in registers: one HBM read and one HBM write per
- * element.  Longer or unaligned rows are computed by the streaming online
+ * Rows that fit on chip (N <= 16384 for fp32, N <= 32768 for bf16; for rows
+ * at a shared offset, N + 3 / N + 7 up to those) are held in registers: one
+ * HBM read and one HBM write per element.  Longer rows, and rows whose
+ * input and output offsets differ, are computed by the streaming online
  * kernel of rk_online_softmax (two reads, one write), with the same result.
  * A row that is all -inf, or holds +inf or NaN, yields NaN (the IEEE value
  * of the definition).
@@ -257,8 +265,8 @@ rk_status rk_row_max(const void *x, void *out, int64_t M, int64_t N, int64_t ldx
  * Elementwise GeLU ([TKE] §3.4; [KTN] "Triton GeLU"): y = GeLU(x), the tanh
  * approximation or the exact erf form, fp32 arithmetic.
  *
- * x [M][ldx], y [M][ldy] of `dtype`; a contiguous, 16-byte aligned buffer is
- * processed as one flat array.  Arguments, aliasing and errors as in
+ * x [M][ldx], y [M][ldy] of `dtype`; a contiguous buffer whose output sits at
+ * the same offset past a 16-byte boundary is processed as one flat array.  Arguments, aliasing and errors as in
  * rk_softmax, plus RK_ERR_INVALID_ARG for an unknown gelu.
  */
 rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
