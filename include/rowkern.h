@@ -149,11 +149,12 @@ int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N);
  * x [M][ldx], y [M][ldy], weight [N], bias [N] (contiguous), all of `dtype`.
  * 16-byte aligned rows of up to 14336 (fp32) / 20480 (bf16) columns, and of
  * exactly 16384 (fp32) / 32768 (bf16), stay in registers (one HBM read and
- * write per element); other rows take one workgroup per row that reads the
- * row twice (statistics by parts merged as in rk_layernorm_gelu_ex, then the
- * output), which measured faster than a register tile filled well below its
- * capacity.  Same as rk_layernorm_gelu_ex
- * with RK_GELU_TANH and num_splits = 1.
+ * write per element), as do rows at a shared offset (see Alignment) with
+ * N + 3 (fp32) / N + 7 (bf16) up to the first two limits; other rows take
+ * one workgroup per row that reads the row twice (statistics by parts merged
+ * as in rk_layernorm_gelu_ex, then the output), which measured faster than a
+ * register tile filled well below its capacity.  Same as
+ * rk_layernorm_gelu_ex with RK_GELU_TANH and num_splits = 1.
  *
  * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight or bias is NULL
  * with M > 0, eps is not finite and > 0, or y overlaps weight or bias.
@@ -209,8 +210,9 @@ int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
  * with no centring; fp32 accumulation, output in `dtype`.
  *
  * x [M][ldx], y [M][ldy], weight [N] (contiguous), all of `dtype`.  Register
- * resident up to the same N as rk_layernorm_gelu (one read and one write
- * per element); other rows are read twice by a looping kernel.
+ * resident up to N = 16384 (fp32) / 32768 (bf16), 16-byte aligned or at a
+ * shared offset (see Alignment; N + 3 / N + 7 up to those), with one read
+ * and one write per element; other rows are read twice by a looping kernel.
  *
  * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight is NULL with
  * M > 0, eps is not finite and > 0, or y overlaps weight.
