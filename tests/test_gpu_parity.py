@@ -14,7 +14,7 @@ import torch
 import oracle
 import row_wise_amd as rk
 import rowgen
-from tolerance import TOL, rel_err_floor1, rel_err_softmax
+from tolerance import TOL, rel_err, rel_err_floor1, rel_err_softmax
 
 pytestmark = pytest.mark.gpu
 EPS = float(np.float32(1e-5))
@@ -355,6 +355,39 @@ def test_shared_offset_and_in_place(dtype, off):
     xd = x.to(DEV)
     rk.rk_online_softmax(xd, num_splits=5, out=xd)
     assert rel_err_softmax(xd, oracle.softmax(x)) <= tol_of(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+def test_phased_rows_different_pitches(dtype):
+    """Input pitch N + 6 and output pitch N + 6 + E: the two differ by one
+    16-byte vector, so every row's offset is the same in both though the
+    pitches are odd and unequal; the gaps between output rows stay untouched."""
+    E = 4 if dtype == torch.float32 else 8
+    M, N = 41, 1003
+    ldx, ldy = N + 6, N + 6 + E
+    canary = -9.0
+    xb = rowgen.randn(M, ldx, seed=E + 70, scale=3.0, dtype=dtype)
+    x = xb[:, :N]
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(E + 71), dtype)
+    xd = xb.to(DEV)[:, :N]
+    res = rowgen.randn(M, N, seed=E + 72, dtype=dtype)
+    for name, run, ref, err in (
+            ("softmax", lambda o: rk.rk_softmax(xd, out=o), oracle.softmax(x), rel_err_softmax),
+            ("online", lambda o: rk.rk_online_softmax(xd, num_splits=3, out=o), oracle.softmax(x),
+             rel_err_softmax),
+            ("layernorm", lambda o: rk.rk_layernorm_gelu(xd, w.to(DEV), b.to(DEV), EPS, out=o),
+             oracle.layernorm_gelu(x, w, b, EPS), rel_err_floor1),
+            ("layernorm split", lambda o: rk.rk_layernorm_gelu_ex(xd, w.to(DEV), b.to(DEV), EPS,
+                                                                   num_splits=4, out=o),
+             oracle.layernorm_gelu(x, w, b, EPS), rel_err_floor1),
+            ("rmsnorm", lambda o: rk.rk_rmsnorm(xd, w.to(DEV), EPS, out=o),
+             oracle.rmsnorm(x, w, EPS), rel_err),
+            ("gelu", lambda o: rk.rk_gelu(xd, out=o), oracle.gelu_tanh(x.double().numpy()),
+             rel_err_floor1)):
+        buf = torch.full((M, ldy), canary, dtype=dtype, device=DEV)
+        run(buf[:, :N])
+        assert err(buf[:, :N], ref) <= tol_of(dtype), name
+        assert torch.all(buf[:, N:].cpu().float() == canary), name
 
 
 def test_in_place():
