@@ -752,10 +752,10 @@ RK_EXPORT rk_status rk_flash_attention(const void *q, const void *k, const void 
         if (st[i][2] > ((int64_t{1} << 30) - d) / 64)
             return RK_ERR_UNSUPPORTED;
     }
-    const int64_t bm = attention_block_rows();
+    const int64_t bm = attention_block_rows(d);
     const int64_t nqb = (T + bm - 1) / bm;
     if (T > INT32_MAX || B * H > INT32_MAX || B * H > INT64_MAX / nqb ||
-        !grid_ok(B * H * nqb, 256))
+        !grid_ok(B * H * nqb, attention_block_threads(d)))
         return RK_ERR_UNSUPPORTED;
     AttentionProblem p{q, k, v, o, B, H, T, d, {}, {}, {}, {}, scale, causal != 0, dtype, stream};
     for (int j = 0; j < 3; ++j) {

@@ -464,24 +464,31 @@ namespace {
 
 AttnStrides strides_of(const int64_t *s) { return AttnStrides{s[0], s[1], s[2]}; }
 
-// Launch shape: kLaunchW waves of kLaunchQT query tiles each.  Measured on
-// 4 x 32 x 4096 x 128 bf16: 8 x 2 (256 rows, two waves per SIMD) 900 TFLOP/s;
-// 4 x 2: 845; 8 x 1 (four waves per SIMD, twice the LDS reads per MFMA):
-// 700; 4 x 4 (one wave per SIMD, spills): 490.  Waves 0-3 and 4-7 run half
-// a step apart (one softmax overlapping the other group's MFMAs, two
-// barriers per step): the same speed as 8 x 2 in step, so not kept.
-constexpr int kLaunchW = 8;
-constexpr int kLaunchQT = 2;
-constexpr int kLaunchBM = 16 * kLaunchQT * kLaunchW;
+// Launch shape by head size: W waves of QT query tiles each (BM = 16 QT W
+// query rows per workgroup).  Measured on 4 x 32 x 4096 x 128 bf16: 8 x 2
+// (256 rows, two waves per SIMD, one workgroup per CU) 900 TFLOP/s; 4 x 2:
+// 845; 8 x 1 (four waves per SIMD, twice the LDS reads per MFMA): 700; 4 x 4
+// (one wave per SIMD, spills): 490.  Waves 0-3 and 4-7 run half a step apart
+// (one softmax overlapping the other group's MFMAs, two barriers per step):
+// the same speed as 8 x 2 in step, so not kept.  With d = 64 the kernel holds
+// 142 registers, so 4 x 2 fits three workgroups per CU, whose independent
+// steps overlap: 816 against 734 TFLOP/s for 8 x 2 on 4 x 32 x 4096 x 64.
+template <int D>
+struct AttnShape {
+    static constexpr int W = D == 64 ? 4 : 8;
+    static constexpr int QT = 2;
+    static constexpr int BM = 16 * QT * W;
+};
 
 template <int DT, int D, bool CAUSAL>
 hipError_t attn_launch(const AttentionProblem &p)
 {
-    const int nqb = static_cast<int>((p.T + kLaunchBM - 1) / kLaunchBM);
+    typedef AttnShape<D> S;
+    const int nqb = static_cast<int>((p.T + S::BM - 1) / S::BM);
     const int BH = static_cast<int>(p.B * p.H);
     const float scale_log2e = p.scale * 1.4426950408889634f;
-    return launch(flash_attention_fwd<DT, D, CAUSAL, kLaunchW, kLaunchQT>,
-                  dim3(static_cast<unsigned>(int64_t{nqb} * BH)), dim3(kLaunchW * kWave),
+    return launch(flash_attention_fwd<DT, D, CAUSAL, S::W, S::QT>,
+                  dim3(static_cast<unsigned>(int64_t{nqb} * BH)), dim3(S::W * kWave),
                   p.stream, static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                   static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o),
                   static_cast<int>(p.H), static_cast<int>(p.T), nqb, BH, strides_of(p.sq),
@@ -502,7 +509,12 @@ hipError_t attn_dim(const AttentionProblem &p)
 
 }  // namespace
 
-int attention_block_rows() { return kLaunchBM; }
+int attention_block_rows(int64_t d) { return d == 64 ? AttnShape<64>::BM : AttnShape<128>::BM; }
+
+int attention_block_threads(int64_t d)
+{
+    return (d == 64 ? AttnShape<64>::W : AttnShape<128>::W) * kWave;
+}
 
 hipError_t flash_attention_run(const AttentionProblem &p)
 {

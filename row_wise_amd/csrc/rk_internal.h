@@ -124,8 +124,10 @@ hipError_t row_reduce_run(const RowProblem &p, int op);
 int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, int *threads);
 // flat: x and y contiguous and 16-byte aligned, processed as one buffer.
 hipError_t gelu_run(const RowProblem &p, bool flat, RowIo io);
-// Query rows per workgroup of the attention kernel.
-int attention_block_rows();
+// Query rows and threads per workgroup of the attention kernel for head
+// size d.
+int attention_block_rows(int64_t d);
+int attention_block_threads(int64_t d);
 hipError_t flash_attention_run(const AttentionProblem &p);
 hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
                           hipStream_t stream);
