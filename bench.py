@@ -88,7 +88,7 @@ class Case:
             self.bytes = 3 * M * N * es  # two reads of x, one write
         elif self.op == "online":
             if self.splits == 0:
-                self.splits = rk.rk_online_softmax_auto_splits(M, N)
+                self.splits = rk.rk_online_softmax_auto_splits(M, N, self.dtype_code)
             self.bytes = 3 * M * N * es + 2 * M * self.splits * 8  # + partials out and in
         else:
             self.bytes = io
@@ -105,7 +105,7 @@ class Case:
         self.b = d["b"].to(dev)
         self.ws = None
         if self.op == "online" and self.splits > 1:
-            nb = rk.rk_online_softmax_workspace_bytes(M, N, self.splits)
+            nb = rk.rk_online_softmax_workspace_bytes(M, N, self.splits, self.dtype_code)
             self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         if self.op == "layernorm_gelu_ex" and self.splits > 1:
             nb = rk.rk_layernorm_gelu_workspace_bytes(M, N, self.splits, self.dtype_code)

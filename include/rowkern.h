@@ -82,8 +82,15 @@ typedef enum rk_status {
  * Rows that fit on chip (N <= 16384 for fp32, N <= 32768 for bf16; for rows
  * at a shared offset, N + 3 / N + 7 up to those) are held in registers: one
  * HBM read and one HBM write per element.  Longer rows, and rows whose
- * input and output offsets differ, are computed by the streaming online
- * kernel of rk_online_softmax (two reads, one write), with the same result.
+ * input and output offsets differ, are computed by the online kernels of
+ * rk_online_softmax (two reads, one write), with the same result: one
+ * workgroup per row, or, for long rows in few rows (the rule of
+ * num_splits == 0 there, tightened for the extra launch) when y does not
+ * alias x, the split-row form with no workspace: each row's chunk partials
+ * are kept in that row's own first output chunk (from its first 8-byte
+ * boundary), a second kernel writes the other chunks, and a third, one
+ * workgroup per row, reads the partials and then writes the first chunk.
+ * The split count is lowered where needed until that chunk holds them.
  * A row that is all -inf, or holds +inf or NaN, yields NaN (the IEEE value
  * of the definition).
  *
@@ -113,11 +120,15 @@ rk_status rk_softmax(const void *x, void *y, int64_t M, int64_t N, int64_t ldx, 
  *                      (m1,d1)+(m2,d2) = (M, d1 e^(m1-M) + d2 e^(m2-M)),
  *                  M = max(m1, m2), (-inf, 0) the identity,
  *                  and writes its chunk.
- * num_splits == 0  the library picks S from M and N (S = 1 when M alone
- *                  fills the GPU).
+ * num_splits == 0  the library picks S from M, N and dtype
+ *                  (rk_online_softmax_auto_splits): S = 1 for 256 rows or
+ *                  more, or where one workgroup per row streams a row in
+ *                  about the time the split kernels take for all rows;
+ *                  otherwise chunks of about 16 KiB, at most 2048
+ *                  workgroups.
  *
  * workspace  device memory of at least
- *            rk_online_softmax_workspace_bytes(M, N, num_splits) bytes,
+ *            rk_online_softmax_workspace_bytes(M, N, num_splits, dtype) bytes,
  *            8-byte aligned, owned by the caller; may be NULL when that size
  *            is 0.  Its contents on entry do not matter; on return (stream
  *            order) it holds the partials as float pairs [M][S][2].
@@ -132,10 +143,12 @@ rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t N, int64_
 
 /* Workspace bytes rk_online_softmax needs for these arguments (0 when the
  * streaming kernel is used or the arguments are invalid). */
-size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t num_splits);
+size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t num_splits,
+                                         rk_dtype dtype);
 
-/* The split count rk_online_softmax uses for num_splits == 0. */
-int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N);
+/* The split count rk_online_softmax uses for num_splits == 0 (1 for invalid
+ * arguments). */
+int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
 
 /*
  * Fused LayerNorm + affine + tanh-approximation GeLU, one pass over each row
@@ -153,8 +166,12 @@ int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N);
  * N + 3 (fp32) / N + 7 (bf16) up to the first two limits; other rows take
  * one workgroup per row that reads the row twice (statistics by parts merged
  * as in rk_layernorm_gelu_ex, then the output), which measured faster than a
- * register tile filled well below its capacity.  Same as
- * rk_layernorm_gelu_ex with RK_GELU_TANH and num_splits = 1.
+ * register tile filled well below its capacity.  Long rows in few rows, when
+ * y does not alias x, take the split-row form of rk_layernorm_gelu_ex with
+ * no workspace, the chunk summaries kept in each row's first output chunk
+ * and that chunk written last by a third kernel, as rk_softmax does.
+ * Otherwise the same as rk_layernorm_gelu_ex with RK_GELU_TANH and
+ * num_splits = 1.
  *
  * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight or bias is NULL
  * with M > 0, eps is not finite and > 0, or y overlaps weight or bias.
@@ -178,7 +195,9 @@ rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias,
  *             it), a second merges the row's S summaries by the
  *             Chan-Golub-LeVeque pairwise update and writes the chunk:
  *             2 reads + 1 write per element, all CUs busy even for a few
- *             long rows.  0: rk_layernorm_gelu_auto_splits.
+ *             long rows.  0: rk_layernorm_gelu_auto_splits (S = 1 for rows
+ *             a register tile holds, else the rule of
+ *             rk_online_softmax_auto_splits with LayerNorm's own rates).
  * workspace   for S > 1: caller-owned device memory of at least
  *             rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype)
  *             bytes, 8-byte aligned, not overlapping x, y, weight or bias;
@@ -200,8 +219,10 @@ size_t rk_layernorm_gelu_workspace_bytes(int64_t M, int64_t N, int32_t num_split
                                          rk_dtype dtype);
 
 /* The split count rk_layernorm_gelu_ex uses for num_splits == 0: 1 when a
- * register tile takes the row (as listed under rk_layernorm_gelu) or M >= 512,
- * else enough chunks of >= 2048 elements to give about 2048 workgroups. */
+ * register tile takes the row (as listed under rk_layernorm_gelu), for 256
+ * rows or more, or where one workgroup per row is expected to be as fast;
+ * else chunks of about 16 KiB, at most 2048 workgroups (1 for invalid
+ * arguments). */
 int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
 
 /*

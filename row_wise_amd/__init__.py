@@ -17,8 +17,8 @@ Functions carry the C entry points' names:
 * ``rk_flash_attention(q, k, v, causal=False, scale=None, out=None)``
 * ``rk_rmsnorm(x, weight, eps=1e-5, out=None)``
 * ``rk_residual_rmsnorm(x, residual, weight, eps=1e-5, out=None, residual_out=None)``
-* ``rk_online_softmax_workspace_bytes(M, N, num_splits)``,
-  ``rk_online_softmax_auto_splits(M, N)``, ``rk_status_string(s)``,
+* ``rk_online_softmax_workspace_bytes(M, N, num_splits, dtype)``,
+  ``rk_online_softmax_auto_splits(M, N, dtype)``, ``rk_status_string(s)``,
   ``rk_version()``
 * tuning: ``rk_probe_copy(src, dst)``, ``rk__softmax_variant(index, x, out)``,
   ``rk__layernorm_gelu_variant(index, x, w, b, eps, out)``, ``variants(op, dtype)``
@@ -76,8 +76,8 @@ def load():
     sig = {
         "rk_softmax": (i32, [vp, vp, i64, i64, i64, i64, i32, vp]),
         "rk_online_softmax": (i32, [vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]),
-        "rk_online_softmax_workspace_bytes": (sz, [i64, i64, i32]),
-        "rk_online_softmax_auto_splits": (i32, [i64, i64]),
+        "rk_online_softmax_workspace_bytes": (sz, [i64, i64, i32, i32]),
+        "rk_online_softmax_auto_splits": (i32, [i64, i64, i32]),
         "rk_layernorm_gelu": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
         "rk_status_string": (ctypes.c_char_p, [i32]),
         "rk_version": (ctypes.c_int, []),
@@ -197,12 +197,12 @@ def rk_version() -> int:
     return int(load().rk_version())
 
 
-def rk_online_softmax_workspace_bytes(M: int, N: int, num_splits: int) -> int:
-    return int(load().rk_online_softmax_workspace_bytes(M, N, num_splits))
+def rk_online_softmax_workspace_bytes(M: int, N: int, num_splits: int, dtype: int) -> int:
+    return int(load().rk_online_softmax_workspace_bytes(M, N, num_splits, dtype))
 
 
-def rk_online_softmax_auto_splits(M: int, N: int) -> int:
-    return int(load().rk_online_softmax_auto_splits(M, N))
+def rk_online_softmax_auto_splits(M: int, N: int, dtype: int) -> int:
+    return int(load().rk_online_softmax_auto_splits(M, N, dtype))
 
 
 def rk_softmax(x, out=None):
@@ -220,7 +220,7 @@ def rk_online_softmax(x, num_splits: int = 1, out=None, workspace=None):
     _check_device(x)
     v, M, N, ldx = _as_rows(x)
     o, ldy = _out_like(x, v, out)
-    need = rk_online_softmax_workspace_bytes(M, N, num_splits) if M > 0 else 0
+    need = rk_online_softmax_workspace_bytes(M, N, num_splits, _dtype_code(x)) if M > 0 else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = workspace.data_ptr() if workspace is not None else None

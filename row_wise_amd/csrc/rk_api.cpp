@@ -148,19 +148,57 @@ constexpr int kSplitThreads = 256;    // online_partials / online_finish
 constexpr int kLoopThreads = 1024;    // largest rmsnorm_loop workgroup
 constexpr int32_t kMaxSplits = 65536;
 
-int32_t auto_splits(int64_t M, int64_t N)
+// Rates of the rows-in-memory kernels, in elements per microsecond, as
+// measured on 1 to 64 rows of 2^18 to 2^20 elements: one workgroup streaming
+// its row on one CU, and the split kernels with rows spread over the chip.
+struct SplitRates {
+    double row, all;
+};
+
+SplitRates split_rates(rk_op op, rk_dtype dtype)
 {
-    // Enough rows to give every CU workgroups of its own: stream.  Otherwise
-    // aim at >= 2048 workgroups with chunks of >= 2048 elements.
-    if (M >= 512)
+    const bool f32 = dtype == RK_F32;
+    if (op == RK_OP_LAYERNORM_GELU)
+        return f32 ? SplitRates{4300.0, 530000.0} : SplitRates{5400.0, 850000.0};
+    return f32 ? SplitRates{5500.0, 530000.0} : SplitRates{8500.0, 1000000.0};
+}
+
+// The first split kernel's launch and the second pass's merge cost about
+// this much over one workgroup per row; keeping the partials in the output
+// adds a third launch.
+constexpr double kSplitExtraUs = 1.5;
+constexpr double kOutputSplitExtraUs = 5.5;
+
+// Split count for M rows of N: 1 where one workgroup per row is expected to
+// be as fast.  A row streamed by one CU takes N / row microseconds; all rows
+// spread over the chip take M N / all.  Splitting pays when the first exceeds
+// the second by more than `extra_us`, and with a workspace also for rows of
+// 2^16 or more in at most 128 rows, which leave half the CUs idle (measured
+// 5-18% faster at 128 rows, 4-20% slower at 200).  Chunks are about 16 KiB
+// (measured best from 4 KiB to 64 KiB) and at most 2048 workgroups run (more
+// cost more to launch than they gain).
+int32_t pick_splits(rk_op op, int64_t M, int64_t N, rk_dtype dtype, double extra_us)
+{
+    if (M < 1 || N < 1 || M >= 256)
         return 1;
-    int64_t s = (2048 + M - 1) / M;
-    const int64_t by_len = (N + 2047) / 2048;
-    if (s > by_len)
-        s = by_len;
+    const SplitRates r = split_rates(op, dtype);
+    const double gain = N / r.row - static_cast<double>(M) * N / r.all;
+    const bool wide = extra_us <= kSplitExtraUs && N >= 65536 && M <= 128;
+    if (!(gain > extra_us || wide))
+        return 1;
+    const int64_t chunk_elems = 16384 / elem_size(dtype);
+    int64_t s = (N + chunk_elems - 1) / chunk_elems;
+    const int64_t by_grid = 2048 / M;
+    if (s > by_grid)
+        s = by_grid;
     if (s > kMaxSplits)
         s = kMaxSplits;
-    return static_cast<int32_t>(s < 1 ? 1 : s);
+    return static_cast<int32_t>(s < 2 ? 1 : s);
+}
+
+int32_t auto_splits(int64_t M, int64_t N, rk_dtype dtype)
+{
+    return pick_splits(RK_OP_SOFTMAX, M, N, dtype, kSplitExtraUs);
 }
 
 bool softmax_vectorized(const RowProblem &p)
@@ -196,6 +234,36 @@ rk_status softmax_generic(const RowProblem &p)
     return hip_status(online_stream_run(p, softmax_io(p)));
 }
 
+// Long rows in few rows split across workgroups even without a workspace:
+// each row keeps its S partials in its own output, inside the first chunk,
+// which the last of three kernels writes after reading them.  That needs an
+// output apart from the input and a first chunk with room for the S partials
+// and the step to the next 8-byte boundary; S is lowered until it has room.
+// Returns the splits to use (1: none) and, for more, their chunk length.
+SplitPartials output_partials(const RowProblem &p)
+{
+    return SplitPartials{static_cast<char *>(p.y), p.ldy * elem_size(p.dtype), true};
+}
+
+int32_t output_splits(const RowProblem &p, int32_t S, RowIo io, int64_t *chunk)
+{
+    if (S <= 1 || p.x == p.y || p.M > INT64_MAX / S || !grid_ok(p.M * S, kSplitThreads))
+        return 1;
+    const int es = elem_size(p.dtype);
+    const int vec = io != kIoElement ? vec_elems(p.dtype) : 1;
+    // a phased row's first vector holds up to E - 1 columns before the row
+    const int64_t lead = io == kIoPhased ? vec - 1 : 0;
+    for (; S > 1; --S) {
+        const int64_t c = split_chunk(p.N, S, vec);
+        const int64_t first = c - lead < p.N ? c - lead : p.N;
+        if (c <= INT32_MAX && first * es >= 8 * int64_t{S} + 8) {
+            *chunk = c;
+            return S;
+        }
+    }
+    return 1;
+}
+
 rk_status layernorm_generic(const RowProblem &p)
 {
     if (!grid_ok(p.M, kStreamThreads))
@@ -205,12 +273,13 @@ rk_status layernorm_generic(const RowProblem &p)
 
 bool valid_gelu(rk_gelu_kind g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
 
-int32_t layernorm_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
+int32_t layernorm_auto_splits(int64_t M, int64_t N, rk_dtype dtype,
+                              double extra_us = kSplitExtraUs)
 {
     // rows a register tile takes are read once there: no split
     if (pick_variant(RK_OP_LAYERNORM_GELU, dtype, N) >= 0)
         return 1;
-    return auto_splits(M, N);
+    return pick_splits(RK_OP_LAYERNORM_GELU, M, N, dtype, extra_us);
 }
 
 // Bytes of the split-row workspace: (mean, M2) as two floats per chunk.
@@ -288,6 +357,24 @@ bool layernorm_aligned(const RowProblem &p)
 {
     return rows_aligned(p.x, p.y, p.ldx, p.ldy, elem_size(p.dtype)) && aligned16(p.w) &&
            aligned16(p.b);
+}
+
+// LayerNorm+GeLU in one kernel: a register tile where one holds the row,
+// else the streaming kernel.
+rk_status layernorm_single(const RowProblem &p)
+{
+    int count = 0;
+    const TileVariant *v = layernorm_gelu_variants(p.dtype, &count);
+    const int idx = pick_variant(RK_OP_LAYERNORM_GELU, p.dtype, p.N);
+    const bool aligned = layernorm_aligned(p);
+    if (aligned && idx >= 0)
+        return run_tile(v[idx], p);
+    if (!aligned && layernorm_vectorized(p)) {
+        const int ph = pick_phased(RK_OP_LAYERNORM_GELU, p.dtype, p.N);
+        if (ph >= 0)
+            return run_tile(v[ph], p, true);
+    }
+    return layernorm_generic(p);
 }
 
 bool valid_eps(float eps) { return std::isfinite(eps) && eps > 0.0f; }
@@ -433,21 +520,29 @@ RK_EXPORT rk_status rk_softmax(const void *x, void *y, int64_t M, int64_t N, int
         if (ph >= 0)
             return run_tile(v[ph], p, true);
     }
+    const RowIo io = softmax_io(p);
+    int64_t C = 0;
+    const int32_t S =
+        output_splits(p, pick_splits(RK_OP_SOFTMAX, M, N, dtype, kOutputSplitExtraUs), io, &C);
+    if (S > 1)
+        return hip_status(online_split_run(p, S, static_cast<int>(C), output_partials(p), io));
     return softmax_generic(p);
 }
 
-RK_EXPORT int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N)
+RK_EXPORT int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
 {
-    if (M < 1 || N < 1)
+    if (M < 1 || N < 1 || !valid_dtype(dtype))
         return 1;
-    return auto_splits(M, N);
+    return auto_splits(M, N, dtype);
 }
 
-RK_EXPORT size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t num_splits)
+RK_EXPORT size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t num_splits,
+                                                   rk_dtype dtype)
 {
-    if (M < 1 || N < 1 || N > kMaxN || num_splits < 0 || num_splits > kMaxSplits)
+    if (M < 1 || N < 1 || N > kMaxN || num_splits < 0 || num_splits > kMaxSplits ||
+        !valid_dtype(dtype))
         return 0;
-    const int64_t S = num_splits == 0 ? auto_splits(M, N) : num_splits;
+    const int64_t S = num_splits == 0 ? auto_splits(M, N, dtype) : num_splits;
     return split_workspace_bytes(M, S);
 }
 
@@ -463,21 +558,22 @@ RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t
     if (M == 0)
         return RK_OK;
     const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
-    const int32_t S = num_splits == 0 ? auto_splits(M, N) : num_splits;
+    const int32_t S = num_splits == 0 ? auto_splits(M, N, dtype) : num_splits;
     if (S <= 1)
         return softmax_generic(p);
     const RowIo io = softmax_io(p);
     const bool vec = io != kIoElement;
 
     const int es = elem_size(dtype);
-    st = check_workspace(workspace, workspace_bytes, rk_online_softmax_workspace_bytes(M, N, S), M,
-                         S, {matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es)});
+    st = check_workspace(workspace, workspace_bytes, split_workspace_bytes(M, S), M, S,
+                         {matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es)});
     if (st != RK_OK)
         return st;
     const int64_t chunk = split_chunk(N, S, vec ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
-    return hip_status(online_split_run(p, S, static_cast<int>(chunk), workspace, io));
+    const SplitPartials pt{static_cast<char *>(workspace), int64_t{S} * 8, false};
+    return hip_status(online_split_run(p, S, static_cast<int>(chunk), pt, io));
 }
 
 RK_EXPORT int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
@@ -512,21 +608,9 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
         return RK_OK;
     RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
     p.gelu = gelu;
-    const bool aligned = layernorm_aligned(p);
     const int32_t S = num_splits == 0 ? layernorm_auto_splits(M, N, dtype) : num_splits;
-    if (S <= 1) {
-        int count = 0;
-        const TileVariant *v = layernorm_gelu_variants(dtype, &count);
-        const int idx = pick_variant(RK_OP_LAYERNORM_GELU, dtype, N);
-        if (aligned && idx >= 0)
-            return run_tile(v[idx], p);
-        if (!aligned && layernorm_vectorized(p)) {
-            const int ph = pick_phased(RK_OP_LAYERNORM_GELU, dtype, N);
-            if (ph >= 0)
-                return run_tile(v[ph], p, true);
-        }
-        return layernorm_generic(p);
-    }
+    if (S <= 1)
+        return layernorm_single(p);
     const int es = elem_size(dtype);
     st = check_workspace(workspace, workspace_bytes, split_workspace_bytes(M, S), M, S,
                          {matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es),
@@ -538,15 +622,26 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
     const int64_t chunk = split_chunk(N, S, vec ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
-    return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), workspace, io));
+    const SplitPartials pt{static_cast<char *>(workspace), int64_t{S} * 8, false};
+    return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), pt, io));
 }
 
 RK_EXPORT rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias, void *y,
                                       int64_t M, int64_t N, int64_t ldx, int64_t ldy, float eps,
                                       rk_dtype dtype, hipStream_t stream)
 {
-    return rk_layernorm_gelu_ex(x, weight, bias, y, M, N, ldx, ldy, eps, dtype, RK_GELU_TANH, 1,
-                                nullptr, 0, stream);
+    rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
+    if (st != RK_OK || M == 0)
+        return st;
+    RowProblem p = make_problem(x, y, weight, bias, M, N, ldx, ldy, eps, dtype, stream);
+    p.gelu = RK_GELU_TANH;
+    const RowIo io = layernorm_io(p);
+    int64_t C = 0;
+    const int32_t S =
+        output_splits(p, layernorm_auto_splits(M, N, dtype, kOutputSplitExtraUs), io, &C);
+    if (S > 1)
+        return hip_status(layernorm_split_run(p, S, static_cast<int>(C), output_partials(p), io));
+    return layernorm_single(p);
 }
 
 RK_EXPORT rk_status rk_rmsnorm(const void *x, const void *weight, void *y, int64_t M, int64_t N,

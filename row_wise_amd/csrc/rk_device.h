@@ -603,6 +603,25 @@ __device__ __forceinline__ void chunk_span(RowSpan<E> sp, int s, int S, int C, i
     jend = static_cast<int>(s == S - 1 || c0 + C >= len ? nv : (c0 + C) / E);
 }
 
+// A row's split partials (two floats each): at the first 8-byte boundary of
+// base + row * row_bytes (a workspace keeps them 8-byte aligned already).
+__device__ __forceinline__ float2 *row_partials(char *base, int64_t row_bytes, int64_t row)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(base + row * row_bytes);
+    return reinterpret_cast<float2 *>((a + 7) & ~uintptr_t{7});
+}
+
+__device__ __forceinline__ const float2 *row_partials(const char *base, int64_t row_bytes,
+                                                      int64_t row)
+{
+    return row_partials(const_cast<char *>(base), row_bytes, row);
+}
+
+// Which chunks a split-row output kernel writes: all of them, all but the
+// first (the partials sit in the first chunk's output), or only the first
+// (one workgroup per row, after its partials have been read).
+enum SplitPart { kAllChunks = 0, kAllButFirst = 1, kFirstOnly = 2 };
+
 // U vectors of a row in flight: vector k of this lane is j0 + k * STRIDE.
 // issue() starts the loads of the vectors below jend (all of them, unmasked,
 // when `full`) and never waits; finish() unpacks to fp32 and replaces

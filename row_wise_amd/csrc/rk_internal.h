@@ -110,12 +110,24 @@ const TileVariant *rmsnorm_variants(rk_dtype dtype, bool residual, int *count);
 // element at a time.
 enum RowIo { kIoElement = 0, kIoAligned = 1, kIoPhased = 2 };
 
+// Where the split-row kernels keep each row's S partials (two floats each):
+// a caller's workspace (row r at base + r row_bytes, 8-byte aligned, S * 8
+// bytes apart), or the row's own output (the first 8-byte boundary of output
+// row r, inside the row's first chunk).  In the output, the second kernel
+// writes every chunk but the first, and a third kernel, one workgroup per
+// row, reads the partials and then writes the first chunk over them.
+struct SplitPartials {
+    char *base;
+    int64_t row_bytes;
+    bool in_output;
+};
+
 // Generic paths (any alignment, any N).
 hipError_t online_stream_run(const RowProblem &p, RowIo io);
-hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
+hipError_t online_split_run(const RowProblem &p, int splits, int chunk, SplitPartials parts,
                             RowIo io);
 hipError_t layernorm_stream_run(const RowProblem &p, RowIo io);
-hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
+hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, SplitPartials parts,
                                RowIo io);
 hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, RowIo io);
 enum { RK_REDUCE_SUM = 0, RK_REDUCE_MAX = 1 };

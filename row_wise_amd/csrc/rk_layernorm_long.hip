@@ -28,7 +28,10 @@
 //                     (row, chunk) writes the chunk's (mean, M2).
 // layernorm_finish    split-row, second kernel: one workgroup per
 //                     (row, chunk) merges the row's S summaries (each lane a
-//                     subset, then DPP) and writes its chunk.
+//                     subset, then DPP) and writes its chunk.  With the
+//                     summaries kept in the output (no workspace), it runs
+//                     twice: all chunks but the first, then the first one
+//                     per row.
 // Rows are read and written as aligned 16-byte vectors from whatever offset
 // they start at (RowSpan), when input and output rows share that offset;
 // weight and bias, aligned at column 0, are shifted into each row's phase
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(W *kWave *RB) void layernorm_stream(
 template <typename T, int E, int W, int U, bool PH>
 __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restrict__ x, int N,
                                                                 int64_t ldx, int S, int C,
-                                                                float2 *__restrict__ ws)
+                                                                char *pbase, int64_t prow)
 {
     __shared__ float sn[W], sm[W], sq[W];
     const int64_t row = blockIdx.x / S;
@@ -234,25 +237,31 @@ __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restri
                                                    Elem<T>::to_f32(xr[0]));
     st = ln_block_merge<W>(st, sn, sm, sq);
     if (threadIdx.x == 0)
-        ws[blockIdx.x] = make_float2(st.mean, st.m2);
+        row_partials(pbase, prow, row)[s] = make_float2(st.mean, st.m2);
 }
 
+// Chunk s of row r: workgroup (r, s) of a grid of M S (kAllChunks,
+// kAllButFirst: the s = 0 workgroups leave at once) or workgroup r of a grid
+// of M, s = 0 (kFirstOnly).  y and pbase may name the same memory (the
+// partials kept in the output).
 template <typename T, int E, int W, int U, int GK, bool PH>
 __global__ __launch_bounds__(W *kWave) void layernorm_finish(
-    const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
-    T *__restrict__ y, int N, int64_t ldx, int64_t ldy, int S, int C, float inv_n, float eps,
-    const float2 *__restrict__ ws)
+    const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b, T *y, int N,
+    int64_t ldx, int64_t ldy, int S, int C, float inv_n, float eps, const char *pbase,
+    int64_t prow, int part)
 {
-    const int64_t row = blockIdx.x / S;
-    const int s = static_cast<int>(blockIdx.x % S);
+    const int64_t row = part == kFirstOnly ? blockIdx.x : blockIdx.x / S;
+    const int s = part == kFirstOnly ? 0 : static_cast<int>(blockIdx.x % S);
+    if (part == kAllButFirst && s == 0)
+        return;
     const T *xr = x + row * ldx;
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     // Every wave merges the row's S summaries on its own (lane l takes
-    // summaries l, l + 64, ...): no LDS, no barrier, and every workgroup of
-    // the row forms the same bits.  A chunk's count is that of the row
-    // columns its vectors hold.
+    // summaries l, l + 64, ...): no LDS, and every workgroup of the row forms
+    // the same bits.  A chunk's count is that of the row columns its vectors
+    // hold.
     Moments st{0.0f, 0.0f, 0.0f};
-    const float2 *wr = ws + row * S;
+    const float2 *wr = row_partials(pbase, prow, row);
     for (int i = static_cast<int>(threadIdx.x % kWave); i < S; i += kWave) {
         int jb, je;
         chunk_span<E>(sp, i, S, C, jb, je);
@@ -263,6 +272,10 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
     }
     st = wave_merge(st);
     const float rstd = __builtin_amdgcn_rsqf(fmaf(st.m2, inv_n, eps));
+    // the summaries in the output are overwritten below: every wave has read
+    // them first
+    if (part == kFirstOnly)
+        __syncthreads();
 
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
@@ -317,21 +330,31 @@ hipError_t stream_run(const RowProblem &p)
 constexpr int split_vectors(int E) { return E == 1 ? 4 : 2; }
 
 template <typename T, int E, bool PH>
-hipError_t split_run(const RowProblem &p, int S, int C, void *ws)
+hipError_t split_run(const RowProblem &p, int S, int C, SplitPartials pt)
 {
     constexpr int U = split_vectors(E);
     const dim3 grid(static_cast<unsigned>(p.M * S));
-    hipError_t err = launch(layernorm_partials<T, E, kSplitW, U, PH>, grid,
-                            dim3(kSplitW * kWave), p.stream, static_cast<const T *>(p.x), p.N,
-                            p.ldx, S, C, static_cast<float2 *>(ws));
+    const dim3 block(kSplitW * kWave);
+    const T *x = static_cast<const T *>(p.x);
+    hipError_t err = launch(layernorm_partials<T, E, kSplitW, U, PH>, grid, block, p.stream, x,
+                            p.N, p.ldx, S, C, pt.base, pt.row_bytes);
     if (err != hipSuccess)
         return err;
     auto kernel = p.gelu == RK_GELU_ERF ? layernorm_finish<T, E, kSplitW, U, 1, PH>
                                         : layernorm_finish<T, E, kSplitW, U, 0, PH>;
-    return launch(kernel, grid, dim3(kSplitW * kWave), p.stream, static_cast<const T *>(p.x),
-                  static_cast<const T *>(p.w), static_cast<const T *>(p.b),
-                  static_cast<T *>(p.y), p.N, p.ldx, p.ldy, S, C, static_cast<float>(1.0 / p.N),
-                  p.eps, static_cast<const float2 *>(ws));
+    const T *w = static_cast<const T *>(p.w);
+    const T *b = static_cast<const T *>(p.b);
+    T *y = static_cast<T *>(p.y);
+    const float inv_n = static_cast<float>(1.0 / p.N);
+    if (!pt.in_output)
+        return launch(kernel, grid, block, p.stream, x, w, b, y, p.N, p.ldx, p.ldy, S, C, inv_n,
+                      p.eps, pt.base, pt.row_bytes, int{kAllChunks});
+    err = launch(kernel, grid, block, p.stream, x, w, b, y, p.N, p.ldx, p.ldy, S, C, inv_n, p.eps,
+                 pt.base, pt.row_bytes, int{kAllButFirst});
+    if (err != hipSuccess)
+        return err;
+    return launch(kernel, dim3(static_cast<unsigned>(p.M)), block, p.stream, x, w, b, y, p.N,
+                  p.ldx, p.ldy, S, C, inv_n, p.eps, pt.base, pt.row_bytes, int{kFirstOnly});
 }
 
 template <typename T>
@@ -346,14 +369,14 @@ hipError_t stream_io(const RowProblem &p, RowIo io)
 }
 
 template <typename T>
-hipError_t split_io(const RowProblem &p, int S, int C, void *ws, RowIo io)
+hipError_t split_io(const RowProblem &p, int S, int C, SplitPartials pt, RowIo io)
 {
     constexpr int E = Elem<T>::kVec;
     if (io == kIoAligned)
-        return split_run<T, E, false>(p, S, C, ws);
+        return split_run<T, E, false>(p, S, C, pt);
     if (io == kIoPhased)
-        return split_run<T, E, true>(p, S, C, ws);
-    return split_run<T, 1, false>(p, S, C, ws);
+        return split_run<T, E, true>(p, S, C, pt);
+    return split_run<T, 1, false>(p, S, C, pt);
 }
 
 }  // namespace
@@ -363,11 +386,11 @@ hipError_t layernorm_stream_run(const RowProblem &p, RowIo io)
     return p.dtype == RK_F32 ? stream_io<float>(p, io) : stream_io<bf16_t>(p, io);
 }
 
-hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, void *workspace,
+hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, SplitPartials parts,
                                RowIo io)
 {
-    return p.dtype == RK_F32 ? split_io<float>(p, splits, chunk, workspace, io)
-                             : split_io<bf16_t>(p, splits, chunk, workspace, io);
+    return p.dtype == RK_F32 ? split_io<float>(p, splits, chunk, parts, io)
+                             : split_io<bf16_t>(p, splits, chunk, parts, io);
 }
 
 }  // namespace rk

@@ -16,7 +16,9 @@
 //                  writes the chunk's (m_s, d_s) to the workspace.
 // online_finish    split-row, second kernel: one workgroup per (row, chunk)
 //                  merges the row's S partials (each lane a subset, then
-//                  DPP) and writes its chunk.
+//                  DPP) and writes its chunk.  With the partials kept in the
+//                  output (no workspace), it runs twice: all chunks but the
+//                  first, then the first one per row.
 // Rows are read and written as aligned 16-byte vectors from whatever offset
 // they start at (RowSpan), when input and output rows share that offset;
 // E = 1 (one element per access) serves the rest.
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(W *kWave *RB) void online_stream(const T *__restric
 template <typename T, int E, int W, int U, bool PH>
 __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict__ x, int N,
                                                              int64_t ldx, int S, int C,
-                                                             float2 *__restrict__ ws)
+                                                             char *pbase, int64_t prow)
 {
     __shared__ float sm[W], sd[W];
     const int64_t row = blockIdx.x / S;
@@ -199,27 +201,37 @@ __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict_
     SoftmaxState st = scan_range<T, E, W, U, kCached>(xr - sp.h, sp, jbeg, jend);
     st = block_merge<W>(st, sm, sd);
     if (threadIdx.x == 0)
-        ws[blockIdx.x] = make_float2(st.m, st.d);
+        row_partials(pbase, prow, row)[s] = make_float2(st.m, st.d);
 }
 
+// Chunk s of row r: workgroup (r, s) of a grid of M S (kAllChunks,
+// kAllButFirst: the s = 0 workgroups leave at once) or workgroup r of a grid
+// of M, s = 0 (kFirstOnly).
+// y and pbase may name the same memory (the partials kept in the output).
 template <typename T, int E, int W, int U, bool PH>
-__global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ x,
-                                                           T *__restrict__ y, int N, int64_t ldx,
-                                                           int64_t ldy, int S, int C,
-                                                           const float2 *__restrict__ ws)
+__global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ x, T *y, int N,
+                                                           int64_t ldx, int64_t ldy, int S, int C,
+                                                           const char *pbase, int64_t prow,
+                                                           int part)
 {
-    const int64_t row = blockIdx.x / S;
-    const int s = static_cast<int>(blockIdx.x % S);
+    const int64_t row = part == kFirstOnly ? blockIdx.x : blockIdx.x / S;
+    const int s = part == kFirstOnly ? 0 : static_cast<int>(blockIdx.x % S);
+    if (part == kAllButFirst && s == 0)
+        return;
     // Every wave merges the row's S partials on its own (lane l takes
-    // partials l, l + 64, ...), so no LDS or barrier is needed, and every
-    // workgroup of the row forms the same bits.
+    // partials l, l + 64, ...), so no LDS is needed, and every workgroup of
+    // the row forms the same bits.
     SoftmaxState st{-INFINITY, 0.0f};
-    const float2 *wr = ws + row * S;
+    const float2 *wr = row_partials(pbase, prow, row);
     for (int i = static_cast<int>(threadIdx.x % kWave); i < S; i += kWave) {
         const float2 p = wr[i];
         st = merge(st, SoftmaxState{p.x, p.y});
     }
     st = wave_merge(st);
+    // the partials in the output are overwritten below: every wave has read
+    // them first
+    if (part == kFirstOnly)
+        __syncthreads();
 
     const T *xr = x + row * ldx;
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
@@ -264,17 +276,26 @@ hipError_t stream_run(const RowProblem &p)
 }
 
 template <typename T, int E, bool PH>
-hipError_t split_run(const RowProblem &p, int S, int C, void *ws)
+hipError_t split_run(const RowProblem &p, int S, int C, SplitPartials pt)
 {
     const dim3 grid(static_cast<unsigned>(p.M * S));
-    hipError_t err = launch(online_partials<T, E, kSplitW, kSplitU, PH>, grid,
-                            dim3(kSplitW * kWave), p.stream, static_cast<const T *>(p.x), p.N,
-                            p.ldx, S, C, static_cast<float2 *>(ws));
+    const dim3 block(kSplitW * kWave);
+    hipError_t err = launch(online_partials<T, E, kSplitW, kSplitU, PH>, grid, block, p.stream,
+                            static_cast<const T *>(p.x), p.N, p.ldx, S, C, pt.base, pt.row_bytes);
     if (err != hipSuccess)
         return err;
-    return launch(online_finish<T, E, kSplitW, kSplitU, PH>, grid, dim3(kSplitW * kWave),
-                  p.stream, static_cast<const T *>(p.x), static_cast<T *>(p.y), p.N, p.ldx, p.ldy,
-                  S, C, static_cast<const float2 *>(ws));
+    auto finish = online_finish<T, E, kSplitW, kSplitU, PH>;
+    const T *x = static_cast<const T *>(p.x);
+    T *y = static_cast<T *>(p.y);
+    if (!pt.in_output)
+        return launch(finish, grid, block, p.stream, x, y, p.N, p.ldx, p.ldy, S, C, pt.base,
+                      pt.row_bytes, int{kAllChunks});
+    err = launch(finish, grid, block, p.stream, x, y, p.N, p.ldx, p.ldy, S, C, pt.base,
+                 pt.row_bytes, int{kAllButFirst});
+    if (err != hipSuccess)
+        return err;
+    return launch(finish, dim3(static_cast<unsigned>(p.M)), block, p.stream, x, y, p.N, p.ldx,
+                  p.ldy, S, C, pt.base, pt.row_bytes, int{kFirstOnly});
 }
 
 template <typename T>
@@ -289,14 +310,14 @@ hipError_t stream_io(const RowProblem &p, RowIo io)
 }
 
 template <typename T>
-hipError_t split_io(const RowProblem &p, int S, int C, void *ws, RowIo io)
+hipError_t split_io(const RowProblem &p, int S, int C, SplitPartials pt, RowIo io)
 {
     constexpr int E = Elem<T>::kVec;
     if (io == kIoAligned)
-        return split_run<T, E, false>(p, S, C, ws);
+        return split_run<T, E, false>(p, S, C, pt);
     if (io == kIoPhased)
-        return split_run<T, E, true>(p, S, C, ws);
-    return split_run<T, 1, false>(p, S, C, ws);
+        return split_run<T, E, true>(p, S, C, pt);
+    return split_run<T, 1, false>(p, S, C, pt);
 }
 
 }  // namespace
@@ -306,10 +327,11 @@ hipError_t online_stream_run(const RowProblem &p, RowIo io)
     return p.dtype == RK_F32 ? stream_io<float>(p, io) : stream_io<bf16_t>(p, io);
 }
 
-hipError_t online_split_run(const RowProblem &p, int splits, int chunk, void *workspace, RowIo io)
+hipError_t online_split_run(const RowProblem &p, int splits, int chunk, SplitPartials parts,
+                            RowIo io)
 {
-    return p.dtype == RK_F32 ? split_io<float>(p, splits, chunk, workspace, io)
-                             : split_io<bf16_t>(p, splits, chunk, workspace, io);
+    return p.dtype == RK_F32 ? split_io<float>(p, splits, chunk, parts, io)
+                             : split_io<bf16_t>(p, splits, chunk, parts, io);
 }
 
 }  // namespace rk

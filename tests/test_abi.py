@@ -259,14 +259,37 @@ def test_online_rejects(lib):
 
 
 def test_workspace_bytes(lib):
-    assert rk.rk_online_softmax_workspace_bytes(64, 262144, 64) == 64 * 64 * 8
-    assert rk.rk_online_softmax_workspace_bytes(64, 262144, 1) == 0
-    assert rk.rk_online_softmax_workspace_bytes(64, 262144, -1) == 0
-    assert rk.rk_online_softmax_workspace_bytes(0, 10, 4) == 0
-    s = rk.rk_online_softmax_auto_splits(64, 262144)
-    assert s >= 2 and rk.rk_online_softmax_workspace_bytes(64, 262144, 0) == 64 * s * 8
-    assert rk.rk_online_softmax_auto_splits(16384, 4096) == 1
-    assert rk.rk_online_softmax_auto_splits(1, 10) == 1
+    assert rk.rk_online_softmax_workspace_bytes(64, 262144, 64, F32) == 64 * 64 * 8
+    assert rk.rk_online_softmax_workspace_bytes(64, 262144, 1, F32) == 0
+    assert rk.rk_online_softmax_workspace_bytes(64, 262144, -1, F32) == 0
+    assert rk.rk_online_softmax_workspace_bytes(0, 10, 4, F32) == 0
+    assert rk.rk_online_softmax_workspace_bytes(64, 262144, 4, 9) == 0
+    for dt in (F32, BF16):
+        s = rk.rk_online_softmax_auto_splits(64, 262144, dt)
+        assert s >= 2 and rk.rk_online_softmax_workspace_bytes(64, 262144, 0, dt) == 64 * s * 8
+    assert rk.rk_online_softmax_auto_splits(16384, 4096, F32) == 1
+    assert rk.rk_online_softmax_auto_splits(1, 10, F32) == 1
+    assert rk.rk_online_softmax_auto_splits(64, 262144, 9) == 1
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_auto_split_policy(dt):
+    """Splits only where rows are long and too few to fill the chip, with
+    chunks of about 16 KiB and at most 2048 workgroups."""
+    es = 4 if dt == F32 else 2
+    for M, N in ((1, 1 << 20), (4, 262144), (16, 65536), (64, 262144), (32, 131072),
+                 (128, 131072), (128, 65536)):
+        s = rk.rk_online_softmax_auto_splits(M, N, dt)
+        assert 2 <= s and M * s <= 2048, (M, N)
+        assert s == min(-(-N * es // 16384), 2048 // M), (M, N)
+    # a full chip of rows, or rows one CU streams quickly: one kernel
+    for M, N in ((256, 1 << 20), (4096, 65536), (200, 65536), (200, 16384), (128, 16384),
+                 (1, 2048)):
+        assert rk.rk_online_softmax_auto_splits(M, N, dt) == 1, (M, N)
+    # LayerNorm+GeLU: rows past the register tiles follow the same rule
+    assert rk.rk_layernorm_gelu_auto_splits(64, 262144, dt) == \
+        rk.rk_online_softmax_auto_splits(64, 262144, dt)
+    assert rk.rk_layernorm_gelu_auto_splits(256, 262144, dt) == 1
 
 
 def test_probe_copy_rejects(lib):

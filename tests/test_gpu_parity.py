@@ -84,11 +84,66 @@ def test_online_f32_64x262144(splits):
     assert err <= TOL["f32"]
 
 
-def test_softmax_long_rows_route_to_streaming():
+def test_softmax_long_rows_few_rows():
+    """8 rows of 262144: rk_softmax splits each row across workgroups with the
+    chunk partials kept in the row's own output; same kernels, same split
+    count and the same bits as rk_online_softmax with a workspace."""
     d = rowgen.make("online_f32_64x262144", rows=8)
     x = d["x_softmax"]
-    y = rk.rk_softmax(x.to(DEV))
+    xd = x.to(DEV)
+    y = rk.rk_softmax(xd)
     assert rel_err_softmax(y, oracle.softmax(x)) <= TOL["f32"]
+    S = rk.rk_online_softmax_auto_splits(8, 262144, rk.RK_F32)
+    assert S > 1
+    assert torch.equal(y, rk.rk_online_softmax(xd, num_splits=S))
+
+
+OUT_SPLIT_CASES = [(1, 1 << 20), (3, 40001), (5, 30000), (64, 65536), (200, 12288)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+@pytest.mark.parametrize("M,N", OUT_SPLIT_CASES)
+def test_partials_in_output(dtype, M, N):
+    """rk_softmax and rk_layernorm_gelu on long rows in few rows keep the split
+    partials inside each output row's first chunk (one bf16 row of 2^20 has
+    its split count lowered until they fit) and write that chunk last:
+    aligned rows, rows at their own offsets (odd N), input and output at
+    different offsets (element access) with padded output pitch whose gaps
+    stay untouched, and in place (one kernel per row instead)."""
+    w, b = rowgen.ln_params(N, torch.Generator().manual_seed(N + M), dtype)
+    wd, bd = w.to(DEV), b.to(DEV)
+    x = rowgen.randn(M, N, seed=M + 3 * N, scale=3.0, dtype=dtype)
+    x[::2] += 20.0
+    ref_s = oracle.softmax(x)
+    ref_l = oracle.layernorm_gelu(x, w, b, EPS)
+    tol = tol_of(dtype)
+    xd = x.to(DEV)
+    say(f"partials in output {key(dtype)} M={M} N={N}")
+    assert rel_err_softmax(rk.rk_softmax(xd), ref_s) <= tol
+    assert rel_err_floor1(rk.rk_layernorm_gelu(xd, wd, bd, EPS), ref_l) <= tol
+    # output one element into a buffer with 5 spare columns per row
+    canary = -5.0
+    buf = torch.full((M, N + 5), canary, dtype=dtype, device=DEV)
+    out = buf.view(-1)[1:1 + (M - 1) * (N + 5) + N].as_strided((M, N), (N + 5, 1))
+    for name, run, ref, err in (
+            ("softmax", lambda o: rk.rk_softmax(xd, out=o), ref_s, rel_err_softmax),
+            ("layernorm", lambda o: rk.rk_layernorm_gelu(xd, wd, bd, EPS, out=o), ref_l,
+             rel_err_floor1)):
+        buf.fill_(canary)
+        run(out)
+        assert err(out, ref) <= tol, name
+        flat = buf.view(-1).cpu()
+        mask = torch.ones(flat.numel(), dtype=torch.bool)
+        for r in range(M):
+            mask[1 + r * (N + 5):1 + r * (N + 5) + N] = False
+        assert torch.all(flat[mask].float() == canary), name
+    # in place
+    xi = x.to(DEV)
+    rk.rk_softmax(xi, out=xi)
+    assert rel_err_softmax(xi, ref_s) <= tol
+    xi = x.to(DEV)
+    rk.rk_layernorm_gelu(xi, wd, bd, EPS, out=xi)
+    assert rel_err_floor1(xi, ref_l) <= tol
 
 
 def test_bf16_16384x4096_layernorm_gelu():

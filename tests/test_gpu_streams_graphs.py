@@ -34,8 +34,8 @@ def test_graph_capture_and_replay():
     xs = rowgen.randn(64, 20000, seed=301).to(DEV)
     res = rowgen.residual("ln_gelu_f32_4096x768").to(DEV)
     q, k, v = (t.to(DEV) for t in rowgen.attention_qkv(1, 4, 300, 128, torch.bfloat16, seed=302))
-    ws = torch.empty(rk.rk_online_softmax_workspace_bytes(64, 20000, 4), dtype=torch.uint8,
-                     device=DEV)
+    ws = torch.empty(rk.rk_online_softmax_workspace_bytes(64, 20000, 4, rk.RK_F32),
+                     dtype=torch.uint8, device=DEV)
     outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn")}
 
     def step():
