@@ -149,21 +149,36 @@ __device__ __forceinline__ Moments ln_block_merge(Moments st, float *sn, float *
     return st;
 }
 
+// The row loads of ln_write_range's first step, issued by the caller ahead of
+// the merge that forms the statistics, so that they are in flight meanwhile.
+template <typename T, int E, int W, int U>
+__device__ __forceinline__ SpanLoad<T, E, U, W * kWave> ln_write_first(const T *__restrict__ xb,
+                                                                       RowSpan<E> sp, int jbeg,
+                                                                       int jend)
+{
+    constexpr int NT = W * kWave;
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    SpanLoad<T, E, U, NT> cur;
+    cur.issue(xb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
+              jbeg >= sp.full_begin() && jbeg + NT * U <= fe);
+    return cur;
+}
+
 // y = GeLU(((x - K) - mean_K) rstd w + b) for vectors [jbeg, jend) of a row
-// (aligned bases xb, yb; w and b by column).
+// (aligned bases xb, yb; w and b by column); the first step's row loads come
+// issued (ln_write_first).
 template <typename T, int E, int W, int U, int GK>
 __device__ __forceinline__ void ln_write_range(const T *__restrict__ xb,
                                                const T *__restrict__ w, const T *__restrict__ b,
                                                T *__restrict__ yb, RowSpan<E> sp, int jbeg,
-                                               int jend, float K, float mean_k, float rstd)
+                                               int jend, float K, float mean_k, float rstd,
+                                               SpanLoad<T, E, U, W * kWave> cur)
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
     const int fb = sp.full_begin();
     const int fe = jend < sp.full_end() ? jend : sp.full_end();
     auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
-    SpanLoad<T, E, U, NT> cur;
-    cur.issue(xb, jbeg + tid, jend, full(jbeg));
     for (int base = jbeg; base < jend; base += NT * U) {
         const bool f = full(base);
         // weight and bias, the next step's row and this step's row are all in
@@ -214,9 +229,11 @@ __global__ __launch_bounds__(W *kWave *RB) void layernorm_stream(
     const int nv = sp.count();
     const float K = Elem<T>::to_f32(xr[0]);
     Moments st = scan_moments<T, E, W, U, kCached>(xb, sp, 0, nv, K);
+    const auto first = ln_write_first<T, E, W, U>(xb, sp, 0, nv);
     st = ln_block_merge<W>(st, sn, sm, sq);
     const float rstd = __builtin_amdgcn_rsqf(fmaf(st.m2, inv_n, eps));
-    ln_write_range<T, E, W, U, GK>(xb, w, b, y + row * ldy - sp.h, sp, 0, nv, K, st.mean, rstd);
+    ln_write_range<T, E, W, U, GK>(xb, w, b, y + row * ldy - sp.h, sp, 0, nv, K, st.mean, rstd,
+                                   first);
 }
 
 template <typename T, int E, int W, int U, bool PH>
@@ -256,6 +273,12 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
         return;
     const T *xr = x + row * ldx;
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
+    // the chunk's first loads and the shift K go out before the summaries
+    // are read
+    const auto first = ln_write_first<T, E, W, U>(xr - sp.h, sp, jbeg, jend);
+    const float K = Elem<T>::to_f32(xr[0]);
     // Every wave merges the row's S summaries on its own (lane l takes
     // summaries l, l + 64, ...): no LDS, and every workgroup of the row forms
     // the same bits.  A chunk's count is that of the row columns its vectors
@@ -276,11 +299,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
     // them first
     if (part == kFirstOnly)
         __syncthreads();
-
-    int jbeg, jend;
-    chunk_span<E>(sp, s, S, C, jbeg, jend);
-    ln_write_range<T, E, W, U, GK>(xr - sp.h, w, b, y + row * ldy - sp.h, sp, jbeg, jend,
-                                   Elem<T>::to_f32(xr[0]), st.mean, rstd);
+    ln_write_range<T, E, W, U, GK>(xr - sp.h, w, b, y + row * ldy - sp.h, sp, jbeg, jend, K,
+                                   st.mean, rstd, first);
 }
 
 // ------------------------------------------------------------------ host

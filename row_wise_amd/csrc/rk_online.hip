@@ -127,10 +127,27 @@ __device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xb, Row
     return st;
 }
 
-// Write exp(x - m) / d for vectors [jbeg, jend) of a row (bases xb, yb).
+// The loads of write_range's first step, issued by the caller ahead of the
+// merge that forms the row's state, so that they are in flight meanwhile.
+template <typename T, int E, int W, int U>
+__device__ __forceinline__ SpanLoad<T, E, U, W * kWave> write_first(const T *__restrict__ xb,
+                                                                    RowSpan<E> sp, int jbeg,
+                                                                    int jend)
+{
+    constexpr int NT = W * kWave;
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    SpanLoad<T, E, U, NT> cur;
+    cur.issue(xb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
+              jbeg >= sp.full_begin() && jbeg + NT * U <= fe);
+    return cur;
+}
+
+// Write exp(x - m) / d for vectors [jbeg, jend) of a row (bases xb, yb); the
+// first step's loads come issued (write_first).
 template <typename T, int E, int W, int U>
 __device__ __forceinline__ void write_range(const T *__restrict__ xb, T *__restrict__ yb,
-                                            RowSpan<E> sp, int jbeg, int jend, SoftmaxState st)
+                                            RowSpan<E> sp, int jbeg, int jend, SoftmaxState st,
+                                            SpanLoad<T, E, U, W * kWave> cur)
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
@@ -139,8 +156,6 @@ __device__ __forceinline__ void write_range(const T *__restrict__ xb, T *__restr
     const int fb = sp.full_begin();
     const int fe = jend < sp.full_end() ? jend : sp.full_end();
     auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
-    SpanLoad<T, E, U, NT> cur;
-    cur.issue(xb, jbeg + tid, jend, full(jbeg));
     for (int base = jbeg; base < jend; base += NT * U) {
         SpanLoad<T, E, U, NT> nxt;
         const int next = base + NT * U;
@@ -179,8 +194,9 @@ __global__ __launch_bounds__(W *kWave *RB) void online_stream(const T *__restric
     const int nv = sp.count();
     // pass 1 leaves the row in the caches for pass 2
     SoftmaxState st = scan_range<T, E, W, U, kCached>(xb, sp, 0, nv);
+    const auto first = write_first<T, E, W, U>(xb, sp, 0, nv);
     st = block_merge<W>(st, sm, sd);
-    write_range<T, E, W, U>(xb, yb, sp, 0, nv, st);
+    write_range<T, E, W, U>(xb, yb, sp, 0, nv, st, first);
 }
 
 // Partials of chunk s = blockIdx.x % S of row blockIdx.x / S.
@@ -218,6 +234,12 @@ __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ 
     const int s = part == kFirstOnly ? 0 : static_cast<int>(blockIdx.x % S);
     if (part == kAllButFirst && s == 0)
         return;
+    const T *xr = x + row * ldx;
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
+    // the chunk's first loads go out before the partials are read
+    const auto first = write_first<T, E, W, U>(xr - sp.h, sp, jbeg, jend);
     // Every wave merges the row's S partials on its own (lane l takes
     // partials l, l + 64, ...), so no LDS is needed, and every workgroup of
     // the row forms the same bits.
@@ -232,12 +254,7 @@ __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ 
     // them first
     if (part == kFirstOnly)
         __syncthreads();
-
-    const T *xr = x + row * ldx;
-    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
-    int jbeg, jend;
-    chunk_span<E>(sp, s, S, C, jbeg, jend);
-    write_range<T, E, W, U>(xr - sp.h, y + row * ldy - sp.h, sp, jbeg, jend, st);
+    write_range<T, E, W, U>(xr - sp.h, y + row * ldy - sp.h, sp, jbeg, jend, st, first);
 }
 
 // ------------------------------------------------------------------ host

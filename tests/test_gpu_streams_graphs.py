@@ -36,11 +36,18 @@ def test_graph_capture_and_replay():
     q, k, v = (t.to(DEV) for t in rowgen.attention_qkv(1, 4, 300, 128, torch.bfloat16, seed=302))
     ws = torch.empty(rk.rk_online_softmax_workspace_bytes(64, 20000, 4, rk.RK_F32),
                      dtype=torch.uint8, device=DEV)
-    outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn")}
+    # 8 rows of 65536: rk_softmax and rk_layernorm_gelu split them with the
+    # partials kept in the output (three kernels, no workspace)
+    xl = rowgen.randn(8, 65536, seed=303).to(DEV)
+    wl, bl = (t.to(DEV) for t in rowgen.ln_params(65536, torch.Generator().manual_seed(304),
+                                                  torch.float32))
+    outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn", "sml", "lnl")}
 
     def step():
         outs["ln"] = rk.rk_layernorm_gelu(x, w, b, EPS, out=outs["ln"])
         outs["sm"] = rk.rk_online_softmax(xs, num_splits=4, out=outs["sm"], workspace=ws)
+        outs["sml"] = rk.rk_softmax(xl, out=outs["sml"])
+        outs["lnl"] = rk.rk_layernorm_gelu(xl, wl, bl, EPS, out=outs["lnl"])
         y, r = rk.rk_residual_rmsnorm(x, res, w, EPS, out=outs["rms"], residual_out=outs["ro"])
         outs["rms"], outs["ro"] = y, r
         outs["attn"] = rk.rk_flash_attention(q, k, v, causal=True, out=outs["attn"])
@@ -60,6 +67,7 @@ def test_graph_capture_and_replay():
         # new inputs each time, written by eager work between replays
         x.copy_(rowgen.randn(4096, 768, seed=310 + rep).to(DEV))
         xs.copy_(rowgen.randn(64, 20000, seed=320 + rep).to(DEV))
+        xl.copy_(rowgen.randn(8, 65536, seed=330 + rep).to(DEV))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
