@@ -233,7 +233,11 @@ int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
  * x [M][ldx], y [M][ldy], weight [N] (contiguous), all of `dtype`.  Register
  * resident up to N = 16384 (fp32) / 32768 (bf16), 16-byte aligned or at a
  * shared offset (see Alignment; N + 3 / N + 7 up to those), with one read
- * and one write per element; other rows are read twice by a looping kernel.
+ * and one write per element; other rows are read twice by a looping kernel,
+ * one workgroup per row, or, for long rows in few rows when y aliases no
+ * input, split across workgroups with each chunk's sum of squares kept in
+ * the row's first output chunk, which a third kernel writes last (as
+ * rk_softmax does).
  *
  * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight is NULL with
  * M > 0, eps is not finite and > 0, or y overlaps weight.

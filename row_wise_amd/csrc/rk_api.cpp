@@ -160,6 +160,8 @@ SplitRates split_rates(rk_op op, rk_dtype dtype)
     const bool f32 = dtype == RK_F32;
     if (op == RK_OP_LAYERNORM_GELU)
         return f32 ? SplitRates{4300.0, 530000.0} : SplitRates{5400.0, 850000.0};
+    if (op == RK_OP_RMSNORM || op == RK_OP_RESIDUAL_RMSNORM)
+        return f32 ? SplitRates{7000.0, 575000.0} : SplitRates{11500.0, 1100000.0};
     return f32 ? SplitRates{5500.0, 530000.0} : SplitRates{8500.0, 1000000.0};
 }
 
@@ -474,6 +476,19 @@ rk_status rmsnorm_generic(const RowProblem &p, bool residual)
     return hip_status(rmsnorm_loop_run(p, residual, rmsnorm_io(p, residual)));
 }
 
+// Long rows in few rows that no tile takes split with the partials kept in
+// y, which may then alias neither input.
+int32_t rmsnorm_output_splits(const RowProblem &p, bool residual, rk_op op, RowIo io,
+                              int64_t *chunk)
+{
+    if (pick_variant(op, p.dtype, p.N) >= 0 || (residual && p.r == p.y))
+        return 1;
+    // the fused form splits exactly where the plain one does, so that its y
+    // stays bitwise the plain RMSNorm of its residual_out
+    return output_splits(p, pick_splits(RK_OP_RMSNORM, p.M, p.N, p.dtype, kOutputSplitExtraUs),
+                         io, chunk);
+}
+
 rk_status rmsnorm_dispatch(const RowProblem &p, bool residual, int32_t index, bool forced)
 {
     int count = 0;
@@ -495,6 +510,12 @@ rk_status rmsnorm_dispatch(const RowProblem &p, bool residual, int32_t index, bo
         if (ph >= 0)
             return run_tile(v[ph], p, true);
     }
+    const RowIo io = rmsnorm_io(p, residual);
+    int64_t C = 0;
+    const int32_t S = rmsnorm_output_splits(p, residual, op, io, &C);
+    if (S > 1)
+        return hip_status(
+            rmsnorm_split_run(p, residual, S, static_cast<int>(C), output_partials(p), io));
     return rmsnorm_generic(p, residual);
 }
 

@@ -130,6 +130,8 @@ hipError_t layernorm_stream_run(const RowProblem &p, RowIo io);
 hipError_t layernorm_split_run(const RowProblem &p, int splits, int chunk, SplitPartials parts,
                                RowIo io);
 hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, RowIo io);
+hipError_t rmsnorm_split_run(const RowProblem &p, bool residual, int splits, int chunk,
+                             SplitPartials parts, RowIo io);
 enum { RK_REDUCE_SUM = 0, RK_REDUCE_MAX = 1 };
 hipError_t row_reduce_run(const RowProblem &p, int op);
 // Workgroups (and threads per workgroup) row_reduce_run launches.

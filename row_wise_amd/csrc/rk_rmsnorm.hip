@@ -13,6 +13,12 @@
 //               row group for its R rows.
 // rmsnorm_loop  1, 4 or 16 waves per row by its length, two passes over the
 //               row in memory; any N, any alignment.
+// rmsnorm_partials + rmsnorm_finish
+//               long rows in few rows, split across workgroups: the first
+//               kernel writes each chunk's sum of squares, the second sums
+//               the row's S partials and writes its chunk (run twice, all
+//               chunks but the first and then the first, when the partials
+//               are kept in the output).
 #include "rk_device.h"
 #include "rk_internal.h"
 
@@ -295,6 +301,112 @@ struct RmsStep {
     }
 };
 
+// This thread's part of the sum of v^2 over vectors [jbeg, jend) of a row
+// (bases xb, rb at the row's phase), software-pipelined, cached loads: the
+// output pass reads the row again.
+template <typename T, int E, int W, int U, bool RES>
+__device__ __forceinline__ float rms_scan(const T *__restrict__ xb, const T *__restrict__ rb,
+                                          RowSpan<E> sp, int jbeg, int jend)
+{
+    constexpr int NT = W * kWave;
+    const int tid = static_cast<int>(threadIdx.x % NT);
+    const int fb = sp.full_begin();
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    float q = 0.0f;
+    RmsStep<T, E, U, NT, kCached, RES> cur;
+    cur.issue(xb, rb, jbeg + tid, jend, full(jbeg));
+    for (int base = jbeg; base < jend; base += NT * U) {
+        RmsStep<T, E, U, NT, kCached, RES> nxt;
+        const int next = base + NT * U;
+        if (next < jend)
+            nxt.issue(xb, rb, next + tid, jend, full(next));
+        float v[U][E];
+        cur.finish(v, sp, jend, full(base));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                q = fmaf(v[u][e], v[u][e], q);
+        cur = nxt;
+    }
+    return q;
+}
+
+// The loads of rms_write's first step, issued by the caller ahead of the
+// reduction that forms inv, so that they are in flight meanwhile.
+template <typename T, int E, int W, int U, bool RES>
+__device__ __forceinline__ RmsStep<T, E, U, W * kWave, kStreaming, RES>
+rms_write_first(const T *__restrict__ xb, const T *__restrict__ rb, RowSpan<E> sp, int jbeg,
+                int jend)
+{
+    constexpr int NT = W * kWave;
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    RmsStep<T, E, U, NT, kStreaming, RES> cur;
+    cur.issue(xb, rb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
+              jbeg >= sp.full_begin() && jbeg + NT * U <= fe);
+    return cur;
+}
+
+// Store residual_out (RES) and y = v inv w for vectors [jbeg, jend) of a row;
+// the first step's loads come issued (rms_write_first).
+template <typename T, int E, int W, int U, bool RES>
+__device__ __forceinline__ void rms_write(const T *__restrict__ xb, const T *__restrict__ rb,
+                                          const T *__restrict__ w, T *yb, T *ob, RowSpan<E> sp,
+                                          int jbeg, int jend, float inv,
+                                          RmsStep<T, E, U, W * kWave, kStreaming, RES> cur)
+{
+    constexpr int NT = W * kWave;
+    const int tid = static_cast<int>(threadIdx.x % NT);
+    const int fb = sp.full_begin();
+    const int fe = jend < sp.full_end() ? jend : sp.full_end();
+    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    for (int base = jbeg; base < jend; base += NT * U) {
+        const bool f = full(base);
+        // the weight, the next step's row and this step's row are all in
+        // flight before the first wait
+        ParamLoad<T, E> wl[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            wl[u].issue(w, base + tid + u * NT, sp.h, sp.n, f);
+        RmsStep<T, E, U, NT, kStreaming, RES> nxt;
+        const int next = base + NT * U;
+        if (next < jend)
+            nxt.issue(xb, rb, next + tid, jend, full(next));
+        float v[U][E], wv[U][E];
+        cur.finish(v, sp, jend, f);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            wl[u].finish(wv[u], base + tid + u * NT, sp.h, sp.n, f);
+        if constexpr (RES)
+            store_span<T, E, U, NT>(ob, base + tid, jend, sp, v, f);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[u][e] = v[u][e] * inv * wv[u][e];
+        store_span<T, E, U, NT>(yb, base + tid, jend, sp, v, f);
+        cur = nxt;
+    }
+}
+
+// Sum of the W waves' parts (wave DPP, then LDS across waves).
+template <int W>
+__device__ __forceinline__ float rms_block_sum(float q, float *red)
+{
+    q = wave_sum(q);
+    if constexpr (W > 1) {
+        if (threadIdx.x % kWave == 0)
+            red[threadIdx.x / kWave] = q;
+        __syncthreads();
+        q = red[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i)
+            q += red[i];
+    }
+    return q;
+}
+
 // One row per W waves, RB rows per workgroup (several only for W == 1,
 // where no barrier is taken).  Pass 1 (cached loads) sums v^2; pass 2
 // re-reads the row, stores residual_out (RES) and y = v inv w.  Rows are
@@ -307,9 +419,8 @@ __global__ __launch_bounds__(W *kWave *RB) void rmsnorm_loop(
     int64_t ldy, int64_t ldo, float inv_n, float eps)
 {
     static_assert(RB == 1 || W == 1, "several rows per workgroup only with one wave each");
-    constexpr int NT = W * kWave;
     __shared__ float red[W];
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * RB + threadIdx.x / NT;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RB + threadIdx.x / (W * kWave);
     if (RB > 1 && row >= M)
         return;
     const T *xr = x + row * ldx;
@@ -317,73 +428,71 @@ __global__ __launch_bounds__(W *kWave *RB) void rmsnorm_loop(
     const T *xb = xr - sp.h;
     const T *rb = RES ? res + row * ldr - sp.h : nullptr;
     const int nv = sp.count();
-    const int tid = static_cast<int>(threadIdx.x % NT);
-    const int fb = sp.full_begin();
-    const int fe = sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
-
-    float q = 0.0f;
-    {
-        RmsStep<T, E, U, NT, kCached, RES> cur;
-        cur.issue(xb, rb, tid, nv, full(0));
-        for (int base = 0; base < nv; base += NT * U) {
-            RmsStep<T, E, U, NT, kCached, RES> nxt;
-            const int next = base + NT * U;
-            if (next < nv)
-                nxt.issue(xb, rb, next + tid, nv, full(next));
-            float v[U][E];
-            cur.finish(v, sp, nv, full(base));
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    q = fmaf(v[u][e], v[u][e], q);
-            cur = nxt;
-        }
-    }
-    q = wave_sum(q);
-    if constexpr (W > 1) {
-        if (threadIdx.x % kWave == 0)
-            red[threadIdx.x / kWave] = q;
-        __syncthreads();
-        q = red[0];
-#pragma unroll
-        for (int i = 1; i < W; ++i)
-            q += red[i];
-    }
+    float q = rms_scan<T, E, W, U, RES>(xb, rb, sp, 0, nv);
+    const auto first = rms_write_first<T, E, W, U, RES>(xb, rb, sp, 0, nv);
+    q = rms_block_sum<W>(q, red);
     const float inv = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
+    rms_write<T, E, W, U, RES>(xb, rb, w, y + row * ldy - sp.h,
+                               RES ? ro + row * ldo - sp.h : nullptr, sp, 0, nv, inv, first);
+}
 
-    T *yb = y + row * ldy - sp.h;
-    T *ob = RES ? ro + row * ldo - sp.h : nullptr;
-    RmsStep<T, E, U, NT, kStreaming, RES> cur;
-    cur.issue(xb, rb, tid, nv, full(0));
-    for (int base = 0; base < nv; base += NT * U) {
-        const bool f = full(base);
-        // the weight, the next step's row and this step's row are all in
-        // flight before the first wait
-        ParamLoad<T, E> wl[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            wl[u].issue(w, base + tid + u * NT, sp.h, N, f);
-        RmsStep<T, E, U, NT, kStreaming, RES> nxt;
-        const int next = base + NT * U;
-        if (next < nv)
-            nxt.issue(xb, rb, next + tid, nv, full(next));
-        float v[U][E], wv[U][E];
-        cur.finish(v, sp, nv, f);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            wl[u].finish(wv[u], base + tid + u * NT, sp.h, N, f);
-        if constexpr (RES)
-            store_span<T, E, U, NT>(ob, base + tid, nv, sp, v, f);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                v[u][e] = v[u][e] * inv * wv[u][e];
-        store_span<T, E, U, NT>(yb, base + tid, nv, sp, v, f);
-        cur = nxt;
-    }
+// Split rows, first kernel: workgroup (row, chunk) writes the chunk's sum of
+// v^2 (as the first float of its partial).
+template <typename T, int E, int W, int U, bool RES, bool PH>
+__global__ __launch_bounds__(W *kWave) void rmsnorm_partials(const T *__restrict__ x,
+                                                             const T *__restrict__ res, int N,
+                                                             int64_t ldx, int64_t ldr, int S,
+                                                             int C, char *pbase, int64_t prow)
+{
+    __shared__ float red[W];
+    const int64_t row = blockIdx.x / S;
+    const int s = static_cast<int>(blockIdx.x % S);
+    const T *xr = x + row * ldx;
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
+    float q = rms_scan<T, E, W, U, RES>(xr - sp.h, RES ? res + row * ldr - sp.h : nullptr, sp,
+                                        jbeg, jend);
+    q = rms_block_sum<W>(q, red);
+    if (threadIdx.x == 0)
+        row_partials(pbase, prow, row)[s] = make_float2(q, 0.0f);
+}
+
+// Split rows, second kernel: chunk s of row r, workgroup (r, s) of a grid of
+// M S (kAllChunks; kAllButFirst: the s = 0 workgroups leave at once) or
+// workgroup r of a grid of M, s = 0 (kFirstOnly).  Every wave sums the row's
+// S partials on its own (lane l takes l, l + 64, ..., then DPP), so every
+// workgroup of the row forms the same bits.  y and pbase may name the same
+// memory (the partials kept in the output).
+template <typename T, int E, int W, int U, bool RES, bool PH>
+__global__ __launch_bounds__(W *kWave) void rmsnorm_finish(
+    const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w, T *y, T *ro,
+    int N, int64_t ldx, int64_t ldr, int64_t ldy, int64_t ldo, int S, int C, float inv_n,
+    float eps, const char *pbase, int64_t prow, int part)
+{
+    const int64_t row = part == kFirstOnly ? blockIdx.x : blockIdx.x / S;
+    const int s = part == kFirstOnly ? 0 : static_cast<int>(blockIdx.x % S);
+    if (part == kAllButFirst && s == 0)
+        return;
+    const T *xr = x + row * ldx;
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
+    const T *xb = xr - sp.h;
+    const T *rb = RES ? res + row * ldr - sp.h : nullptr;
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
+    const auto first = rms_write_first<T, E, W, U, RES>(xb, rb, sp, jbeg, jend);
+    float q = 0.0f;
+    const float2 *pr = row_partials(pbase, prow, row);
+    for (int i = static_cast<int>(threadIdx.x % kWave); i < S; i += kWave)
+        q += pr[i].x;
+    q = wave_sum(q);
+    const float inv = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
+    // the partials in the output are overwritten below: every wave has read
+    // them first
+    if (part == kFirstOnly)
+        __syncthreads();
+    rms_write<T, E, W, U, RES>(xb, rb, w, y + row * ldy - sp.h,
+                               RES ? ro + row * ldo - sp.h : nullptr, sp, jbeg, jend, inv, first);
 }
 
 namespace {
@@ -437,11 +546,67 @@ hipError_t loop_dispatch(const RowProblem &p, RowIo io)
     return p.dtype == RK_F32 ? loop_io<float, RES>(p, io) : loop_io<bf16_t, RES>(p, io);
 }
 
+constexpr int kSplitW = 4;  // 256 threads per chunk
+
+template <typename T, int E, bool RES, bool PH>
+hipError_t split_run(const RowProblem &p, int S, int C, SplitPartials pt)
+{
+    constexpr int U = E == 1 ? 4 : loop_vectors(E);
+    const dim3 grid(static_cast<unsigned>(p.M * S));
+    const dim3 block(kSplitW * kWave);
+    const T *x = static_cast<const T *>(p.x);
+    const T *r = static_cast<const T *>(p.r);
+    hipError_t err = launch(rmsnorm_partials<T, E, kSplitW, U, RES, PH>, grid, block, p.stream, x,
+                            r, p.N, p.ldx, p.ldr, S, C, pt.base, pt.row_bytes);
+    if (err != hipSuccess)
+        return err;
+    auto kernel = rmsnorm_finish<T, E, kSplitW, U, RES, PH>;
+    const T *w = static_cast<const T *>(p.w);
+    T *y = static_cast<T *>(p.y);
+    T *ro = static_cast<T *>(p.ro);
+    const float inv_n = static_cast<float>(1.0 / p.N);
+    if (!pt.in_output)
+        return launch(kernel, grid, block, p.stream, x, r, w, y, ro, p.N, p.ldx, p.ldr, p.ldy,
+                      p.ldo, S, C, inv_n, p.eps, pt.base, pt.row_bytes, int{kAllChunks});
+    err = launch(kernel, grid, block, p.stream, x, r, w, y, ro, p.N, p.ldx, p.ldr, p.ldy, p.ldo, S,
+                 C, inv_n, p.eps, pt.base, pt.row_bytes, int{kAllButFirst});
+    if (err != hipSuccess)
+        return err;
+    return launch(kernel, dim3(static_cast<unsigned>(p.M)), block, p.stream, x, r, w, y, ro, p.N,
+                  p.ldx, p.ldr, p.ldy, p.ldo, S, C, inv_n, p.eps, pt.base, pt.row_bytes,
+                  int{kFirstOnly});
+}
+
+template <typename T, bool RES>
+hipError_t split_io(const RowProblem &p, int S, int C, SplitPartials pt, RowIo io)
+{
+    constexpr int E = Elem<T>::kVec;
+    if (io == kIoAligned)
+        return split_run<T, E, RES, false>(p, S, C, pt);
+    if (io == kIoPhased)
+        return split_run<T, E, RES, true>(p, S, C, pt);
+    return split_run<T, 1, RES, false>(p, S, C, pt);
+}
+
+template <bool RES>
+hipError_t split_dispatch(const RowProblem &p, int S, int C, SplitPartials pt, RowIo io)
+{
+    return p.dtype == RK_F32 ? split_io<float, RES>(p, S, C, pt, io)
+                             : split_io<bf16_t, RES>(p, S, C, pt, io);
+}
+
 }  // namespace
 
 hipError_t rmsnorm_loop_run(const RowProblem &p, bool residual, RowIo io)
 {
     return residual ? loop_dispatch<true>(p, io) : loop_dispatch<false>(p, io);
+}
+
+hipError_t rmsnorm_split_run(const RowProblem &p, bool residual, int splits, int chunk,
+                             SplitPartials parts, RowIo io)
+{
+    return residual ? split_dispatch<true>(p, splits, chunk, parts, io)
+                    : split_dispatch<false>(p, splits, chunk, parts, io);
 }
 
 }  // namespace rk

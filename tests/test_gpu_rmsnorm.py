@@ -359,3 +359,52 @@ def test_deterministic_and_empty():
     assert rk.rk_rmsnorm(e, w1, EPS).shape == (0, 128)
     y, ro = rk.rk_residual_rmsnorm(e, e.clone(), w1, EPS)
     assert y.shape == (0, 128) and ro.shape == (0, 128)
+
+
+LONG_FEW = [(1, 1 << 20), (3, 100001), (6, 65536), (64, 262144)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("M,N", LONG_FEW)
+def test_long_rows_few_rows(dtype, M, N):
+    """Long rows in few rows split across workgroups, the chunk partials kept
+    in y (three kernels): aligned rows and odd N; y one element into a buffer
+    with 5 spare columns per row (element access), whose gaps stay untouched;
+    the fused form with residual_out over the residual; in place (one kernel
+    per row then).  The fused y stays bitwise the plain RMSNorm of its own
+    residual_out."""
+    x = rowgen.randn(M, N, seed=M + 11 * N, scale=2.0, dtype=dtype)
+    res = rowgen.randn(M, N, seed=M + 11 * N + 1, dtype=dtype)
+    w = weight(N, N + M, dtype)
+    wd, xd, rd = w.to(DEV), x.to(DEV), res.to(DEV)
+    ref = oracle.rmsnorm(x, w, EPS)
+    tol = tol_of(dtype)
+    say(f"rms long rows {key(dtype)} M={M} N={N}")
+    assert rel_err(rk.rk_rmsnorm(xd, wd, EPS), ref) <= tol
+    y, ro = rk.rk_residual_rmsnorm(xd, rd, wd, EPS)
+    check_residual(y, ro, x, res, w, dtype, "split")
+    bits = torch.int32 if dtype == torch.float32 else torch.int16
+    assert torch.equal(y.view(bits), rk.rk_rmsnorm(ro, wd, EPS).view(bits))
+    # y at another offset than x, padded pitch
+    canary = -5.0
+    buf = torch.full((M, N + 5), canary, dtype=dtype, device=DEV)
+    out = buf.view(-1)[1:1 + (M - 1) * (N + 5) + N].as_strided((M, N), (N + 5, 1))
+    rk.rk_rmsnorm(xd, wd, EPS, out=out)
+    assert rel_err(out, ref) <= tol
+    flat = buf.view(-1).cpu()
+    mask = torch.ones(flat.numel(), dtype=torch.bool)
+    for r in range(M):
+        mask[1 + r * (N + 5):1 + r * (N + 5) + N] = False
+    assert torch.all(flat[mask].float() == canary)
+    # residual_out over the residual, y apart
+    rd2 = res.to(DEV)
+    y2 = torch.empty_like(xd)
+    rk.rk_residual_rmsnorm(xd, rd2, wd, EPS, out=y2, residual_out=rd2)
+    check_residual(y2, rd2, x, res, w, dtype, "residual_out=residual")
+    # in place: one kernel per row
+    xi = x.to(DEV)
+    rk.rk_rmsnorm(xi, wd, EPS, out=xi)
+    assert rel_err(xi, ref) <= tol
+    xi, ri = x.to(DEV), res.to(DEV)
+    rk.rk_residual_rmsnorm(xi, ri, wd, EPS, out=xi, residual_out=ri)
+    check_residual(xi, ri, x, res, w, dtype, "y=x")
