@@ -573,6 +573,13 @@ struct RowSpan {
     {
         return static_cast<unsigned>(j * E + e - h) < static_cast<unsigned>(n);
     }
+    // the step of `span` vectors from `base` holds row elements only and lies
+    // below jend: it needs no masks
+    __device__ __forceinline__ bool step_full(int base, int jend, int span) const
+    {
+        const int fe = jend < full_end() ? jend : full_end();
+        return base >= full_begin() && base + span <= fe;
+    }
 };
 
 // Phase of a row's first element.  The same for every lane of a wave (a

@@ -101,9 +101,7 @@ __device__ __forceinline__ Moments scan_moments(const T *__restrict__ xb, RowSpa
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
-    const int fb = sp.full_begin();
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
     Moments st{0.0f, 0.0f, 0.0f};
     SpanLoad<T, E, U, NT, CP> cur;
     cur.issue(xb, jbeg + tid, jend, full(jbeg));
@@ -157,10 +155,9 @@ __device__ __forceinline__ SpanLoad<T, E, U, W * kWave> ln_write_first(const T *
                                                                        int jend)
 {
     constexpr int NT = W * kWave;
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
     SpanLoad<T, E, U, NT> cur;
     cur.issue(xb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
-              jbeg >= sp.full_begin() && jbeg + NT * U <= fe);
+              sp.step_full(jbeg, jend, NT * U));
     return cur;
 }
 
@@ -176,9 +173,7 @@ __device__ __forceinline__ void ln_write_range(const T *__restrict__ xb,
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
-    const int fb = sp.full_begin();
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
     for (int base = jbeg; base < jend; base += NT * U) {
         const bool f = full(base);
         // weight and bias, the next step's row and this step's row are all in

@@ -107,9 +107,7 @@ __device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xb, Row
     SoftmaxState st{-INFINITY, 0.0f};
     // a step is full when all its vectors hold row elements only and lie
     // below jend: no masks then
-    const int fb = sp.full_begin();
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
     // software pipeline: the next step's loads are in flight while this
     // step's values are folded
     SpanLoad<T, E, U, NT, CP> cur;
@@ -135,10 +133,9 @@ __device__ __forceinline__ SpanLoad<T, E, U, W * kWave> write_first(const T *__r
                                                                     int jend)
 {
     constexpr int NT = W * kWave;
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
     SpanLoad<T, E, U, NT> cur;
     cur.issue(xb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
-              jbeg >= sp.full_begin() && jbeg + NT * U <= fe);
+              sp.step_full(jbeg, jend, NT * U));
     return cur;
 }
 
@@ -153,9 +150,7 @@ __device__ __forceinline__ void write_range(const T *__restrict__ xb, T *__restr
     const int tid = static_cast<int>(threadIdx.x % NT);
     const float inv = 1.0f / st.d;
     const float mL = st.m * 1.4426950408889634f;
-    const int fb = sp.full_begin();
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
     for (int base = jbeg; base < jend; base += NT * U) {
         SpanLoad<T, E, U, NT> nxt;
         const int next = base + NT * U;

@@ -49,9 +49,7 @@ __global__ __launch_bounds__(W *kWave) void row_reduce(const T *__restrict__ x, 
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     const T *xb = xr - sp.h;
     const int jend = ok ? sp.count() : 0;
-    const int fb = sp.full_begin();
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + L * U <= fe; };
+    auto full = [&](int base) { return sp.step_full(base, jend, L * U); };
 
     float acc[U];
 #pragma unroll
@@ -222,11 +220,9 @@ __global__ __launch_bounds__(kGeluThreads) void gelu_rows(const T *__restrict__ 
     const T *xb = xr - sp.h;
     T *yb = y + row * ldy - sp.h;
     const int nv = sp.count();
-    const int fb = sp.full_begin();
-    const int fe = sp.full_end();
     const int tid = static_cast<int>(threadIdx.x);
     for (int base = 0; base < nv; base += NT * kGeluU) {
-        const bool full = base >= fb && base + NT * kGeluU <= fe;
+        const bool full = sp.step_full(base, nv, NT * kGeluU);
         SpanLoad<T, E, kGeluU, NT> l;
         l.issue(xb, base + tid, nv, full);
         float v[kGeluU][E];

@@ -310,9 +310,7 @@ __device__ __forceinline__ float rms_scan(const T *__restrict__ xb, const T *__r
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
-    const int fb = sp.full_begin();
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
     float q = 0.0f;
     RmsStep<T, E, U, NT, kCached, RES> cur;
     cur.issue(xb, rb, jbeg + tid, jend, full(jbeg));
@@ -341,10 +339,9 @@ rms_write_first(const T *__restrict__ xb, const T *__restrict__ rb, RowSpan<E> s
                 int jend)
 {
     constexpr int NT = W * kWave;
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
     RmsStep<T, E, U, NT, kStreaming, RES> cur;
     cur.issue(xb, rb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
-              jbeg >= sp.full_begin() && jbeg + NT * U <= fe);
+              sp.step_full(jbeg, jend, NT * U));
     return cur;
 }
 
@@ -358,9 +355,7 @@ __device__ __forceinline__ void rms_write(const T *__restrict__ xb, const T *__r
 {
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
-    const int fb = sp.full_begin();
-    const int fe = jend < sp.full_end() ? jend : sp.full_end();
-    auto full = [&](int base) { return base >= fb && base + NT * U <= fe; };
+    auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
     for (int base = jbeg; base < jend; base += NT * U) {
         const bool f = full(base);
         // the weight, the next step's row and this step's row are all in
