@@ -17,7 +17,8 @@
 //   S^T = K Q^T (keys x queries, so that each lane holds one query's scores
 //   for 16 of the keys), the row max across the four 16-lane groups
 //   (permlane16/32 swaps), p = exp2((S - m) scale log2e), and O^T += V^T P^T,
-//   where P^T is the S^T fragments rounded to the operand type in place.  K
+//   where P^T is the S^T fragments rounded to the operand type in place; the
+//   row sum l comes from one more MFMA per 32-key step (A all ones).  K
 //   rows are staged in a permuted order (k_slot) that leaves each lane 8
 //   consecutive keys per 32-key step, so that its V^T operand is one 16-byte
 //   read of the key-ordered V^T.
@@ -50,6 +51,11 @@ struct Operand<RK_BF16> {
         f32x2_t f = {a, b};
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
     }
+    // eight 1.0 values (bf16 0x3f80)
+    __device__ static __forceinline__ vec ones()
+    {
+        return __builtin_bit_cast(vec, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    }
 };
 
 template <>
@@ -63,6 +69,11 @@ struct Operand<RK_F16> {
     {
         f32x2_t f = {a, b};
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+    }
+    // eight 1.0 values (fp16 0x3c00)
+    __device__ static __forceinline__ vec ones()
+    {
+        return __builtin_bit_cast(vec, u32x4_t{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u});
     }
 };
 
@@ -80,20 +91,13 @@ __device__ __forceinline__ u32x2_t swap32(float v)
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return u32x2_t{r[0], r[1]};
 }
-// max / sum over the four lanes l, l^16, l^32, l^48 (same bits in all four)
+// max over the four lanes l, l^16, l^32, l^48 (same bits in all four)
 __device__ __forceinline__ float group4_max(float v)
 {
     u32x2_t a = swap16(v);
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     u32x2_t b = swap32(v);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group4_sum(float v)
-{
-    u32x2_t a = swap16(v);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    u32x2_t b = swap32(v);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 constexpr int kAttnBN = 64;  // keys per step
@@ -187,12 +191,19 @@ void flash_attention_fwd(
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt)
             acc[qt][dt] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m[QT], lsum[QT];  // reference max; this lane's part of the row sum
+    // m: the reference max of each query row.  l, the row sum of p, is
+    // formed on the matrix cores: one more MFMA per 32-key step, with A all
+    // ones and B the step's P^T, sums the rounded p that also weight V, and
+    // leaves the whole row's sum in every lane of the query (in element 0,
+    // the only one read and rescaled; this replaces a VALU add per score).
+    float m[QT];
+    f32x4v_t lacc[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         m[qt] = -INFINITY;
-        lsum[qt] = 0.0f;
+        lacc[qt] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    const vec ones = Op::ones();
 
     // K/V staging: K chunk i of this thread is key (tid + 256 i) / CH,
     // column 8 ((tid + 256 i) % CH).  V: keys LOADS kq .. LOADS kq + LOADS - 1
@@ -356,21 +367,18 @@ void flash_attention_fwd(
                       : (m[qt] == -INFINITY ? 0.0f
                                             : __builtin_amdgcn_exp2f(fmaf(m[qt], scale_log2e, -shift)));
             m[qt] = m_new;
-            float ps = 0.0f;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][r], scale_log2e, -shift));
-                    s[qt][kt][r] = p;
-                    ps += p;
-                }
-            lsum[qt] = fmaf(alpha, lsum[qt], ps);
-            // rescale the output only when some row's reference moved
+                for (int r = 0; r < 4; ++r)
+                    s[qt][kt][r] =
+                        __builtin_amdgcn_exp2f(fmaf(s[qt][kt][r], scale_log2e, -shift));
+            // rescale the output and l only when some row's reference moved
             if (!__all(alpha == 1.0f)) {
 #pragma unroll
                 for (int dt = 0; dt < DT16; ++dt)
                     acc[qt][dt] *= alpha;
+                lacc[qt][0] *= alpha;
             }
             // 32-key step ks: slots 0..3 are keys 32 ks + 8 g + r (tile 2 ks),
             // slots 4..7 keys 32 ks + 8 g + 4 + r (tile 2 ks + 1)
@@ -396,6 +404,7 @@ void flash_attention_fwd(
             for (int qt = 0; qt < QT; ++qt) {
                 u32x4_t w = {pk[qt][ks][0], pk[qt][ks][1], pk[qt][ks][2], pk[qt][ks][3]};
                 bq[qt] = __builtin_bit_cast(vec, w);
+                lacc[qt] = Op::mfma(ones, bq[qt], lacc[qt]);  // l += sum of the step's p
             }
             // V^T fragments (keys 32 ks + 8 g .. + 8 of d row 16 dt + l16, one
             // 16-byte read) are read two d-tiles ahead of their MFMAs
@@ -447,7 +456,7 @@ void flash_attention_fwd(
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const int qi = qw + 16 * qt + l16;
-        const float inv = 1.0f / group4_sum(lsum[qt]);
+        const float inv = 1.0f / lacc[qt][0];
         if (qi < T) {
             uint16_t *orow = oh + qi * so.t;
 #pragma unroll
