@@ -167,6 +167,15 @@ inline int stream_waves(int64_t nvec, int U)
 // masked padding.
 constexpr int64_t kShortRowVectors = 128;
 
+// First vector of the last step of [jbeg, jend) (steps of `span` vectors from
+// jbeg), or jbeg - span for an empty range.  The softmax and RMSNorm output
+// passes run their steps from there down to jbeg: the end of a range, read
+// last by the pass before, is the part most likely still in the caches.
+constexpr int last_step(int jbeg, int jend, int span)
+{
+    return jend > jbeg ? jbeg + (jend - jbeg - 1) / span * span : jbeg - span;
+}
+
 // Chunk length (elements) of the split-row variant: ceil(N / S) rounded up to
 // whole 16-byte vectors when the vector path is used.
 inline int64_t split_chunk(int64_t N, int64_t S, int vec)

@@ -125,22 +125,24 @@ __device__ __forceinline__ SoftmaxState scan_range(const T *__restrict__ xb, Row
     return st;
 }
 
-// The loads of write_range's first step, issued by the caller ahead of the
-// merge that forms the row's state, so that they are in flight meanwhile.
+// The loads of the first step write_range runs (the range's last), issued by
+// the caller ahead of the merge that forms the row's state, so that they are
+// in flight meanwhile.
 template <typename T, int E, int W, int U>
 __device__ __forceinline__ SpanLoad<T, E, U, W * kWave> write_first(const T *__restrict__ xb,
                                                                     RowSpan<E> sp, int jbeg,
                                                                     int jend)
 {
     constexpr int NT = W * kWave;
+    const int base = last_step(jbeg, jend, NT * U);
     SpanLoad<T, E, U, NT> cur;
-    cur.issue(xb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
-              sp.step_full(jbeg, jend, NT * U));
+    cur.issue(xb, base + static_cast<int>(threadIdx.x % NT), jend > jbeg ? jend : base,
+              sp.step_full(base, jend, NT * U));
     return cur;
 }
 
-// Write exp(x - m) / d for vectors [jbeg, jend) of a row (bases xb, yb); the
-// first step's loads come issued (write_first).
+// Write exp(x - m) / d for vectors [jbeg, jend) of a row (bases xb, yb),
+// last step first; that step's loads come issued (write_first).
 template <typename T, int E, int W, int U>
 __device__ __forceinline__ void write_range(const T *__restrict__ xb, T *__restrict__ yb,
                                             RowSpan<E> sp, int jbeg, int jend, SoftmaxState st,
@@ -151,10 +153,10 @@ __device__ __forceinline__ void write_range(const T *__restrict__ xb, T *__restr
     const float inv = 1.0f / st.d;
     const float mL = st.m * 1.4426950408889634f;
     auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
-    for (int base = jbeg; base < jend; base += NT * U) {
+    for (int base = last_step(jbeg, jend, NT * U); base >= jbeg; base -= NT * U) {
         SpanLoad<T, E, U, NT> nxt;
-        const int next = base + NT * U;
-        if (next < jend)
+        const int next = base - NT * U;
+        if (next >= jbeg)
             nxt.issue(xb, next + tid, jend, full(next));
         const bool f = full(base);
         float v[U][E];

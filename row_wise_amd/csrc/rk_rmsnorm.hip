@@ -331,22 +331,24 @@ __device__ __forceinline__ float rms_scan(const T *__restrict__ xb, const T *__r
     return q;
 }
 
-// The loads of rms_write's first step, issued by the caller ahead of the
-// reduction that forms inv, so that they are in flight meanwhile.
+// The loads of the first step rms_write runs (the range's last), issued by
+// the caller ahead of the reduction that forms inv, so that they are in
+// flight meanwhile.
 template <typename T, int E, int W, int U, bool RES>
 __device__ __forceinline__ RmsStep<T, E, U, W * kWave, kStreaming, RES>
 rms_write_first(const T *__restrict__ xb, const T *__restrict__ rb, RowSpan<E> sp, int jbeg,
                 int jend)
 {
     constexpr int NT = W * kWave;
+    const int base = last_step(jbeg, jend, NT * U);
     RmsStep<T, E, U, NT, kStreaming, RES> cur;
-    cur.issue(xb, rb, jbeg + static_cast<int>(threadIdx.x % NT), jend,
-              sp.step_full(jbeg, jend, NT * U));
+    cur.issue(xb, rb, base + static_cast<int>(threadIdx.x % NT), jend > jbeg ? jend : base,
+              sp.step_full(base, jend, NT * U));
     return cur;
 }
 
-// Store residual_out (RES) and y = v inv w for vectors [jbeg, jend) of a row;
-// the first step's loads come issued (rms_write_first).
+// Store residual_out (RES) and y = v inv w for vectors [jbeg, jend) of a row,
+// last step first; that step's loads come issued (rms_write_first).
 template <typename T, int E, int W, int U, bool RES>
 __device__ __forceinline__ void rms_write(const T *__restrict__ xb, const T *__restrict__ rb,
                                           const T *__restrict__ w, T *yb, T *ob, RowSpan<E> sp,
@@ -356,7 +358,7 @@ __device__ __forceinline__ void rms_write(const T *__restrict__ xb, const T *__r
     constexpr int NT = W * kWave;
     const int tid = static_cast<int>(threadIdx.x % NT);
     auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
-    for (int base = jbeg; base < jend; base += NT * U) {
+    for (int base = last_step(jbeg, jend, NT * U); base >= jbeg; base -= NT * U) {
         const bool f = full(base);
         // the weight, the next step's row and this step's row are all in
         // flight before the first wait
@@ -365,8 +367,8 @@ __device__ __forceinline__ void rms_write(const T *__restrict__ xb, const T *__r
         for (int u = 0; u < U; ++u)
             wl[u].issue(w, base + tid + u * NT, sp.h, sp.n, f);
         RmsStep<T, E, U, NT, kStreaming, RES> nxt;
-        const int next = base + NT * U;
-        if (next < jend)
+        const int next = base - NT * U;
+        if (next >= jbeg)
             nxt.issue(xb, rb, next + tid, jend, full(next));
         float v[U][E], wv[U][E];
         cur.finish(v, sp, jend, f);
