@@ -13,12 +13,14 @@
 //                  LDS.  Pass 2 re-reads the row and writes exp(x - m) / d.
 //                  2 reads + 1 write per element.
 // online_partials  split-row, first kernel: one workgroup per (row, chunk)
-//                  writes the chunk's (m_s, d_s) to the workspace.
+//                  writes the chunk's (m_s, d_s) to the workspace (or into
+//                  the row's first output chunk).
 // online_finish    split-row, second kernel: one workgroup per (row, chunk)
 //                  merges the row's S partials (each lane a subset, then
 //                  DPP) and writes its chunk.  With the partials kept in the
 //                  output (no workspace), it runs twice: all chunks but the
-//                  first, then the first one per row.
+//                  first, then the first one per row.  The output pass
+//                  runs each range's steps last first (see last_step).
 // Rows are read and written as aligned 16-byte vectors from whatever offset
 // they start at (RowSpan), when input and output rows share that offset;
 // E = 1 (one element per access) serves the rest.
