@@ -433,8 +433,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(rows shard across GPUs with no communication; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (rows "
+              "would shard across GPUs by row blocks, with no communication)",
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:
