@@ -119,3 +119,37 @@ def test_causal_first_row_and_determinism():
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
     e = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device=DEV)
     assert rk.rk_flash_attention(e, e, e).shape == e.shape
+
+
+def _random_cases(n=40, seed=11):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        out.append((i, int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 400)),
+                    int(rng.choice([64, 128])), "bf16" if rng.random() < 0.6 else "f16",
+                    bool(rng.random() < 0.5), [None, 0.05, 0.3][int(rng.integers(0, 3))],
+                    int(rng.integers(0, 3))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "-".join(str(x) for x in c))
+def test_random_shapes_and_layouts(case):
+    """Seeded B, H, T, d, dtype, mask, scale and layout (contiguous; q and k in
+    [B, T, H, d] storage; output in a padded buffer with canaries), every head
+    against the oracle."""
+    i, B, H, T, d, dt, causal, scale, layout = case
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float16
+    q, k, v = rowgen.attention_qkv(B, H, T, d, dtype, seed=5000 + i)
+    if layout == 1:
+        qd = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        kd = k.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    else:
+        qd, kd = q.to(DEV), k.to(DEV)
+    buf = out = None
+    if layout == 2:
+        buf = torch.full((B, H, T, d + 32), -7.0, dtype=dtype, device=DEV)
+        out = buf[..., :d]
+    o = rk.rk_flash_attention(qd, kd, v.to(DEV), causal=causal, scale=scale, out=out)
+    check(o, q, k, v, causal, scale=scale, what=case)
+    if buf is not None:
+        assert torch.all(buf[..., d:] == -7.0)
