@@ -236,17 +236,18 @@ rk_status softmax_generic(const RowProblem &p)
     return hip_status(online_stream_run(p, softmax_io(p)));
 }
 
+// The split partials kept in each output row.
+SplitPartials output_partials(const RowProblem &p)
+{
+    return SplitPartials{static_cast<char *>(p.y), p.ldy * elem_size(p.dtype), true};
+}
+
 // Long rows in few rows split across workgroups even without a workspace:
 // each row keeps its S partials in its own output, inside the first chunk,
 // which the last of three kernels writes after reading them.  That needs an
 // output apart from the input and a first chunk with room for the S partials
 // and the step to the next 8-byte boundary; S is lowered until it has room.
 // Returns the splits to use (1: none) and, for more, their chunk length.
-SplitPartials output_partials(const RowProblem &p)
-{
-    return SplitPartials{static_cast<char *>(p.y), p.ldy * elem_size(p.dtype), true};
-}
-
 int32_t output_splits(const RowProblem &p, int32_t S, RowIo io, int64_t *chunk)
 {
     if (S <= 1 || p.x == p.y || p.M > INT64_MAX / S || !grid_ok(p.M * S, kSplitThreads))
