@@ -624,10 +624,40 @@ __device__ __forceinline__ const float2 *row_partials(const char *base, int64_t 
     return row_partials(const_cast<char *>(base), row_bytes, row);
 }
 
-// Which chunks a split-row output kernel writes: all of them, all but the
-// first (the partials sit in the first chunk's output), or only the first
-// (one workgroup per row, after its partials have been read).
+// What a split-row output kernel writes: every chunk; every chunk but the
+// first vectors of the first chunk, which hold the partials kept in the
+// output; or only those first vectors (one workgroup per row, after every
+// wave has read the partials).
 enum SplitPart { kAllChunks = 0, kAllButFirst = 1, kFirstOnly = 2 };
+
+// The vectors [0, P) of a row (at phase sp.h from its aligned base) that
+// hold the S partials kept in the output row yrow (at its first 8-byte
+// boundary, as row_partials places them).
+template <typename T, int E>
+__device__ __forceinline__ int partials_prefix(const T *yrow, RowSpan<E> sp, int S)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(yrow);
+    const int pad = static_cast<int>(((a + 7) & ~uintptr_t{7}) - a);
+    constexpr int vb = E * static_cast<int>(sizeof(T));
+    return (sp.h * static_cast<int>(sizeof(T)) + pad + 8 * S + vb - 1) / vb;
+}
+
+// The vector range a split-row output kernel writes for chunk s of a row:
+// [jbeg, jend) of the chunk, less (kAllButFirst) or only (kFirstOnly) the
+// first chunk's partials prefix.
+template <typename T, int E>
+__device__ __forceinline__ void output_range(int part, int s, const T *yrow, RowSpan<E> sp, int S,
+                                             int &jbeg, int &jend)
+{
+    if (part == kAllChunks || s != 0)
+        return;
+    int pre = partials_prefix<T, E>(yrow, sp, S);
+    pre = pre < jend ? pre : jend;
+    if (part == kFirstOnly)
+        jend = pre;
+    else
+        jbeg = pre;
+}
 
 // U vectors of a row in flight: vector k of this lane is j0 + k * STRIDE.
 // issue() starts the loads of the vectors below jend (all of them, unmasked,

@@ -30,8 +30,8 @@
 //                     (row, chunk) merges the row's S summaries (each lane a
 //                     subset, then DPP) and writes its chunk.  With the
 //                     summaries kept in the output (no workspace), it runs
-//                     twice: all chunks but the first, then the first one
-//                     per row.
+//                     twice: everything but the first vectors of each row
+//                     (which hold the summaries), then those vectors.
 // Rows are read and written as aligned 16-byte vectors from whatever offset
 // they start at (RowSpan), when input and output rows share that offset;
 // weight and bias, aligned at column 0, are shifted into each row's phase
@@ -253,8 +253,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restri
 }
 
 // Chunk s of row r: workgroup (r, s) of a grid of M S (kAllChunks,
-// kAllButFirst: the s = 0 workgroups leave at once) or workgroup r of a grid
-// of M, s = 0 (kFirstOnly).  y and pbase may name the same memory (the
+// kAllButFirst) or workgroup r of a grid of M, s = 0 (kFirstOnly), over the
+// range output_range gives.  y and pbase may name the same memory (the
 // partials kept in the output).
 template <typename T, int E, int W, int U, int GK, bool PH>
 __global__ __launch_bounds__(W *kWave) void layernorm_finish(
@@ -264,12 +264,11 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
 {
     const int64_t row = part == kFirstOnly ? blockIdx.x : blockIdx.x / S;
     const int s = part == kFirstOnly ? 0 : static_cast<int>(blockIdx.x % S);
-    if (part == kAllButFirst && s == 0)
-        return;
     const T *xr = x + row * ldx;
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
+    output_range<T, E>(part, s, y + row * ldy, sp, S, jbeg, jend);
     // the chunk's first loads and the shift K go out before the summaries
     // are read
     const auto first = ln_write_first<T, E, W, U>(xr - sp.h, sp, jbeg, jend);

@@ -18,8 +18,9 @@
 // online_finish    split-row, second kernel: one workgroup per (row, chunk)
 //                  merges the row's S partials (each lane a subset, then
 //                  DPP) and writes its chunk.  With the partials kept in the
-//                  output (no workspace), it runs twice: all chunks but the
-//                  first, then the first one per row.  The output pass
+//                  output (no workspace), it runs twice: everything but the
+//                  first vectors of each row (which hold the partials), then
+//                  those vectors, one workgroup per row.  The output pass
 //                  runs each range's steps last first (see last_step).
 // Rows are read and written as aligned 16-byte vectors from whatever offset
 // they start at (RowSpan), when input and output rows share that offset;
@@ -220,8 +221,8 @@ __global__ __launch_bounds__(W *kWave) void online_partials(const T *__restrict_
 }
 
 // Chunk s of row r: workgroup (r, s) of a grid of M S (kAllChunks,
-// kAllButFirst: the s = 0 workgroups leave at once) or workgroup r of a grid
-// of M, s = 0 (kFirstOnly).
+// kAllButFirst) or workgroup r of a grid of M, s = 0 (kFirstOnly), over the
+// range output_range gives.
 // y and pbase may name the same memory (the partials kept in the output).
 template <typename T, int E, int W, int U, bool PH>
 __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ x, T *y, int N,
@@ -231,12 +232,11 @@ __global__ __launch_bounds__(W *kWave) void online_finish(const T *__restrict__ 
 {
     const int64_t row = part == kFirstOnly ? blockIdx.x : blockIdx.x / S;
     const int s = part == kFirstOnly ? 0 : static_cast<int>(blockIdx.x % S);
-    if (part == kAllButFirst && s == 0)
-        return;
     const T *xr = x + row * ldx;
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
+    output_range<T, E>(part, s, y + row * ldy, sp, S, jbeg, jend);
     // the chunk's first loads go out before the partials are read
     const auto first = write_first<T, E, W, U>(xr - sp.h, sp, jbeg, jend);
     // Every wave merges the row's S partials on its own (lane l takes

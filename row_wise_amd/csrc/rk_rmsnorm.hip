@@ -16,9 +16,9 @@
 // rmsnorm_partials + rmsnorm_finish
 //               long rows in few rows, split across workgroups: the first
 //               kernel writes each chunk's sum of squares, the second sums
-//               the row's S partials and writes its chunk (run twice, all
-//               chunks but the first and then the first, when the partials
-//               are kept in the output).
+//               the row's S partials and writes its chunk (run twice when
+//               the partials are kept in the output: everything but the
+//               first vectors of each row, which hold them, then those).
 #include "rk_device.h"
 #include "rk_internal.h"
 
@@ -456,8 +456,8 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_partials(const T *__restrict
 }
 
 // Split rows, second kernel: chunk s of row r, workgroup (r, s) of a grid of
-// M S (kAllChunks; kAllButFirst: the s = 0 workgroups leave at once) or
-// workgroup r of a grid of M, s = 0 (kFirstOnly).  Every wave sums the row's
+// M S (kAllChunks, kAllButFirst) or workgroup r of a grid of M, s = 0
+// (kFirstOnly), over the range output_range gives.  Every wave sums the row's
 // S partials on its own (lane l takes l, l + 64, ..., then DPP), so every
 // workgroup of the row forms the same bits.  y and pbase may name the same
 // memory (the partials kept in the output).
@@ -469,14 +469,13 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_finish(
 {
     const int64_t row = part == kFirstOnly ? blockIdx.x : blockIdx.x / S;
     const int s = part == kFirstOnly ? 0 : static_cast<int>(blockIdx.x % S);
-    if (part == kAllButFirst && s == 0)
-        return;
     const T *xr = x + row * ldx;
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     const T *xb = xr - sp.h;
     const T *rb = RES ? res + row * ldr - sp.h : nullptr;
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
+    output_range<T, E>(part, s, y + row * ldy, sp, S, jbeg, jend);
     const auto first = rms_write_first<T, E, W, U, RES>(xb, rb, sp, jbeg, jend);
     float q = 0.0f;
     const float2 *pr = row_partials(pbase, prow, row);
