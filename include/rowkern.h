@@ -88,9 +88,10 @@ typedef enum rk_status {
  * num_splits == 0 there, tightened for the extra launch) when y does not
  * alias x, the split-row form with no workspace: each row's chunk partials
  * are kept in that row's own first output chunk (from its first 8-byte
- * boundary), a second kernel writes the other chunks, and a third, one
- * workgroup per row, reads the partials and then writes the first chunk.
- * The split count is lowered where needed until that chunk holds them.
+ * boundary), a second kernel writes every output element but the first
+ * vectors of each row, which hold them, and a third, one workgroup per row,
+ * reads the partials and then writes those vectors.  The split count is
+ * lowered where needed until the first chunk holds them.
  * A row that is all -inf, or holds +inf or NaN, yields NaN (the IEEE value
  * of the definition).
  *
@@ -169,7 +170,8 @@ int32_t rk_online_softmax_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
  * register tile filled well below its capacity.  Long rows in few rows, when
  * y does not alias x, take the split-row form of rk_layernorm_gelu_ex with
  * no workspace, the chunk summaries kept in each row's first output chunk
- * and that chunk written last by a third kernel, as rk_softmax does.
+ * and the vectors holding them written last by a third kernel, as
+ * rk_softmax does.
  * Otherwise the same as rk_layernorm_gelu_ex with RK_GELU_TANH and
  * num_splits = 1.
  *
@@ -236,8 +238,8 @@ int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
  * and one write per element; other rows are read twice by a looping kernel,
  * one workgroup per row, or, for long rows in few rows when y aliases no
  * input, split across workgroups with each chunk's sum of squares kept in
- * the row's first output chunk, which a third kernel writes last (as
- * rk_softmax does).
+ * the row's first output chunk, the vectors holding them written last by a
+ * third kernel (as rk_softmax does).
  *
  * Returns RK_ERR_INVALID_ARG as rk_softmax, and when weight is NULL with
  * M > 0, eps is not finite and > 0, or y overlaps weight.
