@@ -60,13 +60,18 @@ void oracle_softmax(const double *x, double *y, int64_t M, int64_t N)
     }
 }
 
-/* Row statistics of the stable softmax: m = max(x), d = sum exp(x - m). */
+/* Row statistics of the stable softmax: m = max(x), d = sum exp(x - m).
+ * A part whose every value is -inf has max -inf and contributes nothing to
+ * any sum of exp(x - M) with M finite: its state is the empty part's
+ * (-inf, 0), the start state of the online recurrence below, and the
+ * undefined terms exp(-inf - (-inf)) are never formed. */
 void oracle_softmax_stats(const double *x, int64_t N, double *m_out, double *d_out)
 {
     double m = row_max(x, N);
     double d = 0.0;
-    for (int64_t j = 0; j < N; ++j)
-        d += exp(x[j] - m);
+    if (m != -INFINITY)
+        for (int64_t j = 0; j < N; ++j)
+            d += exp(x[j] - m);
     *m_out = m;
     *d_out = d;
 }
@@ -100,9 +105,12 @@ void oracle_online_stats(const double *x, int64_t N, int64_t B, double *m_out, d
         double m_new = block_max > m ? block_max : m;
         if (isnan(block_max) || isnan(m))
             m_new = NAN;
+        /* While every value scanned so far is -inf (m_new = -inf) the
+         * state stays the start state (-inf, 0). */
         double block_sum = 0.0;
-        for (int64_t j = s; j < e; ++j)
-            block_sum += exp(x[j] - m_new);
+        if (m_new != -INFINITY)
+            for (int64_t j = s; j < e; ++j)
+                block_sum += exp(x[j] - m_new);
         d = d * rescale(m, m_new) + block_sum;
         m = m_new;
     }

@@ -17,7 +17,8 @@ What pins what (citations are to the pages' titles and sections):
   rows whose statistics are closed-form sums; the merge has (-inf, 0) as its
   identity, is commutative and associative, and merging two halves gives the
   whole; split statistics equal the whole-row statistics for any chunk count,
-  including empty chunks.
+  including empty chunks; a block or chunk holding only -inf has the state
+  (-inf, 0) and leaves the row's statistics those of its finite values.
 * LayerNorm, "Triton Kernel 实现练习" §4.1: mean(x_hat) = 0 and
   var(x_hat) = s2 / (s2 + eps); reduction to torch.nn.functional.layer_norm in
   float64; a constant row gives x_hat = 0 and y = GeLU(b); an eps-sensitive
@@ -214,6 +215,72 @@ def check_online_and_split_outputs(orc):
         assert _rel(orc.online_softmax(x, block), y0) <= 1e-13, block
     for S in (1, 2, 64, 4099):
         assert _rel(orc.split_softmax(x, S), y0) <= 1e-13, S
+
+
+def check_neg_inf_parts(orc):
+    # A value of -inf adds exp(-inf - m) = 0 to the sum of any part with a
+    # finite max m, so a row's (max, sum) are those of its finite values
+    # alone; a part (block or chunk) holding only -inf has the empty part's
+    # state (-inf, 0), the start state of the recurrence ("第 6 讲" §7.2), and
+    # must not turn the merge into NaN.  References: numpy's max and an fsum of
+    # exp(x - max) over the finite values; torch.softmax in float64, which
+    # gives exact zeros at -inf inputs.
+    import torch
+
+    n = 4099
+    base = 3.0 * _rng(41).standard_normal(n)
+
+    def expect(row):
+        fin = row[np.isfinite(row)]
+        m = float(fin.max())
+        return m, math.fsum(np.exp(fin - m).tolist())
+
+    def same(got, want, what):
+        assert got[0] == want[0], (what, got, want)
+        assert abs(got[1] - want[1]) <= 1e-13 * want[1], (what, got, want)
+
+    rows = []
+    for k in (1, 3, 64, 1025, n - 1):  # -inf over the first k values
+        r = base.copy()
+        r[:k] = -math.inf
+        rows.append((f"lead{k}", r))
+    for S in (2, 3, 64):
+        C = -(-n // S)
+        for s in (0, S // 2, S - 1):  # chunk s all -inf, the others finite
+            r = base.copy()
+            r[s * C:min(n, (s + 1) * C)] = -math.inf
+            rows.append((f"S{S}c{s}", r))
+    r = base.copy()
+    r[::5] = -math.inf  # scattered -inf in every block
+    rows.append(("every5", r))
+    for what, r in rows:
+        want = expect(r)
+        same(orc.softmax_stats(r), want, what)
+        for block in (1, 3, 64, 4096, n):
+            same(orc.online_stats(r, block), want, (what, block))
+        for S in (2, 3, 64, n):
+            m, d, mp, dp = orc.split_stats(r, S)
+            same((m, d), want, (what, S))
+            assert not np.any(np.isnan(dp)), (what, S)
+        ref = torch.softmax(torch.from_numpy(r[None, :]), dim=1).numpy()
+        zero = ~np.isfinite(r)
+        for y in (orc.softmax(r[None, :]), orc.online_softmax(r[None, :], 64),
+                  orc.online_softmax(r[None, :], 1), orc.split_softmax(r[None, :], 3),
+                  orc.split_softmax(r[None, :], 64)):
+            assert np.all(y[0, zero] == 0.0), what
+            assert _rel(y[0, ~zero], ref[0, ~zero]) <= 1e-13, what
+    # every value -inf: (-inf, 0) for every part and for the row; the
+    # normalised row is 0/0 = NaN, as the plain definition gives
+    r = np.full(n, -math.inf)
+    assert orc.softmax_stats(r) == (-math.inf, 0.0)
+    for block in (1, 3, n):
+        assert orc.online_stats(r, block) == (-math.inf, 0.0), block
+    for S in (2, 3, 64):
+        m, d, mp, dp = orc.split_stats(r, S)
+        assert (m, d) == (-math.inf, 0.0) and np.all(dp == 0.0), S
+    for y in (orc.softmax(r[None, :]), orc.online_softmax(r[None, :], 3),
+              orc.split_softmax(r[None, :], 64)):
+        assert np.all(np.isnan(y))
 
 
 # ---------------------------------------------------------------- GeLU
@@ -661,6 +728,7 @@ PINS = [
     check_merge_algebra,
     check_split_stats_match_definition,
     check_online_and_split_outputs,
+    check_neg_inf_parts,
     check_gelu_basic,
     check_gelu_torch,
     check_gelu_not_erf,

@@ -21,6 +21,8 @@ MUTANTS = {
     "online_rescale_dropped": ("return exp(m_old - m_new);", "return 1.0;"),
     "online_rescale_inverted": ("return exp(m_old - m_new);", "return exp(m_new - m_old);"),
     "online_block_sum_old_max": ("block_sum += exp(x[j] - m_new);", "block_sum += exp(x[j] - block_max);"),
+    "stats_neg_inf_guard_dropped": ("    if (m != -INFINITY)\n        for (int64_t j = 0; j < N; ++j)\n            d += exp(x[j] - m);", "    for (int64_t j = 0; j < N; ++j)\n        d += exp(x[j] - m);"),
+    "online_neg_inf_guard_dropped": ("        if (m_new != -INFINITY)\n            for (int64_t j = s; j < e; ++j)", "        for (int64_t j = s; j < e; ++j)"),
     "merge_second_unscaled": ("d1 * rescale(m1, M) + d2 * rescale(m2, M)", "d1 * rescale(m1, M) + d2"),
     "split_chunk_size": ("int64_t C = (N + S - 1) / S;\n    double m = -INFINITY", "int64_t C = N / S + 1;\n    double m = -INFINITY"),
     "gelu_cubic_coeff": ("0.044715 * z * z * z", "0.04715 * z * z * z"),
