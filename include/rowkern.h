@@ -193,9 +193,10 @@ rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias,
  *             C = ceil(N / S) elements (rounded up to whole 16-byte vectors
  *             on the vector path); a first kernel writes a summary of each
  *             chunk to the workspace (its mean, taken relative to the row's
- *             first element, and M2, the sum of squared deviations from
- *             it), a second merges the row's S summaries by the
- *             Chan-Golub-LeVeque pairwise update and writes the chunk:
+ *             first element K, and M2, the sum of squared deviations from
+ *             it) and K itself, a second merges the row's S summaries by
+ *             the Chan-Golub-LeVeque pairwise update and writes the chunk,
+ *             taking K from the workspace (so y may be x):
  *             2 reads + 1 write per element, all CUs busy even for a few
  *             long rows.  0: rk_layernorm_gelu_auto_splits (S = 1 for rows
  *             a register tile holds, else the rule of
@@ -215,8 +216,9 @@ rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, const void *bi
                                rk_dtype dtype, rk_gelu_kind gelu, int32_t num_splits,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes rk_layernorm_gelu_ex needs: M * S * 8 for S > 1 (S the
- * resolved split count), 0 for S = 1 or invalid arguments. */
+/* Workspace bytes rk_layernorm_gelu_ex needs: M * (S + 1) * 8 for S > 1 (S
+ * the resolved split count; per row, S chunk summaries and the shift K as
+ * two floats each), 0 for S = 1 or invalid arguments. */
 size_t rk_layernorm_gelu_workspace_bytes(int64_t M, int64_t N, int32_t num_splits,
                                          rk_dtype dtype);
 

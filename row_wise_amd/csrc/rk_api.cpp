@@ -243,12 +243,13 @@ SplitPartials output_partials(const RowProblem &p)
 }
 
 // Long rows in few rows split across workgroups even without a workspace:
-// each row keeps its S partials in its own output, inside the first chunk,
-// which the last of three kernels writes after reading them.  That needs an
-// output apart from the input and a first chunk with room for the S partials
-// and the step to the next 8-byte boundary; S is lowered until it has room.
-// Returns the splits to use (1: none) and, for more, their chunk length.
-int32_t output_splits(const RowProblem &p, int32_t S, RowIo io, int64_t *chunk)
+// each row keeps its S partials (and `extra` more 8-byte slots: LayerNorm's
+// shift) in its own output, inside the first chunk, which the last of three
+// kernels writes after reading them.  That needs an output apart from the
+// input and a first chunk with room for the S + extra slots and the step to
+// the next 8-byte boundary; S is lowered until it has room.  Returns the
+// splits to use (1: none) and, for more, their chunk length.
+int32_t output_splits(const RowProblem &p, int32_t S, RowIo io, int64_t *chunk, int extra = 0)
 {
     if (S <= 1 || p.x == p.y || p.M > INT64_MAX / S || !grid_ok(p.M * S, kSplitThreads))
         return 1;
@@ -259,7 +260,7 @@ int32_t output_splits(const RowProblem &p, int32_t S, RowIo io, int64_t *chunk)
     for (; S > 1; --S) {
         const int64_t c = split_chunk(p.N, S, vec);
         const int64_t first = c - lead < p.N ? c - lead : p.N;
-        if (c <= INT32_MAX && first * es >= 8 * int64_t{S} + 8) {
+        if (c <= INT32_MAX && first * es >= 8 * (int64_t{S} + extra) + 8) {
             *chunk = c;
             return S;
         }
@@ -285,13 +286,20 @@ int32_t layernorm_auto_splits(int64_t M, int64_t N, rk_dtype dtype,
     return pick_splits(RK_OP_LAYERNORM_GELU, M, N, dtype, extra_us);
 }
 
-// Bytes of the split-row workspace: (mean, M2) as two floats per chunk.
-size_t split_workspace_bytes(int64_t M, int64_t S)
+// Bytes of the split-row workspace: two floats per chunk ((m, d) for softmax,
+// (mean, M2) for LayerNorm), plus `extra` 8-byte slots per row.
+size_t split_workspace_bytes(int64_t M, int64_t S, int extra = 0)
 {
-    if (S <= 1 || M > INT64_MAX / 8 / S)
+    if (S <= 1 || M > INT64_MAX / 8 / (S + extra))
         return 0;
-    return static_cast<size_t>(M * S * 8);
+    return static_cast<size_t>(M * (S + extra) * 8);
 }
+
+// LayerNorm's split kernels keep one more slot per row after the S chunk
+// summaries: the row's shift K = x[r][0], stored by the first kernel, so that
+// the output kernel never reads x[r][0] again (in place, another workgroup
+// of the same launch may already have overwritten it).
+constexpr int kLayerNormSlots = 1;
 
 // Workspace checks shared by the split-row entry points: `spans` are the
 // caller's matrices, which the workspace (written by the first kernel) must
@@ -612,7 +620,7 @@ RK_EXPORT size_t rk_layernorm_gelu_workspace_bytes(int64_t M, int64_t N, int32_t
         !valid_dtype(dtype))
         return 0;
     const int64_t S = num_splits == 0 ? layernorm_auto_splits(M, N, dtype) : num_splits;
-    return split_workspace_bytes(M, S);
+    return split_workspace_bytes(M, S, kLayerNormSlots);
 }
 
 RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, const void *bias,
@@ -634,7 +642,8 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
     if (S <= 1)
         return layernorm_single(p);
     const int es = elem_size(dtype);
-    st = check_workspace(workspace, workspace_bytes, split_workspace_bytes(M, S), M, S,
+    st = check_workspace(workspace, workspace_bytes, split_workspace_bytes(M, S, kLayerNormSlots),
+                         M, S,
                          {matrix_span(x, M, N, ldx, es), matrix_span(y, M, N, ldy, es),
                           matrix_span(weight, 1, N, N, es), matrix_span(bias, 1, N, N, es)});
     if (st != RK_OK)
@@ -644,7 +653,8 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
     const int64_t chunk = split_chunk(N, S, vec ? vec_elems(dtype) : 1);
     if (chunk > INT32_MAX)
         return RK_ERR_UNSUPPORTED;
-    const SplitPartials pt{static_cast<char *>(workspace), int64_t{S} * 8, false};
+    const SplitPartials pt{static_cast<char *>(workspace), (int64_t{S} + kLayerNormSlots) * 8,
+                           false};
     return hip_status(layernorm_split_run(p, S, static_cast<int>(chunk), pt, io));
 }
 
@@ -660,7 +670,8 @@ RK_EXPORT rk_status rk_layernorm_gelu(const void *x, const void *weight, const v
     const RowIo io = layernorm_io(p);
     int64_t C = 0;
     const int32_t S =
-        output_splits(p, layernorm_auto_splits(M, N, dtype, kOutputSplitExtraUs), io, &C);
+        output_splits(p, layernorm_auto_splits(M, N, dtype, kOutputSplitExtraUs), io, &C,
+                      kLayerNormSlots);
     if (S > 1)
         return hip_status(layernorm_split_run(p, S, static_cast<int>(C), output_partials(p), io));
     return layernorm_single(p);

@@ -25,13 +25,16 @@
 //                     memory-side cache); pass 2 writes GeLU(z).
 //                     2 reads + 1 write per element.
 // layernorm_partials  split-row, first kernel: one workgroup per
-//                     (row, chunk) writes the chunk's (mean, M2).
+//                     (row, chunk) writes the chunk's (mean, M2) to slot s
+//                     of the row's S + 1 slots; chunk 0 also writes the
+//                     shift K to slot S.
 // layernorm_finish    split-row, second kernel: one workgroup per
 //                     (row, chunk) merges the row's S summaries (each lane a
-//                     subset, then DPP) and writes its chunk.  With the
-//                     summaries kept in the output (no workspace), it runs
-//                     twice: everything but the first vectors of each row
-//                     (which hold the summaries), then those vectors.
+//                     subset, then DPP) and writes its chunk, shifting by
+//                     the K of slot S.  With the slots kept in the output
+//                     (no workspace), it runs twice: everything but the
+//                     first vectors of each row (which hold the slots), then
+//                     those vectors.
 // Rows are read and written as aligned 16-byte vectors from whatever offset
 // they start at (RowSpan), when input and output rows share that offset;
 // weight and bias, aligned at column 0, are shifted into each row's phase
@@ -245,17 +248,25 @@ __global__ __launch_bounds__(W *kWave) void layernorm_partials(const T *__restri
     chunk_span<E>(sp, s, S, C, jbeg, jend);
     // cached: the second kernel reads the chunk again.  Every chunk of a row
     // shifts by the same K, the row's first element.
-    Moments st = scan_moments<T, E, W, U, kCached>(xr - sp.h, sp, jbeg, jend,
-                                                   Elem<T>::to_f32(xr[0]));
+    const float K = Elem<T>::to_f32(xr[0]);
+    Moments st = scan_moments<T, E, W, U, kCached>(xr - sp.h, sp, jbeg, jend, K);
     st = ln_block_merge<W>(st, sn, sm, sq);
-    if (threadIdx.x == 0)
-        row_partials(pbase, prow, row)[s] = make_float2(st.mean, st.m2);
+    if (threadIdx.x == 0) {
+        float2 *pr = row_partials(pbase, prow, row);
+        pr[s] = make_float2(st.mean, st.m2);
+        // slot S: the shift, for the output kernel (x[r][0] may be gone by
+        // then when the output is the input)
+        if (s == 0)
+            pr[S] = make_float2(K, 0.0f);
+    }
 }
 
 // Chunk s of row r: workgroup (r, s) of a grid of M S (kAllChunks,
 // kAllButFirst) or workgroup r of a grid of M, s = 0 (kFirstOnly), over the
 // range output_range gives.  y and pbase may name the same memory (the
-// partials kept in the output).
+// partials kept in the output), and y may be x (in place, with a
+// workspace): the shift K comes from the partials' slot S, never from
+// x[r][0], which chunk 0's workgroup may already have overwritten.
 template <typename T, int E, int W, int U, int GK, bool PH>
 __global__ __launch_bounds__(W *kWave) void layernorm_finish(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b, T *y, int N,
@@ -268,17 +279,16 @@ __global__ __launch_bounds__(W *kWave) void layernorm_finish(
     const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
     int jbeg, jend;
     chunk_span<E>(sp, s, S, C, jbeg, jend);
-    output_range<T, E>(part, s, y + row * ldy, sp, S, jbeg, jend);
-    // the chunk's first loads and the shift K go out before the summaries
-    // are read
+    output_range<T, E>(part, s, y + row * ldy, sp, S + 1, jbeg, jend);
+    // the chunk's first loads go out before the summaries are read
     const auto first = ln_write_first<T, E, W, U>(xr - sp.h, sp, jbeg, jend);
-    const float K = Elem<T>::to_f32(xr[0]);
     // Every wave merges the row's S summaries on its own (lane l takes
     // summaries l, l + 64, ...): no LDS, and every workgroup of the row forms
     // the same bits.  A chunk's count is that of the row columns its vectors
     // hold.
     Moments st{0.0f, 0.0f, 0.0f};
     const float2 *wr = row_partials(pbase, prow, row);
+    const float K = wr[S].x;
     for (int i = static_cast<int>(threadIdx.x % kWave); i < S; i += kWave) {
         int jb, je;
         chunk_span<E>(sp, i, S, C, jb, je);

@@ -146,14 +146,14 @@ def test_residual_rmsnorm_limits(lib):
 
 
 def lnx(lib, x=A, w=A + 0x80000, b=A + 0x90000, y=B, M=4, N=4096, ldx=4096, ldy=4096, eps=1e-5,
-        dt=F32, gelu=0, S=8, ws=0x3000000, wb=4 * 8 * 8):
+        dt=F32, gelu=0, S=8, ws=0x3000000, wb=4 * 9 * 8):
     return lib.rk_layernorm_gelu_ex(x, w, b, y, M, N, ldx, ldy, eps, dt, gelu, S, ws, wb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(gelu=2), INVALID), (dict(gelu=-1), INVALID), (dict(S=-1), INVALID),
     (dict(S=65537), INVALID), (dict(eps=0.0), INVALID), (dict(b=None), INVALID),
-    (dict(ws=None), WORKSPACE), (dict(wb=4 * 8 * 8 - 1), WORKSPACE),
+    (dict(ws=None), WORKSPACE), (dict(wb=4 * 9 * 8 - 1), WORKSPACE),
     (dict(ws=0x3000004), INVALID),  # misaligned workspace
     (dict(ws=A + 64), INVALID),  # workspace overlaps x
     (dict(ws=A + 0x80000 - 8), INVALID),  # workspace overlaps the weight
@@ -165,7 +165,7 @@ def test_layernorm_ex_rejects(lib, kw, status):
 
 
 def test_layernorm_ex_workspace_and_splits(lib):
-    assert rk.rk_layernorm_gelu_workspace_bytes(64, 262144, 64, F32) == 64 * 64 * 8
+    assert rk.rk_layernorm_gelu_workspace_bytes(64, 262144, 64, F32) == 64 * 65 * 8
     assert rk.rk_layernorm_gelu_workspace_bytes(64, 262144, 1, F32) == 0
     assert rk.rk_layernorm_gelu_workspace_bytes(64, 262144, -1, F32) == 0
     assert rk.rk_layernorm_gelu_workspace_bytes(64, 262144, 4, 9) == 0
@@ -175,7 +175,7 @@ def test_layernorm_ex_workspace_and_splits(lib):
     assert rk.rk_layernorm_gelu_auto_splits(8, 16385, F32) > 1
     assert rk.rk_layernorm_gelu_auto_splits(4096, 65536, F32) == 1
     s = rk.rk_layernorm_gelu_auto_splits(64, 262144, F32)
-    assert s >= 2 and rk.rk_layernorm_gelu_workspace_bytes(64, 262144, 0, F32) == 64 * s * 8
+    assert s >= 2 and rk.rk_layernorm_gelu_workspace_bytes(64, 262144, 0, F32) == 64 * (s + 1) * 8
     # S = 1 needs no workspace and M = 0 is a no-op
     assert lnx(lib, M=0, x=None, y=None, ws=None) == 0
     assert lib.rk_layernorm_gelu_ex(None, None, None, None, 0, 8, 8, 8, 1e-5, F32, 1, 1, None, 0,

@@ -170,6 +170,28 @@ def test_split_padded_pitch_and_in_place(dtype):
         assert rel_err_floor1(xi, ref) <= tol_of(dtype), S
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+def test_split_in_place_past_residency(dtype):
+    """In place with a workspace, 96 rows x 64 chunks = 6144 workgroups, far
+    more than run at once: chunk 0 of a row may be written before another
+    chunk of that row starts, so the output kernel must not re-read the
+    row's first element (its shift) from x.  The result equals the
+    out-of-place call bit for bit and the oracle within tolerance."""
+    M, N, S = 96, 65536, 64
+    x = rowgen.randn(M, N, seed=83, scale=3.0, dtype=dtype)
+    x[::3] += 20.0  # a shift error of O(1) is O(1) in x_hat on every row
+    w, b = params(N, 83, dtype)
+    wd, bd = w.to(DEV), b.to(DEV)
+    ref = ref_of(x, w, b, "tanh")
+    y = rk.rk_layernorm_gelu_ex(x.to(DEV), wd, bd, EPS, num_splits=S)
+    xi = x.to(DEV)
+    rk.rk_layernorm_gelu_ex(xi, wd, bd, EPS, num_splits=S, out=xi)
+    err = rel_err_floor1(xi, ref)
+    say(f"ln split in place {key(dtype)} M={M} S={S} err={err:.3e}")
+    assert err <= tol_of(dtype)
+    assert torch.equal(xi.cpu(), y.cpu())
+
+
 def test_split_special_rows_and_determinism():
     M, N = 5, 50000
     x = rowgen.randn(M, N, seed=79)
