@@ -488,6 +488,47 @@ def test_infinities(dtype):
             assert np.all(np.isnan(yc[r])) and np.all(np.isnan(ref[r])), r
 
 
+def _neg_inf_rows(dtype, N=262144):
+    """Rows of 3 N(0,1) with -inf over whole blocks or chunks: the identity
+    state (-inf, 0) of the online recurrence and of the chunk merge.  The
+    regions are whole chunks of S = 2, 4 and 64 (N is a multiple of 64
+    vectors of either format), the first 64 KiB (one streaming step of a
+    16-wave workgroup), all but the last element, and every 7th element."""
+    regions = [(0, 65536 // torch.tensor([], dtype=dtype).element_size()), (0, N - 1),
+               (0, N // 2), (N // 2, N), (N // 4, N // 2), (3 * N // 4, N),
+               (0, N // 64), (32 * N // 64, 33 * N // 64), (63 * N // 64, N)]
+    x = rowgen.randn(len(regions) + 2, N, seed=97, scale=3.0, dtype=dtype)
+    for i, (a, b) in enumerate(regions):
+        x[i, a:b] = -math.inf
+    x[len(regions), ::7] = -math.inf
+    return x  # the last row stays finite
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=key)
+def test_neg_inf_blocks_and_chunks(dtype):
+    """Every online form against the plain definition on rows whose leading
+    blocks or one chunk hold only -inf ("第 6 讲" §7.2 start state;
+    "Triton Kernel 实现练习" §2.5 split version): streaming (S = 1), the
+    workspace split at S = 2, 4, 64, and rk_softmax's split with the
+    partials kept in the output.  -inf inputs give exact zeros."""
+    x = _neg_inf_rows(dtype)
+    M, N = x.shape
+    ref = oracle.softmax(x)
+    zero = torch.isinf(x).numpy()
+    xd = x.to(DEV)
+    outs = {f"S={S}": rk.rk_online_softmax(xd, num_splits=S) for S in (1, 2, 4, 64)}
+    assert rk.rk_online_softmax_auto_splits(M, N, rk.RK_F32 if dtype == torch.float32
+                                            else rk.RK_BF16) > 1
+    outs["rk_softmax"] = rk.rk_softmax(xd)
+    for name, y in outs.items():
+        yc = y.cpu().double().numpy()
+        err = rel_err_softmax(yc, ref)
+        say(f"neg_inf {key(dtype)} {name} err={err:.3e}")
+        assert np.all(yc[zero] == 0.0), name
+        assert err <= tol_of(dtype), name
+        assert yc[1, N - 1] == 1.0, name  # one finite value: exactly 1
+
+
 def test_empty_rows_is_noop():
     x = torch.empty(0, 128, device=DEV)
     assert rk.rk_softmax(x).shape == (0, 128)
