@@ -71,6 +71,7 @@ typedef enum rk_status {
     RK_ERR_UNSUPPORTED = 2, /* valid but beyond what the library handles */
     RK_ERR_WORKSPACE = 3,   /* workspace missing or too small */
     RK_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
+    RK_ERR_SCRATCH = 5,     /* more than rk_online_softmax_noalloc's scratch */
 } rk_status;
 
 /*
@@ -146,6 +147,32 @@ rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t N, int64_
  * streaming kernel is used or the arguments are invalid). */
 size_t rk_online_softmax_workspace_bytes(int64_t M, int64_t N, int32_t num_splits,
                                          rk_dtype dtype);
+
+/*
+ * rk_online_softmax for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, as
+ * rk_online_softmax with the same num_splits, but the split form keeps its
+ * partials in a fixed 1 MiB device array inside the library (one per GPU,
+ * held until the process ends) instead of a caller's workspace.  The call
+ * allocates and frees nothing; the first call on a device looks the array's
+ * address up once.
+ *
+ * Limits and contract
+ *   M * S * 8 bytes of partials (S the resolved split count) must fit the
+ *   1 MiB scratch (M * S <= 131072), else RK_ERR_SCRATCH and nothing is
+ *   enqueued.  S = 1 uses no scratch.  `stream` must belong to the current
+ *   device (else RK_ERR_INVALID_ARG).  Every call on a GPU shares that
+ *   GPU's scratch: calls on one stream are ordered, but split calls that
+ *   overlap in time on one GPU (other streams, other host threads) race on
+ *   it and may return wrong results.  Nothing in the scratch needs clearing:
+ *   the first kernel writes every partial the second reads.
+ * Returns as rk_online_softmax (without the workspace cases), plus
+ * RK_ERR_SCRATCH; RK_ERR_HIP if the scratch address cannot be obtained.
+ */
+rk_status rk_online_softmax_noalloc(const void *x, void *y, int64_t M, int64_t N, int64_t ldx,
+                                    int64_t ldy, rk_dtype dtype, int32_t num_splits,
+                                    hipStream_t stream);
 
 /* The split count rk_online_softmax uses for num_splits == 0 (1 for invalid
  * arguments). */

@@ -9,6 +9,8 @@ Functions carry the C entry points' names:
 
 * ``rk_softmax(x, out=None)``
 * ``rk_online_softmax(x, num_splits=1, out=None, workspace=None)``
+* ``rk_online_softmax_noalloc(x, num_splits=1, out=None)`` (partials in the library's fixed
+  device scratch)
 * ``rk_layernorm_gelu(x, weight, bias, eps=1e-5, out=None)``
 * ``rk_layernorm_gelu_ex(x, weight, bias, eps=1e-5, gelu="tanh", num_splits=1, out=None,
   workspace=None)``, ``rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype)``,
@@ -40,7 +42,7 @@ __all__ = [
     "rk__residual_rmsnorm_variant", "RK_OP_RMSNORM", "RK_OP_RESIDUAL_RMSNORM",
     "rk_layernorm_gelu_ex", "rk_layernorm_gelu_workspace_bytes", "rk_layernorm_gelu_auto_splits",
     "RK_GELU_TANH", "RK_GELU_ERF", "rk_row_sum", "rk_row_max", "rk_gelu", "rk_flash_attention",
-    "RK_F16",
+    "RK_F16", "rk_online_softmax_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.so")
@@ -76,6 +78,7 @@ def load():
     sig = {
         "rk_softmax": (i32, [vp, vp, i64, i64, i64, i64, i32, vp]),
         "rk_online_softmax": (i32, [vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]),
+        "rk_online_softmax_noalloc": (i32, [vp, vp, i64, i64, i64, i64, i32, i32, vp]),
         "rk_online_softmax_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "rk_online_softmax_auto_splits": (i32, [i64, i64, i32]),
         "rk_layernorm_gelu": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
@@ -227,6 +230,17 @@ def rk_online_softmax(x, num_splits: int = 1, out=None, workspace=None):
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _call("rk_online_softmax", v.data_ptr(), o.data_ptr(), M, N, ldx, ldy, _dtype_code(x),
           int(num_splits), wptr, wbytes, _stream(x))
+    return o.reshape(x.shape) if out is None else out
+
+
+def rk_online_softmax_noalloc(x, num_splits: int = 1, out=None):
+    """rk_online_softmax with the split partials in the library's fixed device
+    scratch instead of a workspace (the library allocates nothing)."""
+    _check_device(x)
+    v, M, N, ldx = _as_rows(x)
+    o, ldy = _out_like(x, v, out)
+    _call("rk_online_softmax_noalloc", v.data_ptr(), o.data_ptr(), M, N, ldx, ldy,
+          _dtype_code(x), int(num_splits), _stream(x))
     return o.reshape(x.shape) if out is None else out
 
 

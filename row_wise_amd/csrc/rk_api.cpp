@@ -606,6 +606,46 @@ RK_EXPORT rk_status rk_online_softmax(const void *x, void *y, int64_t M, int64_t
     return hip_status(online_split_run(p, S, static_cast<int>(chunk), pt, io));
 }
 
+RK_EXPORT rk_status rk_online_softmax_noalloc(const void *x, void *y, int64_t M, int64_t N,
+                                              int64_t ldx, int64_t ldy, rk_dtype dtype,
+                                              int32_t num_splits, hipStream_t stream)
+{
+    rk_status st = check_rows(x, y, M, N, ldx, ldy, dtype);
+    if (st != RK_OK)
+        return st;
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const RowProblem p = make_problem(x, y, nullptr, nullptr, M, N, ldx, ldy, 0.0f, dtype, stream);
+    const int32_t S = num_splits == 0 ? auto_splits(M, N, dtype) : num_splits;
+    if (S <= 1)
+        return softmax_generic(p);
+    const size_t need = split_workspace_bytes(M, S);
+    if (need == 0 || need > kScratchBytes)
+        return RK_ERR_SCRATCH;
+    if (!grid_ok(M * S, kSplitThreads))
+        return RK_ERR_UNSUPPORTED;
+    const RowIo io = softmax_io(p);
+    const int64_t chunk = split_chunk(N, S, io != kIoElement ? vec_elems(dtype) : 1);
+    if (chunk > INT32_MAX)
+        return RK_ERR_UNSUPPORTED;
+    // the scratch of the current device, which the stream must run on
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess)
+        return RK_ERR_HIP;
+    if (stream != nullptr) {
+        int stream_device = 0;
+        if (hipStreamGetDevice(stream, &stream_device) != hipSuccess || stream_device != device)
+            return RK_ERR_INVALID_ARG;
+    }
+    void *scratch = nullptr;
+    if (scratch_address(device, &scratch) != hipSuccess)
+        return RK_ERR_HIP;
+    const SplitPartials pt{static_cast<char *>(scratch), int64_t{S} * 8, false};
+    return hip_status(online_split_run(p, S, static_cast<int>(chunk), pt, io));
+}
+
 RK_EXPORT int32_t rk_layernorm_gelu_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
 {
     if (M < 1 || N < 1 || !valid_dtype(dtype))
@@ -908,6 +948,8 @@ RK_EXPORT const char *rk_status_string(rk_status status)
         return "workspace missing or too small";
     case RK_ERR_HIP:
         return "HIP launch failed";
+    case RK_ERR_SCRATCH:
+        return "split partials exceed the library's fixed 1 MiB scratch";
     }
     return "unknown status";
 }

@@ -146,6 +146,13 @@ hipError_t flash_attention_run(const AttentionProblem &p);
 hipError_t probe_copy_run(const void *src, void *dst, size_t bytes, int max_wg,
                           hipStream_t stream);
 
+// Bytes of the fixed device scratch (rk_scratch.hip) that the allocation-free
+// entry point keeps its split partials in: 1 MiB, 131072 (m, d) pairs.
+constexpr size_t kScratchBytes = size_t{1} << 20;
+// Device address of the scratch on `device`, which must be the current
+// device; looked up once per device and kept.
+hipError_t scratch_address(int device, void **address);
+
 inline int elem_size(rk_dtype dt) { return dt == RK_F32 ? 4 : 2; }
 inline int vec_elems(rk_dtype dt) { return 16 / elem_size(dt); }
 

@@ -258,6 +258,21 @@ def test_online_rejects(lib):
     assert online(lib, N=0) == INVALID
 
 
+def test_online_noalloc_rejects(lib):
+    X, Y = 0x10000000, 0x20000000
+
+    def f(M=4, N=4096, S=64, x=X, y=Y, dt=F32):
+        return lib.rk_online_softmax_noalloc(x, y, M, N, N, N, dt, S, None)
+
+    assert f(S=-1) == INVALID and f(S=65537) == INVALID and f(N=0) == INVALID
+    assert f(y=X + 64) == INVALID  # y overlaps x
+    assert f(M=0, x=None, y=None) == 0
+    # partials beyond the 1 MiB scratch (131072 pairs): refused before any
+    # HIP call
+    assert f(M=2049, S=64) == 5 and f(M=3, N=2**20, S=65536) == 5
+    assert rk.rk_status_string(5).startswith("split partials exceed")
+
+
 def test_workspace_bytes(lib):
     assert rk.rk_online_softmax_workspace_bytes(64, 262144, 64, F32) == 64 * 64 * 8
     assert rk.rk_online_softmax_workspace_bytes(64, 262144, 1, F32) == 0
