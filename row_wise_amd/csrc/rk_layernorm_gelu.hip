@@ -11,7 +11,9 @@
 //                      element): sum -> wave DPP / LDS -> centre in registers
 //                      -> sum of squares -> wave DPP / LDS -> epilogue.  A row
 //                      group handles R rows in sequence and loads weight and
-//                      bias once for all of them.
+//                      bias once for all of them.  The exact bf16 tiles take
+//                      both sums of x - x[0] in one pass and one DPP / LDS
+//                      round (SH below).
 // Rows beyond the register capacity, or not 16-byte aligned, go to the
 // streaming and split-row kernels of rk_layernorm_long.hip.
 #include "rk_device.h"
@@ -26,12 +28,16 @@ namespace rk {
 // same offset), read and written as the aligned vectors that cover them
 // (RowSpan), their ends masked; weight and bias are shifted into each row's
 // offset as they are used.  One row per row group.
-template <typename T, int G, int V, int W, int R, bool EXACT, int GK, bool PH>
+// SH (EXACT, not PH): one pass over the registers for both sums, of
+// d = x - K with K the row's first element: mean = K + sum d / N and
+// var = sum d^2 / N - (sum d / N)^2, so both reductions share one barrier.
+template <typename T, int G, int V, int W, int R, bool EXACT, int GK, bool PH, bool SH = false>
 __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
     T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
 {
     static_assert(!PH || (!EXACT && R == 1), "phased rows: general tiles, one row per group");
+    static_assert(!SH || (EXACT && !PH), "one shifted pass: exact tiles");
     constexpr int E = Elem<T>::kVec;
     constexpr int RG = W / G;
     constexpr int L = G * kWave;
@@ -41,7 +47,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     __shared__ float red_sum[2][RG][G];
     __shared__ float red_var[2][RG][G];
 
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform: row bases stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int grp = wave / G;
     const int wig = wave % G;
     const int li = wig * kWave + static_cast<int>(threadIdx.x % kWave);
@@ -86,6 +93,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         xl.issue(x + (ok ? row : 0) * ldx, li, ok ? nv : 0, rs, 0.0f,
                  EXACT || (ok && slots_full));
     }
+    // SH: the shift of the row being issued, loaded with it
+    float k_next = SH ? Elem<T>::to_f32(x[(row_of(0) < M ? row_of(0) : 0) * ldx]) : 0.0f;
     RowLoad<T, E, V, L, kCached> wl, bl;
     if constexpr (!PH) {
         wl.issue(w, li, nv, rs, 0.0f, slots_full);
@@ -108,13 +117,50 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
             xs.finish(v, sp, jend, 0.0f, false);
         else
             xl.finish(v, rs);
+        const float K = k_next;
         if (r + 1 < R) {
             const int64_t nrow = row_of(r + 1);
             const bool nok = nrow < M;
             xl.issue(x + (nok ? nrow : 0) * ldx, li, nok ? nv : 0, rs, 0.0f,
                      EXACT || (nok && slots_full));
+            if constexpr (SH)
+                k_next = Elem<T>::to_f32(x[(nok ? nrow : 0) * ldx]);
         }
 
+        // z = fma(fma(v, rstd, cen), w, b) once the statistics are known
+        float rstd, cen = 0.0f;
+        if constexpr (SH) {
+            float s = 0.0f, q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = v[k][e] - K;
+                    v[k][e] = d;
+                    s += d;
+                    q = fmaf(d, d, q);
+                }
+            s = wave_sum(s);
+            q = wave_sum(q);
+            if constexpr (G > 1) {
+                if (threadIdx.x % kWave == 0) {
+                    red_sum[buf][grp][wig] = s;
+                    red_var[buf][grp][wig] = q;
+                }
+                __syncthreads();
+                s = red_sum[buf][grp][0];
+                q = red_var[buf][grp][0];
+#pragma unroll
+                for (int g = 1; g < G; ++g) {
+                    s += red_sum[buf][grp][g];
+                    q += red_var[buf][grp][g];
+                }
+            }
+            const float mean_k = s * inv_n;
+            const float var = fmaxf(fmaf(q, inv_n, -mean_k * mean_k), 0.0f);
+            rstd = __builtin_amdgcn_rsqf(var + eps);
+            cen = -mean_k * rstd;
+        } else {
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < V; ++k)
@@ -160,7 +206,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
                 q += red_var[buf][grp][g];
         }
         // hardware reciprocal square root (1 ulp), once per row
-        const float rstd = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
+        rstd = __builtin_amdgcn_rsqf(fmaf(q, inv_n, eps));
+        }
 
         if constexpr (R > 1) {
             // weight and bias serve R rows: unpack them once
@@ -172,7 +219,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
             for (int k = 0; k < V; ++k)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    v[k][e] = gelu<GK>(fmaf(v[k][e] * rstd, wv[k][e], bv[k][e]));
+                    v[k][e] = gelu<GK>(fmaf(SH ? fmaf(v[k][e], rstd, cen) : v[k][e] * rstd,
+                                            wv[k][e], bv[k][e]));
         } else {
             // one row: unpack weight and bias a vector at a time, so that they
             // stay packed (half the registers for bf16) until used
@@ -191,7 +239,8 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    v[k][e] = gelu<GK>(fmaf(v[k][e] * rstd, wk[e], bk[e]));
+                    v[k][e] = gelu<GK>(fmaf(SH ? fmaf(v[k][e], rstd, cen) : v[k][e] * rstd,
+                                            wk[e], bk[e]));
             }
         }
         if constexpr (PH) {
@@ -205,14 +254,14 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     }
 }
 
-template <typename T, int G, int V, int W, int R, bool EXACT, bool PH>
+template <typename T, int G, int V, int W, int R, bool EXACT, bool PH, bool SH = false>
 static hipError_t layernorm_gelu_tile_run(const RowProblem &p)
 {
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG * R - 1) / (RG * R);
     const float inv_n = static_cast<float>(1.0 / p.N);
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 1, PH>
-                                        : layernorm_gelu_tile<T, G, V, W, R, EXACT, 0, PH>;
+    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 1, PH, SH>
+                                        : layernorm_gelu_tile<T, G, V, W, R, EXACT, 0, PH, SH>;
     return launch(kernel, dim3(static_cast<unsigned>(blocks)), dim3(W * kWave), p.stream,
                   static_cast<const T *>(p.x), static_cast<const T *>(p.w),
                   static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,
@@ -240,6 +289,14 @@ template <typename T, int G, int V, int W, int R = 1>
 constexpr TileVariant exact()
 {
     return tile<T, G, V, W, R, true>();
+}
+// An exact tile with the one shifted pass (SH).
+template <typename T, int G, int V, int W, int R = 1>
+constexpr TileVariant exact_shifted()
+{
+    return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec, true,
+                       &layernorm_gelu_tile_run<T, G, V, W, R, true, false, true>, false,
+                       nullptr};
 }
 
 // Preference order as for softmax: first exact entry with max_n == N, else
@@ -276,16 +333,20 @@ static const TileVariant kLayerNormF32[] = {
     alt(exact<float, 1, 3, 4, 4>()),
     alt(exact<float, 8, 4, 8>()),
     alt(exact<float, 16, 4, 16>()),
+    alt(exact_shifted<float, 1, 3, 4>()),  // 3x the error of two passes, no faster
 };
 
+// bf16 exact tiles take the one shifted pass (SH): bf16 storage rounding
+// (2^-9) dwarfs the pass's cancellation, and one barrier per row instead of
+// two measured 48.5 -> 47.0 us at 16384 x 4096 (kernel trace average).
 static const TileVariant kLayerNormBF16[] = {
-    exact<bf16_t, 1, 1, 4>(),   // N = 512
-    exact<bf16_t, 1, 2, 4>(),   // N = 1024
-    exact<bf16_t, 1, 4, 4>(),   // N = 2048
-    exact<bf16_t, 4, 2, 4, 2>(), // N = 4096
-    exact<bf16_t, 8, 2, 8>(),   // N = 8192
-    exact<bf16_t, 8, 4, 8>(),   // N = 16384 (measured 49 us vs 55 us for 16 x 2 at 128 MiB)
-    exact<bf16_t, 16, 4, 16>(), // N = 32768
+    exact_shifted<bf16_t, 1, 1, 4>(),    // N = 512
+    exact_shifted<bf16_t, 1, 2, 4>(),    // N = 1024
+    exact_shifted<bf16_t, 1, 4, 4>(),    // N = 2048
+    exact_shifted<bf16_t, 4, 2, 4, 2>(), // N = 4096
+    exact_shifted<bf16_t, 8, 2, 8>(),    // N = 8192
+    exact_shifted<bf16_t, 8, 4, 8>(),    // N = 16384 (8 x 4: 49 us vs 55 us for 16 x 2)
+    exact_shifted<bf16_t, 16, 4, 16>(),  // N = 32768
     tile<bf16_t, 1, 1, 4>(),    // N <= 512
     tile<bf16_t, 1, 2, 4>(),    // N <= 1024
     tile<bf16_t, 1, 4, 4>(),    // N <= 2048
@@ -307,6 +368,15 @@ static const TileVariant kLayerNormBF16[] = {
     alt(exact<bf16_t, 16, 2, 16>()),
     alt(exact<bf16_t, 8, 8, 8>()),
     alt(exact<bf16_t, 4, 8, 4>()),
+    // the two-pass forms of the dispatched exact tiles
+    alt(exact<bf16_t, 1, 1, 4>()),
+    alt(exact<bf16_t, 1, 2, 4>()),
+    alt(exact<bf16_t, 1, 4, 4>()),
+    alt(exact<bf16_t, 4, 2, 4, 2>()),
+    alt(exact<bf16_t, 8, 2, 8>()),
+    alt(exact<bf16_t, 8, 4, 8>()),
+    alt(exact<bf16_t, 16, 4, 16>()),
+    alt(exact_shifted<bf16_t, 2, 4, 4, 2>()),
 };
 
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count)

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(W *kWave) void row_reduce(const T *__restrict__ x, 
     static_assert(W % G == 0, "whole row groups per workgroup");
     __shared__ float red[RG][G];
 
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform: row bases stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int grp = wave / G;
     const int wig = wave % G;
     const int li = wig * kWave + static_cast<int>(threadIdx.x % kWave);

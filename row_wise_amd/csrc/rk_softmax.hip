@@ -34,7 +34,8 @@ __global__ __launch_bounds__(W *kWave) void softmax_tile(const T *__restrict__ x
     __shared__ float red_max[RG][G];
     __shared__ float red_sum[RG][G];
 
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform: row bases stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int grp = wave / G;
     const int wig = wave % G;
     const int li = wig * kWave + static_cast<int>(threadIdx.x % kWave);

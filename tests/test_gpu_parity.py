@@ -209,6 +209,37 @@ def test_layernorm_gelu_variant(dtype, index, N):
     assert rel_err_floor1(y, oracle.layernorm_gelu(base[:, :N], w, b, EPS)) <= tol_of(dtype)
 
 
+def _exact_bf16_layernorm():
+    return [(v["index"], v["max_n"]) for v in rk.variants(rk.RK_OP_LAYERNORM_GELU, rk.RK_BF16)
+            if v["exact"]]
+
+
+@pytest.mark.parametrize("index,N", _exact_bf16_layernorm(), ids=str)
+def test_layernorm_gelu_bf16_exact_hard_rows(index, N):
+    """The exact bf16 tiles, one pass over x - x[0] or two passes: rows whose
+    first element is far from the mean (the shift then cancels most in
+    sum d^2 / N - mean_d^2), rows far from zero, a constant row, a row of two
+    values and one huge outlier; within 1e-2 of the oracle."""
+    g = torch.Generator().manual_seed(N + 7 * index)
+    x = torch.randn(9, N, generator=g)
+    x[0, 0] = 40.0  # the shift 40 sigma from the mean
+    x[1, 0] = -300.0
+    x[2] += 100.0  # mean 100, sigma 1 (bf16 spacing 0.5 there)
+    x[3] = 1.25  # constant: x_hat = 0, y = GeLU(b)
+    x[4] = torch.where(torch.arange(N) % 2 == 0, 3.0, -1.0)
+    x[5] = 0.0
+    x[5, N // 2] = 1000.0  # one outlier: x_hat = +-sqrt(N - 1) and -1 / sqrt(N - 1)
+    x[6] *= 1e-3  # variance near eps
+    x[7] = x[7] * 50.0 + 2000.0
+    x = x.to(torch.bfloat16)
+    w, b = rowgen.ln_params(N, g, torch.bfloat16)
+    y = rk.rk__layernorm_gelu_variant(index, x.to(DEV), w.to(DEV), b.to(DEV), EPS)
+    ref = oracle.layernorm_gelu(x, w, b, EPS)
+    err = rel_err_floor1(y, ref)
+    say(f"ln bf16 exact index {index} N={N} hard rows err={err:.2e}")
+    assert err <= TOL["bf16"]
+
+
 def _phased_cases(op):
     """General one-row-per-group tiles on rows at every offset: odd N, so row
     r starts r N elements into an aligned buffer; N + E - 1 fits the tile."""
