@@ -68,6 +68,8 @@ def _signatures():
         "oracle_row_max": [P, P, i64, i64],
         "oracle_attention": [P, P, P, P, i64, i64, i64, ctypes.c_int, d],
         "oracle_flash_attention": [P, P, P, P, i64, i64, i64, ctypes.c_int, d, i64, i64],
+        "oracle_attention_rows": [P, ctypes.POINTER(i64), i64, P, P, P, i64, i64, ctypes.c_int,
+                                  d],
     }
 
 
@@ -292,6 +294,25 @@ class Oracle:
         self.lib.oracle_attention(_p(q), _p(k), _p(v), _p(o), BH, T, d, int(causal), sc)
         return o
 
+    def attention_rows(self, q_rows, positions, k, v, causal: bool = False,
+                       scale: float | None = None):
+        """The definition for selected query rows of one (batch, head):
+        q_rows [n, d] are the queries at `positions` of the sequence of k and
+        v [T, d]; causal: the query at position p sees keys j <= p."""
+        q, k, v = _f64(q_rows), _f64(k), _f64(v)
+        pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64))
+        if q.ndim != 2 or k.ndim != 2 or k.shape != v.shape or q.shape[1] != k.shape[1] \
+                or pos.shape != (q.shape[0],):
+            raise ValueError("q_rows [n, d], positions [n], k and v [T, d]")
+        T, d = k.shape
+        if pos.size and (pos.min() < 0 or pos.max() >= T):
+            raise ValueError("positions must lie in [0, T)")
+        sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+        o = np.empty_like(q)
+        self.lib.oracle_attention_rows(_p(q), pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                       q.shape[0], _p(k), _p(v), _p(o), T, d, int(causal), sc)
+        return o
+
     def flash_attention(self, q, k, v, causal: bool = False, scale: float | None = None,
                         block_q: int = 16, block_kv: int = 16):
         """The tiled online-softmax form with the given block sizes."""
@@ -328,6 +349,6 @@ for _n in ["softmax", "softmax_stats", "online_stats", "merge", "split_stats", "
            "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
            "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf",
            "chunk_moments", "chan_merge", "split_moments", "layernorm_gelu_ex", "row_sum",
-           "row_max", "attention", "flash_attention"]:
+           "row_max", "attention", "flash_attention", "attention_rows"]:
     globals()[_n] = _forward(_n)
 del _n

@@ -480,6 +480,43 @@ void oracle_attention(const double *q, const double *k, const double *v, double 
     free(w);
 }
 
+/* The definition for selected query rows of one (batch, head): row r of q
+ * (nq rows of d) is the query at position pos[r] of a sequence of T keys and
+ * values; causal: it sees keys j <= pos[r] only.  Each output row is formed
+ * exactly as in oracle_attention (scores, max, exp-weights, their sum, the
+ * weighted sum of value rows), so sampled rows of a long sequence can be
+ * checked without computing the others. */
+void oracle_attention_rows(const double *q, const int64_t *pos, int64_t nq, const double *k,
+                           const double *v, double *o, int64_t T, int64_t d, int causal,
+                           double scale)
+{
+    double *s = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double *w = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int64_t r = 0; r < nq; ++r) {
+        int64_t n = causal ? pos[r] + 1 : T;  /* visible keys 0 .. n-1 */
+        for (int64_t j = 0; j < n; ++j) {
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                dot += q[r * d + c] * k[j * d + c];
+            s[j] = dot * scale;
+        }
+        double m = row_max(s, n);
+        double den = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            w[j] = exp(s[j] - m);
+            den += w[j];
+        }
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                acc += w[j] * v[j * d + c];
+            o[r * d + c] = acc / den;
+        }
+    }
+    free(s);
+    free(w);
+}
+
 /* The tiled form ([L6] §7.3, [TKE] §5.2): query blocks of Br rows; for each,
  * key/value blocks of Bc rows are scanned with a per-row state m (max so
  * far), l (sum of exp so far) and acc (exp-weighted sum of value rows so

@@ -705,6 +705,26 @@ def check_attention_brute_force(orc):
                 assert abs(o[0, i, c] - float(ref)) <= 4e-15 * max(1.0, abs(float(ref)))
 
 
+def check_attention_rows(orc):
+    # selected query rows at their positions equal torch's attention in
+    # float64 at those rows (causal and not), and the first causal row sees
+    # only key 0
+    import torch
+
+    r = _rng(71)
+    T, d = 97, 16
+    q, k, v = (r.standard_normal((T, d)) for _ in range(3))
+    pos = np.array([0, 1, 5, 48, 95, 96])
+    for causal in (False, True):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[None]), torch.from_numpy(k[None]), torch.from_numpy(v[None]),
+            is_causal=causal).numpy()[0]
+        o = orc.attention_rows(q[pos], pos, k, v, causal)
+        assert np.max(np.abs(o - ref[pos])) <= 1e-13, causal
+    o = orc.attention_rows(q[:1], [0], k, v, True)
+    assert np.array_equal(o[0], v[0])
+
+
 def check_flash_attention_tiled(orc):
     r = _rng(131)
     for T, d in ((1, 4), (37, 16), (100, 32)):
@@ -754,4 +774,5 @@ PINS = [
     check_attention_permutation,
     check_attention_brute_force,
     check_flash_attention_tiled,
+    check_attention_rows,
 ]
