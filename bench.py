@@ -275,6 +275,7 @@ def all_cases():
         Case("residual_rmsnorm_f32_4096x768", "residual_rmsnorm", "ln_gelu_f32_4096x768"),
         Case("rmsnorm_bf16_16384x4096", "rmsnorm", "bf16_16384x4096"),
         Case("residual_rmsnorm_bf16_16384x4096", "residual_rmsnorm", "bf16_16384x4096"),
+        AttnCase("attn_bf16_1x8x4096x128", 1, 8, 4096, 128, "bf16", False),
         AttnCase("attn_bf16_4x32x1024x128", 4, 32, 1024, 128, "bf16", False),
         AttnCase("attn_bf16_4x32x4096x128", 4, 32, 4096, 128, "bf16", False),
         AttnCase("attn_causal_bf16_4x32x4096x128", 4, 32, 4096, 128, "bf16", True),

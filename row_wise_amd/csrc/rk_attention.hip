@@ -102,14 +102,16 @@ __device__ __forceinline__ float group4_max(float v)
 
 constexpr int kAttnBN = 64;  // keys per step
 
+// K and V^T row pitches carry 32 bytes of padding.  Each fragment read is
+// one 16-byte ds_read_b128 per lane, lane (g, l16) at row 16 t + l16 and
+// 16-byte chunk 4 s + g.  Measured with the hardware's bank-conflict counter
+// on gfx950 (a probe issuing only such reads): with 16 bytes of padding
+// (272- and 144-byte rows) every such read costs 4 conflict cycles on top of
+// its 4, with 32 bytes (288 and 160) none, as for a linear read.
 template <int D>
 struct AttnLds {
-    static constexpr int kKStride = D + 8;       // K row pitch (elements): 16 B of padding
-    // V^T row pitch: 72 elements (36 words).  Rows stay 16-byte aligned for
-    // the 16-byte operand reads; the 16 rows one read serves start on banks
-    // 36 r mod 64, distinct multiples of 4, and the V^T writes of a wave (rows
-    // 8 apart, 288 words) fall on the other half of the banks.
-    static constexpr int kVStride = kAttnBN + 8;
+    static constexpr int kKStride = D + 16;        // K row pitch (elements)
+    static constexpr int kVStride = kAttnBN + 16;  // V^T row pitch (elements)
     uint16_t k[kAttnBN * kKStride];
     uint16_t vt[D * kVStride];
 };
