@@ -4,7 +4,9 @@ definition) on seeded inputs ("Triton Kernel 实现练习" §5.2; "第 6 讲" §
 Error measure: max |o - r| / max(|r|, 1) (outputs are convex combinations
 of N(0,1) value rows), 1e-2 for bf16 and fp16 I/O with fp32 accumulation.
 Full-size shapes are checked on sampled (batch, head) pairs, each against
-the oracle over its whole T x T problem.
+the oracle over its whole T x T problem, except the unmasked T = 4096 case,
+where four heads are checked on 384 sampled query rows each (unmasked rows
+are independent of one another).
 """
 import numpy as np
 import pytest
@@ -58,10 +60,23 @@ def check(o, q, k, v, causal, scale=None, heads=None, what=""):
 def test_pages_benchmark_shapes(dtype, causal, T):
     q, k, v = rowgen.attention_qkv(4, 32, T, 128, dtype, seed=2000 + T)
     o = rk.rk_flash_attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
-    heads = [(0, 0), (3, 31)] if T >= 1024 else [(0, 0), (1, 7), (3, 31)]
     if T == 4096 and not causal:
-        heads = [(3, 31)]  # the oracle takes ~9 s per head here
-    err = check(o, q, k, v, causal, heads=heads, what=(T, causal))
+        # the oracle takes ~9 s per whole head here; without the mask every
+        # query row depends on its own q row only, so each of four heads is
+        # checked on 384 rows (the first and last 64 and 256 seeded others),
+        # every one of them exactly against the definition
+        rng = np.random.default_rng(T)
+        rows = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T),
+                                         rng.choice(np.arange(64, T - 64), 256, replace=False)]))
+        oc = o.cpu()
+        err = 0.0
+        for b, h in [(0, 0), (1, 9), (2, 22), (3, 31)]:
+            ref = oracle.attention_rows(q[b, h][rows], rows, k[b, h], v[b, h], False)
+            err = max(err, rel_err_floor1(oc[b, h][rows], ref))
+        assert err <= TOL, (T, causal, err)
+    else:
+        heads = [(0, 0), (3, 31)] if T >= 1024 else [(0, 0), (1, 7), (3, 31)]
+        err = check(o, q, k, v, causal, heads=heads, what=(T, causal))
     say(f"attention {key(dtype)} 4x32x{T}x128 causal={causal} err={err:.3e}")
 
 
