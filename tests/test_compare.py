@@ -83,3 +83,24 @@ def test_nonfinite_is_rejected():
     assert rel_err_softmax(np.array([[math.nan, 0.75]]), ref) == math.inf
     assert rel_err_floor1(np.array([[math.inf, 0.75]]), ref) == math.inf
     assert rel_err_softmax(ref, ref) == 0.0
+
+
+def test_pure_relative_above_threshold():
+    from tolerance import rel_err_above
+
+    ref = np.array([1e-4, -0.02, 0.5, 3.0])
+    y = ref * np.array([1.5, 1.0 + 2e-6, 1.0 - 1e-6, 1.0])  # 50% off below the threshold
+    assert rel_err_above(y, ref, 1e-2) <= 2.0001e-6
+    assert rel_err_above(y, ref, 1e-5) >= 0.5
+    assert rel_err_above(y, ref, 10.0) == 0.0
+    assert rel_err_above(np.array([np.nan, 1.0]), np.array([1.0, 1.0]), 0.5) == float("inf")
+    # an fp32 evaluation of config 2 holds 1e-5 as a pure relative error where |r| >= 0.01
+    d = rowgen.make("ln_gelu_f32_4096x768", rows=128)
+    x, w, b = (d[k].numpy().astype(np.float32) for k in ("x", "w", "b"))
+    mean = x.mean(axis=1, keepdims=True, dtype=np.float32)
+    var = ((x - mean) ** 2).mean(axis=1, keepdims=True, dtype=np.float32)
+    z = ((x - mean) / np.sqrt(var + np.float32(EPS)) * w + b).astype(np.float32)
+    k = np.float32(math.sqrt(2 / math.pi))
+    y = (np.float32(0.5) * z * (np.float32(1) + np.tanh(k * (z + np.float32(0.044715) * z ** 3)))).astype(np.float32)
+    ref = oracle.layernorm_gelu(x, w, b, EPS)
+    assert rel_err_above(y, ref, 1e-2) <= TOL["f32"]

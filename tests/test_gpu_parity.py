@@ -14,7 +14,7 @@ import torch
 import oracle
 import row_wise_amd as rk
 import rowgen
-from tolerance import TOL, rel_err, rel_err_floor1, rel_err_softmax
+from tolerance import TOL, rel_err, rel_err_above, rel_err_floor1, rel_err_softmax
 
 pytestmark = pytest.mark.gpu
 EPS = float(np.float32(1e-5))
@@ -60,6 +60,22 @@ def test_ln_gelu_f32_4096x768():
     err = rel_err_floor1(y, ref)
     say(f"ln_gelu_f32_4096x768 err={err:.3e}")
     assert err <= TOL["f32"]
+
+
+@pytest.mark.parametrize("name,rows", [("ln_gelu_f32_4096x768", None), ("bf16_16384x4096", 2048)])
+def test_layernorm_gelu_pure_relative(name, rows):
+    """The stated tolerance as a pure relative error wherever the output is
+    not near zero (|r| >= 0.01), on the LayerNorm+GeLU workloads; the pure
+    relative error down to |r| >= 0.001 is printed beside it."""
+    d = rowgen.make(name, rows=rows)
+    x, w, b = d["x"], d["w"], d["b"]
+    y = rk.rk_layernorm_gelu(x.to(DEV), w.to(DEV), b.to(DEV), EPS)
+    ref = oracle.layernorm_gelu(x, w, b, EPS)
+    tol = tol_of(x.dtype)
+    e2, e3 = rel_err_above(y, ref, 1e-2), rel_err_above(y, ref, 1e-3)
+    say(f"{name} pure relative: |r| >= 1e-2 {e2:.3e}, |r| >= 1e-3 {e3:.3e}, "
+        f"floor 1 {rel_err_floor1(y, ref):.3e}")
+    assert e2 <= tol
 
 
 def test_softmax_f32_8192x1000():

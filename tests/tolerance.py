@@ -8,7 +8,9 @@ exact zero.
 LayerNorm + GeLU: max |y - r| / max(|r|, 1), i.e. relative error with the
 denominator floored at the unit scale of normalized activations.  z = w x_hat + b
 cancels near zero, so a pure relative measure would judge rounding noise of
-fp32 arithmetic around z = 0, not the kernel.
+fp32 arithmetic around z = 0, not the kernel.  Where the output is not near
+zero the tolerance also holds as a pure relative error: rel_err_above(y, r,
+0.01) is max |y - r| / |r| over the elements with |r| >= 0.01.
 
 RMSNorm and fused residual RMSNorm: pure relative error (rel_err), as for
 softmax.  y = v * inv_rms * w is a product with no cancellation, and
@@ -65,6 +67,19 @@ def rel_err_floor1(y, ref, floor: float = 1.0) -> float:
     if not np.all(np.isfinite(y)):
         return float("inf")
     return float((np.abs(y - ref) / np.maximum(np.abs(ref), floor)).max())
+
+
+def rel_err_above(y, ref, threshold: float) -> float:
+    """max |y - r| / |r| over the elements with |r| >= threshold (0 if none)."""
+    y, ref = _arr(y), _arr(ref)
+    if y.shape != ref.shape:
+        raise ValueError(f"shape {y.shape} != {ref.shape}")
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    sel = np.abs(ref) >= threshold
+    if not np.any(sel):
+        return 0.0
+    return float(np.max(np.abs(y[sel] - ref[sel]) / np.abs(ref[sel])))
 
 
 def rel_err(y, ref) -> float:
