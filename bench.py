@@ -315,7 +315,7 @@ def event_time(torch, case, K, W, reps=3, spread=None):
 
 def wall_time(torch, case, K, W, graph):
     """Headline protocol: W untimed steps, then exactly K steps bracketed by
-    device synchronizations; returns (wall seconds, event seconds) for K.
+    device synchronizations; returns the wall seconds of the K steps.
     With `graph`, the K steps (each on its own rotation set) are captured
     into one HIP graph after the warmup, and the timed region is one replay
     of it."""
@@ -337,19 +337,15 @@ def wall_time(torch, case, K, W, graph):
         if hip.hipGraphUpload(g.raw_cuda_graph_exec(), torch.cuda.current_stream().cuda_stream):
             log("hipGraphUpload failed: the timed replay includes the upload")
         torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    s.record()
     if g is not None:
         g.replay()
     else:
         for i in range(K):
             case.launch(W + i)
-    e.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return t1 - t0, s.elapsed_time(e) * 1e-3
+    return t1 - t0
 
 
 def head_kernel_name(rk, N):
@@ -521,9 +517,9 @@ def main():
         c.setup(torch, rk, rowgen)
         spread = {}
         if c.name == HEADLINE:
-            wall, evt = wall_time(torch, c, K, W, args.launch == "graph")
+            wall = wall_time(torch, c, K, W, args.launch == "graph")
             t_evt = event_time(torch, c, K, W)
-            head = (c, wall, evt, t_evt)
+            head = (c, wall, t_evt)
             t = t_evt
         else:
             t = event_time(torch, c, K, W, spread=spread)
@@ -557,7 +553,7 @@ def main():
         print(json.dumps({"detail": detail}))
         return
 
-    c, wall, evt, t_evt = head
+    c, wall, t_evt = head
     value = c.bytes * K / wall / 1e9
     live = c.bytes / t_evt / 1e9
     # device time per dispatch from the committed trace of this command (the

@@ -179,12 +179,12 @@ static const TileVariant kSoftmaxF32[] = {
     tile<float, 1, 1, 4>(),    // N <= 256
     tile<float, 1, 2, 4>(),    // N <= 512
     tile<float, 1, 3, 4>(),    // N <= 768
-    tile<float, 2, 2, 4>(),    // N <= 1024
+    tile<float, 1, 4, 4>(),    // N <= 1024 (8192 x 1000: 12.91 us vs 13.14 for 2 x 2, trace)
     tile<float, 1, 8, 4>(),    // N <= 2048
     tile<float, 4, 4, 4>(),    // N <= 4096
     tile<float, 8, 4, 8>(),    // N <= 8192
     tile<float, 16, 4, 16>(),  // N <= 16384
-    alt(tile<float, 1, 4, 4>()),
+    alt(tile<float, 2, 2, 4>()),
     alt(tile<float, 4, 1, 4>()),
     alt(tile<float, 2, 8, 4>()),
     alt(exact<float, 1, 4, 4>()),
