@@ -120,6 +120,14 @@ class Oracle:
         self.lib.oracle_softmax_stats(_p(r), r.size, ctypes.byref(m), ctypes.byref(d))
         return m.value, d.value
 
+    def softmax_apply(self, values, m: float, d: float) -> np.ndarray:
+        """exp(x - m) / d for the given values of a row whose statistics are
+        (m, d): the output pass of the softmax, for sampled columns."""
+        v = _f64(values).ravel()
+        y = np.empty_like(v)
+        self.lib.oracle_softmax_apply(_p(v), _p(y), v.size, float(m), float(d))
+        return y
+
     def online_stats(self, row, block: int):
         """Streaming (m, d) of one row over blocks of ``block`` elements."""
         r = _f64(row).ravel()
@@ -345,7 +353,7 @@ def _forward(name):
     return f
 
 
-for _n in ["softmax", "softmax_stats", "online_stats", "merge", "split_stats", "online_softmax",
+for _n in ["softmax", "softmax_stats", "softmax_apply", "online_stats", "merge", "split_stats", "online_softmax",
            "split_softmax", "gelu_tanh", "layernorm_stats", "layernorm_normalize",
            "layernorm_gelu", "rms_stats", "rmsnorm", "residual_rmsnorm", "gelu_erf",
            "chunk_moments", "chan_merge", "split_moments", "layernorm_gelu_ex", "row_sum",

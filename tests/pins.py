@@ -217,6 +217,18 @@ def check_online_and_split_outputs(orc):
         assert _rel(orc.split_softmax(x, S), y0) <= 1e-13, S
 
 
+def check_softmax_apply(orc):
+    # the output pass with a row's own statistics gives that row's softmax at
+    # any subset of its columns (torch.softmax in float64)
+    import torch
+
+    x = 5.0 * _rng(43).standard_normal(3001)
+    m, d = orc.softmax_stats(x)
+    cols = np.array([0, 7, 1500, 2999, 3000])
+    ref = torch.softmax(torch.from_numpy(x), dim=0).numpy()[cols]
+    assert _rel(orc.softmax_apply(x[cols], m, d), ref) <= 1e-13
+
+
 def check_neg_inf_parts(orc):
     # A value of -inf adds exp(-inf - m) = 0 to the sum of any part with a
     # finite max m, so a row's (max, sum) are those of its finite values
@@ -749,6 +761,7 @@ PINS = [
     check_split_stats_match_definition,
     check_online_and_split_outputs,
     check_neg_inf_parts,
+    check_softmax_apply,
     check_gelu_basic,
     check_gelu_torch,
     check_gelu_not_erf,

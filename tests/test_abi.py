@@ -77,6 +77,15 @@ def test_rows_beyond_2_30_unsupported(lib):
     assert sm(lib, M=1, N=n) == UNSUPPORTED
 
 
+def test_tallest_grid_refused_before_launch(lib):
+    # 2^26 rows of 8 on a one-wave-per-row tile need 2^32 work-items: refused
+    # before any HIP call (2^26 - 4 rows, the largest accepted, run on the GPU)
+    X = 0x10000000
+    assert lib.rk_softmax(X, X, 1 << 26, 8, 8, 8, F32, None) == UNSUPPORTED
+    assert lib.rk_layernorm_gelu(X, 0x100000, 0x200000, X, 1 << 26, 8, 8, 8, 1e-5, F32,
+                                 None) == UNSUPPORTED
+
+
 def test_m_zero_is_a_noop(lib):
     assert sm(lib, x=None, y=None, M=0) == 0
     assert lib.rk_online_softmax(None, None, 0, 8, 8, 8, F32, 64, None, 0, None) == 0

@@ -65,6 +65,7 @@ MUTANTS = {
     "flash_l_not_rescaled": ("l[r] = alpha * l[r] + psum;", "l[r] = l[r] + psum;"),
     "flash_causal_strict": ("sblk[t] = (causal && j > i) ? -INFINITY", "sblk[t] = (causal && j >= i && j > 0) ? -INFINITY"),
     "flash_alpha_inverted": ("double alpha = m[r] == -INFINITY ? 0.0 : exp(m[r] - m_new);", "double alpha = m[r] == -INFINITY ? 0.0 : exp(m_new - m[r]);"),
+    "apply_without_max": ("y[j] = exp(x[j] - m) / d;", "y[j] = exp(x[j]) / d;"),
     "attn_rows_position_ignored": ("int64_t n = causal ? pos[r] + 1 : T;", "int64_t n = causal ? r + 1 : T;"),
     "attn_rows_query_row": ("dot += q[r * d + c] * k[j * d + c];", "dot += q[c] * k[j * d + c];"),
     "split_moments_chunk_floor": ("    int64_t C = (N + S - 1) / S;\n    double n = 0.0", "    int64_t C = N / S;\n    if (C < 1)\n        C = 1;\n    double n = 0.0"),
