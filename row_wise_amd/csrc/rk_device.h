@@ -72,21 +72,50 @@ struct SumOp {
     __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
 };
 
+// op over aligned groups of L lanes (L = 4, 8 or 16), the result in every
+// lane of the group.  Each step combines a lane with its mirror in the next
+// larger group with a commutative op, so every lane of a group ends with the
+// same bits.  Must be called with every lane of the wave active.
+template <int L, class Op>
+__device__ __forceinline__ float group_reduce(float v, Op op)
+{
+    static_assert(L == 4 || L == 8 || L == 16, "4, 8 or 16 lanes");
+    v = op(v, dpp<kQuadSwap1>(v));
+    v = op(v, dpp<kQuadSwap2>(v));
+    if constexpr (L >= 8)
+        v = op(v, dpp<kHalfMirror>(v));
+    if constexpr (L >= 16)
+        v = op(v, dpp<kRowMirror>(v));
+    return v;
+}
+
 // All-lanes reduction of one float over the 64 lanes of a wave.  Must be
 // called with every lane of the wave active.
 template <class Op>
 __device__ __forceinline__ float wave_reduce(float v, Op op)
 {
-    v = op(v, dpp<kQuadSwap1>(v));
-    v = op(v, dpp<kQuadSwap2>(v));
-    v = op(v, dpp<kHalfMirror>(v));
-    v = op(v, dpp<kRowMirror>(v));
+    v = group_reduce<16>(v, op);
     // each 16-lane row r now holds its value R_r in all lanes
     v = combine_halves(v, op);
     // lanes 0..15 hold op(R0, R2), lanes 16..31 op(R1, R3): combine lanes 0
     // and 16 as uniform (scalar) values
     float a = lane_value(v, 0), b = lane_value(v, 16);
     return op(a, b);
+}
+
+// s_waitcnt vmcnt(0): every vector memory load and store of this wave has
+// completed (expcnt and lgkmcnt at their maxima: no wait on them).  vmcnt
+// counts loads and stores together, and a row's stores issued while the next
+// row's loads are in flight make the next row's first use wait for those
+// stores as well; waiting for the loads just before the stores instead (they
+// have usually arrived by then) leaves nothing older than the stores to wait
+// for.
+// The scheduling barrier keeps the work above it (a row's epilogue) above the
+// wait, so that the loads have that long to arrive.
+__device__ __forceinline__ void wait_vmem()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, MaxOp()); }

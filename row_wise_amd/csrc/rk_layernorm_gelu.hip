@@ -16,6 +16,8 @@
 //                      round (SH below).
 // Rows beyond the register capacity, or not 16-byte aligned, go to the
 // streaming and split-row kernels of rk_layernorm_long.hip.
+#include <atomic>
+
 #include "rk_device.h"
 #include "rk_internal.h"
 
@@ -32,7 +34,9 @@ namespace rk {
 // d = x - K with K the row's first element: mean = K + sum d / N and
 // var = sum d^2 / N - (sum d / N)^2, so both reductions share one barrier.
 template <typename T, int G, int V, int W, int R, bool EXACT, int GK, bool PH, bool SH = false>
-__global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
+__global__ __launch_bounds__(W *kWave)
+__attribute__((amdgpu_waves_per_eu(SH && G == 4 && V == 2 && R == 2 ? 7 : 1)))
+void layernorm_gelu_tile(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
     T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
 {
@@ -46,6 +50,9 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     // while another still reads this row's partials
     __shared__ float red_sum[2][RG][G];
     __shared__ float red_var[2][RG][G];
+    // SH: the (sum, sum of squares) of every 16-lane row of the group's waves
+    constexpr int P = 4 * G;
+    __shared__ f32x2_t red_sq[2][RG][SH && G <= 8 ? P : 1];
 
     // wave-uniform: row bases stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
@@ -130,6 +137,7 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
         // z = fma(fma(v, rstd, cen), w, b) once the statistics are known
         float rstd, cen = 0.0f;
         if constexpr (SH) {
+            // the sums start from the first element (no add to a zero)
             float s = 0.0f, q = 0.0f;
 #pragma unroll
             for (int k = 0; k < V; ++k)
@@ -137,23 +145,44 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
                 for (int e = 0; e < E; ++e) {
                     const float d = v[k][e] - K;
                     v[k][e] = d;
-                    s += d;
-                    q = fmaf(d, d, q);
+                    s = k == 0 && e == 0 ? d : s + d;
+                    q = k == 0 && e == 0 ? d * d : fmaf(d, d, q);
                 }
-            s = wave_sum(s);
-            q = wave_sum(q);
-            if constexpr (G > 1) {
-                if (threadIdx.x % kWave == 0) {
-                    red_sum[buf][grp][wig] = s;
-                    red_var[buf][grp][wig] = q;
-                }
+            if constexpr (G > 1 && G <= 8) {
+                // Sum each 16-lane row, publish the 4 G row sums, and let
+                // every 16-lane row of the group add all of them in the same
+                // order: no cross-row step within the wave, one LDS round
+                // (16 waves: 64 partials, slower than the wave sums below).
+                const int lane = static_cast<int>(threadIdx.x % kWave);
+                s = group_reduce<16>(s, SumOp());
+                q = group_reduce<16>(q, SumOp());
+                if (lane % 16 == 0)
+                    red_sq[buf][grp][4 * wig + lane / 16] = f32x2_t{s, q};
                 __syncthreads();
-                s = red_sum[buf][grp][0];
-                q = red_var[buf][grp][0];
+                const f32x2_t *part = red_sq[buf][grp];
+                constexpr int PL = P < 16 ? P : 16;  // lanes that share the partials
+                f32x2_t t = part[lane % PL];
 #pragma unroll
-                for (int g = 1; g < G; ++g) {
-                    s += red_sum[buf][grp][g];
-                    q += red_var[buf][grp][g];
+                for (int j = 1; j < P / 16; ++j)
+                    t += part[lane % 16 + 16 * j];
+                s = group_reduce<PL>(t[0], SumOp());
+                q = group_reduce<PL>(t[1], SumOp());
+            } else {
+                s = wave_sum(s);
+                q = wave_sum(q);
+                if constexpr (G > 1) {
+                    if (threadIdx.x % kWave == 0) {
+                        red_sum[buf][grp][wig] = s;
+                        red_var[buf][grp][wig] = q;
+                    }
+                    __syncthreads();
+                    s = red_sum[buf][grp][0];
+                    q = red_var[buf][grp][0];
+#pragma unroll
+                    for (int g = 1; g < G; ++g) {
+                        s += red_sum[buf][grp][g];
+                        q += red_var[buf][grp][g];
+                    }
                 }
             }
             const float mean_k = s * inv_n;
@@ -254,6 +283,154 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_tile(
     }
 }
 
+// The exact one-pass (SH) tile as a persistent grid: as many workgroups as
+// are resident at once, each taking rows blockIdx.x, blockIdx.x + gridDim.x,
+// ... in a loop with the next row's loads in flight.  Weight and bias are
+// loaded and unpacked once per workgroup, and the grid ends in one round
+// instead of a partly filled last one.  One row per workgroup (G = W): every
+// row the loop visits exists, so the loads and stores need no branch, and the
+// compiler can count the loads in flight exactly (a branch around them makes
+// it wait for all of them, the next row's included).
+template <typename T, int G, int V, int W, int GK>
+__global__ __launch_bounds__(W *kWave) void layernorm_gelu_rows(
+    const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
+    T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
+{
+    constexpr int E = Elem<T>::kVec;
+    constexpr int L = G * kWave;
+    constexpr int P = 4 * G;  // 16-lane partial sums per row
+    constexpr int PL = P < 16 ? P : 16;
+    static_assert(W == G && G > 1, "one row of several waves per workgroup");
+    // two buffers: a wave may publish the next row's partials while another
+    // still reads this row's
+    __shared__ f32x2_t red_sq[2][P];
+
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+    __builtin_assume(wave >= 0 && wave < W);  // lane offsets are 32-bit and non-negative
+    const int lane = static_cast<int>(threadIdx.x % kWave);
+    const int li = wave * kWave + lane;
+    const RowSplit<E> rs(N);
+    const int nv = rs.count();
+    const int64_t step = gridDim.x;
+    const int64_t first = blockIdx.x;
+
+    // Two load buffers used in turn (the loop is unrolled by two), so that
+    // no register copy waits on the loads; the shift is carried as its raw
+    // 16 bits and converted where it is used.
+    RowLoad<T, E, V, L> xa, xb;
+    T ka, kb;
+    int64_t row = first;  // < M: the grid has no more workgroups than rows
+    xa.issue(x + row * ldx, li, nv, rs, 0.0f, true);
+    ka = x[row * ldx];
+    float wv[V][E], bv[V][E];
+    {
+        RowLoad<T, E, V, L, kCached> wl, bl;
+        wl.issue(w, li, nv, rs, 0.0f, true);
+        bl.issue(b, li, nv, rs, 0.0f, true);
+        wl.finish(wv, rs);
+        bl.finish(bv, rs);
+    }
+    // the first row is needed at once; with no loads in flight on entry the
+    // loop's own waits count only its loads
+    wait_vmem();
+
+    // One row: finish cur, issue the next row into nxt, normalize, store.
+    auto one_row = [&](RowLoad<T, E, V, L> &cur, const T &kc, RowLoad<T, E, V, L> &nxt, T &kn,
+                       int buf) {
+        float v[V][E];
+        cur.finish(v, rs);
+        const float K = Elem<T>::to_f32(kc);
+        // the next row, or after the last one the weight row (L2-resident,
+        // never used): an unconditional load keeps the counts exact
+        const int64_t nrow = row + step;
+        const T *src = nrow < M ? x + nrow * ldx : w;
+        nxt.issue(src, li, nv, rs, 0.0f, true);
+        kn = src[0];
+
+        float s = 0.0f, q = 0.0f;
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float d = v[k][e] - K;
+                v[k][e] = d;
+                s = k == 0 && e == 0 ? d : s + d;
+                q = k == 0 && e == 0 ? d * d : fmaf(d, d, q);
+            }
+        s = group_reduce<16>(s, SumOp());
+        q = group_reduce<16>(q, SumOp());
+        if (lane % 16 == 0)
+            red_sq[buf][4 * wave + lane / 16] = f32x2_t{s, q};
+        __syncthreads();
+        f32x2_t t = red_sq[buf][lane % PL];
+#pragma unroll
+        for (int j = 1; j < P / 16; ++j)
+            t += red_sq[buf][lane % 16 + 16 * j];
+        s = group_reduce<PL>(t[0], SumOp());
+        q = group_reduce<PL>(t[1], SumOp());
+        const float mean_k = s * inv_n;
+        const float var = fmaxf(fmaf(q, inv_n, -mean_k * mean_k), 0.0f);
+        const float rstd = __builtin_amdgcn_rsqf(var + eps);
+        const float cen = -mean_k * rstd;
+
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[k][e] = gelu<GK>(fmaf(fmaf(v[k][e], rstd, cen), wv[k][e], bv[k][e]));
+        wait_vmem();  // the next row's loads (and the previous row's stores)
+        store_row<T, E, V, L>(y + row * ldy, li, nv, rs, v, true);
+        row = nrow;
+    };
+
+    for (;;) {
+        one_row(xa, ka, xb, kb, 0);
+        if (row >= M)
+            break;
+        one_row(xb, kb, xa, ka, 1);
+        if (row >= M)
+            break;
+    }
+}
+
+// Workgroups of the persistent kernel: as many as the device holds at once
+// (per device, from the occupancy calculator), spread so that every
+// workgroup takes the same number of row groups but the last.
+template <typename T, int G, int V, int W>
+static hipError_t layernorm_gelu_rows_run(const RowProblem &p)
+{
+    constexpr int kDevices = 64;
+    static std::atomic<int> resident[2][kDevices];
+    const int gk = p.gelu == RK_GELU_ERF ? 1 : 0;
+    auto kernel = gk ? layernorm_gelu_rows<T, G, V, W, 1> : layernorm_gelu_rows<T, G, V, W, 0>;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    int n = dev < kDevices ? resident[gk][dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
+                                                         W * kWave, 0);
+        if (e != hipSuccess)
+            return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        n = per_cu * cus > 0 ? per_cu * cus : 1;
+        if (dev < kDevices)
+            resident[gk][dev].store(n, std::memory_order_relaxed);
+    }
+    const int64_t groups = p.M;
+    const int64_t iters = (groups + n - 1) / n;
+    const int64_t blocks = iters > 0 ? (groups + iters - 1) / iters : 0;
+    const float inv_n = static_cast<float>(1.0 / p.N);
+    return launch(kernel, dim3(static_cast<unsigned>(blocks)), dim3(W * kWave), p.stream,
+                  static_cast<const T *>(p.x), static_cast<const T *>(p.w),
+                  static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,
+                  inv_n, p.eps);
+}
+
 template <typename T, int G, int V, int W, int R, bool EXACT, bool PH, bool SH = false>
 static hipError_t layernorm_gelu_tile_run(const RowProblem &p)
 {
@@ -297,6 +474,15 @@ constexpr TileVariant exact_shifted()
     return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec, true,
                        &layernorm_gelu_tile_run<T, G, V, W, R, true, false, true>, false,
                        nullptr};
+}
+
+// The persistent form of an exact one-pass tile.  rows_per_group 1: the
+// grid never has more workgroups than a one-row tile's.
+template <typename T, int G, int V, int W>
+constexpr TileVariant exact_rows()
+{
+    return TileVariant{G, V, W, 1, G * V * kWave * Elem<T>::kVec, true,
+                       &layernorm_gelu_rows_run<T, G, V, W>, false, nullptr};
 }
 
 // Preference order as for softmax: first exact entry with max_n == N, else
@@ -344,8 +530,9 @@ static const TileVariant kLayerNormBF16[] = {
     exact_shifted<bf16_t, 1, 2, 4>(),    // N = 1024
     exact_shifted<bf16_t, 1, 4, 4>(),    // N = 2048
     exact_shifted<bf16_t, 4, 2, 4, 2>(), // N = 4096
-    exact_shifted<bf16_t, 8, 2, 8>(),    // N = 8192
-    exact_shifted<bf16_t, 8, 4, 8>(),    // N = 16384 (8 x 4: 49 us vs 55 us for 16 x 2)
+    exact_rows<bf16_t, 8, 2, 8>(),       // N = 8192 (persistent: 47.6 us vs 51.3 us at 8192 rows)
+    exact_rows<bf16_t, 8, 4, 8>(),       // N = 16384 (persistent: 46.4 vs 50.4 us; 8 x 4 tile:
+                                         // 49 us vs 55 us for 16 x 2)
     exact_shifted<bf16_t, 16, 4, 16>(),  // N = 32768
     tile<bf16_t, 1, 1, 4>(),    // N <= 512
     tile<bf16_t, 1, 2, 4>(),    // N <= 1024
@@ -377,6 +564,17 @@ static const TileVariant kLayerNormBF16[] = {
     alt(exact<bf16_t, 8, 4, 8>()),
     alt(exact<bf16_t, 16, 4, 16>()),
     alt(exact_shifted<bf16_t, 2, 4, 4, 2>()),
+    // measured at 16384 x 4096 against the dispatched 4 x 2 x 4, two rows
+    // (47.5 us): one wave per row 51-55 us, two waves 48.0, 8 x 1 48.3,
+    // four rows 47.4; persistent 4 x 2 48.8 (80 VGPRs: six waves per SIMD)
+    alt(exact_shifted<bf16_t, 1, 8, 4>()),
+    alt(exact_shifted<bf16_t, 2, 4, 4>()),
+    alt(exact_shifted<bf16_t, 4, 2, 4, 4>()),
+    alt(exact_rows<bf16_t, 4, 2, 4>()),
+    // the one-pass tiles the persistent form replaced (a persistent 16 x 4
+    // for N = 32768 measured 90.6 us against 60.7 us for the tile)
+    alt(exact_shifted<bf16_t, 8, 2, 8>()),
+    alt(exact_shifted<bf16_t, 8, 4, 8>()),
 };
 
 const TileVariant *layernorm_gelu_variants(rk_dtype dtype, int *count)

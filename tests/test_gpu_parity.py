@@ -256,6 +256,28 @@ def test_layernorm_gelu_bf16_exact_hard_rows(index, N):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("index,N", _exact_bf16_layernorm(), ids=str)
+def test_layernorm_gelu_bf16_exact_many_rows(index, N):
+    """Every exact bf16 tile on an odd number of rows (up to 5001, 2^26
+    elements at most): the persistent forms then loop several times per
+    workgroup, through both halves of their unrolled loop and with the
+    prefetch past the last row.  Sampled rows (the first and last 64 and 128
+    seeded others) within 1e-2 of the oracle; the rest finite."""
+    M = min(5001, (1 << 26) // N) | 1
+    g = torch.Generator().manual_seed(3 * N + index)
+    x = (torch.randn(M, N, generator=g) * 1.5 + 0.25).to(torch.bfloat16)
+    w, b = rowgen.ln_params(N, g, torch.bfloat16)
+    xd = x.to(DEV)
+    y = rk.rk__layernorm_gelu_variant(index, xd, w.to(DEV), b.to(DEV), EPS)
+    assert bool(torch.isfinite(y.float()).all())
+    rows = torch.cat([torch.arange(64), torch.arange(M - 64, M),
+                      torch.randint(64, M - 64, (128,), generator=g)]).unique()
+    ref = oracle.layernorm_gelu(x[rows], w, b, EPS)
+    err = rel_err_floor1(y[rows.to(DEV)], ref)
+    say(f"ln bf16 exact index {index} N={N} M={M} sampled err={err:.2e}")
+    assert err <= TOL["bf16"]
+
+
 def _phased_cases(op):
     """General one-row-per-group tiles on rows at every offset: odd N, so row
     r starts r N elements into an aligned buffer; N + E - 1 fits the tile."""
