@@ -64,8 +64,18 @@ void layernorm_gelu_tile(
     // every vector slot of a row group holds a complete vector of the row
     const bool slots_full = EXACT || V * L <= rs.nfull;
 
+    // kSame (an exact one-pass tile of one row group and two rows): a second
+    // row past M is the first row again.  It is read before the first row's
+    // stores and written twice with the same bytes (in place too), so every
+    // store is unconditional, and the second row's loads can be awaited just
+    // before the first row's stores (wait_vmem) without also waiting for
+    // those stores, which a branch around them would make the compiler do.
+    constexpr bool kSame = EXACT && SH && R == 2 && RG == 1;
     // Row r of this row group.
-    auto row_of = [&](int r) { return (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp; };
+    auto row_of = [&](int r) {
+        const int64_t i = (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp;
+        return kSame && i >= M ? M - 1 : i;
+    };
 
     // Loads in flight before any is waited for: the first row, then weight
     // and bias (shared by all R rows).  Each later row is issued while the
@@ -112,7 +122,7 @@ void layernorm_gelu_tile(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t row = row_of(r);
-        const bool row_ok = row < M;
+        const bool row_ok = kSame || row < M;
         const int64_t rr = row_ok ? row : 0;
         const T *xr = x + rr * ldx;
         T *yr = y + rr * ldy;
@@ -127,7 +137,7 @@ void layernorm_gelu_tile(
         const float K = k_next;
         if (r + 1 < R) {
             const int64_t nrow = row_of(r + 1);
-            const bool nok = nrow < M;
+            const bool nok = kSame || nrow < M;
             xl.issue(x + (nok ? nrow : 0) * ldx, li, nok ? nv : 0, rs, 0.0f,
                      EXACT || (nok && slots_full));
             if constexpr (SH)
@@ -275,6 +285,9 @@ void layernorm_gelu_tile(
         if constexpr (PH) {
             store_span<T, E, V, L>(yr - sp.h, li, jend, sp, v, false);
         } else if (EXACT) {
+            if constexpr (kSame)
+                if (r + 1 < R)
+                    wait_vmem();
             if (row_ok)
                 store_row<T, E, V, L>(yr, li, vend, rs, v, true);
         } else {
