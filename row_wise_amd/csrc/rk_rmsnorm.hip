@@ -78,7 +78,17 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
     const int nv = rs.count();
     const bool slots_full = EXACT || V * L <= rs.nfull;
 
-    auto row_of = [&](int r) { return (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp; };
+    // kSame (an exact tile of one row group and two rows): a second row past
+    // M is the first row again.  Its loads are issued before any store of the
+    // first row, and it writes the same bytes again (in place too), so every
+    // store is unconditional and the second row's loads can be awaited just
+    // before the first row's output stores (wait_vmem) without also waiting
+    // for those stores, which a branch around them would make the compiler do.
+    constexpr bool kSame = EXACT && !PH && R == 2 && RG == 1;
+    auto row_of = [&](int r) {
+        const int64_t i = (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp;
+        return kSame && i >= M ? M - 1 : i;
+    };
 
     RowLoad<T, E, V, L> xl, rl;
     SpanLoad<T, E, V, L> xs, rsl;  // PH
@@ -86,7 +96,7 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
     int jend = 0;
     auto issue_row = [&](int r) {
         const int64_t row = row_of(r);
-        const bool ok = row < M;
+        const bool ok = kSame || row < M;
         const int64_t rr = ok ? row : 0;
         if constexpr (PH) {
             sp.h = row_phase<T, E>(x + rr * ldx);
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t row = row_of(r);
-        const bool row_ok = row < M;
+        const bool row_ok = kSame || row < M;
         const int64_t rr = row_ok ? row : 0;
         const int vend = row_ok ? nv : 0;
         const bool store_full = EXACT || (row_ok && slots_full);
@@ -181,6 +191,9 @@ __global__ __launch_bounds__(W *kWave) void rmsnorm_tile(
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[k][e] = v[k][e] * inv * wv[k][e];
+        if constexpr (kSame)
+            if (r + 1 < R)
+                wait_vmem();
         if constexpr (PH)
             store_span<T, E, V, L>(y + rr * ldy - sp.h, li, jend, sp, v, false);
         else if (!EXACT || row_ok)

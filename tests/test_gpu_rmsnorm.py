@@ -292,8 +292,10 @@ def test_shared_offset(dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=key)
 @pytest.mark.parametrize("N", [768, 4096, 1000, 40000, 3001])
-def test_in_place(dtype, N):
-    M = 64
+@pytest.mark.parametrize("M", [64, 63, 1], ids=str)
+def test_in_place(dtype, N, M):
+    """In place, also on odd M: a two-row tile takes a missing second row as
+    the first row again (read before any store, the same bytes written)."""
     x = rowgen.randn(M, N, seed=N + 7, dtype=dtype)
     res = rowgen.randn(M, N, seed=N + 8, dtype=dtype)
     w = weight(N, N, dtype)
