@@ -452,14 +452,21 @@ def cpu_baseline(seconds):
 
 
 def cpu_model():
-    """The host CPU's model name as lscpu prints it (else /proc/cpuinfo)."""
+    """The host CPU's model name as lscpu prints it (else /proc/cpuinfo), with
+    lscpu's CPU family, model and stepping (a virtualised host may report only
+    a generic name such as "AMD EPYC")."""
     import subprocess
 
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        fields = {}
         for line in out.splitlines():
-            if line.startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields.setdefault(k.strip(), v.strip())
+        if "Model name" in fields:
+            ids = [f"{k.lower()} {fields[k]}" for k in ("CPU family", "Model", "Stepping") if k in fields]
+            return fields["Model name"] + (f" ({', '.join(ids)})" if ids else "")
     except (OSError, subprocess.SubprocessError):
         pass
     try:
