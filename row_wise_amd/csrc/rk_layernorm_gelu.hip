@@ -41,7 +41,7 @@ void layernorm_gelu_tile(
     T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
 {
     static_assert(!PH || (!EXACT && R == 1), "phased rows: general tiles, one row per group");
-    static_assert(!SH || (EXACT && !PH), "one shifted pass: exact tiles");
+    static_assert(!SH || !PH, "one shifted pass: rows at 16-byte boundaries");
     constexpr int E = Elem<T>::kVec;
     constexpr int RG = W / G;
     constexpr int L = G * kWave;
@@ -147,17 +147,22 @@ void layernorm_gelu_tile(
         // z = fma(fma(v, rstd, cen), w, b) once the statistics are known
         float rstd, cen = 0.0f;
         if constexpr (SH) {
-            // the sums start from the first element (no add to a zero)
+            // the sums start from the first element (no add to a zero); a
+            // padded slot of a general tile adds d = 0 to both
             float s = 0.0f, q = 0.0f;
 #pragma unroll
-            for (int k = 0; k < V; ++k)
+            for (int k = 0; k < V; ++k) {
+                const int vi = k * L + li;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float d = v[k][e] - K;
+                    const bool valid =
+                        EXACT || vi < rs.nfull || (vi == rs.nfull && e < rs.tail);
+                    const float d = valid ? v[k][e] - K : 0.0f;
                     v[k][e] = d;
                     s = k == 0 && e == 0 ? d : s + d;
                     q = k == 0 && e == 0 ? d * d : fmaf(d, d, q);
                 }
+            }
             if constexpr (G > 1 && G <= 8) {
                 // Sum each 16-lane row, publish the 4 G row sums, and let
                 // every 16-lane row of the group add all of them in the same
@@ -489,6 +494,16 @@ constexpr TileVariant exact_shifted()
                        nullptr};
 }
 
+// A general tile with the one shifted pass; its phased form (rows at any
+// offset) keeps the two passes.
+template <typename T, int G, int V, int W, int R = 1>
+constexpr TileVariant tile_shifted()
+{
+    return TileVariant{G, V, W, R, G * V * kWave * Elem<T>::kVec, false,
+                       &layernorm_gelu_tile_run<T, G, V, W, R, false, false, true>, false,
+                       phased_run<T, G, V, W, R, false>()};
+}
+
 // The persistent form of an exact one-pass tile.  rows_per_group 1: the
 // grid never has more workgroups than a one-row tile's.
 template <typename T, int G, int V, int W>
@@ -547,15 +562,27 @@ static const TileVariant kLayerNormBF16[] = {
     exact_rows<bf16_t, 8, 4, 8>(),       // N = 16384 (persistent: 46.4 vs 50.4 us; 8 x 4 tile:
                                          // 49 us vs 55 us for 16 x 2)
     exact_shifted<bf16_t, 16, 4, 16>(),  // N = 32768
-    tile<bf16_t, 1, 1, 4>(),    // N <= 512
-    tile<bf16_t, 1, 2, 4>(),    // N <= 1024
-    tile<bf16_t, 1, 4, 4>(),    // N <= 2048
-    tile<bf16_t, 4, 2, 4>(),    // N <= 4096 (N = 3000: 59 us vs 65 us for 2 x 4)
-    tile<bf16_t, 4, 3, 4>(),    // N <= 6144
-    tile<bf16_t, 8, 2, 8>(),    // N <= 8192
-    tile<bf16_t, 8, 3, 8>(),    // N <= 12288
-    tile<bf16_t, 8, 4, 8>(),    // N <= 16384 (N = 14000: 60 us vs 87 us for 16 x 2)
-    tile<bf16_t, 8, 5, 8>(),    // N <= 20480
+    // General tiles: the one shifted pass where it measured faster (128 MiB,
+    // one process, alternating with the two-pass build): N = 7168 53.0 vs
+    // 59.4 us, 12288 53.5 vs 55.8, 3000 55.2 vs 57.6, 3072 55.5 vs 56.2.  The
+    // others keep two passes: there its registers cost a wave of occupancy
+    // (N = 1000: 53.2 vs 47.9 us; 1536 57.2 vs 55.9; 6144 53.9 vs 52.1;
+    // 5120 and 14336 the same).
+    tile<bf16_t, 1, 1, 4>(),            // N <= 512
+    tile<bf16_t, 1, 2, 4>(),            // N <= 1024
+    tile<bf16_t, 1, 4, 4>(),            // N <= 2048
+    tile_shifted<bf16_t, 4, 2, 4>(),    // N <= 4096 (N = 3000: 59 us vs 65 us for 2 x 4)
+    tile<bf16_t, 4, 3, 4>(),            // N <= 6144
+    tile_shifted<bf16_t, 8, 2, 8>(),    // N <= 8192
+    tile_shifted<bf16_t, 8, 3, 8>(),    // N <= 12288
+    tile<bf16_t, 8, 4, 8>(),            // N <= 16384 (N = 14000: 60 us vs 87 us for 16 x 2)
+    tile<bf16_t, 8, 5, 8>(),            // N <= 20480
+    // the other form of the dispatched general tiles
+    alt(tile_shifted<bf16_t, 1, 2, 4>()),
+    alt(tile_shifted<bf16_t, 4, 3, 4>()),
+    alt(tile<bf16_t, 4, 2, 4>()),
+    alt(tile<bf16_t, 8, 2, 8>()),
+    alt(tile<bf16_t, 8, 3, 8>()),
     alt(tile<bf16_t, 2, 4, 4>()),
     alt(tile<bf16_t, 16, 2, 16>()),
     alt(tile<bf16_t, 16, 4, 16>()),

@@ -256,6 +256,41 @@ def test_layernorm_gelu_bf16_exact_hard_rows(index, N):
     assert err <= TOL["bf16"]
 
 
+def _general_bf16_layernorm():
+    cases = []
+    for v in rk.variants(rk.RK_OP_LAYERNORM_GELU, rk.RK_BF16):
+        if v["exact"] or v["max_n"] > 32768:
+            continue
+        for N in sorted({v["max_n"] - 37, v["max_n"] // 2 + 3}):
+            cases.append((v["index"], N))
+    return cases
+
+
+@pytest.mark.parametrize("index,N", _general_bf16_layernorm(), ids=str)
+def test_layernorm_gelu_bf16_general_hard_rows(index, N):
+    """The general bf16 tiles (one shifted pass or two passes, padded slots
+    excluded) on ragged widths with the adversarial rows of the exact test;
+    within 1e-2 of the oracle."""
+    g = torch.Generator().manual_seed(N + 11 * index)
+    x = torch.randn(9, N, generator=g)
+    x[0, 0] = 40.0
+    x[1, 0] = -300.0
+    x[2] += 100.0
+    x[3] = 1.25
+    x[4] = torch.where(torch.arange(N) % 2 == 0, 3.0, -1.0)
+    x[5] = 0.0
+    x[5, N // 2] = 1000.0
+    x[6] *= 1e-3
+    x[7] = x[7] * 50.0 + 2000.0
+    x = x.to(torch.bfloat16)
+    w, b = rowgen.ln_params(N, g, torch.bfloat16)
+    y = rk.rk__layernorm_gelu_variant(index, x.to(DEV), w.to(DEV), b.to(DEV), EPS)
+    ref = oracle.layernorm_gelu(x, w, b, EPS)
+    err = rel_err_floor1(y, ref)
+    say(f"ln bf16 general index {index} N={N} hard rows err={err:.2e}")
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("index,N", _exact_bf16_layernorm(), ids=str)
 def test_layernorm_gelu_bf16_exact_many_rows(index, N):
     """Every exact bf16 tile on an odd number of rows (up to 5001, 2^26
