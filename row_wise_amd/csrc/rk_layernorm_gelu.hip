@@ -35,7 +35,7 @@ namespace rk {
 // var = sum d^2 / N - (sum d / N)^2, so both reductions share one barrier.
 template <typename T, int G, int V, int W, int R, bool EXACT, int GK, bool PH, bool SH = false>
 __global__ __launch_bounds__(W *kWave)
-__attribute__((amdgpu_waves_per_eu(SH && G == 4 && V == 2 && R == 2 ? 7 : 1)))
+__attribute__((amdgpu_waves_per_eu(SH && EXACT && G == 4 && V == 2 && R == 2 ? 7 : 1)))
 void layernorm_gelu_tile(
     const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
     T *__restrict__ y, int64_t M, int N, int64_t ldx, int64_t ldy, float inv_n, float eps)
@@ -64,13 +64,13 @@ void layernorm_gelu_tile(
     // every vector slot of a row group holds a complete vector of the row
     const bool slots_full = EXACT || V * L <= rs.nfull;
 
-    // kSame (an exact one-pass tile of one row group and two rows): a second
+    // kSame (a one-pass tile of one row group and two rows): a second
     // row past M is the first row again.  It is read before the first row's
     // stores and written twice with the same bytes (in place too), so every
     // store is unconditional, and the second row's loads can be awaited just
     // before the first row's stores (wait_vmem) without also waiting for
     // those stores, which a branch around them would make the compiler do.
-    constexpr bool kSame = EXACT && SH && R == 2 && RG == 1;
+    constexpr bool kSame = SH && !PH && R == 2 && RG == 1;
     // Row r of this row group.
     auto row_of = [&](int r) {
         const int64_t i = (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp;
@@ -296,6 +296,9 @@ void layernorm_gelu_tile(
             if (row_ok)
                 store_row<T, E, V, L>(yr, li, vend, rs, v, true);
         } else {
+            if constexpr (kSame)
+                if (r + 1 < R)
+                    wait_vmem();
             store_row<T, E, V, L>(yr, li, vend, rs, v, row_ok && slots_full);
         }
     }
@@ -562,6 +565,19 @@ static const TileVariant kLayerNormBF16[] = {
     exact_rows<bf16_t, 8, 4, 8>(),       // N = 16384 (persistent: 46.4 vs 50.4 us; 8 x 4 tile:
                                          // 49 us vs 55 us for 16 x 2)
     exact_shifted<bf16_t, 16, 4, 16>(),  // N = 32768
+    // Common hidden sizes between the powers of two, 128 MiB of input, µs
+    // against the general tile that would take them (two passes or one,
+    // masked): 1536 46.6 vs 60.5; 2560 49.0 vs 66.8; 3072 46.8 vs 57.5;
+    // 5120 49.2 vs 54.6; 6144 47.3 vs 54.4; 7168 47.1 vs 56.2; 12288 47.9
+    // vs 55.3; 14336 48.3 vs 59.8.
+    exact_shifted<bf16_t, 1, 3, 4>(),    // N = 1536
+    exact_shifted<bf16_t, 1, 5, 4>(),    // N = 2560
+    exact_shifted<bf16_t, 2, 3, 2, 2>(), // N = 3072
+    exact_rows<bf16_t, 2, 5, 2>(),       // N = 5120
+    exact_shifted<bf16_t, 4, 3, 4, 2>(), // N = 6144
+    exact_rows<bf16_t, 2, 7, 2>(),       // N = 7168
+    exact_rows<bf16_t, 8, 3, 8>(),       // N = 12288
+    exact_rows<bf16_t, 4, 7, 4>(),       // N = 14336
     // General tiles: the one shifted pass where it measured faster (128 MiB,
     // one process, alternating with the two-pass build): N = 7168 53.0 vs
     // 59.4 us, 12288 53.5 vs 55.8, 3000 55.2 vs 57.6, 3072 55.5 vs 56.2.  The
@@ -578,6 +594,11 @@ static const TileVariant kLayerNormBF16[] = {
     tile<bf16_t, 8, 4, 8>(),            // N <= 16384 (N = 14000: 60 us vs 87 us for 16 x 2)
     tile<bf16_t, 8, 5, 8>(),            // N <= 20480
     // the other form of the dispatched general tiles
+    alt(tile_shifted<bf16_t, 4, 2, 4, 2>()),
+    alt(tile_shifted<bf16_t, 4, 3, 4, 2>()),
+    alt(tile_shifted<bf16_t, 8, 2, 8, 2>()),
+    alt(tile_shifted<bf16_t, 8, 3, 8, 2>()),
+    alt(tile_shifted<bf16_t, 8, 4, 8, 2>()),
     alt(tile_shifted<bf16_t, 1, 2, 4>()),
     alt(tile_shifted<bf16_t, 4, 3, 4>()),
     alt(tile<bf16_t, 4, 2, 4>()),
@@ -611,6 +632,13 @@ static const TileVariant kLayerNormBF16[] = {
     alt(exact_shifted<bf16_t, 2, 4, 4>()),
     alt(exact_shifted<bf16_t, 4, 2, 4, 4>()),
     alt(exact_rows<bf16_t, 4, 2, 4>()),
+    // the runners-up at the common hidden sizes (above)
+    alt(exact_rows<bf16_t, 2, 3, 2>()),        // 3072: 48.3 us
+    alt(exact_shifted<bf16_t, 2, 5, 2, 2>()),  // 5120: 50.2 us
+    alt(exact_rows<bf16_t, 4, 3, 4>()),        // 6144: 48.3 us
+    alt(exact_shifted<bf16_t, 2, 7, 2, 2>()),  // 7168: 52.7 us
+    alt(exact_shifted<bf16_t, 8, 3, 8, 2>()),  // 12288: 51.4 us
+    alt(exact_shifted<bf16_t, 4, 7, 4>()),     // 14336: 52.2 us
     // the one-pass tiles the persistent form replaced (a persistent 16 x 4
     // for N = 32768 measured 90.6 us against 60.7 us for the tile)
     alt(exact_shifted<bf16_t, 8, 2, 8>()),

@@ -257,11 +257,17 @@ def test_layernorm_gelu_bf16_exact_hard_rows(index, N):
 
 
 def _general_bf16_layernorm():
+    """Ragged widths for every general bf16 tile: two multiples of 8 (rows on
+    16-byte boundaries: the tile itself, one shifted pass or two) and, for a
+    one-row tile, an odd width (rows at every offset: its phased form)."""
     cases = []
     for v in rk.variants(rk.RK_OP_LAYERNORM_GELU, rk.RK_BF16):
         if v["exact"] or v["max_n"] > 32768:
             continue
-        for N in sorted({v["max_n"] - 37, v["max_n"] // 2 + 3}):
+        widths = {v["max_n"] - 40, v["max_n"] // 2 + 8}
+        if v["rows_per_group"] == 1:
+            widths.add(v["max_n"] - 37)
+        for N in sorted(widths):
             cases.append((v["index"], N))
     return cases
 
@@ -269,8 +275,9 @@ def _general_bf16_layernorm():
 @pytest.mark.parametrize("index,N", _general_bf16_layernorm(), ids=str)
 def test_layernorm_gelu_bf16_general_hard_rows(index, N):
     """The general bf16 tiles (one shifted pass or two passes, padded slots
-    excluded) on ragged widths with the adversarial rows of the exact test;
-    within 1e-2 of the oracle."""
+    excluded) on ragged widths with the adversarial rows of the exact test,
+    on 9 rows (a two-row tile's last row repeated); within 1e-2 of the
+    oracle."""
     g = torch.Generator().manual_seed(N + 11 * index)
     x = torch.randn(9, N, generator=g)
     x[0, 0] = 40.0
@@ -571,7 +578,7 @@ def test_layernorm_gelu_bf16_exact_in_place_odd_rows(M):
     before any store, written twice with the same bytes), the persistent
     tiles prefetch past the last row.  Every row within 1e-2 of the oracle
     and equal, bit for bit, to the out-of-place call."""
-    for N in (4096, 8192, 16384):
+    for N in (3072, 4096, 5120, 6144, 8192, 16384):
         g = torch.Generator().manual_seed(M * 31 + N)
         x = (torch.randn(M, N, generator=g) + 0.5).to(torch.bfloat16)
         w, b = rowgen.ln_params(N, g, torch.bfloat16)
