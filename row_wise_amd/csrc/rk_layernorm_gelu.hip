@@ -64,13 +64,13 @@ void layernorm_gelu_tile(
     // every vector slot of a row group holds a complete vector of the row
     const bool slots_full = EXACT || V * L <= rs.nfull;
 
-    // kSame (a one-pass tile of one row group and two rows): a second
+    // kSame (a tile of one row group and two rows): a second
     // row past M is the first row again.  It is read before the first row's
     // stores and written twice with the same bytes (in place too), so every
     // store is unconditional, and the second row's loads can be awaited just
     // before the first row's stores (wait_vmem) without also waiting for
     // those stores, which a branch around them would make the compiler do.
-    constexpr bool kSame = SH && !PH && R == 2 && RG == 1;
+    constexpr bool kSame = !PH && R == 2 && RG == 1;
     // Row r of this row group.
     auto row_of = [&](int r) {
         const int64_t i = (static_cast<int64_t>(blockIdx.x) * R + r) * RG + grp;
@@ -530,9 +530,21 @@ static const TileVariant kLayerNormF32[] = {
     exact<float, 1, 3, 4>(),    // N = 768
     exact<float, 1, 4, 4>(),    // N = 1024
     exact<float, 1, 8, 4>(),    // N = 2048
-    exact<float, 4, 4, 4>(),    // N = 4096
-    exact<float, 4, 8, 4>(),    // N = 8192 (measured 48 us vs 50 us for 8 x 4 at 128 MiB)
+    exact<float, 4, 4, 4, 2>(), // N = 4096 (two rows: 47.1 us vs 51.5 for one, 64 MiB)
+    exact<float, 8, 4, 8, 2>(), // N = 8192 (two rows: 47.6 us vs 50.0 for 4 x 8, one row)
     exact<float, 8, 8, 8>(),    // N = 16384 (48 us vs 54 us for 16 x 4)
+    // Common hidden sizes between the powers of two, 64 MiB of input, µs
+    // against the general tile that would take them: 1536 46.9 vs 48.1;
+    // 2560 48.0 vs 50.1; 3072 47.4 vs 50.5; 5120 48.0 vs 51.2; 6144 47.7 vs
+    // 51.0; 12288 51.3 vs 55.2; 14336 51.1 vs 56.1 (7168: no gain).  Two rows
+    // per group take a missing last row as the first row again.
+    exact<float, 2, 3, 2, 2>(), // N = 1536
+    exact<float, 2, 5, 2, 2>(), // N = 2560
+    exact<float, 4, 3, 4, 2>(), // N = 3072
+    exact<float, 4, 5, 4, 2>(), // N = 5120
+    exact<float, 8, 3, 8, 2>(), // N = 6144
+    exact<float, 8, 6, 8>(),    // N = 12288
+    exact<float, 8, 7, 8>(),    // N = 14336
     tile<float, 1, 1, 4>(),     // N <= 256
     tile<float, 1, 2, 4>(),     // N <= 512
     tile<float, 1, 3, 4>(),     // N <= 768
@@ -551,6 +563,9 @@ static const TileVariant kLayerNormF32[] = {
     alt(exact<float, 8, 4, 8>()),
     alt(exact<float, 16, 4, 16>()),
     alt(exact_shifted<float, 1, 3, 4>()),  // 3x the error of two passes, no faster
+    // the one-row exact tiles the two-row ones replaced
+    alt(exact<float, 4, 4, 4>()),
+    alt(exact<float, 4, 8, 4>()),
 };
 
 // bf16 exact tiles take the one shifted pass (SH): bf16 storage rounding
@@ -558,7 +573,7 @@ static const TileVariant kLayerNormF32[] = {
 // two measured 48.5 -> 47.0 us at 16384 x 4096 (kernel trace average).
 static const TileVariant kLayerNormBF16[] = {
     exact_shifted<bf16_t, 1, 1, 4>(),    // N = 512
-    exact_shifted<bf16_t, 1, 2, 4>(),    // N = 1024
+    exact_shifted<bf16_t, 2, 1, 2, 2>(), // N = 1024 (43.7 us vs 45.7 for one wave per row)
     exact_shifted<bf16_t, 1, 4, 4>(),    // N = 2048
     exact_shifted<bf16_t, 4, 2, 4, 2>(), // N = 4096
     exact_rows<bf16_t, 8, 2, 8>(),       // N = 8192 (persistent: 47.6 us vs 51.3 us at 8192 rows)
@@ -632,6 +647,7 @@ static const TileVariant kLayerNormBF16[] = {
     alt(exact_shifted<bf16_t, 2, 4, 4>()),
     alt(exact_shifted<bf16_t, 4, 2, 4, 4>()),
     alt(exact_rows<bf16_t, 4, 2, 4>()),
+    alt(exact_shifted<bf16_t, 1, 2, 4>()),     // N = 1024: 45.7 us
     // the runners-up at the common hidden sizes (above)
     alt(exact_rows<bf16_t, 2, 3, 2>()),        // 3072: 48.3 us
     alt(exact_shifted<bf16_t, 2, 5, 2, 2>()),  // 5120: 50.2 us

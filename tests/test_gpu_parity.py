@@ -593,6 +593,48 @@ def test_layernorm_gelu_bf16_exact_in_place_odd_rows(M):
         assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("M", [1, 3, 257, 4097], ids=str)
+def test_layernorm_gelu_f32_exact_in_place_odd_rows(M):
+    """The dispatched exact fp32 tiles of two rows per group (two passes) in
+    place on an odd number of rows: a missing second row is the first row
+    again.  Every row within 1e-5 of the oracle and equal, bit for bit, to the
+    out-of-place call."""
+    for N in (1536, 2560, 3072, 4096, 5120, 6144, 8192):
+        g = torch.Generator().manual_seed(M * 37 + N)
+        x = torch.randn(M, N, generator=g) + 0.5
+        w, b = rowgen.ln_params(N, g, torch.float32)
+        wd, bd = w.to(DEV), b.to(DEV)
+        out = rk.rk_layernorm_gelu(x.to(DEV), wd, bd, EPS)
+        xi = x.to(DEV)
+        rk.rk_layernorm_gelu(xi, wd, bd, EPS, out=xi)
+        assert torch.equal(xi.view(torch.int32), out.view(torch.int32)), N
+        rows = torch.arange(M) if M <= 257 else torch.cat([torch.arange(64), torch.arange(M - 64, M)])
+        err = rel_err_floor1(xi[rows.to(DEV)], oracle.layernorm_gelu(x[rows], w, b, EPS))
+        say(f"ln f32 in place M={M} N={N} err={err:.2e}")
+        assert err <= TOL["f32"]
+
+
+def _exact_f32_layernorm():
+    return [(v["index"], v["max_n"]) for v in rk.variants(rk.RK_OP_LAYERNORM_GELU, rk.RK_F32)
+            if v["exact"]]
+
+
+@pytest.mark.parametrize("index,N", _exact_f32_layernorm(), ids=str)
+def test_layernorm_gelu_f32_exact_many_rows(index, N):
+    """Every exact fp32 tile on an odd number of rows (up to 4001, 2^25
+    elements at most), sampled rows within 1e-5 of the oracle."""
+    M = min(4001, (1 << 25) // N) | 1
+    g = torch.Generator().manual_seed(5 * N + index)
+    x = torch.randn(M, N, generator=g) * 1.5 + 0.25
+    w, b = rowgen.ln_params(N, g, torch.float32)
+    y = rk.rk__layernorm_gelu_variant(index, x.to(DEV), w.to(DEV), b.to(DEV), EPS)
+    rows = torch.cat([torch.arange(64), torch.arange(M - 64, M),
+                      torch.randint(64, M - 64, (128,), generator=g)]).unique()
+    err = rel_err_floor1(y[rows.to(DEV)], oracle.layernorm_gelu(x[rows], w, b, EPS))
+    say(f"ln f32 exact index {index} N={N} M={M} sampled err={err:.2e}")
+    assert err <= TOL["f32"]
+
+
 def test_deterministic():
     d = rowgen.make("bf16_16384x4096", rows=2048)
     x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
