@@ -358,11 +358,38 @@ def head_kernel_name(rk, N):
 # ------------------------------------------------------- counters / cpu
 
 
+def code_tokens(text):
+    """C++ source with comments and whitespace removed (string literals kept):
+    a comment-only edit leaves the compiled kernel, and this, unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif c.isspace():
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash():
+    """Hash of the headline kernel's sources, comments and whitespace aside."""
     h = hashlib.sha256()
     for f in ("rk_layernorm_gelu.hip", "rk_device.h"):
-        with open(os.path.join(ROOT, "row_wise_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "row_wise_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

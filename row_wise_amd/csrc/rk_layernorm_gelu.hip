@@ -414,9 +414,9 @@ __global__ __launch_bounds__(W *kWave) void layernorm_gelu_rows(
     }
 }
 
-// Workgroups of the persistent kernel: as many as the device holds at once
-// (per device, from the occupancy calculator), spread so that every
-// workgroup takes the same number of row groups but the last.
+// Workgroups of the persistent kernel: at most as many as the device holds at
+// once (per device, from the occupancy calculator), and no more than needed
+// for every workgroup to take the same number of rows, give or take one.
 template <typename T, int G, int V, int W>
 static hipError_t layernorm_gelu_rows_run(const RowProblem &p)
 {
