@@ -352,7 +352,6 @@ void flash_attention_fwd(
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     mx = fmaxf(mx, s[qt][kt][r]);
-            mx = group4_max(mx);
             // m is the reference max of the row in raw score units, and
             // p = exp(scale (s - m)) = exp2(s c - m c), c = scale log2(e).
             // Softmax does not depend on the reference as long as l and acc
@@ -360,8 +359,15 @@ void flash_attention_fwd(
             // more than 2^8 in p (p stays <= 256, far inside the operand
             // range); a moved m rescales l and acc by alpha.  A row that has
             // seen no key keeps m = -inf (the comparison with NaN is false)
-            // and shifts by 0, so that its -inf scores give p = 0.
-            const bool bump = (mx - m[qt]) * scale_log2e > 8.0f;
+            // and shifts by 0, so that its -inf scores give p = 0.  The row
+            // max across its four lanes is formed only when some lane's own
+            // max would move m (rare after the first block): otherwise no
+            // lane's scores exceed the bound and m stays, the same in all.
+            bool bump = false;
+            if (__any((mx - m[qt]) * scale_log2e > 8.0f)) {
+                mx = group4_max(mx);
+                bump = (mx - m[qt]) * scale_log2e > 8.0f;
+            }
             const float m_new = bump ? mx : m[qt];
             const float shift = m_new == -INFINITY ? 0.0f : m_new * scale_log2e;
             const float alpha =
