@@ -15,8 +15,12 @@
  *
  * Conventions common to all entry points
  *   Ownership   All pointers are device memory owned by the caller.  The
- *               library allocates and frees nothing, keeps no mutable global
- *               state, and is safe to call from several host threads.
+ *               library allocates and frees nothing and is safe to call from
+ *               several host threads.  Its only global state is a per-device
+ *               count of how many workgroups of each persistent LayerNorm
+ *               kernel fit on the chip at once (asked of the occupancy
+ *               calculator on first use, kept in atomics) and the fixed
+ *               scratch array of rk_online_softmax_noalloc.
  *   Streams     Work is enqueued on `stream` (0 = the null stream) of the
  *               current device and the call returns without synchronizing.
  *               Multi-kernel operations are ordered by the stream alone.
