@@ -41,7 +41,11 @@ def test_graph_capture_and_replay():
     xl = rowgen.randn(8, 65536, seed=303).to(DEV)
     wl, bl = (t.to(DEV) for t in rowgen.ln_params(65536, torch.Generator().manual_seed(304),
                                                   torch.float32))
-    outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn", "sml", "lnl")}
+    # bf16 rows of 8192: the persistent LayerNorm kernel, both GeLU forms
+    xp = rowgen.randn(300, 8192, seed=305).to(torch.bfloat16).to(DEV)
+    wp, bp = (t.to(DEV) for t in rowgen.ln_params(8192, torch.Generator().manual_seed(306),
+                                                  torch.bfloat16))
+    outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn", "sml", "lnl", "lnp", "lnpe")}
 
     def step():
         outs["ln"] = rk.rk_layernorm_gelu(x, w, b, EPS, out=outs["ln"])
@@ -51,6 +55,8 @@ def test_graph_capture_and_replay():
         y, r = rk.rk_residual_rmsnorm(x, res, w, EPS, out=outs["rms"], residual_out=outs["ro"])
         outs["rms"], outs["ro"] = y, r
         outs["attn"] = rk.rk_flash_attention(q, k, v, causal=True, out=outs["attn"])
+        outs["lnp"] = rk.rk_layernorm_gelu(xp, wp, bp, EPS, out=outs["lnp"])
+        outs["lnpe"] = rk.rk_layernorm_gelu_ex(xp, wp, bp, EPS, gelu="erf", out=outs["lnpe"])
 
     step()  # allocates the outputs, eagerly
     torch.cuda.synchronize()
@@ -68,6 +74,7 @@ def test_graph_capture_and_replay():
         x.copy_(rowgen.randn(4096, 768, seed=310 + rep).to(DEV))
         xs.copy_(rowgen.randn(64, 20000, seed=320 + rep).to(DEV))
         xl.copy_(rowgen.randn(8, 65536, seed=330 + rep).to(DEV))
+        xp.copy_(rowgen.randn(300, 8192, seed=340 + rep).to(torch.bfloat16).to(DEV))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -79,9 +86,13 @@ def test_graph_capture_and_replay():
 
 
 def test_threads_and_streams():
+    # fp32 rows of 1000-1111 (general tiles), and bf16 rows of 8192 (the
+    # persistent LayerNorm kernel, whose per-device workgroup count is shared)
     inputs = [rowgen.randn(2048, 1000 + 37 * i, seed=400 + i).to(DEV) for i in range(4)]
-    ws = [torch.ones(x.shape[1], device=DEV) for x in inputs]
-    bs = [torch.zeros(x.shape[1], device=DEV) for x in inputs]
+    inputs += [rowgen.randn(700 + 9 * i, 8192, seed=410 + i).to(torch.bfloat16).to(DEV)
+               for i in range(4)]
+    ws = [torch.ones(x.shape[1], dtype=x.dtype, device=DEV) for x in inputs]
+    bs = [torch.zeros(x.shape[1], dtype=x.dtype, device=DEV) for x in inputs]
     ref = [(rk.rk_softmax(x), rk.rk_layernorm_gelu(x, w, b, EPS))
            for x, w, b in zip(inputs, ws, bs)]
     torch.cuda.synchronize()
@@ -101,7 +112,7 @@ def test_threads_and_streams():
         except Exception as e:  # noqa: BLE001 - reported below
             errors.append((i, repr(e)))
 
-    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(inputs))]
     for t in threads:
         t.start()
     for t in threads:
