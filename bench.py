@@ -88,6 +88,14 @@ class Case:
         elif self.op in ("row_sum", "row_max"):
             self.bytes = M * N * es + M * es  # one read of x, M results
             footprint = M * N * es
+        elif self.op == "row_sum_ex":
+            if self.splits == 0:
+                self.splits = rk.rk_row_reduce_auto_splits(M, N, self.dtype_code)
+            # one read of x, M results (+ one float per chunk out and in)
+            self.bytes = M * N * es + M * es
+            if self.splits > 1:
+                self.bytes += 2 * M * self.splits * 4
+            footprint = M * N * es
         elif self.op == "rmsnorm":
             self.bytes = io + N * es  # x, y, and w once
         elif self.op == "residual_rmsnorm":
@@ -119,6 +127,9 @@ class Case:
         if self.op == "layernorm_gelu_ex" and self.splits > 1:
             nb = rk.rk_layernorm_gelu_workspace_bytes(M, N, self.splits, self.dtype_code)
             self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        if self.op == "row_sum_ex" and self.splits > 1:
+            nb = rk.rk_row_reduce_workspace_bytes(M, N, self.splits, self.dtype_code)
+            self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         lib = rk.load()
         stream = torch.cuda.current_stream().cuda_stream
         self.stream = stream
@@ -140,6 +151,13 @@ class Case:
             self.ys = [torch.empty(M, dtype=x.dtype, device=dev) for _ in range(self.R)]
             self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, self.dtype_code, stream)
                          for xx, yy in zip(self.xs, self.ys)]
+        elif self.op == "row_sum_ex":
+            fn = lib.rk_row_sum_ex
+            wp = self.ws.data_ptr() if self.ws is not None else None
+            wb = self.ws.numel() if self.ws is not None else 0
+            self.ys = [torch.empty(M, dtype=x.dtype, device=dev) for _ in range(self.R)]
+            self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, self.dtype_code, self.splits,
+                          wp, wb, stream) for xx, yy in zip(self.xs, self.ys)]
         elif self.op == "gelu":
             fn = lib.rk_gelu
             self.args = [(xx.data_ptr(), yy.data_ptr(), M, N, N, N, self.dtype_code, 0, stream)
@@ -269,6 +287,7 @@ def all_cases():
         Case("row_sum_f32_8192x1000", "row_sum", "softmax_f32_8192x1000"),
         Case("row_max_f32_8192x1000", "row_max", "softmax_f32_8192x1000"),
         Case("row_sum_f32_64x262144", "row_sum", "online_f32_64x262144"),
+        Case("row_sum_split_f32_64x262144", "row_sum_ex", "online_f32_64x262144", splits=0),
         Case("row_sum_bf16_16384x4096", "row_sum", "bf16_16384x4096"),
         Case("gelu_bf16_16384x4096", "gelu", "bf16_16384x4096"),
         Case("rmsnorm_f32_4096x768", "rmsnorm", "ln_gelu_f32_4096x768"),

@@ -324,6 +324,48 @@ rk_status rk_row_max(const void *x, void *out, int64_t M, int64_t N, int64_t ldx
                      rk_dtype dtype, hipStream_t stream);
 
 /*
+ * rk_row_sum / rk_row_max with long rows cut into pieces ([TKE] §2.2, §2.3,
+ * and §6.3 on reducing a long dimension in pieces).  One workgroup per row
+ * leaves most of the chip idle when there are few long rows; the split form
+ * spreads every row over many workgroups.
+ *
+ * num_splits  1: as rk_row_sum / rk_row_max.  S > 1: each row is cut into S
+ *             chunks of C = ceil(N / S) elements rounded up to whole 16-byte
+ *             vectors (trailing chunks may be empty); a first kernel writes
+ *             each chunk's fp32 sum (max) to the workspace as
+ *             float [M][S], a second reduces each row's S partials and
+ *             writes out[i].  Both add in an order fixed by N and S, so the
+ *             results are reproducible bit for bit for a given S (a sum may
+ *             differ from S = 1 by rounding; the max is the same).  0:
+ *             rk_row_reduce_auto_splits.
+ * workspace   for S > 1: caller-owned device memory of at least
+ *             rk_row_reduce_workspace_bytes(M, N, num_splits, dtype) bytes,
+ *             8-byte aligned, not overlapping x or out; its contents on
+ *             entry do not matter.  Ignored (may be NULL) for S = 1.
+ *
+ * Returns as rk_row_sum, plus RK_ERR_INVALID_ARG for num_splits outside
+ * [0, 65536] or a misaligned or overlapping workspace; RK_ERR_WORKSPACE when
+ * it is NULL or too small; RK_ERR_UNSUPPORTED when M * S workgroups exceed
+ * the launch limits.
+ */
+rk_status rk_row_sum_ex(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                        rk_dtype dtype, int32_t num_splits, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+rk_status rk_row_max_ex(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                        rk_dtype dtype, int32_t num_splits, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes rk_row_sum_ex / rk_row_max_ex need: M * S * 4 for S > 1
+ * (S the resolved split count), 0 for S = 1 or invalid arguments. */
+size_t rk_row_reduce_workspace_bytes(int64_t M, int64_t N, int32_t num_splits, rk_dtype dtype);
+
+/* The split count of num_splits == 0: 1 for 256 rows or more, or where one
+ * workgroup per row is expected to be as fast (by the reductions' own
+ * measured rates); else chunks of about 16 KiB, at most 2048 workgroups (1
+ * for invalid arguments). */
+int32_t rk_row_reduce_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
+
+/*
  * Elementwise GeLU ([TKE] §3.4; [KTN] "Triton GeLU"): y = GeLU(x), the tanh
  * approximation or the exact erf form, fp32 arithmetic.
  *

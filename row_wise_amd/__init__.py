@@ -16,6 +16,9 @@ Functions carry the C entry points' names:
   workspace=None)``, ``rk_layernorm_gelu_workspace_bytes(M, N, num_splits, dtype)``,
   ``rk_layernorm_gelu_auto_splits(M, N, dtype)``
 * ``rk_row_sum(x, out=None)``, ``rk_row_max(x, out=None)``, ``rk_gelu(x, gelu="tanh", out=None)``
+* ``rk_row_sum_ex(x, num_splits=0, out=None, workspace=None)``, ``rk_row_max_ex(...)``,
+  ``rk_row_reduce_workspace_bytes(M, N, num_splits, dtype)``,
+  ``rk_row_reduce_auto_splits(M, N, dtype)``
 * ``rk_flash_attention(q, k, v, causal=False, scale=None, out=None)``
 * ``rk_rmsnorm(x, weight, eps=1e-5, out=None)``
 * ``rk_residual_rmsnorm(x, residual, weight, eps=1e-5, out=None, residual_out=None)``
@@ -42,7 +45,8 @@ __all__ = [
     "rk__residual_rmsnorm_variant", "RK_OP_RMSNORM", "RK_OP_RESIDUAL_RMSNORM",
     "rk_layernorm_gelu_ex", "rk_layernorm_gelu_workspace_bytes", "rk_layernorm_gelu_auto_splits",
     "RK_GELU_TANH", "RK_GELU_ERF", "rk_row_sum", "rk_row_max", "rk_gelu", "rk_flash_attention",
-    "RK_F16", "rk_online_softmax_noalloc",
+    "RK_F16", "rk_online_softmax_noalloc", "rk_row_sum_ex", "rk_row_max_ex",
+    "rk_row_reduce_workspace_bytes", "rk_row_reduce_auto_splits",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.so")
@@ -102,6 +106,10 @@ def load():
         "rk_flash_attention": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, f32, i32,
                                      i32, vp]),
         "rk_row_max": (i32, [vp, vp, i64, i64, i64, i32, vp]),
+        "rk_row_sum_ex": (i32, [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]),
+        "rk_row_max_ex": (i32, [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]),
+        "rk_row_reduce_workspace_bytes": (sz, [i64, i64, i32, i32]),
+        "rk_row_reduce_auto_splits": (i32, [i64, i64, i32]),
         "rk_gelu": (i32, [vp, vp, i64, i64, i64, i64, i32, i32, vp]),
         "rk_rmsnorm": (i32, [vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]),
         "rk_residual_rmsnorm": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32,
@@ -313,6 +321,46 @@ def rk_row_sum(x, out=None):
 def rk_row_max(x, out=None):
     """max over the last dimension (NaN if a row holds a NaN)."""
     return _row_reduce("rk_row_max", x, out)
+
+
+def rk_row_reduce_workspace_bytes(M: int, N: int, num_splits: int, dtype: int) -> int:
+    return int(load().rk_row_reduce_workspace_bytes(M, N, num_splits, dtype))
+
+
+def rk_row_reduce_auto_splits(M: int, N: int, dtype: int) -> int:
+    return int(load().rk_row_reduce_auto_splits(M, N, dtype))
+
+
+def _row_reduce_ex(name, x, num_splits, out, workspace):
+    torch = _torch()
+    _check_device(x)
+    v, M, N, ldx = _as_rows(x)
+    shape = x.shape[:-1] if x.dim() > 1 else ()
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif out.shape != shape or out.dtype != x.dtype or out.device != x.device \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of the input's rows, dtype and device")
+    dt = _dtype_code(x)
+    need = rk_row_reduce_workspace_bytes(M, N, num_splits, dt) if M > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _call(name, v.data_ptr(), out.data_ptr(), M, N, ldx, dt, int(num_splits), wptr, wbytes,
+          _stream(x))
+    return out
+
+
+def rk_row_sum_ex(x, num_splits: int = 0, out=None, workspace=None):
+    """rk_row_sum with long rows split across workgroups (num_splits 0: auto,
+    1: one workgroup per row, >= 2: that many chunks per row)."""
+    return _row_reduce_ex("rk_row_sum_ex", x, num_splits, out, workspace)
+
+
+def rk_row_max_ex(x, num_splits: int = 0, out=None, workspace=None):
+    """rk_row_max with long rows split across workgroups (as rk_row_sum_ex)."""
+    return _row_reduce_ex("rk_row_max_ex", x, num_splits, out, workspace)
 
 
 def rk_gelu(x, gelu: str = "tanh", out=None):

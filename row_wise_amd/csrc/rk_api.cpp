@@ -179,11 +179,10 @@ constexpr double kOutputSplitExtraUs = 5.5;
 // 5-18% faster at 128 rows, 4-20% slower at 200).  Chunks are about 16 KiB
 // (measured best from 4 KiB to 64 KiB) and at most 2048 workgroups run (more
 // cost more to launch than they gain).
-int32_t pick_splits(rk_op op, int64_t M, int64_t N, rk_dtype dtype, double extra_us)
+int32_t pick_splits(SplitRates r, int64_t M, int64_t N, rk_dtype dtype, double extra_us)
 {
     if (M < 1 || N < 1 || M >= 256)
         return 1;
-    const SplitRates r = split_rates(op, dtype);
     const double gain = N / r.row - static_cast<double>(M) * N / r.all;
     const bool wide = extra_us <= kSplitExtraUs && N >= 65536 && M <= 128;
     if (!(gain > extra_us || wide))
@@ -196,6 +195,11 @@ int32_t pick_splits(rk_op op, int64_t M, int64_t N, rk_dtype dtype, double extra
     if (s > kMaxSplits)
         s = kMaxSplits;
     return static_cast<int32_t>(s < 2 ? 1 : s);
+}
+
+int32_t pick_splits(rk_op op, int64_t M, int64_t N, rk_dtype dtype, double extra_us)
+{
+    return pick_splits(split_rates(op, dtype), M, N, dtype, extra_us);
 }
 
 int32_t auto_splits(int64_t M, int64_t N, rk_dtype dtype)
@@ -784,6 +788,61 @@ rk_status row_reduce_entry(const void *x, void *out, int64_t M, int64_t N, int64
     return hip_status(row_reduce_run(p, op));
 }
 
+// Rates of the row reductions (one read per element), elements per
+// microsecond, measured on 1 to 64 rows of 2^18 to 2^20: one workgroup per
+// row on one CU, and the split kernels with every CU busy.
+SplitRates reduce_rates(rk_dtype dtype)
+{
+    return dtype == RK_F32 ? SplitRates{13000.0, 1600000.0} : SplitRates{20000.0, 2600000.0};
+}
+
+// The split's second launch: about 3 us back to back, against a single
+// kernel that reads the data once.  Measured: 128 rows of 65536 take 8.3 us
+// in one kernel and 8.8-9.3 split (fp32), 5.5 against 7.2 (bf16), so rows of
+// 2^16 in at most 128 rows are not split here as they are for softmax.
+constexpr double kReduceSplitExtraUs = 3.5;
+
+int32_t reduce_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
+{
+    return pick_splits(reduce_rates(dtype), M, N, dtype, kReduceSplitExtraUs);
+}
+
+// One float per (row, chunk).
+size_t reduce_workspace_bytes(int64_t M, int64_t S)
+{
+    if (S <= 1 || M > INT64_MAX / 4 / S)
+        return 0;
+    return static_cast<size_t>(M * S * 4);
+}
+
+rk_status row_reduce_ex_entry(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                              rk_dtype dtype, int op, int32_t num_splits, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream)
+{
+    rk_status st = check_reduce(x, out, M, N, ldx, dtype);
+    if (st != RK_OK)
+        return st;
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return RK_ERR_INVALID_ARG;
+    if (M == 0)
+        return RK_OK;
+    const int32_t S = num_splits == 0 ? reduce_auto_splits(M, N, dtype) : num_splits;
+    if (S <= 1)
+        return row_reduce_entry(x, out, M, N, ldx, dtype, op, stream);
+    const int es = elem_size(dtype);
+    st = check_workspace(workspace, workspace_bytes, reduce_workspace_bytes(M, S), M, S,
+                         {matrix_span(x, M, N, ldx, es), matrix_span(out, 1, M, M, es)});
+    if (st != RK_OK)
+        return st;
+    // rows are read as the aligned vectors that cover them, at any offset
+    const int64_t chunk = split_chunk(N, S, vec_elems(dtype));
+    if (chunk > INT32_MAX || !grid_ok((M + 3) / 4, kSplitThreads))
+        return RK_ERR_UNSUPPORTED;
+    const RowProblem p = make_problem(x, out, nullptr, nullptr, M, N, ldx, 1, 0.0f, dtype, stream);
+    return hip_status(row_reduce_split_run(p, op, S, static_cast<int>(chunk),
+                                           static_cast<float *>(workspace)));
+}
+
 }  // namespace
 
 RK_EXPORT rk_status rk_row_sum(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
@@ -796,6 +855,39 @@ RK_EXPORT rk_status rk_row_max(const void *x, void *out, int64_t M, int64_t N, i
                                rk_dtype dtype, hipStream_t stream)
 {
     return row_reduce_entry(x, out, M, N, ldx, dtype, RK_REDUCE_MAX, stream);
+}
+
+RK_EXPORT int32_t rk_row_reduce_auto_splits(int64_t M, int64_t N, rk_dtype dtype)
+{
+    if (M < 1 || N < 1 || !valid_dtype(dtype))
+        return 1;
+    return reduce_auto_splits(M, N, dtype);
+}
+
+RK_EXPORT size_t rk_row_reduce_workspace_bytes(int64_t M, int64_t N, int32_t num_splits,
+                                               rk_dtype dtype)
+{
+    if (M < 1 || N < 1 || N > kMaxN || num_splits < 0 || num_splits > kMaxSplits ||
+        !valid_dtype(dtype))
+        return 0;
+    const int64_t S = num_splits == 0 ? reduce_auto_splits(M, N, dtype) : num_splits;
+    return reduce_workspace_bytes(M, S);
+}
+
+RK_EXPORT rk_status rk_row_sum_ex(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                                  rk_dtype dtype, int32_t num_splits, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream)
+{
+    return row_reduce_ex_entry(x, out, M, N, ldx, dtype, RK_REDUCE_SUM, num_splits, workspace,
+                               workspace_bytes, stream);
+}
+
+RK_EXPORT rk_status rk_row_max_ex(const void *x, void *out, int64_t M, int64_t N, int64_t ldx,
+                                  rk_dtype dtype, int32_t num_splits, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream)
+{
+    return row_reduce_ex_entry(x, out, M, N, ldx, dtype, RK_REDUCE_MAX, num_splits, workspace,
+                               workspace_bytes, stream);
 }
 
 RK_EXPORT rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_t ldx,

@@ -136,6 +136,11 @@ enum { RK_REDUCE_SUM = 0, RK_REDUCE_MAX = 1 };
 hipError_t row_reduce_run(const RowProblem &p, int op);
 // Workgroups (and threads per workgroup) row_reduce_run launches.
 int64_t row_reduce_blocks(int64_t M, int64_t N, rk_dtype dtype, int *threads);
+// Split form: M * splits workgroups of 256 threads write one float per
+// (row, chunk) to part ([M][splits]), then ceil(M / 4) workgroups reduce
+// each row's partials into out.  chunk: elements per chunk, a multiple of
+// the vector width.
+hipError_t row_reduce_split_run(const RowProblem &p, int op, int splits, int chunk, float *part);
 // flat: x and y contiguous and 16-byte aligned, processed as one buffer.
 hipError_t gelu_run(const RowProblem &p, bool flat, RowIo io);
 // Query rows and threads per workgroup of the attention kernel for head

@@ -10,6 +10,12 @@
 //             element; the M results are the only writes.  A row at any
 //             offset is read as the aligned 16-byte vectors that cover it
 //             (RowSpan), its ends masked.
+// row_reduce_partials + row_reduce_finish
+//             long rows in few rows, split across workgroups ("Triton Kernel
+//             实现练习" §6.3 on reducing a long dimension in pieces): the
+//             first kernel writes each chunk's fp32 sum or max to a
+//             workspace, the second reduces each row's S partials in a fixed
+//             order and writes the result.
 // gelu_flat   y = GeLU(x) elementwise over a contiguous buffer: 16-byte
 //             vectors, U per thread per step, from whatever offset the
 //             buffer starts at (the output at the same offset).
@@ -149,6 +155,132 @@ static hipError_t reduce_run(const RowProblem &p)
 hipError_t row_reduce_run(const RowProblem &p, int op)
 {
     return op == RK_REDUCE_SUM ? reduce_run<RK_REDUCE_SUM>(p) : reduce_run<RK_REDUCE_MAX>(p);
+}
+
+// ------------------------------------------------------ split row reduce
+
+constexpr int kSplitReduceWaves = 4;  // 256-thread workgroups
+
+// Chunk s = blockIdx.x % S of row blockIdx.x / S (the vectors chunk_span
+// gives, over the aligned vectors that cover the row): its fp32 sum or max,
+// U vectors per thread in flight, to part[row * S + s].  An empty chunk
+// gives the identity (0 or -inf).
+template <typename T, int E, int U, int OP, bool PH>
+__global__ __launch_bounds__(kSplitReduceWaves *kWave) void row_reduce_partials(
+    const T *__restrict__ x, float *__restrict__ part, int N, int64_t ldx, int S, int C)
+{
+    constexpr int W = kSplitReduceWaves;
+    constexpr int NT = W * kWave;
+    constexpr float kPad = OP == RK_REDUCE_SUM ? 0.0f : -INFINITY;
+    __shared__ float red[W];
+
+    const int64_t row = blockIdx.x / S;
+    const int s = static_cast<int>(blockIdx.x % S);
+    const T *xr = x + row * ldx;
+    const RowSpan<E> sp{row_phase<T, E, PH>(xr), N};
+    const T *xb = xr - sp.h;
+    int jbeg, jend;
+    chunk_span<E>(sp, s, S, C, jbeg, jend);
+    const int tid = static_cast<int>(threadIdx.x);
+    auto full = [&](int base) { return sp.step_full(base, jend, NT * U); };
+
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        acc[u] = kPad;
+    SpanLoad<T, E, U, NT> cur;
+    cur.issue(xb, jbeg + tid, jend, full(jbeg));
+    for (int base = jbeg; base < jend; base += NT * U) {
+        SpanLoad<T, E, U, NT> nxt;
+        const int next = base + NT * U;
+        if (next < jend)
+            nxt.issue(xb, next + tid, jend, full(next));
+        float v[U][E];
+        cur.finish(v, sp, jend, kPad, full(base));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[u] = reduce_op<OP>(acc[u], v[u][e]);
+        cur = nxt;
+    }
+    float a = acc[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u)
+        a = reduce_op<OP>(a, acc[u]);
+    if constexpr (OP == RK_REDUCE_SUM)
+        a = wave_sum(a);
+    else
+        a = wave_max(a);
+    if (tid % kWave == 0)
+        red[tid / kWave] = a;
+    __syncthreads();
+    if (tid == 0) {
+        float r = red[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            r = reduce_op<OP>(r, red[w]);
+        part[row * S + s] = r;
+    }
+}
+
+// out[row] from the row's S partials: one wave per row, four rows per
+// workgroup; lane l folds partials l, l + 64, ... in that order, then the
+// wave reduces (DPP), so every call adds in the same order.
+template <typename T, int OP>
+__global__ __launch_bounds__(kSplitReduceWaves *kWave) void row_reduce_finish(
+    const float *__restrict__ part, T *__restrict__ out, int64_t M, int S)
+{
+    constexpr float kPad = OP == RK_REDUCE_SUM ? 0.0f : -INFINITY;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kSplitReduceWaves + threadIdx.x / kWave;
+    const int lane = static_cast<int>(threadIdx.x % kWave);
+    if (row >= M)  // the whole wave: no barrier follows
+        return;
+    const float *pr = part + row * S;
+    float a = kPad;
+    for (int i = lane; i < S; i += kWave)
+        a = reduce_op<OP>(a, pr[i]);
+    if constexpr (OP == RK_REDUCE_SUM)
+        a = wave_sum(a);
+    else
+        a = wave_max(a);
+    if (lane == 0)
+        out[row] = Elem<T>::from_f32(a);
+}
+
+template <typename T, int OP, bool PH>
+static hipError_t reduce_split_launch(const RowProblem &p, int splits, int chunk, float *part)
+{
+    constexpr int E = Elem<T>::kVec;
+    constexpr int U = 16 / E > 4 ? 4 : (16 / E < 2 ? 2 : 16 / E);
+    const hipError_t e = launch(row_reduce_partials<T, E, U, OP, PH>,
+                                dim3(static_cast<unsigned>(p.M * splits)),
+                                dim3(kSplitReduceWaves * kWave), p.stream,
+                                static_cast<const T *>(p.x), part, p.N, p.ldx, splits, chunk);
+    if (e != hipSuccess)
+        return e;
+    const int64_t blocks = (p.M + kSplitReduceWaves - 1) / kSplitReduceWaves;
+    return launch(row_reduce_finish<T, OP>, dim3(static_cast<unsigned>(blocks)),
+                  dim3(kSplitReduceWaves * kWave), p.stream, static_cast<const float *>(part),
+                  static_cast<T *>(p.y), p.M, splits);
+}
+
+template <int OP>
+static hipError_t reduce_split_run(const RowProblem &p, int splits, int chunk, float *part)
+{
+    const int es = elem_size(p.dtype);
+    const bool aligned = reinterpret_cast<uintptr_t>(p.x) % 16 == 0 && (p.ldx * es) % 16 == 0;
+    if (p.dtype == RK_F32)
+        return aligned ? reduce_split_launch<float, OP, false>(p, splits, chunk, part)
+                       : reduce_split_launch<float, OP, true>(p, splits, chunk, part);
+    return aligned ? reduce_split_launch<bf16_t, OP, false>(p, splits, chunk, part)
+                   : reduce_split_launch<bf16_t, OP, true>(p, splits, chunk, part);
+}
+
+hipError_t row_reduce_split_run(const RowProblem &p, int op, int splits, int chunk, float *part)
+{
+    return op == RK_REDUCE_SUM ? reduce_split_run<RK_REDUCE_SUM>(p, splits, chunk, part)
+                               : reduce_split_run<RK_REDUCE_MAX>(p, splits, chunk, part);
 }
 
 // ----------------------------------------------------------- elementwise

@@ -208,6 +208,46 @@ def test_row_reduce_rejects(lib, fn):
     assert f(A, B, 1, 2**30 + 1, 2**30 + 1, F32, None) == UNSUPPORTED
 
 
+def rsx(lib, fn="rk_row_sum_ex", x=A, out=B, M=4, N=4096, ldx=4096, dt=F32, S=8,
+        ws=0x3000000, wb=4 * 8 * 4):
+    return getattr(lib, fn)(x, out, M, N, ldx, dt, S, ws, wb, None)
+
+
+@pytest.mark.parametrize("fn", ["rk_row_sum_ex", "rk_row_max_ex"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=-1), INVALID), (dict(S=65537), INVALID), (dict(N=0), INVALID),
+    (dict(ldx=4095), INVALID), (dict(dt=5), INVALID), (dict(x=None), INVALID),
+    (dict(out=A + 64), INVALID),  # out inside x
+    (dict(ws=None), WORKSPACE), (dict(wb=4 * 8 * 4 - 1), WORKSPACE),
+    (dict(ws=0x3000004), INVALID),  # misaligned workspace
+    (dict(ws=A + 64), INVALID),  # workspace overlaps x
+    (dict(ws=B - 8), INVALID),  # workspace overlaps out
+    (dict(N=2**30 + 1, ldx=2**30 + 1), UNSUPPORTED),
+])
+def test_row_reduce_ex_rejects(lib, fn, kw, status):
+    assert rsx(lib, fn, **kw) == status
+
+
+def test_row_reduce_ex_workspace_and_splits(lib):
+    assert rk.rk_row_reduce_workspace_bytes(64, 262144, 32, F32) == 64 * 32 * 4
+    assert rk.rk_row_reduce_workspace_bytes(64, 262144, 1, F32) == 0
+    assert rk.rk_row_reduce_workspace_bytes(64, 262144, -1, F32) == 0
+    assert rk.rk_row_reduce_workspace_bytes(64, 262144, 4, 9) == 0
+    assert rk.rk_row_reduce_workspace_bytes(0, 10, 4, F32) == 0
+    for dt, es in ((F32, 4), (BF16, 2)):
+        for M, N in ((1, 1 << 20), (4, 262144), (64, 262144), (16, 262144)):
+            s = rk.rk_row_reduce_auto_splits(M, N, dt)
+            assert s == min(-(-N * es // 16384), 2048 // M), (M, N)
+            assert rk.rk_row_reduce_workspace_bytes(M, N, 0, dt) == M * s * 4
+        # a full chip of rows, or rows one workgroup reads about as fast as
+        # the split's two launches take
+        for M, N in ((256, 1 << 20), (8192, 1000), (16384, 4096), (200, 65536), (128, 65536)):
+            assert rk.rk_row_reduce_auto_splits(M, N, dt) == 1, (M, N)
+    # S = 1 needs no workspace; M = 0 is a no-op
+    assert rsx(lib, M=0, x=None, out=None, ws=None) == 0
+    assert lib.rk_row_sum_ex(None, None, 0, 8, 8, F32, 1, None, 0, None) == 0
+
+
 def test_gelu_rejects(lib):
     g = lib.rk_gelu
     assert g(A, B, 4, 8, 8, 8, F32, 2, None) == INVALID

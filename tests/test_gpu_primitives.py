@@ -104,6 +104,87 @@ def test_sum_deterministic_and_empty():
     assert rk.rk_row_sum(e).shape == (0,) and rk.rk_row_max(e).shape == (0,)
 
 
+# ------------------------------------------- split row sum and max (_ex)
+
+
+def check_split(x, xd, dtype, S, what=""):
+    """rk_row_sum_ex / rk_row_max_ex at split count S against the oracle:
+    the sum within the tolerance of sum |x|, the max bit-exact and equal to
+    rk_row_max (max is exact whatever the order)."""
+    s = rk.rk_row_sum_ex(xd, num_splits=S)
+    err = rel_err_sum(s, oracle.row_sum(x), x.double().numpy())
+    assert err <= tol_of(dtype), (what, S, "sum", err)
+    m = rk.rk_row_max_ex(xd, num_splits=S)
+    assert np.array_equal(m.cpu().double().numpy(), oracle.row_max(x), equal_nan=True), \
+        (what, S, "max")
+    return err
+
+
+SPLIT_N = [1, 5, 1000, 4099, 65536, 262147]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("N", SPLIT_N)
+def test_split_shapes(dtype, N):
+    """Every split count from 1 to past the vector count (empty chunks),
+    ragged N, rows offset by +7 every third row."""
+    for M in (1, 3, 70):
+        x = rowgen.randn(M, N, seed=5 * M + N, scale=3.0, dtype=dtype)
+        x[::3] += 7.0
+        xd = x.to(DEV)
+        for S in (0, 1, 2, 3, 7, 64, 1000):
+            check_split(x, xd, dtype, S, (M, N))
+    say(f"split reduce {key(dtype)} N={N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+def test_split_workload_and_layouts(dtype):
+    """64 rows of 262144 (the auto split), padded pitch, rows at an odd
+    offset, and the result bitwise reproducible for a given split count."""
+    x = rowgen.randn(64, 262144, seed=1004, scale=3.0, dtype=dtype)
+    xd = x.to(DEV)
+    assert rk.rk_row_reduce_auto_splits(64, 262144, rk.RK_F32 if dtype == torch.float32
+                                        else rk.RK_BF16) > 1
+    err = check_split(x, xd, dtype, 0, "64x262144")
+    say(f"split row_sum {key(dtype)} 64x262144 err={err:.3e}")
+    a, b = rk.rk_row_sum_ex(xd), rk.rk_row_sum_ex(xd)
+    bits = torch.int32 if dtype == torch.float32 else torch.int16
+    assert torch.equal(a.view(bits), b.view(bits))
+    M, N, ld = 37, 30001, 30080
+    xb = rowgen.randn(M, ld, seed=1005, dtype=dtype)
+    for S in (0, 5, 64):
+        check_split(xb[:, :N], xb.to(DEV)[:, :N], dtype, S, "pitch")
+    flat = rowgen.randn(1, M * N + 3, seed=1006, dtype=dtype)[0]
+    for S in (0, 5, 64):
+        check_split(flat[3:].view(M, N), flat.to(DEV)[3:].view(M, N), dtype, S, "offset")
+
+
+def test_split_special_rows():
+    """NaN, -inf and +inf in one chunk only, an all -inf row, exact
+    cancellation across chunks; and a caller's workspace reused."""
+    x = rowgen.randn(6, 100000, seed=102)
+    x[0, 70000] = math.nan
+    x[1, :] = -math.inf
+    x[2, 99999] = math.inf
+    x[3, :50000] = 0.25
+    x[3, 50000:] = -0.25  # each chunk's sum cancels with another's
+    x[4, 10:20] = -math.inf
+    xd = x.to(DEV)
+    ws = torch.empty(rk.rk_row_reduce_workspace_bytes(6, 100000, 16, rk.RK_F32),
+                     dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        m = rk.rk_row_max_ex(xd, num_splits=16, workspace=ws).cpu().numpy()
+        assert np.isnan(m[0]) and m[1] == -np.inf and m[2] == np.inf
+        assert m[3] == 0.25 and m[4] == x[4].max().item()
+        s = rk.rk_row_sum_ex(xd, num_splits=16, workspace=ws).cpu().numpy()
+        assert np.isnan(s[0]) and s[1] == -np.inf and s[2] == np.inf and s[3] == 0.0
+        assert s[4] == -np.inf
+        ref = oracle.row_sum(x[5:])
+        assert abs(s[5] - ref[0]) <= 1e-5 * x[5].abs().sum().item()
+    e = torch.empty(0, 10, device=DEV)
+    assert rk.rk_row_sum_ex(e, num_splits=4).shape == (0,)
+
+
 # ----------------------------------------------------------------- GeLU
 
 
