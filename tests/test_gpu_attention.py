@@ -80,6 +80,26 @@ def test_pages_benchmark_shapes(dtype, causal, T):
     say(f"attention {key(dtype)} 4x32x{T}x128 causal={causal} err={err:.3e}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=key)
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_head_dim_64_long(dtype, causal):
+    """d = 64 (four-wave workgroups of 128 query rows) at the benchmark length
+    T = 4096: 384 rows of each of four heads (the first and last 64 and 256
+    seeded others) against the definition for those rows, masked or not."""
+    T = 4096
+    q, k, v = rowgen.attention_qkv(4, 32, T, 64, dtype, seed=2100 + int(causal))
+    o = rk.rk_flash_attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal).cpu()
+    rng = np.random.default_rng(T + int(causal))
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T),
+                                     rng.choice(np.arange(64, T - 64), 256, replace=False)]))
+    err = 0.0
+    for b, h in [(0, 0), (1, 9), (2, 22), (3, 31)]:
+        ref = oracle.attention_rows(q[b, h][rows], rows, k[b, h], v[b, h], causal)
+        err = max(err, rel_err_floor1(o[b, h][rows], ref))
+    assert err <= TOL, (causal, err)
+    say(f"attention {key(dtype)} 4x32x{T}x64 causal={causal} err={err:.3e}")
+
+
 EDGE_T = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 200, 257]
 
 
