@@ -1,9 +1,10 @@
 """The largest problems the entry points accept, against the oracle.
 
 The longest row is N = 2^30 elements (4 GiB in fp32): every form of the
-softmax and the row sum and max take it as one row, and the oracle's
-statistics of the whole row check 2304 sampled outputs (the first and last
-128 columns and 2048 seeded others; "Triton Kernel 实现练习" §2.4, §2.5).  A
+softmax and of the row sum and max (one workgroup per row, and split) take
+it as one row, and the oracle's statistics of the whole row check 2304
+sampled outputs (the first and last 128 columns and 2048 seeded others;
+"Triton Kernel 实现练习" §2.4, §2.5).  A
 2^28-column bf16 LayerNorm+GeLU row is checked whole.  The tallest grid a
 register tile takes is 2^26 - 4 rows of 8 (one wave per row, four rows per
 workgroup, 2^32 - 256 work-items); one more workgroup's rows are refused
@@ -79,13 +80,18 @@ def test_longest_row_sum_and_max():
     x = xd.cpu()
     s = rk.rk_row_sum(xd).cpu().double().numpy()
     mx = rk.rk_row_max(xd).cpu()
+    # the split forms (auto: 2048 chunks of 2^19)
+    assert rk.rk_row_reduce_auto_splits(1, N, rk.RK_F32) == 2048
+    s_split = rk.rk_row_sum_ex(xd).cpu().double().numpy()
+    mx_split = rk.rk_row_max_ex(xd).cpu()
     say("longest row: oracle sum and max of 2^30 values")
     xn = x.double().numpy()
     ref_s = oracle.row_sum(xn)
     ref_m = oracle.row_max(xn)
     scale = np.abs(xn).sum()
     assert abs(s[0] - ref_s[0]) / scale <= TOL["f32"]
-    assert mx[0].item() == ref_m[0]
+    assert abs(s_split[0] - ref_s[0]) / scale <= TOL["f32"]
+    assert mx[0].item() == ref_m[0] and mx_split[0].item() == ref_m[0]
 
 
 def test_long_bf16_layernorm_row():
