@@ -1,5 +1,5 @@
 """Seeded random shapes and memory layouts for every row entry point, against
-the CPU oracle ("Triton Kernel 实现练习" §2.4, §2.5, §4.1, §4.2, §4.3).
+the CPU oracle ("Triton Kernel 实现练习" §2.2-§2.5, §4.1, §4.2, §4.3).
 
 Each case draws a dtype, a row count, a row length (short, register-tile,
 past the tiles, long rows in few rows) and a layout: contiguous, input and
@@ -18,7 +18,7 @@ import torch
 import oracle
 import row_wise_amd as rk
 import rowgen
-from tolerance import TOL, rel_err, rel_err_floor1, rel_err_softmax
+from tolerance import TOL, rel_err, rel_err_floor1, rel_err_softmax, rel_err_sum
 
 pytestmark = pytest.mark.gpu
 EPS = float(np.float32(1e-5))
@@ -143,3 +143,12 @@ def test_random_layout(case):
         assert _gaps_untouched(ybuf, yo, M, N, ldy), "residual rmsnorm gaps"
     assert rel_err(rd, r_ref) <= tol, "residual_out"
     assert rel_err(yd, y_ref) <= tol, "residual rmsnorm"
+
+    # row sum and max, one workgroup per row or split (the input at the
+    # case's offset and pitch)
+    S = [0, 1, 3][idx % 3]
+    xd = _layout(x, layout, idx)[0]
+    s_got = rk.rk_row_sum_ex(xd, num_splits=S)
+    assert rel_err_sum(s_got, oracle.row_sum(x), x.double().numpy()) <= tol, ("row sum", S)
+    m_got = rk.rk_row_max_ex(xd, num_splits=S).cpu().double().numpy()
+    assert np.array_equal(m_got, oracle.row_max(x)), ("row max", S)
