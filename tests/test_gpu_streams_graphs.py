@@ -45,7 +45,10 @@ def test_graph_capture_and_replay():
     xp = rowgen.randn(300, 8192, seed=305).to(torch.bfloat16).to(DEV)
     wp, bp = (t.to(DEV) for t in rowgen.ln_params(8192, torch.Generator().manual_seed(306),
                                                   torch.bfloat16))
-    outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn", "sml", "lnl", "lnp", "lnpe")}
+    wsr = torch.empty(rk.rk_row_reduce_workspace_bytes(64, 20000, 8, rk.RK_F32),
+                      dtype=torch.uint8, device=DEV)
+    outs = {n: None for n in ("ln", "sm", "rms", "ro", "attn", "sml", "lnl", "lnp", "lnpe",
+                              "rs", "rm")}
 
     def step():
         outs["ln"] = rk.rk_layernorm_gelu(x, w, b, EPS, out=outs["ln"])
@@ -57,6 +60,9 @@ def test_graph_capture_and_replay():
         outs["attn"] = rk.rk_flash_attention(q, k, v, causal=True, out=outs["attn"])
         outs["lnp"] = rk.rk_layernorm_gelu(xp, wp, bp, EPS, out=outs["lnp"])
         outs["lnpe"] = rk.rk_layernorm_gelu_ex(xp, wp, bp, EPS, gelu="erf", out=outs["lnpe"])
+        # the split row sum and max on a preallocated workspace
+        outs["rs"] = rk.rk_row_sum_ex(xs, num_splits=8, out=outs["rs"], workspace=wsr)
+        outs["rm"] = rk.rk_row_max_ex(xs, num_splits=8, out=outs["rm"], workspace=wsr)
 
     step()  # allocates the outputs, eagerly
     torch.cuda.synchronize()
