@@ -258,13 +258,14 @@ class Oracle:
 
     def layernorm_gelu_ex(self, x, w, b, eps: float, gelu: str = "tanh",
                           splits: int = 0) -> np.ndarray:
-        """LayerNorm + affine + GeLU ("tanh" or "erf"); splits = 0 takes the
-        whole-row statistics, splits >= 1 the Chan-merged split statistics."""
+        """LayerNorm + affine + GeLU ("tanh" or "erf"; "none": the LayerNorm
+        alone); splits = 0 takes the whole-row statistics, splits >= 1 the
+        Chan-merged split statistics."""
         x = _rows(x)
         w = _f64(w).ravel()
         b = _f64(b).ravel()
         assert w.size == x.shape[1] and b.size == x.shape[1]
-        kind = {"tanh": 0, "erf": 1}[gelu]
+        kind = {"tanh": 0, "erf": 1, "none": 2}[gelu]
         y = np.empty_like(x)
         self.lib.oracle_layernorm_gelu_ex(_p(x), _p(w), _p(b), _p(y), x.shape[0], x.shape[1],
                                           float(eps), kind, int(splits))

@@ -393,7 +393,8 @@ void oracle_split_moments(const double *x, int64_t N, int64_t S, double *n_parts
 /* LayerNorm + affine + GeLU with a choice of statistics and activation:
  * S = 0 takes the whole-row two-pass statistics of oracle_layernorm_stats,
  * S >= 1 the split statistics above (rstd = 1 / sqrt(M2 / N + eps));
- * gelu = 0 is the tanh approximation, 1 the exact erf form. */
+ * gelu = 0 is the tanh approximation, 1 the exact erf form, 2 no activation
+ * (y = z: the LayerNorm of [TKE] §4.1 "LayerNorm" alone). */
 void oracle_layernorm_gelu_ex(const double *x, const double *w, const double *b, double *y,
                               int64_t M, int64_t N, double eps, int gelu, int64_t S)
 {
@@ -410,7 +411,10 @@ void oracle_layernorm_gelu_ex(const double *x, const double *w, const double *b,
         }
         for (int64_t j = 0; j < N; ++j) {
             double z = (xr[j] - mean) * rstd * w[j] + b[j];
-            yr[j] = gelu ? oracle_gelu_erf(z) : oracle_gelu_tanh(z);
+            if (gelu == 2)
+                yr[j] = z;
+            else
+                yr[j] = gelu ? oracle_gelu_erf(z) : oracle_gelu_tanh(z);
         }
     }
 }

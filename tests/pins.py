@@ -587,6 +587,14 @@ def check_layernorm_gelu_ex(orc):
         y = orc.layernorm_gelu_ex(x, w, b, EPS, "erf", S)
         assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1.0)) <= 1e-13, S
     assert np.max(np.abs(orc.layernorm_gelu_ex(x, w, b, EPS, "erf", 0) - base)) > 1e-4
+    # no activation: the LayerNorm alone ([TKE] §4.1) is F.layer_norm, whole-row
+    # and split statistics; a constant row gives exactly the bias
+    ln = ln.numpy()
+    for S in (0, 7):
+        y = orc.layernorm_gelu_ex(x, w, b, EPS, "none", S)
+        assert np.max(np.abs(y - ln) / np.maximum(np.abs(ln), 1.0)) <= 1e-13, S
+    c = np.full((1, n), 3.25)
+    assert np.array_equal(orc.layernorm_gelu_ex(c, w, b, EPS, "none", 0)[0], b)
 
 
 # ------------------------------------------------------ row sum and max

@@ -34,7 +34,7 @@ MUTANTS = {
     "ln_eps_dropped": ("*rstd_out = 1.0 / sqrt(var + eps);", "*rstd_out = 1.0 / sqrt(var);"),
     "ln_bias_sign": ("* rstd * w[j] + b[j];\n            yr[j] = oracle_gelu_tanh(z);", "* rstd * w[j] - b[j];\n            yr[j] = oracle_gelu_tanh(z);"),
     "ln_weight_dropped": ("* rstd * w[j] + b[j];\n            yr[j] = oracle_gelu_tanh(z);", "* rstd + b[j];\n            yr[j] = oracle_gelu_tanh(z);"),
-    "ex_bias_sign": ("* rstd * w[j] + b[j];\n            yr[j] = gelu", "* rstd * w[j] - b[j];\n            yr[j] = gelu"),
+    "ex_bias_sign": ("* rstd * w[j] + b[j];\n            if (gelu == 2)", "* rstd * w[j] - b[j];\n            if (gelu == 2)"),
     "ln_mean_divisor": ("double mean = s / (double)N;", "double mean = s / (double)(N + 1);"),
     "ln_var_uncentered": ("q += (x[j] - mean) * (x[j] - mean);\n    double var", "q += x[j] * x[j];\n    double var"),
     "chunk_mean_divisor": ("double mean = s / (double)n;", "double mean = s / (double)(n + 1);"),
@@ -52,6 +52,7 @@ MUTANTS = {
     "chan_identity_swapped": ("*n_out = n2, *mean_out = mean2, *m2_out = m2_2;", "*n_out = n1, *mean_out = mean1, *m2_out = m2_1;"),
     "split_var_divisor": ("rstd = 1.0 / sqrt(m2 / (double)N + eps);", "rstd = 1.0 / sqrt(m2 / (double)(N - 1) + eps);"),
     "ex_gelu_kind_ignored": ("yr[j] = gelu ? oracle_gelu_erf(z) : oracle_gelu_tanh(z);", "yr[j] = oracle_gelu_tanh(z);"),
+    "ex_plain_layernorm_activated": ("            if (gelu == 2)\n                yr[j] = z;", "            if (gelu == 2)\n                yr[j] = oracle_gelu_tanh(z);"),
     "row_sum_drops_last": ("        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];", "        for (int64_t j = 0; j + 1 < N; ++j)\n            s += x[i * N + j];"),
     "row_sum_first_twice": ("        double s = 0.0;\n        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];", "        double s = x[i * N];\n        for (int64_t j = 0; j < N; ++j)\n            s += x[i * N + j];"),
     "row_max_ignores_nan": ("        if (isnan(x[j]))\n            return NAN;\n", ""),
