@@ -67,6 +67,8 @@ typedef enum rk_dtype {
 typedef enum rk_gelu_kind {
     RK_GELU_TANH = 0, /* 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
     RK_GELU_ERF = 1,  /* 0.5 z (1 + erf(z / sqrt(2))), the exact form */
+    RK_GELU_NONE = 2, /* no activation, y = z: the LayerNorm of [TKE] §4.1
+                         alone (rk_layernorm_gelu_ex only; rk_gelu rejects it) */
 } rk_gelu_kind;
 
 typedef enum rk_status {
@@ -218,7 +220,8 @@ rk_status rk_layernorm_gelu(const void *x, const void *weight, const void *bias,
  * split ([TKE] §4.1 "LayerNorm", §3.4 "Approx Activation", and §6.3 on
  * reducing a long dimension in pieces).
  *
- * gelu        RK_GELU_TANH or RK_GELU_ERF.
+ * gelu        RK_GELU_TANH, RK_GELU_ERF, or RK_GELU_NONE for the LayerNorm
+ *             alone (y = z, same kernels and statistics).
  * num_splits  1: one workgroup (or register tile) per row, as
  *             rk_layernorm_gelu.  S > 1: each row is cut into S chunks of
  *             C = ceil(N / S) elements (rounded up to whole 16-byte vectors
@@ -370,8 +373,9 @@ int32_t rk_row_reduce_auto_splits(int64_t M, int64_t N, rk_dtype dtype);
  * approximation or the exact erf form, fp32 arithmetic.
  *
  * x [M][ldx], y [M][ldy] of `dtype`; a contiguous buffer whose output sits at
- * the same offset past a 16-byte boundary is processed as one flat array.  Arguments, aliasing and errors as in
- * rk_softmax, plus RK_ERR_INVALID_ARG for an unknown gelu.
+ * the same offset past a 16-byte boundary is processed as one flat array.
+ * Arguments, aliasing and errors as in rk_softmax, plus RK_ERR_INVALID_ARG
+ * for a gelu other than RK_GELU_TANH and RK_GELU_ERF.
  */
 rk_status rk_gelu(const void *x, void *y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
                   rk_dtype dtype, rk_gelu_kind gelu, hipStream_t stream);

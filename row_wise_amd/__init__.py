@@ -44,7 +44,7 @@ __all__ = [
     "RK_OP_LAYERNORM_GELU", "rk_rmsnorm", "rk_residual_rmsnorm", "rk__rmsnorm_variant",
     "rk__residual_rmsnorm_variant", "RK_OP_RMSNORM", "RK_OP_RESIDUAL_RMSNORM",
     "rk_layernorm_gelu_ex", "rk_layernorm_gelu_workspace_bytes", "rk_layernorm_gelu_auto_splits",
-    "RK_GELU_TANH", "RK_GELU_ERF", "rk_row_sum", "rk_row_max", "rk_gelu", "rk_flash_attention",
+    "RK_GELU_TANH", "RK_GELU_ERF", "RK_GELU_NONE", "rk_row_sum", "rk_row_max", "rk_gelu", "rk_flash_attention",
     "RK_F16", "rk_online_softmax_noalloc", "rk_row_sum_ex", "rk_row_max_ex",
     "rk_row_reduce_workspace_bytes", "rk_row_reduce_auto_splits",
 ]
@@ -53,8 +53,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librowkern.
 
 RK_F32, RK_BF16, RK_F16 = 0, 1, 2
 RK_OP_SOFTMAX, RK_OP_LAYERNORM_GELU, RK_OP_RMSNORM, RK_OP_RESIDUAL_RMSNORM = 0, 1, 2, 3
-RK_GELU_TANH, RK_GELU_ERF = 0, 1
-_GELU = {"tanh": RK_GELU_TANH, "erf": RK_GELU_ERF}
+RK_GELU_TANH, RK_GELU_ERF, RK_GELU_NONE = 0, 1, 2
+_GELU = {"tanh": RK_GELU_TANH, "erf": RK_GELU_ERF, "none": RK_GELU_NONE}
 RK_OK = 0
 
 
@@ -281,8 +281,9 @@ def rk_layernorm_gelu_auto_splits(M: int, N: int, dtype: int) -> int:
 
 def rk_layernorm_gelu_ex(x, weight, bias, eps: float = 1e-5, gelu: str = "tanh",
                          num_splits: int = 1, out=None, workspace=None):
-    """LayerNorm + affine + GeLU ("tanh" or "erf"); num_splits 1: one
-    workgroup or tile per row, >= 2: split-row, 0: auto."""
+    """LayerNorm + affine + GeLU ("tanh" or "erf"; "none": the LayerNorm
+    alone); num_splits 1: one workgroup or tile per row, >= 2: split-row, 0:
+    auto."""
     torch = _torch()
     _check_device(x, weight, bias)
     v, M, N, ldx = _as_rows(x)

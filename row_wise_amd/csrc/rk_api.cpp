@@ -281,6 +281,9 @@ rk_status layernorm_generic(const RowProblem &p)
 
 bool valid_gelu(rk_gelu_kind g) { return g == RK_GELU_TANH || g == RK_GELU_ERF; }
 
+// The LayerNorm epilogue also takes no activation (the LayerNorm alone).
+bool valid_layernorm_act(rk_gelu_kind g) { return valid_gelu(g) || g == RK_GELU_NONE; }
+
 int32_t layernorm_auto_splits(int64_t M, int64_t N, rk_dtype dtype,
                               double extra_us = kSplitExtraUs)
 {
@@ -676,7 +679,7 @@ RK_EXPORT rk_status rk_layernorm_gelu_ex(const void *x, const void *weight, cons
     rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
     if (st != RK_OK)
         return st;
-    if (!valid_gelu(gelu) || num_splits < 0 || num_splits > kMaxSplits)
+    if (!valid_layernorm_act(gelu) || num_splits < 0 || num_splits > kMaxSplits)
         return RK_ERR_INVALID_ARG;
     if (M == 0)
         return RK_OK;
@@ -1130,7 +1133,7 @@ RK_EXPORT rk_status rk__layernorm_gelu_variant(int32_t index, const void *x, con
     rk_status st = check_layernorm(x, weight, bias, y, M, N, ldx, ldy, eps, dtype);
     if (st != RK_OK)
         return st;
-    if (!valid_gelu(gelu))
+    if (!valid_layernorm_act(gelu))
         return RK_ERR_INVALID_ARG;
     int count = 0;
     const TileVariant *v = variants(RK_OP_LAYERNORM_GELU, dtype, &count);

@@ -241,14 +241,17 @@ __device__ __forceinline__ float gelu_erf(float z)
     return 0.5f * z * erfcf(-z * kRsqrt2);
 }
 
-// GeLU by kind: 0 the tanh approximation, 1 the exact erf form.
+// GeLU by kind: 0 the tanh approximation, 1 the exact erf form, 2 none (the
+// LayerNorm epilogue then returns z itself).
 template <int GK>
 __device__ __forceinline__ float gelu(float z)
 {
     if constexpr (GK == 0)
         return gelu_tanh(z);
-    else
+    else if constexpr (GK == 1)
         return gelu_erf(z);
+    else
+        return z;
 }
 
 // ----------------------------------------------------- LayerNorm moments

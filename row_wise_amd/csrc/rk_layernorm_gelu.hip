@@ -5,7 +5,7 @@
 // Per row: mu = sum x / N; var = sum (x - mu)^2 / N, both over the N true
 // columns (padding never enters); rstd = 1 / sqrt(var + eps);
 // z = (x - mu) rstd w + b; y = GeLU(z), the tanh approximation (GK = 0) or the
-// exact erf form (GK = 1).
+// exact erf form (GK = 1); or y = z (GK = 2: the LayerNorm of §4.1 alone).
 //
 // layernorm_gelu_tile  the row stays in VGPRs (one HBM read and write per
 //                      element): sum -> wave DPP / LDS -> centre in registers
@@ -421,9 +421,11 @@ template <typename T, int G, int V, int W>
 static hipError_t layernorm_gelu_rows_run(const RowProblem &p)
 {
     constexpr int kDevices = 64;
-    static std::atomic<int> resident[2][kDevices];
-    const int gk = p.gelu == RK_GELU_ERF ? 1 : 0;
-    auto kernel = gk ? layernorm_gelu_rows<T, G, V, W, 1> : layernorm_gelu_rows<T, G, V, W, 0>;
+    static std::atomic<int> resident[3][kDevices];
+    const int gk = p.gelu == RK_GELU_ERF ? 1 : (p.gelu == RK_GELU_NONE ? 2 : 0);
+    auto kernel = gk == 1   ? layernorm_gelu_rows<T, G, V, W, 1>
+                  : gk == 2 ? layernorm_gelu_rows<T, G, V, W, 2>
+                            : layernorm_gelu_rows<T, G, V, W, 0>;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -458,8 +460,9 @@ static hipError_t layernorm_gelu_tile_run(const RowProblem &p)
     constexpr int RG = W / G;
     const int64_t blocks = (p.M + RG * R - 1) / (RG * R);
     const float inv_n = static_cast<float>(1.0 / p.N);
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 1, PH, SH>
-                                        : layernorm_gelu_tile<T, G, V, W, R, EXACT, 0, PH, SH>;
+    auto kernel = p.gelu == RK_GELU_ERF    ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 1, PH, SH>
+                  : p.gelu == RK_GELU_NONE ? layernorm_gelu_tile<T, G, V, W, R, EXACT, 2, PH, SH>
+                                           : layernorm_gelu_tile<T, G, V, W, R, EXACT, 0, PH, SH>;
     return launch(kernel, dim3(static_cast<unsigned>(blocks)), dim3(W * kWave), p.stream,
                   static_cast<const T *>(p.x), static_cast<const T *>(p.w),
                   static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,

@@ -323,8 +323,9 @@ hipError_t stream_launch(const RowProblem &p)
 {
     // one-wave rows go four to a workgroup
     constexpr int RB = W == 1 ? 4 : 1;
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_stream<T, E, W, U, 1, RB, PH>
-                                        : layernorm_stream<T, E, W, U, 0, RB, PH>;
+    auto kernel = p.gelu == RK_GELU_ERF    ? layernorm_stream<T, E, W, U, 1, RB, PH>
+                  : p.gelu == RK_GELU_NONE ? layernorm_stream<T, E, W, U, 2, RB, PH>
+                                           : layernorm_stream<T, E, W, U, 0, RB, PH>;
     return launch(kernel, dim3(static_cast<unsigned>((p.M + RB - 1) / RB)), dim3(W * kWave * RB),
                   p.stream, static_cast<const T *>(p.x), static_cast<const T *>(p.w),
                   static_cast<const T *>(p.b), static_cast<T *>(p.y), p.M, p.N, p.ldx, p.ldy,
@@ -364,8 +365,9 @@ hipError_t split_run(const RowProblem &p, int S, int C, SplitPartials pt)
                             p.N, p.ldx, S, C, pt.base, pt.row_bytes);
     if (err != hipSuccess)
         return err;
-    auto kernel = p.gelu == RK_GELU_ERF ? layernorm_finish<T, E, kSplitW, U, 1, PH>
-                                        : layernorm_finish<T, E, kSplitW, U, 0, PH>;
+    auto kernel = p.gelu == RK_GELU_ERF    ? layernorm_finish<T, E, kSplitW, U, 1, PH>
+                  : p.gelu == RK_GELU_NONE ? layernorm_finish<T, E, kSplitW, U, 2, PH>
+                                           : layernorm_finish<T, E, kSplitW, U, 0, PH>;
     const T *w = static_cast<const T *>(p.w);
     const T *b = static_cast<const T *>(p.b);
     T *y = static_cast<T *>(p.y);

@@ -160,7 +160,7 @@ def lnx(lib, x=A, w=A + 0x80000, b=A + 0x90000, y=B, M=4, N=4096, ldx=4096, ldy=
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(gelu=2), INVALID), (dict(gelu=-1), INVALID), (dict(S=-1), INVALID),
+    (dict(gelu=3), INVALID), (dict(gelu=-1), INVALID), (dict(S=-1), INVALID),
     (dict(S=65537), INVALID), (dict(eps=0.0), INVALID), (dict(b=None), INVALID),
     (dict(ws=None), WORKSPACE), (dict(wb=4 * 9 * 8 - 1), WORKSPACE),
     (dict(ws=0x3000004), INVALID),  # misaligned workspace
@@ -250,7 +250,7 @@ def test_row_reduce_ex_workspace_and_splits(lib):
 
 def test_gelu_rejects(lib):
     g = lib.rk_gelu
-    assert g(A, B, 4, 8, 8, 8, F32, 2, None) == INVALID
+    assert g(A, B, 4, 8, 8, 8, F32, 2, None) == INVALID  # RK_GELU_NONE: LayerNorm only
     assert g(A, B, 4, 8, 8, 8, F32, -1, None) == INVALID
     assert g(A, A + 16, 4, 8, 8, 8, F32, 0, None) == INVALID
     assert g(None, B, 4, 8, 8, 8, F32, 0, None) == INVALID
@@ -415,7 +415,7 @@ def test_variant_entry_points_reject(lib):
     assert lib.rk__layernorm_gelu_variant(0, A, A + 0x80000, A + 0x90000, B, 4, 8, 8, 8, 0.0,
                                           F32, 0, None) == INVALID
     assert lib.rk__layernorm_gelu_variant(0, A, A + 0x80000, A + 0x90000, B, 4, 8, 8, 8, 1e-5,
-                                          F32, 2, None) == INVALID
+                                          F32, 3, None) == INVALID
     n = lib.rk__variant_count(rk.RK_OP_RMSNORM, F32)
     assert n == lib.rk__variant_count(rk.RK_OP_RESIDUAL_RMSNORM, F32) > 0
     assert lib.rk__rmsnorm_variant(n, A, A + 0x80000, B, 4, 8, 8, 8, 1e-5, F32, None) == INVALID

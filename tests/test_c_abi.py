@@ -43,8 +43,9 @@ int main(void)
     CHECK(rk_online_softmax_workspace_bytes(64, 262144, 64, RK_F32) == (size_t)64 * 64 * 8);
     CHECK(rk_online_softmax_auto_splits(16384, 4096, RK_F32) == 1);
     CHECK(rk_layernorm_gelu(x, 0, 0, y, 4, 8, 8, 8, 1e-5f, RK_BF16, 0) == RK_ERR_INVALID_ARG);
-    CHECK(rk_layernorm_gelu_ex(x, x, x, y, 4, 8, 8, 8, 1e-5f, RK_F32, (rk_gelu_kind)2, 1, 0, 0,
+    CHECK(rk_layernorm_gelu_ex(x, x, x, y, 4, 8, 8, 8, 1e-5f, RK_F32, (rk_gelu_kind)3, 1, 0, 0,
                                0) == RK_ERR_INVALID_ARG);
+    CHECK(rk_gelu(x, y, 4, 8, 8, 8, RK_F32, RK_GELU_NONE, 0) == RK_ERR_INVALID_ARG);
     CHECK(rk_layernorm_gelu_workspace_bytes(64, 262144, 64, RK_F32) == (size_t)64 * 65 * 8);
     CHECK(rk_rmsnorm(x, x, y, 4, 8, 8, 8, 0.0f, RK_F32, 0) == RK_ERR_INVALID_ARG);
     CHECK(rk_row_sum(x, y, -1, 8, 8, RK_F32, 0) == RK_ERR_INVALID_ARG);

@@ -1,7 +1,8 @@
-"""Parity of rk_layernorm_gelu_ex with the CPU oracle: the exact-erf GeLU on
-every register tile, and rows held in memory (the streaming kernel and the
-split-row pair with a Chan merge of per-chunk (mean, M2)) with either GeLU
-("Triton Kernel 实现练习" §4.1 "LayerNorm", §3.4 "Approx Activation", §6.3).
+"""Parity of rk_layernorm_gelu_ex with the CPU oracle: the exact-erf GeLU and
+no activation (the LayerNorm alone) on every register tile, and rows held in
+memory (the streaming kernel and the split-row pair with a Chan merge of
+per-chunk (mean, M2)) with each epilogue ("Triton Kernel 实现练习" §4.1
+"LayerNorm", §3.4 "Approx Activation", §6.3).
 
 The reference is the oracle's LayerNorm + GeLU with whole-row statistics:
 the split statistics compute the same function.  Error measure as for
@@ -17,7 +18,7 @@ import torch
 import oracle
 import row_wise_amd as rk
 import rowgen
-from tolerance import TOL, rel_err_floor1
+from tolerance import TOL, rel_err_above, rel_err_floor1
 
 pytestmark = pytest.mark.gpu
 EPS = float(np.float32(1e-5))
@@ -67,9 +68,10 @@ def _variant_cases():
     return cases
 
 
+@pytest.mark.parametrize("gelu", ["erf", "none"])
 @pytest.mark.parametrize("dtype,index,N", _variant_cases(),
                          ids=lambda v: str(v).replace("torch.", ""))
-def test_erf_tile_variant(dtype, index, N):
+def test_erf_and_plain_tile_variant(dtype, index, N, gelu):
     M = 37
     E = 4 if dtype == torch.float32 else 8
     ld = (N + E - 1) // E * E
@@ -78,8 +80,8 @@ def test_erf_tile_variant(dtype, index, N):
     w, b = rowgen.ln_params(N, g, dtype)
     y = rk.rk__layernorm_gelu_variant(index, base.to(DEV)[:, :N], w.to(DEV), b.to(DEV), EPS,
                                       out=torch.empty(M, ld, dtype=dtype, device=DEV)[:, :N],
-                                      gelu="erf")
-    assert rel_err_floor1(y, ref_of(base[:, :N], w, b, "erf")) <= tol_of(dtype)
+                                      gelu=gelu)
+    assert rel_err_floor1(y, ref_of(base[:, :N], w, b, gelu)) <= tol_of(dtype)
 
 
 @pytest.mark.parametrize("name", ["ln_gelu_f32_4096x768", "bf16_16384x4096"])
@@ -93,6 +95,23 @@ def test_erf_workloads(name):
     t = rk.rk_layernorm_gelu_ex(d["x"].to(DEV), d["w"].to(DEV), d["b"].to(DEV), EPS)
     if d["x"].dtype == torch.float32:
         assert (y - t).abs().max().item() > 1e-4
+
+
+@pytest.mark.parametrize("name", ["ln_gelu_f32_4096x768", "bf16_16384x4096"])
+def test_plain_layernorm_workloads(name):
+    """No activation: the LayerNorm alone, also as a pure relative error
+    wherever |r| >= 0.01."""
+    d = rowgen.make(name)
+    y = rk.rk_layernorm_gelu_ex(d["x"].to(DEV), d["w"].to(DEV), d["b"].to(DEV), EPS,
+                                gelu="none")
+    ref = ref_of(d["x"], d["w"], d["b"], "none")
+    err = rel_err_floor1(y, ref)
+    rel = rel_err_above(y, ref, 0.01)
+    say(f"plain LayerNorm {name} err={err:.3e} pure relative (|r| >= 0.01) {rel:.3e}")
+    assert err <= tol_of(d["x"].dtype) and rel <= tol_of(d["x"].dtype)
+    # negative z is where GeLU and identity differ most: the kinds are not mixed up
+    t = rk.rk_layernorm_gelu_ex(d["x"].to(DEV), d["w"].to(DEV), d["b"].to(DEV), EPS)
+    assert (y - t).abs().max().item() > 0.1
 
 
 # --------------------------------------------------- rows held in memory
@@ -112,6 +131,8 @@ def test_long_rows_workload():
     assert rel_err_floor1(y, ref) <= TOL["f32"]
     y = rk.rk_layernorm_gelu_ex(xd, wd, bd, EPS, gelu="erf", num_splits=0)
     assert rel_err_floor1(y, ref_of(x, w, b, "erf")) <= TOL["f32"]
+    y = rk.rk_layernorm_gelu_ex(xd, wd, bd, EPS, gelu="none", num_splits=0)
+    assert rel_err_floor1(y, ref_of(x, w, b, "none")) <= TOL["f32"]
 
 
 SPLIT_N = [1, 5, 1000, 4099, 16384, 16385, 40000, 100003]
@@ -119,7 +140,7 @@ SPLIT_N = [1, 5, 1000, 4099, 16384, 16385, 40000, 100003]
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=key)
 @pytest.mark.parametrize("N", SPLIT_N)
-@pytest.mark.parametrize("gelu", ["tanh", "erf"])
+@pytest.mark.parametrize("gelu", ["tanh", "erf", "none"])
 def test_split_and_stream(dtype, N, gelu):
     w, b = params(N, N, dtype)
     wd, bd = w.to(DEV), b.to(DEV)

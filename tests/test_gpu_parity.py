@@ -351,10 +351,10 @@ def test_layernorm_gelu_variant_phased(dtype, index, N):
     g = torch.Generator().manual_seed(N * 19 + index)
     x = (torch.randn(M, N, generator=g) + 5.0).to(dtype)
     w, b = rowgen.ln_params(N, g, dtype)
-    for gelu in ("tanh", "erf"):
+    for gelu in ("tanh", "erf", "none"):
         y = rk.rk__layernorm_gelu_variant(index, x.to(DEV), w.to(DEV), b.to(DEV), EPS, gelu=gelu)
         ref = (oracle.layernorm_gelu(x, w, b, EPS) if gelu == "tanh"
-               else oracle.layernorm_gelu_ex(x, w, b, EPS, "erf"))
+               else oracle.layernorm_gelu_ex(x, w, b, EPS, gelu))
         assert rel_err_floor1(y, ref) <= tol_of(dtype), gelu
 
 
